@@ -1,0 +1,255 @@
+/*
+ * kvattn.h — C ABI of libkvattn.so: softmax attention of a few query tokens,
+ * or of a prefill chunk, over a long paged KV cache whose keys are stored as
+ * Q8_0 and values as Q4_0 in 128-token pages, with log-sum-exp (LSE) merging
+ * of partial results and KVMem-style top-k block selection.
+ *
+ * Sources (the method is described, not specified, by these pages):
+ *  [KVMEM]  lcz.me topic 1972, KVMem reproduction report on one RX 7900 XTX:
+ *           section "長上下文實測結果（主矩陣）/ 測試口徑" (the server flags
+ *           --kvmem-budget 32768, --kvmem-gen-reserve 16384,
+ *           --kvmem-block-tokens 128, --kv-dtype q8_0), section
+ *           "Recall 測試" (256 of 485 blocks kept at budget 32768) and section
+ *           "Full-KV 對照" (attention runs only over the ~48K-token working set).
+ *  [STREAM] alphalab.site, "Adaptive KV Streaming 是什麼？AMD 16GB 長 Context
+ *           六步驗收", step ④ (flags -ctk q8_0 -ctv q4_0, -ub 512; the stream
+ *           path needs flash attention with Q8_0 K / Q4_0 V).
+ *  [RDNA4]  wqu.guru, "Qwen 27B (IQ4_XS, Q8/Q4 KV) at full 262k context on a
+ *           16GB RX 9070 XT: 80+ t/s decode with Adaptive KV Streaming",
+ *           bullets "Online Log-Sum-Exp prefill & pipelined prefetch" and
+ *           "Stream-optimized speculative decoding" (paged decode attention
+ *           extended to verify batches).
+ *  [VULKAN] lcz.me topic 1398, "單張 RX 7900 XTX 24GB 把 Qwen3.8-27B 推到
+ *           124 t/s —— Vulkan 路線實測報告": section "模型結構" (16
+ *           full-attention layers x 4 KV heads x 256 = 16384 elements per token
+ *           for K and for V), section "坑 2" (q4_0 K+V = 18 KiB per token),
+ *           section "坑 3" (only the legacy block types are KV types) and the
+ *           closing remark that q8_0 K carries 8.5 bits per element.
+ * None of the pages defines the bit layout, scale rule or rounding of Q8_0 and
+ * Q4_0, the block-scoring function, or a page layout; the definitions below
+ * are this library's, and the CPU oracle implements the same definitions
+ * independently.
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument except `geom`, `workspace_bytes` and the status
+ *    out-parameters is a DEVICE pointer on the current HIP device. The caller
+ *    owns every buffer; the library never allocates, frees or synchronises.
+ *    Work is only enqueued on `stream` (a hipStream_t; NULL = null stream).
+ *  - Float arrays must be 16-byte aligned; pools 256-byte aligned.
+ *  - All validation happens on the host before anything is enqueued; on any
+ *    error nothing is enqueued and no output is touched.
+ *  - Status codes: KVATTN_OK; KVATTN_E_INVALID (bad pointer, size, range or
+ *    alignment); KVATTN_E_UNSUPPORTED (head_dim != 256, page_tokens != 128,
+ *    too many query rows, or a device that is not gfx950); KVATTN_E_WORKSPACE
+ *    (workspace smaller than required); KVATTN_E_DEVICE (a HIP runtime error
+ *    while querying the device or launching). No exceptions cross the ABI and
+ *    nothing is printed. There is no CPU fallback.
+ *  - Workspace protocol: when `workspace` is NULL the function stores the
+ *    required byte count in *workspace_bytes, returns KVATTN_OK and enqueues
+ *    nothing. Otherwise *workspace_bytes is the size of `workspace`.
+ *  - Calls that overlap on one stream are ordered by the stream; concurrent
+ *    calls on different streams must not share outputs or workspace.
+ *
+ * Pool byte layout (part of the ABI; page quantisation is bit-exact)
+ *  A layer's pool is two arrays of records, k_pool and v_pool, indexed by
+ *  (physical page P, KV head h): record (P * n_kv_heads + h). Token position
+ *  `pos` lives in logical page pos / 128, slot t = pos % 128; the page table
+ *  maps logical page -> physical page.
+ *  K record, KVATTN_K_RECORD_BYTES = 34816:
+ *   [0, 32768)      int8 Q8_0 code of (slot t, dim n) at byte t*256 + n.
+ *   [32768, 34816)  IEEE binary16 scale of (slot t, 32-dim block b = n/32) at
+ *                   byte 32768 + 2*(t*8 + b), little endian.
+ *  V record, KVATTN_V_RECORD_BYTES = 18432:
+ *   [0, 16384)      4096 little-endian 32-bit words of 4-bit Q4_0 codes. For
+ *                   c in [0,4), q in [0,4), g in [0,4), d in [0,16),
+ *                   e in [0,4), word w = (((c*4 + q)*4 + g)*16 + d)*4 + e
+ *                   holds the codes of dim n = 16*(4*q + e) + d for the eight
+ *                   slots t(c,g,j) = 32*c + 16*(j/4) + 4*g + (j%4), j = 0..7;
+ *                   slot j's code sits at bit 4*(j/2) + 16*(j%2).
+ *   [16384, 18432)  binary16 scale of (slot t(c,g,j), block b) at byte
+ *                   16384 + 2*(((c*8 + b)*4 + g)*8 + j).
+ *  The V word order places, for each group of 32 slots, the eight slots that
+ *  one lane of a 16x16x32 matrix-core tile consumes in one 32-bit word, so a
+ *  lane turns a word into four f16 pairs with one shift and one mask each.
+ *
+ * Quantisation (per token, per KV head, per 32-dim block x[0..31]; RN32 and
+ * RN16 are IEEE round-to-nearest-even to binary32 / binary16, rint rounds
+ * half to even):
+ *  Q8_0 (keys): amax = max|x_i|; d = RN16(RN32(amax / 127)). If d == 0 every
+ *   code is 0 and the stored scale is +0. Otherwise inv = RN32(1 / d) and
+ *   code_i = clamp(rint(RN32(x_i * inv)), -127, 127). Dequantised: d * code.
+ *   34 bytes per 32 elements = 8.5 bits per element ([VULKAN] closing remark).
+ *  Q4_0 (values): j* = lowest index with |x_j*| = amax; m = x_j* (signed);
+ *   d = RN16(RN32(-m / 8)). If amax == 0 or d == 0, the stored scale is +0
+ *   and every code is 8. Otherwise inv = RN32(1 / d) and
+ *   code_i = clamp(rint(RN32(x_i * inv)), -8, 7) + 8. Dequantised:
+ *   d * (code - 8). 18 bytes per 32 elements; K (Q8_0) + V (Q4_0) is 26 KiB
+ *   per token at 16 layers x 4 KV heads x 256 ([VULKAN] "模型結構", "坑 2").
+ *  Block summary (KVMem scoring input): for a full logical page p and head h,
+ *   summary[h][p][n] = RN32((sum over t = 0..127, ascending, in binary64, of
+ *   dequantised K[t][n]) / 128), i.e. the mean dequantised key of the block.
+ */
+#ifndef KVATTN_H
+#define KVATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kvattn_status;
+#define KVATTN_OK 0
+#define KVATTN_E_INVALID 1
+#define KVATTN_E_UNSUPPORTED 2
+#define KVATTN_E_WORKSPACE 3
+#define KVATTN_E_DEVICE 4
+
+#define KVATTN_HEAD_DIM 256
+#define KVATTN_PAGE_TOKENS 128
+#define KVATTN_K_RECORD_BYTES 34816
+#define KVATTN_V_RECORD_BYTES 18432
+#define KVATTN_MAX_QUERY_ROWS 32 /* n_q_tok * gqa per KV head in decode */
+
+/* Geometry of one layer's pool. head_dim must be 256 and page_tokens 128
+ * (the pages' shape: [VULKAN] "模型結構"; [KVMEM] --kvmem-block-tokens 128).
+ * Query head hq uses KV head hq / gqa (grouped-query attention). */
+typedef struct kvattn_geom {
+  int32_t n_kv_heads;   /* >= 1 */
+  int32_t gqa;          /* query heads per KV head, >= 1 */
+  int32_t head_dim;     /* 256 */
+  int32_t page_tokens;  /* 128 */
+  int32_t n_phys_pages; /* physical pages in k_pool / v_pool, >= 1 */
+} kvattn_geom;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *kvattn_status_string(kvattn_status s);
+
+/* Number of blocks kvattn_select_blocks writes per KV head:
+ * min(k_top, n_blocks - min(n_recent, n_blocks)) + min(n_recent, n_blocks);
+ * -1 if an argument is negative or n_blocks < 1. Host-only, no device use. */
+int32_t kvattn_select_count(int32_t n_blocks, int32_t n_recent, int32_t k_top);
+
+/* a1 — quantise tokens into pages, and summarise completed pages.
+ * Writes the Q8_0 keys and Q4_0 values of positions pos0 .. pos0+n_tok-1 into
+ * their slots (layout and rounding above); every other byte of the pools is
+ * left as it was ([STREAM] step ④: -ctk q8_0 -ctv q4_0; [KVMEM] 128-token
+ * blocks). When k_summary is not NULL, the summary of every logical page p
+ * that this call writes into and that is full afterwards
+ * ((p+1)*128 <= pos0+n_tok; positions are assumed written in order) is
+ * recomputed from the pool; other summaries are untouched.
+ *  k, v        fp32 [n_tok][n_kv_heads][256], read only.
+ *  page_table  int32 [n_logical_pages], values in [0, n_phys_pages).
+ *              Requires pos0 >= 0, n_tok >= 1 and
+ *              pos0 + n_tok <= n_logical_pages * 128.
+ *  k_pool      n_phys_pages * n_kv_heads * 34816 bytes.
+ *  v_pool      n_phys_pages * n_kv_heads * 18432 bytes.
+ *  k_summary   fp32 [n_kv_heads][n_logical_pages][256] or NULL.
+ * Logical pages that map to the same physical page race. A page-table entry
+ * outside [0, n_phys_pages) makes the kernel skip that page's writes. */
+kvattn_status kvattn_quantize_pages(const kvattn_geom *geom, const float *k,
+                                    const float *v, int64_t pos0, int32_t n_tok,
+                                    const int32_t *page_table,
+                                    int32_t n_logical_pages, uint8_t *k_pool,
+                                    uint8_t *v_pool, float *k_summary,
+                                    void *stream);
+
+/* a2 — KVMem block scoring and top-k selection ([KVMEM] 測試口徑 and
+ * "Recall 測試": keep budget/128 history blocks plus a reserved recent window
+ * on the GPU; attention then runs over that working set only). Per KV head h:
+ *  q_sel[n] = RN32(sum over g = 0..gqa-1, ascending, in binary64, of
+ *             q[h*gqa + g][n]);
+ *  score[b] = sum over n = 0..255, ascending, in binary64, of
+ *             q_sel[n] * summary[h][b][n], for candidates b in [0, NB - R),
+ *  with R = min(n_recent, n_blocks) and NB = n_blocks. Candidates are ranked
+ *  by (score descending, b ascending; -0 equals +0) and the first
+ *  min(k_top, NB - R) are kept. out_blocks[h][...] receives the kept blocks
+ *  together with the recent blocks NB-R .. NB-1, in ascending order;
+ *  kvattn_select_count() gives the count per head.
+ *  q           fp32 [n_kv_heads*gqa][256], one query token.
+ *  k_summary   fp32 [n_kv_heads][n_logical_pages][256]; candidate blocks must
+ *              be full pages whose summary has been written.
+ *  n_blocks    1 <= n_blocks <= n_logical_pages. n_recent, k_top >= 0.
+ *  out_blocks  int32 [n_kv_heads][kvattn_select_count(...)].
+ *  workspace   8 * n_kv_heads * (NB - R) bytes (fp64 scores); query with
+ *              workspace == NULL. */
+kvattn_status kvattn_select_blocks(const kvattn_geom *geom, const float *q,
+                                   const float *k_summary,
+                                   int32_t n_logical_pages, int32_t n_blocks,
+                                   int32_t n_recent, int32_t k_top,
+                                   int32_t *out_blocks, void *workspace,
+                                   size_t *workspace_bytes, void *stream);
+
+/* a3/a5 — decode and verify attention over the paged cache, split over pages
+ * with an LSE merge ([RDNA4] paged decode attention extended to verify
+ * batches; [STREAM] step ④). Query token t (0 <= t < n_q_tok) sits at
+ * position p_t = kv_len - n_q_tok + t and sees keys at positions <= p_t.
+ * For query head hq = h*gqa + g and its key set J:
+ *  s_j = scale * dot(q[t][hq], Khat_j), m = max s_j, l = sum exp(s_j - m),
+ *  out[t][hq] = sum exp(s_j - m) * Vhat_j / l, lse[t][hq] = m + ln l (natural
+ *  log); an empty key set gives out = 0 and lse = -inf.
+ *  Dense (blocks == NULL): J = positions 0 .. kv_len-1 through logical pages
+ *   0 .. ceil(kv_len/128)-1. Sparse: J = the tokens (< kv_len) of the logical
+ *   pages listed in blocks[h][0 .. n_blk-1] (the output of
+ *   kvattn_select_blocks); entries should be distinct — a repeated entry is
+ *   attended as often as it appears; an entry outside [0, n_logical_pages),
+ *   or mapping to a physical page outside [0, n_phys_pages), contributes
+ *   nothing.
+ *  q        fp32 [n_q_tok][n_kv_heads*gqa][256]; n_q_tok >= 1 and
+ *           n_q_tok*gqa <= 32 (else KVATTN_E_UNSUPPORTED).
+ *  kv_len   n_q_tok <= kv_len <= n_logical_pages*128.
+ *  out      fp32 [n_q_tok][n_kv_heads*gqa][256]; lse fp32 [n_q_tok][..].
+ *  n_splits work splits per KV head, 0 = chosen by the library.
+ *  workspace holds the split partials; query its size with workspace==NULL
+ *           (the size depends on every argument above, including n_splits).
+ * Arithmetic: f16 matrix-core products with fp32 accumulation; the result is
+ * within 2e-3 (max-abs) of exact attention over the dequantised pages. */
+kvattn_status kvattn_decode(const kvattn_geom *geom, const float *q,
+                            int32_t n_q_tok, const uint8_t *k_pool,
+                            const uint8_t *v_pool, const int32_t *page_table,
+                            int32_t n_logical_pages, const int32_t *blocks,
+                            int32_t n_blk, int64_t kv_len, float scale,
+                            float *out, float *lse, int32_t n_splits,
+                            void *workspace, size_t *workspace_bytes,
+                            void *stream);
+
+/* a6 — chunked prefill attention ([RDNA4] "Online Log-Sum-Exp prefill":
+ * chunked prefill across pages with online LSE accumulation; [STREAM] step ④
+ * -ub 512). Query token t (0 <= t < chunk) sits at position pos0 + t and sees
+ * keys at positions <= pos0 + t, read through logical pages
+ * 0 .. ceil((pos0+chunk)/128)-1; the chunk's own keys and values must already
+ * be in the pool (kvattn_quantize_pages). Output definition as kvattn_decode.
+ *  q        fp32 [chunk][n_kv_heads*gqa][256]; chunk >= 1; pos0 >= 0;
+ *           pos0 + chunk <= n_logical_pages*128.
+ *  out      fp32 [chunk][n_kv_heads*gqa][256]; lse fp32 [chunk][..].
+ *  n_groups page groups per (KV head, query tile) merged by LSE; 0 = chosen
+ *           by the library.
+ * Arithmetic: K/V tiles dequantised to f16 in LDS, f16 matrix-core products,
+ * fp32 accumulation; within 1e-2 (max-abs) of exact attention. */
+kvattn_status kvattn_prefill_chunk(const kvattn_geom *geom, const float *q,
+                                   int32_t chunk, const uint8_t *k_pool,
+                                   const uint8_t *v_pool,
+                                   const int32_t *page_table,
+                                   int32_t n_logical_pages, int64_t pos0,
+                                   float scale, float *out, float *lse,
+                                   int32_t n_groups, void *workspace,
+                                   size_t *workspace_bytes, void *stream);
+
+/* a4 — merge partial attention results by log-sum-exp ([RDNA4] "Online
+ * Log-Sum-Exp prefill"). For each row r:
+ *  M = max_s lse_parts[s][r]; L = M + ln sum_s exp(lse_parts[s][r] - M);
+ *  out[r] = sum_s exp(lse_parts[s][r] - L) * o_parts[s][r]; lse[r] = L.
+ *  A part with lse = -inf contributes nothing; if every part is -inf the row
+ *  is out = 0, lse = -inf. fp32 throughout, parts summed in ascending s.
+ *  o_parts fp32 [n_parts][rows][head_dim]; lse_parts fp32 [n_parts][rows];
+ *  out fp32 [rows][head_dim]; lse fp32 [rows]. n_parts >= 1, rows >= 1,
+ *  head_dim >= 1. out must not alias o_parts. */
+kvattn_status kvattn_merge_lse(int32_t n_parts, int64_t rows, int32_t head_dim,
+                               const float *o_parts, const float *lse_parts,
+                               float *out, float *lse, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVATTN_H */

@@ -1,0 +1,264 @@
+"""Oracle: Q8_0 / Q4_0 block quantisation, the page byte layout, and block
+summaries. Test infrastructure only (see the package docstring).
+
+The pages name the two cache types and their sizes but define neither the
+scale rule nor the rounding:
+  - keys Q8_0, values Q4_0: [STREAM] step ④ (-ctk q8_0 -ctv q4_0) and
+    [RDNA4] opening paragraph (Q8_0/Q4_0 KV cache);
+  - q8_0 K is 8.5 bits per element: [VULKAN] closing remark on K precision;
+  - q4_0 K+V is 18 KiB per token at 16 layers x 4 KV heads x 256:
+    [VULKAN] "坑 2" together with "模型結構".
+The definitions used (amax/127 for Q8_0; signed max-magnitude element mapped
+to -8 for Q4_0; every rounding IEEE round-to-nearest-even; codes computed with
+the stored binary16 scale) are this build's reading and are written out in
+include/kvattn.h next to the ABI they define.
+"""
+import numpy as np
+
+HEAD_DIM = 256
+PAGE_TOKENS = 128
+BLOCK = 32
+N_BLOCKS = HEAD_DIM // BLOCK
+K_CODES_BYTES = PAGE_TOKENS * HEAD_DIM          # 32768
+K_RECORD_BYTES = K_CODES_BYTES + PAGE_TOKENS * N_BLOCKS * 2   # 34816
+V_CODES_BYTES = PAGE_TOKENS * HEAD_DIM // 2     # 16384
+V_RECORD_BYTES = V_CODES_BYTES + PAGE_TOKENS * N_BLOCKS * 2   # 18432
+
+
+def rn16(x):
+    """Round binary32 values to the nearest binary16 (ties to even) and return
+    them as binary32. numpy's float32->float16 cast is IEEE round-to-nearest-
+    even, overflowing to infinity."""
+    with np.errstate(over="ignore"):
+        return np.asarray(x, np.float32).astype(np.float16).astype(np.float32)
+
+
+def f16_bits(x):
+    """binary16 bit patterns (uint16) of binary32 values rounded to nearest-even."""
+    with np.errstate(over="ignore"):
+        return np.asarray(x, np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_from_bits(bits):
+    """binary32 values of binary16 bit patterns."""
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float32)
+
+
+def q8_0_quantize(x):
+    """Q8_0 of 32-element blocks along the last axis (keys).
+
+    x: float32 [..., 32]. Returns (codes int8 [..., 32], scale_bits uint16 [...]).
+    amax = max|x|; d = RN16(RN32(amax / 127)); d == 0 -> codes 0, scale +0;
+    else inv = RN32(1/d), code = clamp(rint(RN32(x*inv)), -127, 127).
+    """
+    x = np.asarray(x, np.float32)
+    assert x.shape[-1] == BLOCK
+    amax = np.max(np.abs(x), axis=-1)
+    d32 = amax / np.float32(127.0)                 # binary32 division, RN
+    d16 = rn16(d32)
+    zero = d16 == 0
+    d_safe = np.where(zero, np.float32(1.0), d16)
+    inv = np.float32(1.0) / d_safe                 # RN32(1/d)
+    prod = x * inv[..., None]                      # RN32(x*inv)
+    codes = np.clip(np.rint(prod), -127, 127)
+    codes = np.where(zero[..., None], 0, codes).astype(np.int8)
+    bits = np.where(zero, np.uint16(0), f16_bits(d16)).astype(np.uint16)
+    return codes, bits
+
+
+def q8_0_dequantize(codes, scale_bits):
+    """Dequantised Q8_0 block values d*code, exact in binary64."""
+    d = f16_from_bits(scale_bits).astype(np.float64)
+    return np.asarray(codes, np.float64) * d[..., None]
+
+
+def q4_0_quantize(x):
+    """Q4_0 of 32-element blocks along the last axis (values).
+
+    x: float32 [..., 32]. Returns (codes uint8 in [0,15] [..., 32], scale_bits).
+    j* = lowest index with |x_j*| = amax, m = x_j*, d = RN16(RN32(-m/8)).
+    amax == 0 or d == 0 -> scale +0 and every code 8; else inv = RN32(1/d),
+    code = clamp(rint(RN32(x*inv)), -8, 7) + 8. The signed extreme maps to
+    code 0 (value -8*d), so all 16 codes are used ("offset 8").
+    """
+    x = np.asarray(x, np.float32)
+    assert x.shape[-1] == BLOCK
+    ax = np.abs(x)
+    jstar = np.argmax(ax, axis=-1)                 # argmax returns the lowest index
+    m = np.take_along_axis(x, jstar[..., None], axis=-1)[..., 0]
+    amax = np.take_along_axis(ax, jstar[..., None], axis=-1)[..., 0]
+    d32 = (-m) / np.float32(8.0)
+    d16 = rn16(d32)
+    zero = (amax == 0) | (d16 == 0)
+    d_safe = np.where(zero, np.float32(1.0), d16)
+    inv = np.float32(1.0) / d_safe
+    prod = x * inv[..., None]
+    codes = np.clip(np.rint(prod), -8, 7) + 8
+    codes = np.where(zero[..., None], 8, codes).astype(np.uint8)
+    bits = np.where(zero, np.uint16(0), f16_bits(d16)).astype(np.uint16)
+    return codes, bits
+
+
+def q4_0_dequantize(codes, scale_bits):
+    """Dequantised Q4_0 block values d*(code-8), exact in binary64."""
+    d = f16_from_bits(scale_bits).astype(np.float64)
+    return (np.asarray(codes, np.float64) - 8.0) * d[..., None]
+
+
+# ---- page record layout (include/kvattn.h, "Pool byte layout") -------------
+
+def _v_word_index_tables():
+    """For each of the 4096 V-code words: the dim it holds and, for each of
+    its 8 nibble slots j, the token slot and bit position (layout as written
+    in include/kvattn.h)."""
+    w = np.arange(4096)
+    e = w % 4
+    d = (w // 4) % 16
+    g = (w // 64) % 4
+    q = (w // 256) % 4
+    c = w // 1024
+    dim = 16 * (4 * q + e) + d
+    j = np.arange(8)
+    tok = 32 * c[:, None] + 16 * (j[None, :] // 4) + 4 * g[:, None] + (j[None, :] % 4)
+    bit = 4 * (j // 2) + 16 * (j % 2)
+    return dim, tok, bit
+
+
+def _v_scale_index_tables():
+    """For each of the 1024 V scales: (token slot, block) it belongs to."""
+    i = np.arange(1024)
+    j = i % 8
+    g = (i // 8) % 4
+    b = (i // 32) % 8
+    c = i // 256
+    tok = 32 * c + 16 * (j // 4) + 4 * g + (j % 4)
+    return tok, b
+
+
+_V_DIM, _V_TOK, _V_BIT = _v_word_index_tables()
+_VS_TOK, _VS_BLK = _v_scale_index_tables()
+
+
+def pack_k_record(codes, scale_bits):
+    """K record bytes from Q8_0 codes int8 [..., 128, 256] and scales uint16
+    [..., 128, 8]; returns uint8 [..., 34816]."""
+    codes = np.asarray(codes, np.int8)
+    lead = codes.shape[:-2]
+    rec = np.zeros(lead + (K_RECORD_BYTES,), np.uint8)
+    rec[..., :K_CODES_BYTES] = codes.reshape(lead + (-1,)).view(np.uint8)
+    sb = np.ascontiguousarray(np.asarray(scale_bits, np.uint16).astype('<u2'))
+    rec[..., K_CODES_BYTES:] = sb.reshape(lead + (-1,)).view(np.uint8)
+    return rec
+
+
+def unpack_k_record(rec):
+    """(codes int8 [..., 128, 256], scale_bits uint16 [..., 128, 8]) of K records."""
+    rec = np.ascontiguousarray(np.asarray(rec, np.uint8))
+    lead = rec.shape[:-1]
+    codes = rec[..., :K_CODES_BYTES].view(np.int8).reshape(lead + (PAGE_TOKENS, HEAD_DIM))
+    bits = np.ascontiguousarray(rec[..., K_CODES_BYTES:]).view('<u2')
+    return codes.copy(), bits.reshape(lead + (PAGE_TOKENS, N_BLOCKS)).astype(np.uint16)
+
+
+def pack_v_record(codes, scale_bits):
+    """V record bytes from Q4_0 codes uint8 [..., 128, 256] (0..15) and scales
+    uint16 [..., 128, 8]; returns uint8 [..., 18432]."""
+    codes = np.asarray(codes, np.uint32)
+    lead = codes.shape[:-2]
+    nib = codes[..., _V_TOK, _V_DIM[:, None]]                   # [..., 4096, 8]
+    words = np.zeros(lead + (4096,), np.uint32)
+    for j in range(8):
+        words |= nib[..., j] << np.uint32(_V_BIT[j])
+    rec = np.zeros(lead + (V_RECORD_BYTES,), np.uint8)
+    rec[..., :V_CODES_BYTES] = np.ascontiguousarray(words.astype('<u4')).view(np.uint8)
+    sc = np.asarray(scale_bits, np.uint16)[..., _VS_TOK, _VS_BLK]
+    rec[..., V_CODES_BYTES:] = np.ascontiguousarray(sc.astype('<u2')).view(np.uint8)
+    return rec
+
+
+def unpack_v_record(rec):
+    """(codes uint8 [..., 128, 256], scale_bits uint16 [..., 128, 8]) of V records."""
+    rec = np.ascontiguousarray(np.asarray(rec, np.uint8))
+    lead = rec.shape[:-1]
+    words = np.ascontiguousarray(rec[..., :V_CODES_BYTES]).view('<u4').astype(np.uint32)
+    codes = np.zeros(lead + (PAGE_TOKENS, HEAD_DIM), np.uint8)
+    for j in range(8):
+        codes[..., _V_TOK[:, j], _V_DIM] = (words >> np.uint32(_V_BIT[j])) & 0xF
+    bits = np.zeros(lead + (PAGE_TOKENS, N_BLOCKS), np.uint16)
+    bits[..., _VS_TOK, _VS_BLK] = np.ascontiguousarray(rec[..., V_CODES_BYTES:]).view('<u2')
+    return codes, bits
+
+
+def quantize_into_pool(k, v, pos0, page_table, k_pool, v_pool):
+    """Write positions pos0 .. pos0+n_tok-1 into the pools (kvattn_quantize_pages
+    semantics without summaries). k, v: float32 [n_tok, n_kv, 256].
+    k_pool: uint8 [n_phys, n_kv, 34816]; v_pool: uint8 [n_phys, n_kv, 18432],
+    both modified in place. Slots outside the written range keep their bytes.
+    A page-table entry outside [0, n_phys) skips that page.
+
+    [KVMEM] 測試口徑 (--kvmem-block-tokens 128: history held in 128-token
+    blocks); [RDNA4] "paged decode attention". The page layout is this
+    build's, written out in include/kvattn.h.
+    """
+    k = np.asarray(k, np.float32)
+    v = np.asarray(v, np.float32)
+    n_tok, n_kv, D = k.shape
+    assert D == HEAD_DIM and v.shape == k.shape
+    n_phys = k_pool.shape[0]
+    kc, ks = q8_0_quantize(k.reshape(n_tok, n_kv, N_BLOCKS, BLOCK))
+    vc, vs = q4_0_quantize(v.reshape(n_tok, n_kv, N_BLOCKS, BLOCK))
+    kc = kc.reshape(n_tok, n_kv, HEAD_DIM)
+    vc = vc.reshape(n_tok, n_kv, HEAD_DIM)
+    pos = pos0 + np.arange(n_tok)
+    lps = pos // PAGE_TOKENS
+    pages = np.unique(lps)
+    phys = np.asarray(page_table, np.int64)[pages]
+    keep = (phys >= 0) & (phys < n_phys)
+    pages, phys = pages[keep], phys[keep]
+    if pages.size == 0:
+        return
+    # page index within `pages` of every token; tokens of skipped pages drop out
+    where = np.searchsorted(pages, lps)
+    ok = (where < pages.size) & (pages[np.minimum(where, pages.size - 1)] == lps)
+    tsel = np.nonzero(ok)[0]
+    pidx, slot = where[tsel], pos[tsel] % PAGE_TOKENS
+    kcodes, kbits = unpack_k_record(k_pool[phys])                # [P, n_kv, 128, ...]
+    vcodes, vbits = unpack_v_record(v_pool[phys])
+    for h in range(n_kv):
+        kcodes[pidx, h, slot] = kc[tsel, h]
+        kbits[pidx, h, slot] = ks[tsel, h]
+        vcodes[pidx, h, slot] = vc[tsel, h]
+        vbits[pidx, h, slot] = vs[tsel, h]
+    k_pool[phys] = pack_k_record(kcodes, kbits)
+    v_pool[phys] = pack_v_record(vcodes, vbits)
+
+
+def page_summaries(k_records):
+    """Block summaries of full pages: RN32(binary64 sum over the 128 slots, in
+    ascending slot order, of the dequantised keys, divided by 128).
+    k_records uint8 [..., 34816] -> float32 [..., 256].
+
+    The pages give no scoring function for KVMem ([KVMEM] "Recall 測試" only
+    says retrieval picks the blocks relevant to the last user turn's query);
+    the summary is the mean key of the block, the reading the workload
+    description gives ("per-block summary = mean key").
+    """
+    codes, bits = unpack_k_record(k_records)
+    lead = codes.shape[:-2]
+    khat = q8_0_dequantize(codes.reshape(lead + (PAGE_TOKENS, N_BLOCKS, BLOCK)), bits)
+    khat = khat.reshape(lead + (PAGE_TOKENS, HEAD_DIM))
+    acc = np.zeros(lead + (HEAD_DIM,), np.float64)
+    for t in range(PAGE_TOKENS):                     # ascending t, binary64
+        acc = acc + khat[..., t, :]
+    return (acc / 128.0).astype(np.float32)
+
+
+def page_summary(k_record):
+    """Summary of one full page (page_summaries of a single record)."""
+    return page_summaries(np.asarray(k_record)[None])[0]
+
+
+def summaries_from_pool(k_pool, page_table, n_pages, n_kv):
+    """float32 [n_kv, n_pages, 256]: summaries of logical pages 0..n_pages-1."""
+    phys = np.asarray(page_table, np.int64)[:n_pages]
+    return np.ascontiguousarray(np.swapaxes(page_summaries(k_pool[phys][:, :n_kv]), 0, 1))

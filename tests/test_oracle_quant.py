@@ -1,0 +1,249 @@
+"""Pins for the oracle's quantisation, page layout and block summaries.
+
+Each test checks the oracle against something other than itself: sizes the
+pages print (tests/golden/page_figures.json), IEEE-754 facts, closed forms,
+round-trip bounds, idempotence, and a hand-built layout word.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import quant
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
+
+
+def test_record_sizes_match_page_figures():
+    """Block sizes reproduce the pages' per-token byte counts.
+    [VULKAN] 模型結構: 16 layers x 4 KV heads x 256 = 16384 elements per token;
+    f16 K+V at 64K tokens = 4 GiB. [VULKAN] 坑 2: q4_0 K+V = 18 KiB/token.
+    [VULKAN] closing remark: q8_0 K = 8.5 bits per element."""
+    elems = GOLD["elements_per_token_per_kv"]["value"]
+    assert 16 * 4 * quant.HEAD_DIM == elems
+    assert elems * 2 * 2 * 65536 == GOLD["f16_bytes_per_64k_tokens"]["value"]
+    q8_block = quant.K_RECORD_BYTES // (quant.PAGE_TOKENS * quant.N_BLOCKS)
+    q4_block = quant.V_RECORD_BYTES // (quant.PAGE_TOKENS * quant.N_BLOCKS)
+    assert q8_block == 34 and q4_block == 18
+    assert q8_block * 8 / 32 == GOLD["q8_0_bits_per_element"]["value"]
+    assert elems * 2 * q4_block // 32 == GOLD["q4_0_kv_bytes_per_token"]["value"]
+    # this build's Q8_0 K + Q4_0 V: 26 KiB per token over the 16 x 4 x 256 shape
+    assert elems * (q8_block + q4_block) // 32 == 26 * 1024
+    assert quant.PAGE_TOKENS == GOLD["kvmem_block_tokens"]["value"]
+
+
+@pytest.mark.parametrize("x,expect", [
+    (1.0 + 2.0 ** -11, 1.0),                 # exact tie -> even (1.0)
+    (1.0 + 3 * 2.0 ** -11, 1.0 + 2.0 ** -9),  # exact tie -> even
+    (1.0 + 2.0 ** -11 + 2.0 ** -20, 1.0 + 2.0 ** -10),  # above the tie
+    (2049.0, 2048.0),
+    (2051.0, 2052.0),
+    (65504.0, 65504.0),
+    (65519.0, 65504.0),
+    (65520.0, np.inf),                        # tie at the overflow threshold
+    (2.0 ** -24, 2.0 ** -24),                 # smallest subnormal
+    (2.0 ** -25, 0.0),                        # tie between 0 and 2^-24 -> even (0)
+    (3 * 2.0 ** -26, 2.0 ** -24),
+])
+def test_rn16_ieee_facts(x, expect):
+    assert float(quant.rn16(np.float32(x))) == expect
+
+
+def test_q8_0_closed_forms():
+    # zero block: codes 0, scale +0 (bits 0x0000)
+    c, b = quant.q8_0_quantize(np.zeros(32, np.float32))
+    assert (c == 0).all() and b == 0
+    # x_i = k_i * d with d = 2^-7 and max |k| = 127: exact round trip
+    g = np.random.default_rng(1)
+    k = g.integers(-127, 128, 32)
+    k[5] = -127
+    x = (k * 2.0 ** -7).astype(np.float32)
+    c, b = quant.q8_0_quantize(x)
+    assert (c == k).all() and quant.f16_from_bits(b) == 2.0 ** -7
+    # one-hot: the hot element gets code +-127, the rest 0
+    x = np.zeros(32, np.float32)
+    x[9] = -3.0
+    c, b = quant.q8_0_quantize(x)
+    assert c[9] == -127 and (np.delete(c, 9) == 0).all()
+    assert quant.f16_from_bits(b) == quant.rn16(np.float32(3.0) / np.float32(127.0))
+    # constant block: every code 127
+    c, _ = quant.q8_0_quantize(np.full(32, 0.37, np.float32))
+    assert (c == 127).all()
+
+
+def test_q4_0_closed_forms():
+    # zero block: every code 8 and scale +0
+    c, b = quant.q4_0_quantize(np.zeros(32, np.float32))
+    assert (c == 8).all() and b == 0
+    # constant block c: the signed extreme maps to code 0, d = -c/8, xhat = c exactly
+    for val in (0.5, -4.0):
+        c, b = quant.q4_0_quantize(np.full(32, val, np.float32))
+        assert (c == 0).all()
+        assert quant.f16_from_bits(b) == -val / 8
+        assert (quant.q4_0_dequantize(c, b) == val).all()
+    # exact grid: x = k*d, k in [-8, 7], unique extreme k=-8 at index 3
+    g = np.random.default_rng(2)
+    k = g.integers(-7, 8, 32)
+    k[3] = -8
+    x = (k * 2.0 ** -5).astype(np.float32)
+    c, b = quant.q4_0_quantize(x)
+    assert (c.astype(int) - 8 == k).all() and quant.f16_from_bits(b) == 2.0 ** -5
+    # magnitude tie: the LOWEST index sets the sign of the scale
+    x = np.zeros(32, np.float32)
+    x[3], x[7] = 1.0, -1.0
+    c, b = quant.q4_0_quantize(x)
+    assert quant.f16_from_bits(b) == -0.125 and c[3] == 0 and c[7] == 15
+    x[3], x[7] = -1.0, 1.0
+    c, b = quant.q4_0_quantize(x)
+    assert quant.f16_from_bits(b) == 0.125 and c[3] == 0 and c[7] == 15
+    # scale underflow in binary16: stored as +0, codes 8
+    x = np.zeros(32, np.float32)
+    x[0] = 1e-9
+    c, b = quant.q4_0_quantize(x)
+    assert b == 0 and (c == 8).all()
+
+
+def _random_blocks(n, seed, outlier=False):
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((n, 32)).astype(np.float32)
+    x[: n // 4] *= np.float32(8.0)
+    x[n // 4: n // 2] *= np.float32(1e-3)
+    if outlier:
+        x[:, 7] *= np.float32(50.0)
+    return x
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_roundtrip_bounds(seed):
+    """|x - xhat| <= d/2 (plus binary32 product rounding) for Q8_0;
+    <= |d|/2 for unclamped Q4_0 codes. On the clamped +7 side |x| <= |m| and
+    binary16 rounding gives |d| >= |m|/8 * (1 - 2^-11), so
+    |x - xhat| <= |d| * (8 / (1 - 2^-11) - 7)."""
+    x = _random_blocks(4096, seed, outlier=bool(seed))
+    c, b = quant.q8_0_quantize(x)
+    d = quant.f16_from_bits(b).astype(np.float64)
+    err = np.abs(x - quant.q8_0_dequantize(c, b))
+    assert (err <= d[:, None] * (0.5 + 2.0 ** -14)).all()
+    c, b = quant.q4_0_quantize(x)
+    d = np.abs(quant.f16_from_bits(b).astype(np.float64))
+    err = np.abs(x - quant.q4_0_dequantize(c, b))
+    clamped = c == 15
+    assert (err[~clamped] <= np.broadcast_to(d[:, None], x.shape)[~clamped] * (0.5 + 2.0 ** -14)).all()
+    assert (err <= d[:, None] * (8.0 / (1.0 - 2.0 ** -11) - 7.0 + 2.0 ** -14)).all()
+    # every Q4_0 block uses code 0 for its signed extreme
+    assert (c.min(axis=1) == 0).all()
+
+
+@pytest.mark.parametrize("seed", [3, 4])
+def test_idempotence(seed):
+    x = _random_blocks(4096, seed)
+    c, b = quant.q8_0_quantize(x)
+    c2, b2 = quant.q8_0_quantize(quant.q8_0_dequantize(c, b).astype(np.float32))
+    assert (c == c2).all() and (b == b2).all()
+    c, b = quant.q4_0_quantize(x)
+    c2, b2 = quant.q4_0_quantize(quant.q4_0_dequantize(c, b).astype(np.float32))
+    assert (c == c2).all() and (b == b2).all()
+
+
+def test_pack_unpack_roundtrip():
+    g = np.random.default_rng(5)
+    kc = g.integers(-127, 128, (3, 128, 256)).astype(np.int8)
+    kb = g.integers(0, 65536, (3, 128, 8)).astype(np.uint16)
+    vc = g.integers(0, 16, (3, 128, 256)).astype(np.uint8)
+    vb = g.integers(0, 65536, (3, 128, 8)).astype(np.uint16)
+    rk = quant.pack_k_record(kc, kb)
+    rv = quant.pack_v_record(vc, vb)
+    assert rk.shape == (3, quant.K_RECORD_BYTES) and rv.shape == (3, quant.V_RECORD_BYTES)
+    kc2, kb2 = quant.unpack_k_record(rk)
+    vc2, vb2 = quant.unpack_v_record(rv)
+    assert (kc2 == kc).all() and (kb2 == kb).all() and (vc2 == vc).all() and (vb2 == vb).all()
+
+
+def test_layout_words_by_hand():
+    """Hand-built bytes for the layout written in include/kvattn.h.
+    K: code (t, n) at t*256 + n; scale (t, b) at 32768 + 2*(t*8 + b).
+    V word w = (((c*4+q)*4+g)*16+d)*4+e holds dim 16*(4q+e)+d for slots
+    32c + 16*(j//4) + 4g + j%4, slot j at bit 4*(j//2) + 16*(j%2)."""
+    kc = np.zeros((128, 256), np.int8)
+    kb = np.zeros((128, 8), np.uint16)
+    kc[5, 200] = -3
+    kb[5, 6] = 0x3C00
+    rk = quant.pack_k_record(kc, kb)
+    assert rk[5 * 256 + 200] == 0xFD
+    assert rk[32768 + 2 * (5 * 8 + 6)] == 0x00 and rk[32768 + 2 * (5 * 8 + 6) + 1] == 0x3C
+    assert rk.sum() == 0xFD + 0x3C
+    # V: word with c=1, q=2, g=3, d=5, e=1 -> dim 16*(8+1)+5 = 149;
+    # slots j=0..7 -> tokens 32+12+{0,1,2,3} and 32+16+12+{0,1,2,3}
+    vc = np.full((128, 256), 0, np.uint8)
+    toks = [44, 45, 46, 47, 60, 61, 62, 63]
+    for j, t in enumerate(toks):
+        vc[t, 149] = j + 1                      # codes 1..8
+    vb = np.zeros((128, 8), np.uint16)
+    vb[61, 4] = 0xABCD                          # slot j=5 of (c=1, g=3), block 4
+    rv = quant.pack_v_record(vc, vb)
+    w = (((1 * 4 + 2) * 4 + 3) * 16 + 5) * 4 + 1
+    word = int.from_bytes(rv[4 * w: 4 * w + 4].tobytes(), "little")
+    expect = 0
+    for j in range(8):
+        expect |= (j + 1) << (4 * (j // 2) + 16 * (j % 2))
+    assert word == expect == 0x86427531
+    others = np.frombuffer(rv[:16384].tobytes(), "<u4").copy()
+    others[w] = 0
+    assert (others == 0).all()
+    si = ((1 * 8 + 4) * 4 + 3) * 8 + 5
+    assert rv[16384 + 2 * si] == 0xCD and rv[16384 + 2 * si + 1] == 0xAB
+    assert rv[16384:].astype(int).sum() == 0xCD + 0xAB
+
+
+def test_quantize_into_pool_partial_and_skip():
+    """Writes land in the right slots through the page table, untouched bytes
+    survive, and an out-of-range page-table entry is skipped."""
+    g = np.random.default_rng(6)
+    n_kv, n_phys = 2, 5
+    kp = g.integers(0, 256, (n_phys, n_kv, quant.K_RECORD_BYTES)).astype(np.uint8)
+    vp = g.integers(0, 256, (n_phys, n_kv, quant.V_RECORD_BYTES)).astype(np.uint8)
+    kp0, vp0 = kp.copy(), vp.copy()
+    table = np.array([3, 0, 4, 99], np.int32)   # logical page 3 maps outside the pool
+    pos0, n = 100, 300                          # positions 100..399: pages 0,1,2,3
+    K = g.standard_normal((n, n_kv, 256)).astype(np.float32)
+    V = g.standard_normal((n, n_kv, 256)).astype(np.float32)
+    quant.quantize_into_pool(K, V, pos0, table, kp, vp)
+    assert (kp[[1, 2]] == kp0[[1, 2]]).all() and (vp[[1, 2]] == vp0[[1, 2]]).all()
+    for h in range(n_kv):
+        for pos in (100, 127, 128, 255, 256, 383):
+            lp, t = pos // 128, pos % 128
+            c, b = quant.unpack_k_record(kp[table[lp], h])
+            cq, bq = quant.q8_0_quantize(K[pos - pos0, h].reshape(8, 32))
+            assert (c[t] == cq.reshape(-1)).all() and (b[t] == bq).all()
+            c, b = quant.unpack_v_record(vp[table[lp], h])
+            cq, bq = quant.q4_0_quantize(V[pos - pos0, h].reshape(8, 32))
+            assert (c[t] == cq.reshape(-1)).all() and (b[t] == bq).all()
+        # slot 99 of logical page 0 (physical 3) was not written
+        c, b = quant.unpack_k_record(kp[3, h])
+        c0, b0 = quant.unpack_k_record(kp0[3, h])
+        assert (c[:100] == c0[:100]).all() and (b[:100] == b0[:100]).all()
+        c, b = quant.unpack_v_record(vp[3, h])
+        c0, b0 = quant.unpack_v_record(vp0[3, h])
+        assert (c[:100] == c0[:100]).all() and (b[:100] == b0[:100]).all()
+
+
+def test_page_summary_closed_forms():
+    # every key in a page equal to a constant grid vector -> summary equals it exactly
+    vec = (np.arange(256) % 17 - 8).astype(np.float32) * np.float32(0.25)
+    codes, bits = quant.q8_0_quantize(np.tile(vec, (128, 1)).reshape(128, 8, 32))
+    rec = quant.pack_k_record(codes.reshape(128, 256), bits)
+    khat = quant.q8_0_dequantize(codes, bits).reshape(128, 256)
+    assert (quant.page_summary(rec) == khat[0].astype(np.float32)).all()
+    # alternating +a / -a keys sum to zero exactly
+    codes = np.zeros((128, 256), np.int8)
+    codes[0::2] = 100
+    codes[1::2] = -100
+    bits = np.full((128, 8), 0x3C00, np.uint16)
+    assert (quant.page_summary(quant.pack_k_record(codes, bits)) == 0).all()
+    # one token with code 128*... : summary = d * c / 128 exactly
+    codes = np.zeros((128, 256), np.int8)
+    codes[17, 3] = 64
+    s = quant.page_summary(quant.pack_k_record(codes, bits))
+    assert s[3] == 0.5 and (np.delete(s, 3) == 0).all()
