@@ -1,1 +1,288 @@
-"""Paged Q8_0/Q4_0 attention for MI355X (gfx950): Python binding of libkvattn.so."""
+"""Paged Q8_0/Q4_0 attention for MI355X (gfx950): thin Python binding of
+libkvattn.so (include/kvattn.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels. Tensors are torch tensors on the current GPU; outputs and workspaces
+that are not passed in are allocated with torch (device memory plumbing) and
+work is enqueued on torch's current stream. If the library is not built, or
+the device is not gfx950, calls raise: there is no CPU fallback.
+"""
+import ctypes
+import os
+
+__all__ = [
+    "Geom", "KvattnError", "library_path", "load_library",
+    "kvattn_quantize_pages", "kvattn_select_blocks", "kvattn_decode",
+    "kvattn_prefill_chunk", "kvattn_merge_lse", "kvattn_select_count",
+    "K_RECORD_BYTES", "V_RECORD_BYTES", "HEAD_DIM", "PAGE_TOKENS",
+]
+
+HEAD_DIM = 256
+PAGE_TOKENS = 128
+K_RECORD_BYTES = 34816
+V_RECORD_BYTES = 18432
+STATUS = {0: "OK", 1: "E_INVALID", 2: "E_UNSUPPORTED", 3: "E_WORKSPACE", 4: "E_DEVICE"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class KvattnError(RuntimeError):
+    def __init__(self, func, code):
+        self.code = code
+        super().__init__(f"{func} failed: {STATUS.get(code, code)}")
+
+
+class Geom(ctypes.Structure):
+    _fields_ = [("n_kv_heads", ctypes.c_int32), ("gqa", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_tokens", ctypes.c_int32),
+                ("n_phys_pages", ctypes.c_int32)]
+
+    def __init__(self, n_kv_heads, gqa, n_phys_pages, head_dim=HEAD_DIM, page_tokens=PAGE_TOKENS):
+        super().__init__(n_kv_heads, gqa, head_dim, page_tokens, n_phys_pages)
+
+
+def library_path():
+    return os.path.join(_HERE, "libkvattn.so")
+
+
+def load_library():
+    """Load libkvattn.so (built by build.py) and declare its signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run long_context_attention_paged_amd/build.py")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, F32, SZP = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                             ctypes.POINTER(ctypes.c_size_t))
+    G = ctypes.POINTER(Geom)
+    sigs = {
+        "kvattn_status_string": ([I32], ctypes.c_char_p),
+        "kvattn_select_count": ([I32, I32, I32], I32),
+        "kvattn_quantize_pages": ([G, P, P, I64, I32, P, I32, P, P, P, P], I32),
+        "kvattn_select_blocks": ([G, P, P, I32, I32, I32, I32, P, P, SZP, P], I32),
+        "kvattn_decode": ([G, P, I32, P, P, P, I32, P, I32, I64, F32, P, P, I32, P, SZP, P], I32),
+        "kvattn_prefill_chunk": ([G, P, I32, P, P, P, I32, I64, F32, P, P, I32, P, SZP, P], I32),
+        "kvattn_merge_lse": ([I32, I64, I32, P, P, P, P, P], I32),
+    }
+    for name, (args, res) in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _LIB = lib
+    return lib
+
+
+# ---- marshalling helpers ---------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
+def _size(t, name, need):
+    if t.numel() < need:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {need}")
+
+
+def _pools(geom, k_pool, v_pool):
+    _size(k_pool, "k_pool", geom.n_phys_pages * geom.n_kv_heads * K_RECORD_BYTES)
+    _size(v_pool, "v_pool", geom.n_phys_pages * geom.n_kv_heads * V_RECORD_BYTES)
+
+
+def _check(func, code):
+    if code != 0:
+        raise KvattnError(func, code)
+
+
+def _workspace(query, workspace, device):
+    """Size the workspace with a NULL query, allocate it if not given."""
+    torch = _torch()
+    size = ctypes.c_size_t(0)
+    _check("workspace query", query(None, ctypes.byref(size)))
+    if workspace is None:
+        workspace = torch.empty(max(int(size.value), 256), dtype=torch.uint8, device=device)
+    _need(workspace, "workspace", torch.uint8)
+    return workspace, ctypes.c_size_t(workspace.numel())
+
+
+def kvattn_select_count(n_blocks, n_recent, k_top):
+    return int(load_library().kvattn_select_count(n_blocks, n_recent, k_top))
+
+
+def kvattn_quantize_pages(geom, k, v, pos0, page_table, k_pool, v_pool, k_summary=None,
+                          stream=None):
+    """Quantise positions pos0 .. pos0+k.shape[0]-1 into the pools (a1)."""
+    torch = _torch()
+    lib = load_library()
+    for name, t, dt in (("k", k, torch.float32), ("v", v, torch.float32),
+                        ("page_table", page_table, torch.int32),
+                        ("k_pool", k_pool, torch.uint8), ("v_pool", v_pool, torch.uint8)):
+        _need(t, name, dt)
+    n_tok = k.shape[0]
+    _size(k, "k", n_tok * geom.n_kv_heads * HEAD_DIM)
+    _size(v, "v", n_tok * geom.n_kv_heads * HEAD_DIM)
+    _pools(geom, k_pool, v_pool)
+    if k_summary is not None:
+        _need(k_summary, "k_summary", torch.float32)
+        _size(k_summary, "k_summary", geom.n_kv_heads * page_table.numel() * HEAD_DIM)
+    code = lib.kvattn_quantize_pages(ctypes.byref(geom), _ptr(k), _ptr(v), int(pos0), k.shape[0],
+                                     _ptr(page_table), page_table.numel(), _ptr(k_pool),
+                                     _ptr(v_pool), _ptr(k_summary), _stream(stream))
+    _check("kvattn_quantize_pages", code)
+
+
+def kvattn_select_blocks(geom, q, k_summary, n_logical_pages, n_blocks, n_recent, k_top,
+                         out_blocks=None, workspace=None, stream=None):
+    """KVMem block selection (a2); returns int32 [n_kv, count] ascending blocks."""
+    torch = _torch()
+    lib = load_library()
+    _need(q, "q", torch.float32)
+    _need(k_summary, "k_summary", torch.float32)
+    n_out = kvattn_select_count(n_blocks, n_recent, k_top)
+    if n_out < 0:
+        raise ValueError("invalid selection sizes")
+    _size(q, "q", geom.n_kv_heads * geom.gqa * HEAD_DIM)
+    _size(k_summary, "k_summary", geom.n_kv_heads * n_logical_pages * HEAD_DIM)
+    if out_blocks is None:
+        out_blocks = torch.empty((geom.n_kv_heads, max(n_out, 1)), dtype=torch.int32,
+                                 device=q.device)
+    _need(out_blocks, "out_blocks", torch.int32)
+    if out_blocks.dim() != 2 or out_blocks.shape[0] != geom.n_kv_heads or \
+            out_blocks.shape[1] < n_out:
+        raise ValueError("out_blocks must be [n_kv_heads, >= count]")
+    if out_blocks.shape[1] != max(n_out, 1):
+        raise ValueError("out_blocks rows must hold exactly kvattn_select_count() entries")
+    if n_out == 0:
+        return out_blocks[:, :0]
+
+    def call(ws, nbytes):
+        return lib.kvattn_select_blocks(ctypes.byref(geom), _ptr(q), _ptr(k_summary),
+                                        n_logical_pages, n_blocks, n_recent, k_top,
+                                        _ptr(out_blocks), ws, nbytes, _stream(stream))
+
+    workspace, nbytes = _workspace(call, workspace, q.device)
+    _check("kvattn_select_blocks", call(_ptr(workspace), ctypes.byref(nbytes)))
+    return out_blocks[:, :n_out]
+
+
+def kvattn_decode(geom, q, k_pool, v_pool, page_table, kv_len, scale, blocks=None, out=None,
+                  lse=None, n_splits=0, workspace=None, stream=None):
+    """Decode / verify attention (a3, a5); q [n_q_tok, n_heads, 256] -> (out, lse)."""
+    torch = _torch()
+    lib = load_library()
+    _need(q, "q", torch.float32)
+    for name, t, dt in (("k_pool", k_pool, torch.uint8), ("v_pool", v_pool, torch.uint8),
+                        ("page_table", page_table, torch.int32)):
+        _need(t, name, dt)
+    n_q_tok = q.shape[0]
+    n_heads = geom.n_kv_heads * geom.gqa
+    if q.dim() != 3 or q.shape[1] != n_heads or q.shape[2] != HEAD_DIM:
+        raise ValueError(f"q must be [n_q_tok, {n_heads}, {HEAD_DIM}]")
+    _pools(geom, k_pool, v_pool)
+    n_blk = 0
+    if blocks is not None:
+        _need(blocks, "blocks", torch.int32)
+        if blocks.dim() != 2 or blocks.shape[0] != geom.n_kv_heads:
+            raise ValueError("blocks must be [n_kv_heads, n_blk]")
+        n_blk = blocks.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32)
+    _need(lse, "lse", torch.float32)
+    _size(out, "out", q.numel())
+    _size(lse, "lse", n_q_tok * n_heads)
+
+    def call(ws, nbytes):
+        return lib.kvattn_decode(ctypes.byref(geom), _ptr(q), n_q_tok, _ptr(k_pool), _ptr(v_pool),
+                                 _ptr(page_table), page_table.numel(), _ptr(blocks), n_blk,
+                                 int(kv_len), float(scale), _ptr(out), _ptr(lse), int(n_splits),
+                                 ws, nbytes, _stream(stream))
+
+    workspace, nbytes = _workspace(call, workspace, q.device)
+    _check("kvattn_decode", call(_ptr(workspace), ctypes.byref(nbytes)))
+    return out, lse
+
+
+def kvattn_prefill_chunk(geom, q, k_pool, v_pool, page_table, pos0, scale, out=None, lse=None,
+                         n_groups=0, workspace=None, stream=None):
+    """Chunked prefill attention (a6); q [chunk, n_heads, 256] -> (out, lse)."""
+    torch = _torch()
+    lib = load_library()
+    _need(q, "q", torch.float32)
+    for name, t, dt in (("k_pool", k_pool, torch.uint8), ("v_pool", v_pool, torch.uint8),
+                        ("page_table", page_table, torch.int32)):
+        _need(t, name, dt)
+    n_heads = geom.n_kv_heads * geom.gqa
+    if q.dim() != 3 or q.shape[1] != n_heads or q.shape[2] != HEAD_DIM:
+        raise ValueError(f"q must be [chunk, {n_heads}, {HEAD_DIM}]")
+    _pools(geom, k_pool, v_pool)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32)
+    _need(lse, "lse", torch.float32)
+    _size(out, "out", q.numel())
+    _size(lse, "lse", q.shape[0] * n_heads)
+
+    def call(ws, nbytes):
+        return lib.kvattn_prefill_chunk(ctypes.byref(geom), _ptr(q), q.shape[0], _ptr(k_pool),
+                                        _ptr(v_pool), _ptr(page_table), page_table.numel(),
+                                        int(pos0), float(scale), _ptr(out), _ptr(lse),
+                                        int(n_groups), ws, nbytes, _stream(stream))
+
+    workspace, nbytes = _workspace(call, workspace, q.device)
+    _check("kvattn_prefill_chunk", call(_ptr(workspace), ctypes.byref(nbytes)))
+    return out, lse
+
+
+def kvattn_merge_lse(o_parts, lse_parts, out=None, lse=None, stream=None):
+    """LSE merge (a4): o_parts [S, rows, D], lse_parts [S, rows] -> (out, lse)."""
+    torch = _torch()
+    lib = load_library()
+    _need(o_parts, "o_parts", torch.float32)
+    _need(lse_parts, "lse_parts", torch.float32)
+    S, rows, D = o_parts.shape
+    if out is None:
+        out = torch.empty((rows, D), dtype=torch.float32, device=o_parts.device)
+    if lse is None:
+        lse = torch.empty((rows,), dtype=torch.float32, device=o_parts.device)
+    _need(out, "out", torch.float32)
+    _need(lse, "lse", torch.float32)
+    _size(out, "out", rows * D)
+    _size(lse, "lse", rows)
+    _size(lse_parts, "lse_parts", S * rows)
+    code = lib.kvattn_merge_lse(S, rows, D, _ptr(o_parts), _ptr(lse_parts), _ptr(out), _ptr(lse),
+                                _stream(stream))
+    _check("kvattn_merge_lse", code)
+    return out, lse

@@ -1,0 +1,302 @@
+// C ABI of libkvattn: argument validation, device checks, workspace sizing
+// and kernel launches. The operations and the pool layout are specified in
+// include/kvattn.h; every check here runs on the host before anything is
+// enqueued, and no path falls back to the CPU.
+#include <atomic>
+#include <cstring>
+
+#include "../../include/kvattn.h"
+#include "launch.hpp"
+
+using namespace kvattn;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr float kLog2e = 1.4426950408889634f;  // softmax runs in base 2 on the device
+
+struct DeviceInfo {
+  std::atomic<int> state{0};  // 0 unknown, 1 gfx950, 2 other arch
+  int n_cu = 0;
+};
+DeviceInfo g_devices[kMaxDevices];
+
+// Checks (once per device) that the current device is gfx950: a code object
+// for another architecture is never silently used (the KVMem report,
+// section on the HIP general-protection fault, shows a missing gfx target
+// crashing without an error).
+kvattn_status current_device(int* n_cu) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return KVATTN_E_DEVICE;
+  }
+  DeviceInfo& info = g_devices[dev];
+  int s = info.state.load(std::memory_order_acquire);
+  if (s == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return KVATTN_E_DEVICE;
+    }
+    info.n_cu = prop.multiProcessorCount;
+    s = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    info.state.store(s, std::memory_order_release);
+  }
+  if (s != 1) return KVATTN_E_UNSUPPORTED;
+  if (n_cu) *n_cu = info.n_cu > 0 ? info.n_cu : 256;
+  return KVATTN_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+kvattn_status check_geom(const kvattn_geom* g) {
+  if (!g) return KVATTN_E_INVALID;
+  if (g->n_kv_heads < 1 || g->gqa < 1 || g->n_phys_pages < 1) return KVATTN_E_INVALID;
+  if (g->head_dim != KVATTN_HEAD_DIM || g->page_tokens != KVATTN_PAGE_TOKENS)
+    return KVATTN_E_UNSUPPORTED;
+  if ((int64_t)g->n_kv_heads * g->gqa > (1 << 20)) return KVATTN_E_INVALID;
+  return KVATTN_OK;
+}
+
+kvattn_status check_pools(const kvattn_geom* g, const uint8_t* k_pool, const uint8_t* v_pool) {
+  if (!k_pool || !v_pool || !aligned(k_pool, 256) || !aligned(v_pool, 256))
+    return KVATTN_E_INVALID;
+  return KVATTN_OK;
+}
+
+size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+kvattn_status launched(hipError_t e) {
+  if (e != hipSuccess) return KVATTN_E_DEVICE;
+  if (hipGetLastError() != hipSuccess) return KVATTN_E_DEVICE;
+  return KVATTN_OK;
+}
+
+// Workspace protocol shared by every entry point that needs one.
+kvattn_status workspace_check(void* workspace, size_t* workspace_bytes, size_t need,
+                              bool* query_only) {
+  *query_only = false;
+  if (!workspace_bytes) return KVATTN_E_INVALID;
+  if (!workspace) {
+    *workspace_bytes = need;
+    *query_only = true;
+    return KVATTN_OK;
+  }
+  if (*workspace_bytes < need) return KVATTN_E_WORKSPACE;
+  if (!aligned(workspace, 256)) return KVATTN_E_INVALID;
+  return KVATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvattn_status_string(kvattn_status s) {
+  switch (s) {
+    case KVATTN_OK: return "ok";
+    case KVATTN_E_INVALID: return "invalid argument";
+    case KVATTN_E_UNSUPPORTED: return "unsupported shape or device";
+    case KVATTN_E_WORKSPACE: return "workspace too small";
+    case KVATTN_E_DEVICE: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int32_t kvattn_select_count(int32_t n_blocks, int32_t n_recent, int32_t k_top) {
+  if (n_blocks < 1 || n_recent < 0 || k_top < 0) return -1;
+  const int32_t r = n_recent < n_blocks ? n_recent : n_blocks;
+  const int32_t cand = n_blocks - r;
+  return (k_top < cand ? k_top : cand) + r;
+}
+
+kvattn_status kvattn_quantize_pages(const kvattn_geom* geom, const float* k, const float* v,
+                                    int64_t pos0, int32_t n_tok, const int32_t* page_table,
+                                    int32_t n_logical_pages, uint8_t* k_pool, uint8_t* v_pool,
+                                    float* k_summary, void* stream) {
+  kvattn_status st = check_geom(geom);
+  if (st) return st;
+  if ((st = check_pools(geom, k_pool, v_pool))) return st;
+  if (!k || !v || !page_table || !aligned(k, 16) || !aligned(v, 16)) return KVATTN_E_INVALID;
+  if (k_summary && !aligned(k_summary, 16)) return KVATTN_E_INVALID;
+  if (pos0 < 0 || n_tok < 1 || n_logical_pages < 1) return KVATTN_E_INVALID;
+  if (pos0 + n_tok > (int64_t)n_logical_pages * KVATTN_PAGE_TOKENS) return KVATTN_E_INVALID;
+  if ((st = current_device(nullptr))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = launched(launch_quantize(k, v, pos0, n_tok, geom->n_kv_heads, page_table,
+                                geom->n_phys_pages, k_pool, v_pool, s));
+  if (st || !k_summary) return st;
+  const int64_t first = pos0 / KVATTN_PAGE_TOKENS;
+  const int64_t last_full = (pos0 + n_tok) / KVATTN_PAGE_TOKENS - 1;
+  if (last_full < first) return KVATTN_OK;
+  return launched(launch_summarize(k_pool, page_table, geom->n_kv_heads, geom->n_phys_pages,
+                                   n_logical_pages, (int32_t)first,
+                                   (int32_t)(last_full - first + 1), k_summary, s));
+}
+
+kvattn_status kvattn_select_blocks(const kvattn_geom* geom, const float* q,
+                                   const float* k_summary, int32_t n_logical_pages,
+                                   int32_t n_blocks, int32_t n_recent, int32_t k_top,
+                                   int32_t* out_blocks, void* workspace,
+                                   size_t* workspace_bytes, void* stream) {
+  kvattn_status st = check_geom(geom);
+  if (st) return st;
+  if (n_blocks < 1 || n_blocks > n_logical_pages || n_recent < 0 || k_top < 0)
+    return KVATTN_E_INVALID;
+  if (!q || !k_summary || !out_blocks || !aligned(q, 16) || !aligned(k_summary, 16))
+    return KVATTN_E_INVALID;
+  const int32_t r = n_recent < n_blocks ? n_recent : n_blocks;
+  const int32_t n_cand = n_blocks - r;
+  const int32_t k_sel = k_top < n_cand ? k_top : n_cand;
+  const int32_t n_out = k_sel + r;
+  const size_t need = round_up(sizeof(double) * (size_t)geom->n_kv_heads * (size_t)n_cand);
+  bool query_only = false;
+  if ((st = workspace_check(workspace, workspace_bytes, need, &query_only))) return st;
+  if (query_only) return KVATTN_OK;
+  if ((st = current_device(nullptr))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  double* scores = static_cast<double*>(workspace);
+  if (k_sel > 0 && k_sel < n_cand) {
+    if ((st = launched(launch_score(q, k_summary, geom->n_kv_heads, geom->gqa, n_logical_pages,
+                                    n_cand, scores, s))))
+      return st;
+  }
+  return launched(launch_topk(k_sel > 0 && k_sel < n_cand ? scores : nullptr, geom->n_kv_heads,
+                              n_cand, k_sel, r, n_out, out_blocks, s));
+}
+
+kvattn_status kvattn_decode(const kvattn_geom* geom, const float* q, int32_t n_q_tok,
+                            const uint8_t* k_pool, const uint8_t* v_pool,
+                            const int32_t* page_table, int32_t n_logical_pages,
+                            const int32_t* blocks, int32_t n_blk, int64_t kv_len, float scale,
+                            float* out, float* lse, int32_t n_splits, void* workspace,
+                            size_t* workspace_bytes, void* stream) {
+  kvattn_status st = check_geom(geom);
+  if (st) return st;
+  if ((st = check_pools(geom, k_pool, v_pool))) return st;
+  if (!q || !page_table || !out || !lse || !aligned(q, 16) || !aligned(out, 16))
+    return KVATTN_E_INVALID;
+  if (n_q_tok < 1 || n_logical_pages < 1 || n_splits < 0) return KVATTN_E_INVALID;
+  if ((int64_t)n_q_tok * geom->gqa > KVATTN_MAX_QUERY_ROWS) return KVATTN_E_UNSUPPORTED;
+  if (kv_len < n_q_tok || kv_len > (int64_t)n_logical_pages * KVATTN_PAGE_TOKENS)
+    return KVATTN_E_INVALID;
+  if (blocks && n_blk < 1) return KVATTN_E_INVALID;
+  if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+    return KVATTN_E_INVALID;
+  const int32_t n_units =
+      blocks ? n_blk : (int32_t)((kv_len + KVATTN_PAGE_TOKENS - 1) / KVATTN_PAGE_TOKENS);
+  int n_cu = 256;
+  int32_t splits = n_splits;
+  if (splits == 0) {
+    // With a workspace query on a machine without a device, size for the
+    // default CU count; the launch below recomputes with the real count, so
+    // query and launch must run on the same device.
+    if (workspace && (st = current_device(&n_cu))) return st;
+    if (!workspace && current_device(&n_cu) != KVATTN_OK) n_cu = 256;
+    splits = (n_cu + geom->n_kv_heads - 1) / geom->n_kv_heads;
+  }
+  if (splits > n_units) splits = n_units;
+  if (splits < 1) splits = 1;
+  const int64_t rows = (int64_t)n_q_tok * geom->n_kv_heads * geom->gqa;
+  const size_t o_bytes = round_up(sizeof(float) * (size_t)splits * rows * KVATTN_HEAD_DIM);
+  const size_t need = o_bytes + round_up(sizeof(float) * (size_t)splits * rows);
+  bool query_only = false;
+  if ((st = workspace_check(workspace, workspace_bytes, need, &query_only))) return st;
+  if (query_only) return KVATTN_OK;
+  if ((st = current_device(nullptr))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  DecodeParams p;
+  p.q = q;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.page_table = page_table;
+  p.blocks = blocks;
+  p.o_part = static_cast<float*>(workspace);
+  p.lse_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + o_bytes);
+  p.kv_len = kv_len;
+  p.n_units = n_units;
+  p.n_splits = splits;
+  p.n_kv = geom->n_kv_heads;
+  p.gqa = geom->gqa;
+  p.n_q_tok = n_q_tok;
+  p.n_logical = n_logical_pages;
+  p.n_phys = geom->n_phys_pages;
+  p.n_blk = blocks ? n_blk : 0;
+  p.qscale = scale * kLog2e;
+  if ((st = launched(launch_decode(p, s)))) return st;
+  return launched(launch_merge(splits, rows, KVATTN_HEAD_DIM, p.o_part, p.lse_part, out, lse, s));
+}
+
+kvattn_status kvattn_prefill_chunk(const kvattn_geom* geom, const float* q, int32_t chunk,
+                                   const uint8_t* k_pool, const uint8_t* v_pool,
+                                   const int32_t* page_table, int32_t n_logical_pages,
+                                   int64_t pos0, float scale, float* out, float* lse,
+                                   int32_t n_groups, void* workspace, size_t* workspace_bytes,
+                                   void* stream) {
+  kvattn_status st = check_geom(geom);
+  if (st) return st;
+  if ((st = check_pools(geom, k_pool, v_pool))) return st;
+  if (!q || !page_table || !out || !lse || !aligned(q, 16) || !aligned(out, 16))
+    return KVATTN_E_INVALID;
+  if (chunk < 1 || pos0 < 0 || n_logical_pages < 1 || n_groups < 0) return KVATTN_E_INVALID;
+  if (pos0 + chunk > (int64_t)n_logical_pages * KVATTN_PAGE_TOKENS) return KVATTN_E_INVALID;
+  if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+    return KVATTN_E_INVALID;
+  const int64_t kv_len = pos0 + chunk;
+  const int32_t n_pages = (int32_t)((kv_len + KVATTN_PAGE_TOKENS - 1) / KVATTN_PAGE_TOKENS);
+  const int64_t rows = (int64_t)chunk * geom->n_kv_heads * geom->gqa;
+  int32_t groups = n_groups;
+  if (groups == 0) {
+    int n_cu = 256;
+    if (workspace && (st = current_device(&n_cu))) return st;
+    if (!workspace && current_device(&n_cu) != KVATTN_OK) n_cu = 256;
+    const int64_t rows_per_head = (int64_t)chunk * geom->gqa;
+    const int64_t tiles = geom->n_kv_heads * ((rows_per_head + prefill_rows_per_tile() - 1) /
+                                              prefill_rows_per_tile());
+    int64_t gr = (3 * (int64_t)n_cu + tiles - 1) / tiles;  // about three rounds of the grid
+    if (gr < 1) gr = 1;
+    groups = (int32_t)gr;
+  }
+  if (groups > n_pages) groups = n_pages;
+  if (groups < 1) groups = 1;
+  const size_t o_bytes = round_up(sizeof(float) * (size_t)groups * rows * KVATTN_HEAD_DIM);
+  const size_t need = o_bytes + round_up(sizeof(float) * (size_t)groups * rows);
+  bool query_only = false;
+  if ((st = workspace_check(workspace, workspace_bytes, need, &query_only))) return st;
+  if (query_only) return KVATTN_OK;
+  if ((st = current_device(nullptr))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  PrefillParams p;
+  p.q = q;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.page_table = page_table;
+  p.o_part = static_cast<float*>(workspace);
+  p.lse_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + o_bytes);
+  p.pos0 = pos0;
+  p.chunk = chunk;
+  p.n_groups = groups;
+  p.n_kv = geom->n_kv_heads;
+  p.gqa = geom->gqa;
+  p.n_logical = n_logical_pages;
+  p.n_phys = geom->n_phys_pages;
+  p.qscale = scale * kLog2e;
+  if ((st = launched(launch_prefill(p, s)))) return st;
+  return launched(launch_merge(groups, rows, KVATTN_HEAD_DIM, p.o_part, p.lse_part, out, lse, s));
+}
+
+kvattn_status kvattn_merge_lse(int32_t n_parts, int64_t rows, int32_t head_dim,
+                               const float* o_parts, const float* lse_parts, float* out,
+                               float* lse, void* stream) {
+  if (n_parts < 1 || rows < 1 || head_dim < 1) return KVATTN_E_INVALID;
+  if (!o_parts || !lse_parts || !out || !lse) return KVATTN_E_INVALID;
+  if (!aligned(o_parts, 4) || !aligned(lse_parts, 4) || !aligned(out, 4) || !aligned(lse, 4))
+    return KVATTN_E_INVALID;
+  if (rows > (int64_t)1 << 31) return KVATTN_E_INVALID;
+  kvattn_status st = current_device(nullptr);
+  if (st) return st;
+  return launched(launch_merge(n_parts, rows, head_dim, o_parts, lse_parts, out, lse,
+                               static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

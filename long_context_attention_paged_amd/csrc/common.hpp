@@ -1,0 +1,90 @@
+// Shared device definitions for libkvattn (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvattn {
+
+constexpr int D = 256;            // head_dim
+constexpr int PAGE = 128;         // tokens per page
+constexpr int K_REC = 34816;      // bytes per (page, KV head) key record
+constexpr int V_REC = 18432;      // bytes per (page, KV head) value record
+constexpr int K_SCALE_OFF = 32768;
+constexpr int V_SCALE_OFF = 16384;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+__device__ __forceinline__ uint16_t f16_bits(float x) {
+  _Float16 h = (_Float16)x;  // v_cvt_f16_f32, round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float f16_value(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// 16x16x32 f16 matrix-core product, fp32 accumulate.
+__device__ __forceinline__ floatx4 mfma16(half8_t a, half8_t b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ half2_t as_h2(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
+__device__ __forceinline__ uint32_t as_u32(half2_t x) { return __builtin_bit_cast(uint32_t, x); }
+
+// Eight signed int8 codes (two dwords) -> eight f16 values code*d, where the
+// f16 pair d2 holds the block scale twice. Bytes are offset to unsigned
+// (xor 0x80), placed under the exponent byte 0x64 (f16 1024 + byte), and the
+// 1152 offset is removed exactly before the scale multiply.
+__device__ __forceinline__ half8_t k_codes_to_f16(uint32_t w0, uint32_t w1, half2_t d2) {
+  const half2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const uint32_t y0 = w0 ^ 0x80808080u, y1 = w1 ^ 0x80808080u;
+  half2_t a = (as_h2(__builtin_amdgcn_perm(0x64646464u, y0, 0x04010400u)) - off) * d2;
+  half2_t b = (as_h2(__builtin_amdgcn_perm(0x64646464u, y0, 0x04030402u)) - off) * d2;
+  half2_t c = (as_h2(__builtin_amdgcn_perm(0x64646464u, y1, 0x04010400u)) - off) * d2;
+  half2_t e = (as_h2(__builtin_amdgcn_perm(0x64646464u, y1, 0x04030402u)) - off) * d2;
+  half8_t r = {a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
+  return r;
+}
+
+// One V word (eight 4-bit codes, slot 2p at bit 4p, slot 2p+1 at bit 16+4p)
+// -> eight exact f16 values (code - 8) in slot order.
+__device__ __forceinline__ half8_t v_codes_to_f16(uint32_t w) {
+  const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  half2_t p0 = as_h2((w & 0x000F000Fu) | 0x64006400u) - off;
+  half2_t p1 = as_h2(((w >> 4) & 0x000F000Fu) | 0x64006400u) - off;
+  half2_t p2 = as_h2(((w >> 8) & 0x000F000Fu) | 0x64006400u) - off;
+  half2_t p3 = as_h2(((w >> 12) & 0x000F000Fu) | 0x64006400u) - off;
+  half8_t r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  return r;
+}
+
+__device__ __forceinline__ u32x4 load16(const uint8_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x4 load16_nt(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ uint32_t load4_nt(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
+__device__ __forceinline__ float wave_max_xor_16_32(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float wave_sum_xor_16_32(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+}  // namespace kvattn

@@ -1,0 +1,349 @@
+// a3/a5: decode and verify attention over the paged Q8_0/Q4_0 cache, split
+// over pages; each split writes a partial (o, lse) that merge.hip combines by
+// log-sum-exp.
+//
+// Sources: the RX 9070 XT announcement (wqu.guru), bullet "Stream-optimized
+// speculative decoding": paged decode attention extended to verify batches;
+// the Adaptive KV Streaming guide (alphalab.site), step ④: flash attention
+// over Q8_0 K / Q4_0 V. The kernel design below is this library's.
+//
+// Work decomposition. Grid (splits, KV heads); 256 threads = 4 wavefronts.
+// A split owns a contiguous run of pages (or block-list entries); wavefront w
+// handles 32-token group w of every page in the run, so the four waves stream
+// the four quarters of one page together. Per 32-token group a wave computes
+//   S^T (32 tokens x R rows) = Khat (32 x 256) . Q'^T      (16 mfma per N-tile)
+//   O^T (256 dims x R rows) += Vhat^T (256 x 32) . P'^T    (16 mfma per N-tile)
+// with v_mfma_f32_16x16x32_f16, R = query rows (n_q_tok * gqa) padded to 16
+// (NT = 1) or 32 (NT = 2). Query rows ride in the N dimension so the row-wise
+// softmax needs only the 4-lane-group reduction of one column, and the
+// S^T accumulator layout is exactly the B-operand layout of the PV product,
+// so probabilities never leave registers.
+//
+// Dequantisation happens in registers: K bytes -> f16 via the 0x64 exponent
+// trick and one f16 multiply by the block scale; V nibbles -> exact f16
+// (code - 8), with the per-(token, block) V scale folded into P' instead.
+// Q' = q * scale * log2(e) in f16; softmax runs in base 2 with a lazily
+// updated reference max (rescale only when a tile max exceeds it by 8), so
+// P' <= 256 fits f16 and the O accumulators are rarely touched.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace kvattn {
+namespace {
+
+constexpr int DEC_THREADS = 256;
+constexpr float RESCALE_MARGIN = 8.0f;  // log2 units
+
+struct Tile {
+  u32x4 kc[2][4];   // key codes: M-tile m, 64 bytes (dims 64g..64g+63) of token 16m+r16
+  uint32_t ksc[2];  // key scales of blocks 2g, 2g+1 for that token
+  u32x4 vc[4];      // value words: q = 0..3, e = 0..3 -> M-tile 4q+e, dim 16(4q+e)+r16
+  uint64_t vs;      // bytes 8l..8l+7 of the group's 512 bytes of value scales (lane l)
+};
+
+__device__ __forceinline__ void load_tile(Tile& t, const uint8_t* krec, const uint8_t* vrec,
+                                          int c, int r16, int g) {
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int slot = c * 32 + 16 * m + r16;
+    const uint8_t* kp = krec + slot * D + 64 * g;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t.kc[m][j] = load16_nt(kp + 16 * j);
+    t.ksc[m] = load4_nt(krec + K_SCALE_OFF + (slot * 8 + 2 * g) * 2);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    t.vc[q] = load16_nt(vrec + ((((c * 4 + q) * 4 + g) * 16 + r16) * 4) * 4);
+  t.vs = __builtin_nontemporal_load(
+      reinterpret_cast<const uint64_t*>(vrec + V_SCALE_OFF + c * 512) + (r16 + 16 * g));
+}
+
+constexpr int Q_LDS_STRIDE = 264;  // halves per query row in LDS (256 + pad)
+
+template <int NT>
+struct State {
+  const _Float16* q_lds; // q' = q * scale * log2(e) in f16, [NT*16 rows][264]
+  int64_t limit[NT];   // last visible key position of this lane's row
+  float m[NT];         // reference max (log2 units) of this lane's row
+  float l[NT];         // this lane's share of the row's sum of P'
+  floatx4 o[NT][16];   // O^T accumulators: dims 16mt + 4g + i, row nt*16 + r16
+};
+
+template <int NT>
+__device__ __forceinline__ void compute_tile(State<NT>& st, const Tile& t, int64_t tok0,
+                                             int64_t kv_len, int64_t min_limit, int r16, int g,
+                                             uint64_t* vs_lds) {
+  // The 512 bytes of value scales go through this wave's LDS slot: lane
+  // group g then reads its 16 bytes per block as a broadcast.
+  vs_lds[r16 + 16 * g] = t.vs;
+  __builtin_amdgcn_wave_barrier();
+  // ---- S^T = Khat . Q'^T --------------------------------------------------
+  floatx4 s[2][NT];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const uint32_t sw = t.ksc[m];
+    const half2_t dlo = as_h2((sw & 0xFFFFu) | (sw << 16));
+    const half2_t dhi = as_h2((sw >> 16) | (sw & 0xFFFF0000u));
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) s[m][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const u32x4 w4 = t.kc[m][ks >> 1];
+      const uint32_t w0 = (ks & 1) ? w4.z : w4.x;
+      const uint32_t w1 = (ks & 1) ? w4.w : w4.y;
+      const half8_t a = k_codes_to_f16(w0, w1, ks < 4 ? dlo : dhi);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const half8_t qb = *reinterpret_cast<const half8_t*>(
+            st.q_lds + (nt * 16 + r16) * Q_LDS_STRIDE + 64 * g + 8 * ks);
+        s[m][nt] = mfma16(a, qb, s[m][nt]);
+      }
+    }
+  }
+  // ---- masks: causal rows, tokens past kv_len ------------------------------
+  u32x4 vmask = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+  if (tok0 + 31 > min_limit) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (tok0 + 16 * m + 4 * g + i > st.limit[nt]) s[m][nt][i] = neg_inf();
+    // slots past kv_len hold unwritten bytes: zero their V scales
+    uint32_t mk[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int j0 = 2 * p, j1 = 2 * p + 1;
+      const int u0 = 16 * (j0 >> 2) + 4 * g + (j0 & 3);
+      const int u1 = 16 * (j1 >> 2) + 4 * g + (j1 & 3);
+      mk[p] = (tok0 + u0 < kv_len ? 0x0000FFFFu : 0u) | (tok0 + u1 < kv_len ? 0xFFFF0000u : 0u);
+    }
+    vmask = u32x4{mk[0], mk[1], mk[2], mk[3]};
+  }
+  // ---- online softmax (base 2, lazy reference max) ------------------------
+  half8_t pb[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float mx = s[0][nt][0];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[m][nt][i]);
+    mx = wave_max_xor_16_32(mx);
+    if (mx > st.m[nt] + RESCALE_MARGIN) {
+      const float alpha = __builtin_amdgcn_exp2f(st.m[nt] - mx);
+      st.l[nt] *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < 16; ++mt) st.o[nt][mt] *= alpha;
+      st.m[nt] = mx;
+    }
+    const float mref = st.m[nt] == neg_inf() ? 0.0f : st.m[nt];
+    float p[8];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[4 * m + i] = __builtin_amdgcn_exp2f(s[m][nt][i] - mref);
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sum += p[j];
+    st.l[nt] += sum;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pb[nt][j] = (_Float16)p[j];
+  }
+  // ---- O^T += Vhat^T . (P' * d_V)^T ----------------------------------------
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const u32x4 sc = reinterpret_cast<const u32x4*>(vs_lds)[b * 4 + g] & vmask;
+    const uint32_t scw[4] = {sc.x, sc.y, sc.z, sc.w};
+    half8_t bb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int p2 = 0; p2 < 4; ++p2) {
+        const half2_t pr = {pb[nt][2 * p2], pb[nt][2 * p2 + 1]};
+        const half2_t r = pr * as_h2(scw[p2]);
+        bb[nt][2 * p2] = r[0];
+        bb[nt][2 * p2 + 1] = r[1];
+      }
+#pragma unroll
+    for (int e2 = 0; e2 < 2; ++e2) {
+      const int mt = 2 * b + e2;
+      const u32x4 vq = t.vc[mt >> 2];
+      const uint32_t w = (mt & 3) == 0 ? vq.x : (mt & 3) == 1 ? vq.y : (mt & 3) == 2 ? vq.z : vq.w;
+      const half8_t a = v_codes_to_f16(w);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) st.o[nt][mt] = mfma16(a, bb[nt], st.o[nt][mt]);
+    }
+  }
+}
+
+template <int NT>
+__global__ __launch_bounds__(DEC_THREADS, 1) void decode_kernel(DecodeParams p) {
+  extern __shared__ float smem[];  // q' rows during the loop, then the combine buffer
+  __shared__ float s_m[4][32], s_l[4][32];
+  __shared__ uint64_t s_vs[4][64];  // per-wave value-scale broadcast slot
+  const int h = blockIdx.y, split = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int R = p.n_q_tok * p.gqa;
+  const int n_heads = p.n_kv * p.gqa;
+
+  // q' rows (f16) into LDS, shared by the four waves; padding rows are zero
+  _Float16* q_lds = reinterpret_cast<_Float16*>(smem);
+  for (int i = threadIdx.x; i < NT * 16 * D; i += DEC_THREADS) {
+    const int r = i / D, dim = i % D;
+    float x = 0.f;
+    if (r < R) {
+      const int tq = r / p.gqa, gi = r - tq * p.gqa;
+      x = p.q[((int64_t)tq * n_heads + h * p.gqa + gi) * D + dim] * p.qscale;
+    }
+    q_lds[r * Q_LDS_STRIDE + dim] = (_Float16)x;
+  }
+  State<NT> st;
+  st.q_lds = q_lds;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = nt * 16 + r16;
+    // padding rows see every key (harmless, never written out)
+    st.limit[nt] = r < R ? p.kv_len - p.n_q_tok + r / p.gqa : p.kv_len - 1;
+    st.m[nt] = neg_inf();
+    st.l[nt] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt) st.o[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();
+  const int64_t min_limit = p.kv_len - p.n_q_tok;
+
+  const int64_t u0 = (int64_t)p.n_units * split / p.n_splits;
+  const int64_t u1 = (int64_t)p.n_units * (split + 1) / p.n_splits;
+  const int c = wave;  // 32-token group of every page handled by this wave
+
+  // Page lookups for 64 upcoming units at a time, one per lane, read back
+  // with readlane so every address below is wavefront-uniform.
+  int lp_vec = -1, ph_vec = -1;
+  auto refill = [&](int64_t ub) {
+    const int64_t u = ub + lane;
+    int lp = -1, ph = -1;
+    if (u < u1) {
+      lp = p.blocks ? p.blocks[(int64_t)h * p.n_blk + u] : (int)u;
+      if (lp >= 0 && lp < p.n_logical && (int64_t)lp * PAGE + c * 32 < p.kv_len) {
+        ph = p.page_table[lp];
+        if (ph < 0 || ph >= p.n_phys) ph = -1;
+      }
+    }
+    lp_vec = lp;
+    ph_vec = ph;
+  };
+
+  Tile ta, tb;
+  int64_t tok_a = 0, tok_b = 0;
+  bool va = false, vb = false;
+  auto fetch = [&](int64_t u, Tile& t, int64_t& tok, bool& valid) {
+    if ((u - u0) % 64 == 0) refill(u);
+    const int j = (int)((u - u0) % 64);
+    const int lp = __builtin_amdgcn_readlane(lp_vec, j);
+    const int ph = __builtin_amdgcn_readlane(ph_vec, j);
+    valid = ph >= 0;
+    if (valid) {
+      tok = (int64_t)lp * PAGE + c * 32;
+      const uint8_t* krec = p.k_pool + ((int64_t)ph * p.n_kv + h) * K_REC;
+      const uint8_t* vrec = p.v_pool + ((int64_t)ph * p.n_kv + h) * V_REC;
+      load_tile(t, krec, vrec, c, r16, g);
+    }
+  };
+
+  int64_t u = u0;
+  if (u < u1) fetch(u, ta, tok_a, va);
+  while (u < u1) {
+    if (u + 1 < u1) fetch(u + 1, tb, tok_b, vb);
+    if (va) compute_tile<NT>(st, ta, tok_a, p.kv_len, min_limit, r16, g, s_vs[wave]);
+    ++u;
+    if (u >= u1) break;
+    if (u + 1 < u1) fetch(u + 1, ta, tok_a, va);
+    if (vb) compute_tile<NT>(st, tb, tok_b, p.kv_len, min_limit, r16, g, s_vs[wave]);
+    ++u;
+  }
+
+  // ---- combine the four wavefronts, write this split's partial --------------
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) st.l[nt] = wave_sum_xor_16_32(st.l[nt]);
+  __syncthreads();  // every wave is done with q_lds; smem becomes the combine buffer
+  if (g == 0) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      s_m[wave][nt * 16 + r16] = st.m[nt];
+      s_l[wave][nt * 16 + r16] = st.l[nt];
+    }
+  }
+  __syncthreads();
+  constexpr int RS = 260;  // padded row stride of the combine buffer
+  float* buf = smem + (size_t)wave * NT * 16 * RS;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int row = nt * 16 + r16;
+    float M = neg_inf();
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][row]);
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (s_m[w][row] != neg_inf()) L += s_l[w][row] * __builtin_amdgcn_exp2f(s_m[w][row] - M);
+    const float f =
+        (L > 0.f && st.m[nt] != neg_inf()) ? __builtin_amdgcn_exp2f(st.m[nt] - M) / L : 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt) {
+      const floatx4 v = st.o[nt][mt] * f;
+      *reinterpret_cast<floatx4*>(buf + row * RS + 16 * mt + 4 * g) = v;
+    }
+  }
+  __syncthreads();
+  const int64_t rows_total = (int64_t)p.n_q_tok * n_heads;
+  const int dim = threadIdx.x;
+  for (int r = 0; r < R; ++r) {
+    const int tq = r / p.gqa, gi = r - tq * p.gqa;
+    const int64_t rowg = (int64_t)tq * n_heads + h * p.gqa + gi;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) v += smem[((size_t)w * NT * 16 + r) * RS + dim];
+    p.o_part[((int64_t)split * rows_total + rowg) * D + dim] = v;
+  }
+  if (threadIdx.x < R) {
+    const int r = threadIdx.x;
+    const int tq = r / p.gqa, gi = r - tq * p.gqa;
+    const int64_t rowg = (int64_t)tq * n_heads + h * p.gqa + gi;
+    float M = neg_inf();
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][r]);
+    float L = 0.f;
+    for (int w = 0; w < 4; ++w)
+      if (s_m[w][r] != neg_inf()) L += s_l[w][r] * __builtin_amdgcn_exp2f(s_m[w][r] - M);
+    p.lse_part[(int64_t)split * rows_total + rowg] = (L > 0.f) ? (M + __log2f(L)) * LN2 : neg_inf();
+  }
+}
+
+template <int NT>
+hipError_t launch_nt(const DecodeParams& p, hipStream_t stream) {
+  const size_t combine = sizeof(float) * 4 * NT * 16 * 260;
+  const size_t qbytes = sizeof(_Float16) * NT * 16 * Q_LDS_STRIDE;
+  const size_t shmem = combine > qbytes ? combine : qbytes;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<NT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  dim3 grid((unsigned)p.n_splits, (unsigned)p.n_kv);
+  hipLaunchKernelGGL(decode_kernel<NT>, grid, dim3(DEC_THREADS), shmem, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
+  const int R = p.n_q_tok * p.gqa;
+  if (R <= 16) return launch_nt<1>(p, stream);
+  return launch_nt<2>(p, stream);
+}
+
+}  // namespace kvattn

@@ -1,0 +1,72 @@
+// Internal launch interface between the C ABI (api.hip) and the kernel units.
+// Every launcher assumes its arguments were validated by the caller and only
+// enqueues work on `stream`; it returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvattn {
+
+hipError_t launch_quantize(const float* k, const float* v, int64_t pos0, int32_t n_tok,
+                           int32_t n_kv, const int32_t* page_table, int32_t n_phys,
+                           uint8_t* k_pool, uint8_t* v_pool, hipStream_t stream);
+
+hipError_t launch_summarize(const uint8_t* k_pool, const int32_t* page_table, int32_t n_kv,
+                            int32_t n_phys, int32_t n_logical, int32_t first_page,
+                            int32_t n_pages, float* k_summary, hipStream_t stream);
+
+hipError_t launch_score(const float* q, const float* k_summary, int32_t n_kv, int32_t gqa,
+                        int32_t n_logical, int32_t n_cand, double* scores,
+                        hipStream_t stream);
+
+hipError_t launch_topk(const double* scores, int32_t n_kv, int32_t n_cand, int32_t k_sel,
+                       int32_t n_recent, int32_t n_out, int32_t* out_blocks,
+                       hipStream_t stream);
+
+struct DecodeParams {
+  const float* q;            // [n_q_tok][n_kv*gqa][256]
+  const uint8_t* k_pool;
+  const uint8_t* v_pool;
+  const int32_t* page_table;
+  const int32_t* blocks;     // [n_kv][n_blk] or nullptr (dense)
+  float* o_part;             // [n_splits][n_q_tok*n_kv*gqa][256]
+  float* lse_part;           // [n_splits][n_q_tok*n_kv*gqa]
+  int64_t kv_len;
+  int32_t n_units;           // pages (dense) or block-list entries (sparse)
+  int32_t n_splits;
+  int32_t n_kv;
+  int32_t gqa;
+  int32_t n_q_tok;
+  int32_t n_logical;
+  int32_t n_phys;
+  int32_t n_blk;
+  float qscale;              // softmax scale * log2(e)
+};
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
+struct PrefillParams {
+  const float* q;            // [chunk][n_kv*gqa][256]
+  const uint8_t* k_pool;
+  const uint8_t* v_pool;
+  const int32_t* page_table;
+  float* o_part;             // [n_groups][chunk*n_kv*gqa][256]
+  float* lse_part;           // [n_groups][chunk*n_kv*gqa]
+  int64_t pos0;
+  int32_t chunk;
+  int32_t n_groups;
+  int32_t n_kv;
+  int32_t gqa;
+  int32_t n_logical;
+  int32_t n_phys;
+  float qscale;
+};
+
+int32_t prefill_rows_per_tile();
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+
+hipError_t launch_merge(int32_t n_parts, int64_t rows, int32_t head_dim, const float* o_parts,
+                        const float* lse_parts, float* out, float* lse, hipStream_t stream);
+
+}  // namespace kvattn

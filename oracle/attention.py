@@ -26,8 +26,10 @@ def dequant_page(k_records, v_records):
     vc, vb = unpack_v_record(v_records)
     lead = kc.shape[:-2]
     shp = lead + (PAGE_TOKENS, N_BLOCKS, BLOCK)
-    khat = q8_0_dequantize(kc.reshape(shp), kb).reshape(lead + (PAGE_TOKENS, HEAD_DIM))
-    vhat = q4_0_dequantize(vc.reshape(shp), vb).reshape(lead + (PAGE_TOKENS, HEAD_DIM))
+    # unwritten slots may hold any bytes (inf/nan scales); callers drop them
+    with np.errstate(invalid="ignore", over="ignore"):
+        khat = q8_0_dequantize(kc.reshape(shp), kb).reshape(lead + (PAGE_TOKENS, HEAD_DIM))
+        vhat = q4_0_dequantize(vc.reshape(shp), vb).reshape(lead + (PAGE_TOKENS, HEAD_DIM))
     return khat, vhat
 
 

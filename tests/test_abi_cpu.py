@@ -1,0 +1,155 @@
+"""The C-ABI library loads, exports every entry point include/kvattn.h declares,
+and rejects bad arguments on the host before touching a device. No compute
+call is made here (no GPU in this environment)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_attention_paged_amd as kv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvattn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kv.library_path()),
+                                reason="libkvattn.so not built (run __graft_entry__.build())")
+
+OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_DEVICE = range(5)
+FAKE = 1 << 20            # a 256-byte-aligned non-null address; never dereferenced
+P = ctypes.c_void_p
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(kvattn_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = kv.load_library()
+    names = declared_functions()
+    assert {"kvattn_quantize_pages", "kvattn_select_blocks", "kvattn_decode",
+            "kvattn_prefill_chunk", "kvattn_merge_lse"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_count():
+    lib = kv.load_library()
+    for code in range(5):
+        assert lib.kvattn_status_string(code)
+    assert lib.kvattn_status_string(99) == b"unknown status"
+    assert kv.kvattn_select_count(4088, 128, 256) == 384
+    assert kv.kvattn_select_count(485, 0, 256) == 256
+    assert kv.kvattn_select_count(10, 20, 5) == 10
+    assert kv.kvattn_select_count(0, 1, 1) == -1
+    assert kv.kvattn_select_count(5, -1, 1) == -1
+
+
+def geom(n_kv=4, gqa=6, n_phys=16, head_dim=256, page=128):
+    return kv.Geom(n_kv, gqa, n_phys, head_dim, page)
+
+
+def decode(g, **kw):
+    a = dict(q=FAKE, n_q_tok=1, k_pool=FAKE, v_pool=FAKE, table=FAKE, n_logical=16, blocks=None,
+             n_blk=0, kv_len=1000, scale=0.0625, out=FAKE, lse=FAKE, n_splits=0, ws=FAKE,
+             nbytes=1 << 30)
+    a.update(kw)
+    nb = ctypes.c_size_t(a["nbytes"])
+    code = kv.load_library().kvattn_decode(
+        ctypes.byref(g) if g is not None else None, P(a["q"]), a["n_q_tok"], P(a["k_pool"]),
+        P(a["v_pool"]), P(a["table"]), a["n_logical"], P(a["blocks"]), a["n_blk"], a["kv_len"],
+        a["scale"], P(a["out"]), P(a["lse"]), a["n_splits"], P(a["ws"]), ctypes.byref(nb), None)
+    return code, nb.value
+
+
+def test_decode_validation_before_device():
+    assert decode(None)[0] == E_INVALID
+    assert decode(geom(head_dim=128))[0] == E_UNSUPPORTED
+    assert decode(geom(page=64))[0] == E_UNSUPPORTED
+    assert decode(geom(n_kv=0))[0] == E_INVALID
+    assert decode(geom(), n_q_tok=6)[0] == E_UNSUPPORTED       # 36 rows > 32
+    assert decode(geom(gqa=33))[0] == E_UNSUPPORTED
+    assert decode(geom(), n_q_tok=0)[0] == E_INVALID
+    assert decode(geom(), kv_len=16 * 128 + 1)[0] == E_INVALID
+    assert decode(geom(), kv_len=0)[0] == E_INVALID
+    assert decode(geom(), n_q_tok=4, kv_len=3)[0] == E_INVALID
+    assert decode(geom(), q=0)[0] == E_INVALID
+    assert decode(geom(), q=FAKE + 4)[0] == E_INVALID          # misaligned
+    assert decode(geom(), k_pool=FAKE + 16)[0] == E_INVALID    # pools need 256-byte alignment
+    assert decode(geom(), blocks=FAKE, n_blk=0)[0] == E_INVALID
+    assert decode(geom(), scale=float("nan"))[0] == E_INVALID
+    assert decode(geom(), n_splits=-1)[0] == E_INVALID
+
+
+def test_decode_workspace_protocol():
+    code, need = decode(geom(), ws=None, nbytes=0, n_splits=8)
+    assert code == OK
+    # 8 splits x 24 rows x 256 floats, plus 8 x 24 lse (768 bytes, a multiple of 256)
+    assert need == 8 * 24 * 256 * 4 + 768
+    code, _ = decode(geom(), n_splits=8, nbytes=need - 1)
+    assert code == E_WORKSPACE
+    code, need1 = decode(geom(), ws=None, nbytes=0, n_splits=0)
+    assert code == OK and need1 > 0
+
+
+def test_prefill_and_select_validation():
+    lib = kv.load_library()
+    g = geom()
+    nb = ctypes.c_size_t(0)
+    f = lib.kvattn_prefill_chunk
+    assert f(ctypes.byref(g), P(FAKE), 0, P(FAKE), P(FAKE), P(FAKE), 16, 0, 0.0625, P(FAKE),
+             P(FAKE), 0, None, ctypes.byref(nb), None) == E_INVALID           # chunk 0
+    assert f(ctypes.byref(g), P(FAKE), 100, P(FAKE), P(FAKE), P(FAKE), 16, 2000, 0.0625,
+             P(FAKE), P(FAKE), 0, None, ctypes.byref(nb), None) == E_INVALID  # past the table
+    assert f(ctypes.byref(g), P(FAKE), 100, P(FAKE), P(FAKE), P(FAKE), 16, 1000, 0.0625,
+             P(FAKE), P(FAKE), 4, None, ctypes.byref(nb), None) == OK
+    assert nb.value == 4 * 2400 * 256 * 4 + 4 * 2400 * 4       # 4 groups x 2400 rows
+    assert f(ctypes.byref(g), P(FAKE), 100, P(FAKE), P(FAKE), P(FAKE), 16, 0, 0.0625,
+             P(FAKE), P(FAKE), 4, None, ctypes.byref(nb), None) == OK
+    assert nb.value == 2400 * 256 * 4 + 9728                   # groups capped at 1 page
+    s = lib.kvattn_select_blocks
+    assert s(ctypes.byref(g), P(FAKE), P(FAKE), 16, 17, 2, 4, P(FAKE), None, ctypes.byref(nb),
+             None) == E_INVALID                                               # NB > pages
+    assert s(ctypes.byref(g), P(FAKE), P(FAKE), 16, 16, -1, 4, P(FAKE), None, ctypes.byref(nb),
+             None) == E_INVALID
+    assert s(ctypes.byref(g), P(FAKE), P(FAKE), 16, 16, 2, 4, P(FAKE), None, ctypes.byref(nb),
+             None) == OK
+    assert nb.value == 8 * 4 * 14 + (256 - (8 * 4 * 14) % 256)
+    assert s(ctypes.byref(g), P(FAKE), P(FAKE), 16, 16, 2, 4, P(FAKE), P(FAKE),
+             ctypes.byref(ctypes.c_size_t(8)), None) == E_WORKSPACE
+
+
+def test_quantize_and_merge_validation():
+    lib = kv.load_library()
+    g = geom()
+    q = lib.kvattn_quantize_pages
+    assert q(ctypes.byref(g), P(FAKE), P(FAKE), -1, 4, P(FAKE), 16, P(FAKE), P(FAKE), None,
+             None) == E_INVALID
+    assert q(ctypes.byref(g), P(FAKE), P(FAKE), 2040, 9, P(FAKE), 16, P(FAKE), P(FAKE), None,
+             None) == E_INVALID
+    assert q(ctypes.byref(g), P(FAKE), P(FAKE), 0, 4, P(FAKE), 16, P(FAKE + 8), P(FAKE), None,
+             None) == E_INVALID
+    assert q(ctypes.byref(geom(head_dim=64)), P(FAKE), P(FAKE), 0, 4, P(FAKE), 16, P(FAKE),
+             P(FAKE), None, None) == E_UNSUPPORTED
+    m = lib.kvattn_merge_lse
+    assert m(0, 4, 256, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None) == E_INVALID
+    assert m(2, 0, 256, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None) == E_INVALID
+    assert m(2, 4, 256, None, P(FAKE), P(FAKE), P(FAKE), None) == E_INVALID
+
+
+def test_valid_call_without_device_is_a_device_error():
+    """With valid arguments and no usable GPU the call reports E_DEVICE (or
+    E_UNSUPPORTED on a non-gfx950 GPU) and never falls back to the CPU."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    lib = kv.load_library()
+    code = lib.kvattn_merge_lse(2, 4, 256, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None)
+    assert code in (E_DEVICE, E_UNSUPPORTED)
+
+
+def test_python_binding_requires_gpu_tensors():
+    import torch
+    with pytest.raises((ValueError, TypeError)):
+        kv.kvattn_merge_lse(torch.zeros(2, 4, 256), torch.zeros(2, 4))
