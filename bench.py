@@ -1,0 +1,406 @@
+"""Benchmark of the paged Q8_0/Q4_0 attention hot path on one MI355X.
+
+Headline: decode-attention KV GB/s at 262K context (the verify workload: 16
+layers x 4 KV heads x 24 query heads, head_dim 256, 262144 cached tokens, 4
+query tokens causal among themselves) and chunked-prefill TFLOP/s (512-token
+chunk after 262144 prior tokens), both against the chip's peaks.
+
+A step is one pass over all 16 layers of one workload:
+  verify-262k : per layer, quantise the 4 new tokens into their pages, then
+                decode attention over 2048 pages with the LSE merge;
+  prefill-262k: per layer, quantise the 512-token chunk into pages, then
+                chunked-prefill attention over 2052 pages with the LSE merge;
+  (optional) decode-131k, kvmem-523k (selection + sparse decode).
+Inputs are seeded synthetic tensors (long_context_attention_paged_amd.synth),
+resident in HBM before timing; every layer has its own pool so repeated steps
+stream from HBM, not from the 256 MB last-level cache. Steps are captured
+once in a HIP graph and replayed. Prints one JSON line.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs 3,4]
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16/bf16 matrix peak, published
+K_REC, V_REC = 34816, 18432
+METRIC = "decode-attn KV GB/s (% HBM peak) @262K; prefill-chunk TFLOP/s (% MFMA peak)"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class LayerPools:
+    """One workload's 16 per-layer pools on the GPU plus per-layer queries."""
+
+    def __init__(self, w, dev, with_summary=False, chunk_tokens=32768):
+        import torch
+        from long_context_attention_paged_amd import synth
+        import long_context_attention_paged_amd as kv
+        self.w = w
+        self.table_np = synth.page_table(w)
+        self.table = torch.from_numpy(self.table_np).to(dev)
+        self.n_phys = w.n_pages
+        self.geom = kv.Geom(w.n_kv, w.gqa, self.n_phys)
+        self.kp, self.vp, self.q, self.summ = [], [], [], []
+        self.new_k, self.new_v = [], []
+        n_new = w.chunk if w.chunk else w.n_q_tok
+        for layer in range(w.n_layers):
+            t0 = time.time()
+            q = synth.queries(w, layer)
+            K, V = synth.kv_layer(w, layer, q, threads=16)
+            kp = torch.zeros(self.n_phys * w.n_kv * K_REC, dtype=torch.uint8, device=dev)
+            vp = torch.zeros(self.n_phys * w.n_kv * V_REC, dtype=torch.uint8, device=dev)
+            summ = (torch.zeros((w.n_kv, w.n_pages, 256), dtype=torch.float32, device=dev)
+                    if with_summary else None)
+            for a in range(0, w.kv_len, chunk_tokens):
+                b = min(w.kv_len, a + chunk_tokens)
+                kv.kvattn_quantize_pages(self.geom, torch.from_numpy(K[a:b]).to(dev),
+                                         torch.from_numpy(V[a:b]).to(dev), a, self.table, kp, vp,
+                                         summ)
+            self.kp.append(kp)
+            self.vp.append(vp)
+            self.summ.append(summ)
+            self.q.append(torch.from_numpy(q).to(dev))
+            self.new_k.append(torch.from_numpy(K[w.kv_len - n_new:]).to(dev))
+            self.new_v.append(torch.from_numpy(V[w.kv_len - n_new:]).to(dev))
+            torch.cuda.synchronize()
+            log(f"{w.name}: layer {layer} ready ({time.time() - t0:.1f} s)")
+
+
+def time_graph(step_fn, steps, warmup):
+    """Warm up eagerly, capture one step in a HIP graph, replay: returns ms/step."""
+    import torch
+    for _ in range(warmup):
+        step_fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step_fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step_fn()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps, g
+
+
+def time_launches(call_fn, n_layers, reps):
+    """Average duration of one call (one kernel launch group) with HIP events on
+    the stream the work is launched on: each layer's call is captured in its own
+    graph, and events bracket every replay."""
+    import torch
+    graphs = []
+    for layer in range(n_layers):
+        call_fn(layer)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call_fn(layer)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps * n_layers)]
+    i = 0
+    for _ in range(reps):
+        for layer in range(n_layers):
+            ev[i][0].record()
+            graphs[layer].replay()
+            ev[i][1].record()
+            i += 1
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    return sum(ms) / len(ms)
+
+
+def bench_decode(w, dev, steps, warmup, sparse=False):
+    """Decode / verify workload: quantise the new tokens, attend, merge (x16)."""
+    import torch
+    import long_context_attention_paged_amd as kv
+    pools = LayerPools(w, dev, with_summary=sparse)
+    n_out = kv.kvattn_select_count(w.n_pages, w.n_recent, w.k_top) if sparse else 0
+    outs = [torch.empty_like(q) for q in pools.q]
+    lses = [torch.empty(q.shape[:2], dtype=torch.float32, device=dev) for q in pools.q]
+    blocks = [torch.empty((w.n_kv, max(n_out, 1)), dtype=torch.int32, device=dev)
+              for _ in range(w.n_layers)]
+    ws = None
+    pos_new = w.kv_len - w.n_q_tok
+
+    def decode_call(layer):
+        nonlocal ws
+        if ws is None:
+            ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+        kv.kvattn_decode(pools.geom, pools.q[layer], pools.kp[layer], pools.vp[layer],
+                         pools.table, w.kv_len, 1.0 / 16.0,
+                         blocks=blocks[layer] if sparse else None, out=outs[layer],
+                         lse=lses[layer], workspace=ws)
+
+    sel_ws = torch.empty(8 << 20, dtype=torch.uint8, device=dev) if sparse else None
+
+    def step():
+        for layer in range(w.n_layers):
+            kv.kvattn_quantize_pages(pools.geom, pools.new_k[layer], pools.new_v[layer],
+                                     pos_new, pools.table, pools.kp[layer], pools.vp[layer],
+                                     pools.summ[layer])
+            if sparse:
+                kv.kvattn_select_blocks(pools.geom, pools.q[layer][-1], pools.summ[layer],
+                                        w.n_pages, w.n_pages, w.n_recent, w.k_top,
+                                        out_blocks=blocks[layer], workspace=sel_ws)
+            decode_call(layer)
+
+    ms, _ = time_graph(step, steps, warmup)
+    launch_ms = time_launches(decode_call, w.n_layers, max(steps, 3))
+    tokens = (w.k_top + w.n_recent) * 128 if sparse else w.kv_len
+    bytes_per_launch = tokens * w.n_kv * (272 + 144)
+    res = {
+        "ms_per_step": ms,
+        "kv_bytes_per_step": bytes_per_launch * w.n_layers,
+        "gbs": bytes_per_launch * w.n_layers / (ms * 1e-3) / 1e9,
+        "launch_ms": launch_ms,
+        "launch_gbs": bytes_per_launch / (launch_ms * 1e-3) / 1e9,
+        "bytes_per_launch": bytes_per_launch,
+    }
+    if sparse:
+        res["recall"] = needle_recall(w, pools, blocks)
+    return res, pools
+
+
+def needle_recall(w, pools, blocks):
+    from long_context_attention_paged_amd import synth
+    needles = set(int(b) for b in synth.needle_blocks(w))
+    hits = []
+    for layer in range(w.n_layers):
+        b = blocks[layer].cpu().numpy()
+        for h in range(w.n_kv):
+            hits.append(len(needles & set(b[h].tolist())))
+    return {"needles": len(needles), "min_found": min(hits), "mean_found": sum(hits) / len(hits)}
+
+
+def prefill_flops_per_layer(w):
+    """4 * D flops per unmasked (query head, key) pair, one layer."""
+    pairs = w.chunk * w.pos0 + w.chunk * (w.chunk + 1) // 2
+    return 4 * 256 * pairs * w.n_heads
+
+
+def bench_prefill(w, dev, steps, warmup):
+    import torch
+    import long_context_attention_paged_amd as kv
+    pools = LayerPools(w, dev)
+    outs = [torch.empty_like(q) for q in pools.q]
+    lses = [torch.empty(q.shape[:2], dtype=torch.float32, device=dev) for q in pools.q]
+    ws = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def prefill_call(layer):
+        kv.kvattn_prefill_chunk(pools.geom, pools.q[layer], pools.kp[layer], pools.vp[layer],
+                                pools.table, w.pos0, 1.0 / 16.0, out=outs[layer],
+                                lse=lses[layer], workspace=ws)
+
+    def step():
+        for layer in range(w.n_layers):
+            kv.kvattn_quantize_pages(pools.geom, pools.new_k[layer], pools.new_v[layer], w.pos0,
+                                     pools.table, pools.kp[layer], pools.vp[layer])
+            prefill_call(layer)
+
+    ms, _ = time_graph(step, steps, warmup)
+    launch_ms = time_launches(prefill_call, w.n_layers, max(2, min(steps, 3)))
+    fl = prefill_flops_per_layer(w)
+    return {
+        "ms_per_step": ms,
+        "flops_per_step": fl * w.n_layers,
+        "tflops": fl * w.n_layers / (ms * 1e-3) / 1e12,
+        "tokens_per_s": w.chunk / (ms * 1e-3),
+        "launch_ms": launch_ms,
+        "flops_per_launch": fl,
+        "launch_tflops": fl / (launch_ms * 1e-3) / 1e12,
+    }, pools
+
+
+def cpu_baseline_decode(w, pools):
+    """The oracle, as it stands, on one (layer, KV head) of the workload."""
+    import numpy as np
+    import oracle
+    from long_context_attention_paged_amd import synth
+    kp = pools.kp[0].cpu().numpy().reshape(pools.n_phys, w.n_kv, K_REC)
+    vp = pools.vp[0].cpu().numpy().reshape(pools.n_phys, w.n_kv, V_REC)
+    q = pools.q[0].cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.decode(q, w.gqa, kp, vp, pools.table_np, w.n_pages, w.kv_len, 1.0 / 16.0,
+                  kv_heads=[0])
+    dt = time.perf_counter() - t0
+    nbytes = w.kv_len * (272 + 144)
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": blas_threads(),
+            "kind": "oracle", "seconds": dt,
+            "sample": f"{w.name}: layer 0, KV head 0 ({w.kv_len} tokens x {w.gqa * w.n_q_tok} "
+                      f"query rows), binary64, numpy + OpenBLAS"}
+
+
+def cpu_baseline_prefill(w, pools, n_tok=24):
+    import numpy as np
+    import oracle
+    kp = pools.kp[0].cpu().numpy().reshape(pools.n_phys, w.n_kv, K_REC)
+    vp = pools.vp[0].cpu().numpy().reshape(pools.n_phys, w.n_kv, V_REC)
+    q = pools.q[0].cpu().numpy()
+    toks = np.linspace(0, w.chunk - 1, n_tok).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.prefill_chunk(q, w.gqa, kp, vp, pools.table_np, w.n_pages, w.pos0, 1.0 / 16.0,
+                         tokens=toks, kv_heads=[0])
+    dt = time.perf_counter() - t0
+    fl = 4 * 256 * w.gqa * int(sum(w.pos0 + t + 1 for t in toks))
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+            "kind": "oracle", "seconds": dt,
+            "sample": f"{w.name}: layer 0, KV head 0, {n_tok} of {w.chunk} query tokens "
+                      f"({n_tok * w.gqa} rows over {w.kv_len} keys), binary64, numpy + OpenBLAS"}
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--configs", default="3,4",
+                    help="workloads to run: 2 decode-131k, 3 verify-262k, 4 prefill, 5 kvmem")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import long_context_attention_paged_amd as kv
+    from long_context_attention_paged_amd import synth
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    kv.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfgs = [int(c) for c in args.configs.split(",") if c]
+    extra = {}
+    decode_res = prefill_res = None
+    cpu = None
+    for c in cfgs:
+        w = synth.WORKLOADS[c]
+        log(f"workload {w.name}")
+        if c in (1, 2, 3):
+            res, pools = bench_decode(w, dev, args.steps, args.warmup)
+            if c == 3:
+                decode_res = res
+                if not args.no_cpu_baseline:
+                    cpu = cpu_baseline_decode(w, pools)
+            extra[w.name] = res
+        elif c == 4:
+            res, pools = bench_prefill(w, dev, args.steps, args.warmup)
+            prefill_res = res
+            if not args.no_cpu_baseline:
+                res["cpu_baseline"] = cpu_baseline_prefill(w, pools)
+            extra[w.name] = res
+        elif c == 5:
+            res, pools = bench_decode(w, dev, args.steps, args.warmup, sparse=True)
+            extra[w.name] = res
+        del pools
+        torch.cuda.empty_cache()
+        log(f"{w.name}: {json.dumps(res)}")
+
+    head = decode_res or next(iter(extra.values()))
+    w3 = synth.WORKLOADS[3]
+    line = {
+        "metric": METRIC,
+        "value": round(head.get("gbs", 0.0), 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "verify-262k: 16 layers x 4 KV heads x 24 query heads (GQA 6), head_dim 256, "
+                        "262144 cached tokens in 2048 128-token pages (seeded permutation), "
+                        "4 query tokens causal among themselves, Q8_0 K / Q4_0 V, N(0,1)",
+            "layers": w3.n_layers, "kv_heads": w3.n_kv, "q_heads": w3.n_heads,
+            "head_dim": 256, "context": w3.kv_len, "query_tokens": w3.n_q_tok,
+        },
+        "hbm_frac": round(head.get("gbs", 0.0) / HBM_PEAK_GBS, 4),
+    }
+    if decode_res:
+        line["roofline"] = {
+            "kernel": "decode_kernel<2> + merge_kernel (one kvattn_decode call)",
+            "bound": "hbm",
+            "achieved": round(decode_res["launch_gbs"], 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(decode_res["launch_gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "launch_us": round(decode_res["launch_ms"] * 1e3, 2),
+            "bytes_per_launch": decode_res["bytes_per_launch"],
+        }
+    if prefill_res:
+        line["prefill"] = {
+            "workload": "prefill-262k: 512-token chunk (causal) after 262144 prior tokens, "
+                        "2052 pages, 16 layers x 4 KV heads x 24 query heads",
+            "tflops": round(prefill_res["tflops"], 2),
+            "mfma_frac": round(prefill_res["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
+            "ms_per_step": round(prefill_res["ms_per_step"], 3),
+            "tokens_per_s": round(prefill_res["tokens_per_s"], 1),
+            "roofline": {
+                "kernel": "prefill_kernel + merge_kernel (one kvattn_prefill_chunk call)",
+                "bound": "mfma",
+                "achieved": round(prefill_res["launch_tflops"], 2),
+                "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s",
+                "frac": round(prefill_res["launch_tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
+                "traffic": None,
+                "launch_ms": round(prefill_res["launch_ms"], 4),
+            },
+        }
+        if "cpu_baseline" in prefill_res:
+            line["prefill"]["cpu_baseline"] = prefill_res["cpu_baseline"]
+    if cpu:
+        cpu["cpu_model"] = cpu_model()
+        line["cpu_baseline"] = cpu
+    others = {k: v for k, v in extra.items() if k not in (w3.name, synth.WORKLOADS[4].name)}
+    if others:
+        line["other_workloads"] = others
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -66,6 +66,18 @@ __device__ __forceinline__ half8_t v_codes_to_f16(uint32_t w) {
   return r;
 }
 
+// As v_codes_to_f16, with the nibble mask 0x000F000F passed in a VGPR so each
+// pair unpacks with one v_and_or_b32 (the 0x64006400 exponent from an SGPR).
+__device__ __forceinline__ half8_t v_codes_to_f16_m(uint32_t w, uint32_t mask) {
+  const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  half2_t p0 = as_h2((w & mask) | 0x64006400u) - off;
+  half2_t p1 = as_h2(((w >> 4) & mask) | 0x64006400u) - off;
+  half2_t p2 = as_h2(((w >> 8) & mask) | 0x64006400u) - off;
+  half2_t p3 = as_h2(((w >> 12) & mask) | 0x64006400u) - off;
+  half8_t r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  return r;
+}
+
 __device__ __forceinline__ u32x4 load16(const uint8_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

@@ -33,70 +33,84 @@ namespace {
 
 constexpr int DEC_THREADS = 256;
 constexpr float RESCALE_MARGIN = 8.0f;  // log2 units
+constexpr int NSTAGE = 2;               // tiles in flight per wave (LDS ring depth)
+constexpr int SLOT_BYTES = 13 * 1024;   // one 32-token tile of one KV head
+constexpr int SLOT_K = 0;               // 8 x 1 KB: key codes, lane-ordered
+constexpr int SLOT_V = 8 * 1024;        // 4 x 1 KB: value words, lane-ordered
+constexpr int SLOT_S = 12 * 1024;       // 512 B key scales + 512 B value scales
+constexpr int LOADS_PER_TILE = 13;      // 1 KB direct-to-LDS loads per tile
+constexpr int Q_LDS_STRIDE = 264;       // halves per query row in LDS (256 + pad)
 
-struct Tile {
-  u32x4 kc[2][4];   // key codes: M-tile m, 64 bytes (dims 64g..64g+63) of token 16m+r16
-  uint32_t ksc[2];  // key scales of blocks 2g, 2g+1 for that token
-  u32x4 vc[4];      // value words: q = 0..3, e = 0..3 -> M-tile 4q+e, dim 16(4q+e)+r16
-  uint64_t vs;      // bytes 8l..8l+7 of the group's 512 bytes of value scales (lane l)
-};
+typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ void load_tile(Tile& t, const uint8_t* krec, const uint8_t* vrec,
-                                          int c, int r16, int g) {
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int slot = c * 32 + 16 * m + r16;
-    const uint8_t* kp = krec + slot * D + 64 * g;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) t.kc[m][j] = load16_nt(kp + 16 * j);
-    t.ksc[m] = load4_nt(krec + K_SCALE_OFF + (slot * 8 + 2 * g) * 2);
-  }
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    t.vc[q] = load16_nt(vrec + ((((c * 4 + q) * 4 + g) * 16 + r16) * 4) * 4);
-  t.vs = __builtin_nontemporal_load(
-      reinterpret_cast<const uint64_t*>(vrec + V_SCALE_OFF + c * 512) + (r16 + 16 * g));
+__device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* lds_dst) {
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                   (lds_void*)(lds_dst), 16, 0, 0);
 }
 
-constexpr int Q_LDS_STRIDE = 264;  // halves per query row in LDS (256 + pad)
+// Wait until at most n direct-to-LDS loads of this wave are outstanding
+// (vmcnt counts them in issue order), then fence the compiler.
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  static_assert(N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  __asm__ __volatile__("" ::: "memory");
+}
+
+// Issue the 13 direct loads of one tile (32-token group c of a page record)
+// into an LDS slot. Lane (r16, g) brings exactly the 16-byte chunks it will
+// feed to the matrix cores, so every later LDS read is lane-local and
+// conflict-free; scales are fetched by lanes 0..31 (keys) and 32..63 (values).
+__device__ __forceinline__ void issue_tile(uint8_t* slot, const uint8_t* krec, const uint8_t* vrec,
+                                           int c, int lane, int r16, int g) {
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dma16(krec + (c * 32 + 16 * m + r16) * D + 64 * g + 16 * j, slot + SLOT_K + (m * 4 + j) * 1024);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    dma16(vrec + ((((c * 4 + q) * 4 + g) * 16 + r16) * 4) * 4, slot + SLOT_V + q * 1024);
+  const uint8_t* sp = lane < 32 ? krec + K_SCALE_OFF + (c * 32 + lane) * 16
+                                : vrec + V_SCALE_OFF + c * 512 + (lane - 32) * 16;
+  dma16(sp, slot + SLOT_S);
+}
 
 template <int NT>
 struct State {
-  const _Float16* q_lds; // q' = q * scale * log2(e) in f16, [NT*16 rows][264]
-  int64_t limit[NT];   // last visible key position of this lane's row
-  float m[NT];         // reference max (log2 units) of this lane's row
-  float l[NT];         // this lane's share of the row's sum of P'
-  floatx4 o[NT][16];   // O^T accumulators: dims 16mt + 4g + i, row nt*16 + r16
+  const _Float16* q_lds;  // q' = q * scale * log2(e) in f16, [NT*16 rows][264]
+  int64_t limit[NT];      // last visible key position of this lane's row
+  float m[NT];            // reference max (log2 units) of this lane's row
+  float l[NT];            // this lane's share of the row's sum of P'
+  floatx4 o[NT][16];      // O^T accumulators: dims 16mt + 4g + i, row nt*16 + r16
 };
 
 template <int NT>
-__device__ __forceinline__ void compute_tile(State<NT>& st, const Tile& t, int64_t tok0,
-                                             int64_t kv_len, int64_t min_limit, int r16, int g,
-                                             uint64_t* vs_lds) {
-  // The 512 bytes of value scales go through this wave's LDS slot: lane
-  // group g then reads its 16 bytes per block as a broadcast.
-  vs_lds[r16 + 16 * g] = t.vs;
-  __builtin_amdgcn_wave_barrier();
+__device__ __forceinline__ void compute_tile(State<NT>& st, const uint8_t* slot, int64_t tok0,
+                                             int64_t kv_len, int64_t min_limit, int lane, int r16,
+                                             int g, uint32_t nib_mask) {
   // ---- S^T = Khat . Q'^T --------------------------------------------------
   floatx4 s[2][NT];
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
-    const uint32_t sw = t.ksc[m];
+    const uint32_t sw = *reinterpret_cast<const uint32_t*>(slot + SLOT_S + (16 * m + r16) * 16 + 4 * g);
     const half2_t dlo = as_h2((sw & 0xFFFFu) | (sw << 16));
     const half2_t dhi = as_h2((sw >> 16) | (sw & 0xFFFF0000u));
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) s[m][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const u32x4 w4 = t.kc[m][ks >> 1];
-      const uint32_t w0 = (ks & 1) ? w4.z : w4.x;
-      const uint32_t w1 = (ks & 1) ? w4.w : w4.y;
-      const half8_t a = k_codes_to_f16(w0, w1, ks < 4 ? dlo : dhi);
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 w4 = *reinterpret_cast<const u32x4*>(slot + SLOT_K + (m * 4 + j) * 1024 + lane * 16);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const half8_t qb = *reinterpret_cast<const half8_t*>(
-            st.q_lds + (nt * 16 + r16) * Q_LDS_STRIDE + 64 * g + 8 * ks);
-        s[m][nt] = mfma16(a, qb, s[m][nt]);
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int ks = 2 * j + h2;
+        const half8_t a = k_codes_to_f16(h2 ? w4.z : w4.x, h2 ? w4.w : w4.y, ks < 4 ? dlo : dhi);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const half8_t qb = *reinterpret_cast<const half8_t*>(
+              st.q_lds + (nt * 16 + r16) * Q_LDS_STRIDE + 64 * g + 8 * ks);
+          s[m][nt] = mfma16(a, qb, s[m][nt]);
+        }
       }
     }
   }
@@ -152,9 +166,14 @@ __device__ __forceinline__ void compute_tile(State<NT>& st, const Tile& t, int64
     for (int j = 0; j < 8; ++j) pb[nt][j] = (_Float16)p[j];
   }
   // ---- O^T += Vhat^T . (P' * d_V)^T ----------------------------------------
+  u32x4 vw[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    vw[q] = *reinterpret_cast<const u32x4*>(slot + SLOT_V + q * 1024 + lane * 16);
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
-    const u32x4 sc = reinterpret_cast<const u32x4*>(vs_lds)[b * 4 + g] & vmask;
+    const u32x4 sc =
+        *reinterpret_cast<const u32x4*>(slot + SLOT_S + 512 + (b * 4 + g) * 16) & vmask;
     const uint32_t scw[4] = {sc.x, sc.y, sc.z, sc.w};
     half8_t bb[NT];
 #pragma unroll
@@ -169,9 +188,9 @@ __device__ __forceinline__ void compute_tile(State<NT>& st, const Tile& t, int64
 #pragma unroll
     for (int e2 = 0; e2 < 2; ++e2) {
       const int mt = 2 * b + e2;
-      const u32x4 vq = t.vc[mt >> 2];
+      const u32x4 vq = vw[mt >> 2];
       const uint32_t w = (mt & 3) == 0 ? vq.x : (mt & 3) == 1 ? vq.y : (mt & 3) == 2 ? vq.z : vq.w;
-      const half8_t a = v_codes_to_f16(w);
+      const half8_t a = v_codes_to_f16_m(w, nib_mask);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) st.o[nt][mt] = mfma16(a, bb[nt], st.o[nt][mt]);
     }
@@ -180,17 +199,21 @@ __device__ __forceinline__ void compute_tile(State<NT>& st, const Tile& t, int64
 
 template <int NT>
 __global__ __launch_bounds__(DEC_THREADS, 1) void decode_kernel(DecodeParams p) {
-  extern __shared__ float smem[];  // q' rows during the loop, then the combine buffer
+  // LDS: [q' rows | 4 waves x NSTAGE tile slots] during the loop, then the
+  // combine buffer [4 waves][NT*16 rows][260] floats.
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
+  float* smem = reinterpret_cast<float*>(smem_raw);
   __shared__ float s_m[4][32], s_l[4][32];
-  __shared__ uint64_t s_vs[4][64];  // per-wave value-scale broadcast slot
   const int h = blockIdx.y, split = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, g = lane >> 4;
   const int R = p.n_q_tok * p.gqa;
   const int n_heads = p.n_kv * p.gqa;
+  constexpr int Q_BYTES = ((NT * 16 * Q_LDS_STRIDE * 2) + 1023) / 1024 * 1024;
+  uint8_t* slots = smem_raw + Q_BYTES + wave * NSTAGE * SLOT_BYTES;
 
   // q' rows (f16) into LDS, shared by the four waves; padding rows are zero
-  _Float16* q_lds = reinterpret_cast<_Float16*>(smem);
+  _Float16* q_lds = reinterpret_cast<_Float16*>(smem_raw);
   for (int i = threadIdx.x; i < NT * 16 * D; i += DEC_THREADS) {
     const int r = i / D, dim = i % D;
     float x = 0.f;
@@ -212,15 +235,19 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void decode_kernel(DecodeParams p) 
 #pragma unroll
     for (int mt = 0; mt < 16; ++mt) st.o[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
-  __syncthreads();
   const int64_t min_limit = p.kv_len - p.n_q_tok;
+  uint32_t nib_mask;  // kept in a VGPR so the nibble unpack fuses into v_and_or
+  __asm__ volatile("v_mov_b32 %0, 0x000f000f" : "=v"(nib_mask));
+  __syncthreads();
 
   const int64_t u0 = (int64_t)p.n_units * split / p.n_splits;
   const int64_t u1 = (int64_t)p.n_units * (split + 1) / p.n_splits;
+  const int n_tiles = (int)(u1 - u0);
   const int c = wave;  // 32-token group of every page handled by this wave
 
   // Page lookups for 64 upcoming units at a time, one per lane, read back
-  // with readlane so every address below is wavefront-uniform.
+  // with readlane so every address is wavefront-uniform. Invalid tiles still
+  // issue their 13 loads (from record 0) so the wait counts stay constant.
   int lp_vec = -1, ph_vec = -1;
   auto refill = [&](int64_t ub) {
     const int64_t u = ub + lane;
@@ -235,34 +262,32 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void decode_kernel(DecodeParams p) 
     lp_vec = lp;
     ph_vec = ph;
   };
-
-  Tile ta, tb;
-  int64_t tok_a = 0, tok_b = 0;
-  bool va = false, vb = false;
-  auto fetch = [&](int64_t u, Tile& t, int64_t& tok, bool& valid) {
-    if ((u - u0) % 64 == 0) refill(u);
-    const int j = (int)((u - u0) % 64);
-    const int lp = __builtin_amdgcn_readlane(lp_vec, j);
-    const int ph = __builtin_amdgcn_readlane(ph_vec, j);
+  auto issue = [&](int i, int64_t& tok, bool& valid) {
+    if (i % 64 == 0) refill(u0 + i);
+    const int lp = __builtin_amdgcn_readlane(lp_vec, i % 64);
+    const int ph = __builtin_amdgcn_readlane(ph_vec, i % 64);
     valid = ph >= 0;
-    if (valid) {
-      tok = (int64_t)lp * PAGE + c * 32;
-      const uint8_t* krec = p.k_pool + ((int64_t)ph * p.n_kv + h) * K_REC;
-      const uint8_t* vrec = p.v_pool + ((int64_t)ph * p.n_kv + h) * V_REC;
-      load_tile(t, krec, vrec, c, r16, g);
-    }
+    tok = (int64_t)lp * PAGE + c * 32;
+    const int64_t rec = valid ? (int64_t)ph * p.n_kv + h : 0;
+    issue_tile(slots + (i % NSTAGE) * SLOT_BYTES, p.k_pool + rec * K_REC, p.v_pool + rec * V_REC,
+               valid ? c : 0, lane, r16, g);
   };
 
-  int64_t u = u0;
-  if (u < u1) fetch(u, ta, tok_a, va);
-  while (u < u1) {
-    if (u + 1 < u1) fetch(u + 1, tb, tok_b, vb);
-    if (va) compute_tile<NT>(st, ta, tok_a, p.kv_len, min_limit, r16, g, s_vs[wave]);
-    ++u;
-    if (u >= u1) break;
-    if (u + 1 < u1) fetch(u + 1, ta, tok_a, va);
-    if (vb) compute_tile<NT>(st, tb, tok_b, p.kv_len, min_limit, r16, g, s_vs[wave]);
-    ++u;
+  int64_t tok[NSTAGE];
+  bool valid[NSTAGE];
+  if (n_tiles > 0) issue(0, tok[0], valid[0]);
+  for (int i = 0; i < n_tiles; ++i) {
+    const int cur = i % NSTAGE, nxt = (i + 1) % NSTAGE;
+    if (i + 1 < n_tiles) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): earlier LDS reads of the slot are done
+      issue(i + 1, tok[nxt], valid[nxt]);
+      wait_loads<LOADS_PER_TILE>();
+    } else {
+      wait_loads<0>();
+    }
+    if (valid[cur])
+      compute_tile<NT>(st, slots + cur * SLOT_BYTES, tok[cur], p.kv_len, min_limit, lane, r16, g,
+                       nib_mask);
   }
 
   // ---- combine the four wavefronts, write this split's partial --------------
@@ -324,8 +349,9 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void decode_kernel(DecodeParams p) 
 template <int NT>
 hipError_t launch_nt(const DecodeParams& p, hipStream_t stream) {
   const size_t combine = sizeof(float) * 4 * NT * 16 * 260;
-  const size_t qbytes = sizeof(_Float16) * NT * 16 * Q_LDS_STRIDE;
-  const size_t shmem = combine > qbytes ? combine : qbytes;
+  const size_t qbytes = ((NT * 16 * Q_LDS_STRIDE * 2) + 1023) / 1024 * 1024;
+  const size_t loop = qbytes + 4 * NSTAGE * SLOT_BYTES;
+  const size_t shmem = combine > loop ? combine : loop;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<NT>),

@@ -26,7 +26,7 @@ namespace kvattn {
 namespace {
 
 constexpr int PF_THREADS = 256;
-constexpr int PF_NT = 4;                        // 16-row N-tiles per wave
+constexpr int PF_NT = 2;                        // 16-row N-tiles per wave
 constexpr int PF_ROWS = 4 * 16 * PF_NT;         // rows per workgroup
 constexpr int K_LDS_STRIDE = 264;               // halves per key row (256 + pad)
 constexpr int V_LDS_STRIDE = 40;                // halves per value dim row (32 + pad)
