@@ -241,7 +241,8 @@ kvattn_status kvattn_prefill_chunk(const kvattn_geom *geom, const float *q,
  *  M = max_s lse_parts[s][r]; L = M + ln sum_s exp(lse_parts[s][r] - M);
  *  out[r] = sum_s exp(lse_parts[s][r] - L) * o_parts[s][r]; lse[r] = L.
  *  A part with lse = -inf contributes nothing; if every part is -inf the row
- *  is out = 0, lse = -inf. fp32 throughout, parts summed in ascending s.
+ *  is out = 0, lse = -inf. fp32 throughout; sums are taken in a fixed order,
+ *  so results are deterministic.
  *  o_parts fp32 [n_parts][rows][head_dim]; lse_parts fp32 [n_parts][rows];
  *  out fp32 [rows][head_dim]; lse fp32 [rows]. n_parts >= 1, rows >= 1,
  *  head_dim >= 1. out must not alias o_parts. */

@@ -193,7 +193,9 @@ kvattn_status kvattn_decode(const kvattn_geom* geom, const float* q, int32_t n_q
     // query and launch must run on the same device.
     if (workspace && (st = current_device(&n_cu))) return st;
     if (!workspace && current_device(&n_cu) != KVATTN_OK) n_cu = 256;
-    splits = (n_cu + geom->n_kv_heads - 1) / geom->n_kv_heads;
+    // two resident workgroups per CU (the decode kernel is built for two
+    // waves per SIMD), so that many splits over the KV heads
+    splits = (2 * n_cu + geom->n_kv_heads - 1) / geom->n_kv_heads;
   }
   if (splits > n_units) splits = n_units;
   if (splits < 1) splits = 1;

@@ -33,11 +33,19 @@ namespace {
 
 constexpr int DEC_THREADS = 256;
 constexpr float RESCALE_MARGIN = 8.0f;  // log2 units
-constexpr int NSTAGE = 2;               // tiles in flight per wave (LDS ring depth)
-constexpr int SLOT_BYTES = 13 * 1024;   // one 32-token tile of one KV head
-constexpr int SLOT_K = 0;               // 8 x 1 KB: key codes, lane-ordered
-constexpr int SLOT_V = 8 * 1024;        // 4 x 1 KB: value words, lane-ordered
-constexpr int SLOT_S = 12 * 1024;       // 512 B key scales + 512 B value scales
+// One 32-token tile of one KV head in LDS:
+//   [0, 8320)      key codes: 8 loads of 4 whole token rows (1 KB contiguous in
+//                  the page); load i lands at kbase(i) with its 16-byte chunks
+//                  rotated by 4 per row, so the matrix-core operand reads
+//                  (16 rows x one 16-byte column each) hit 16 distinct bank groups;
+//   [8320, 8832)   key scales;
+//   [8832, 12928)  value words (4 x 1 KB, lane-ordered: each lane reads its own);
+//   [12928, 13440) value scales.
+constexpr int SLOT_K = 0;
+constexpr int SLOT_KS = 8320;
+constexpr int SLOT_V = 8832;
+constexpr int SLOT_VS = 12928;
+constexpr int SLOT_BYTES = 13440;
 constexpr int LOADS_PER_TILE = 13;      // 1 KB direct-to-LDS loads per tile
 constexpr int Q_LDS_STRIDE = 264;       // halves per query row in LDS (256 + pad)
 
@@ -57,23 +65,37 @@ __device__ __forceinline__ void wait_loads() {
   __asm__ __volatile__("" ::: "memory");
 }
 
-// Issue the 13 direct loads of one tile (32-token group c of a page record)
-// into an LDS slot. Lane (r16, g) brings exactly the 16-byte chunks it will
-// feed to the matrix cores, so every later LDS read is lane-local and
-// conflict-free; scales are fetched by lanes 0..31 (keys) and 32..63 (values).
-__device__ __forceinline__ void issue_tile(uint8_t* slot, const uint8_t* krec, const uint8_t* vrec,
-                                           int c, int lane, int r16, int g) {
+// Direct loads of one tile (32-token group c of a page record) into an LDS
+// slot, in two parts so each can be refilled as soon as it is consumed:
+//   keys   (9 loads): 8 x 1 KB codes + 512 B scales (lanes 0..31);
+//   values (5 loads): 4 x 1 KB words + 512 B scales (lanes 0..31).
+// Lane (r16, g) brings exactly the 16-byte code chunks it will feed to the
+// matrix cores, so those LDS reads are lane-local and conflict-free.
+constexpr int K_LOADS = 9;
+constexpr int V_LOADS = 5;
+
+// LDS base of key load i (4 token rows): 1 KB apart plus a 16-byte shift per
+// row quad (i % 4) and 64 bytes per M-tile (i / 4), so loads never overlap.
+__device__ __forceinline__ int kbase(int i) { return i * 1024 + 16 * (i & 3) + 64 * (i >> 2); }
+// Position (16-byte unit) inside a key load of chunk s (0..15) of row a (0..3).
+__device__ __forceinline__ int kpos(int a, int s) { return 16 * a + ((s + 4 * a) & 15); }
+
+__device__ __forceinline__ void issue_keys(uint8_t* slot, const uint8_t* krec, int c, int lane,
+                                           int r16, int g) {
+  // lane p of load i brings chunk s = (p%16 - 4a) & 15 of row a = p/16
+  const int a = lane >> 4, s = ((lane & 15) - 4 * a) & 15;
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      dma16(krec + (c * 32 + 16 * m + r16) * D + 64 * g + 16 * j, slot + SLOT_K + (m * 4 + j) * 1024);
+  for (int i = 0; i < 8; ++i)
+    dma16(krec + (c * 32 + 4 * i + a) * D + 16 * s, slot + SLOT_K + kbase(i));
+  if (lane < 32) dma16(krec + K_SCALE_OFF + (c * 32 + lane) * 16, slot + SLOT_KS);
+}
+
+__device__ __forceinline__ void issue_values(uint8_t* slot, const uint8_t* vrec, int c, int lane,
+                                             int r16, int g) {
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     dma16(vrec + ((((c * 4 + q) * 4 + g) * 16 + r16) * 4) * 4, slot + SLOT_V + q * 1024);
-  const uint8_t* sp = lane < 32 ? krec + K_SCALE_OFF + (c * 32 + lane) * 16
-                                : vrec + V_SCALE_OFF + c * 512 + (lane - 32) * 16;
-  dma16(sp, slot + SLOT_S);
+  if (lane < 32) dma16(vrec + V_SCALE_OFF + c * 512 + lane * 16, slot + SLOT_VS);
 }
 
 template <int NT>
@@ -85,22 +107,24 @@ struct State {
   floatx4 o[NT][16];      // O^T accumulators: dims 16mt + 4g + i, row nt*16 + r16
 };
 
-template <int NT>
+template <int NT, typename MidFn>
 __device__ __forceinline__ void compute_tile(State<NT>& st, const uint8_t* slot, int64_t tok0,
                                              int64_t kv_len, int64_t min_limit, int lane, int r16,
-                                             int g, uint32_t nib_mask) {
+                                             int g, uint32_t nib_mask, MidFn&& after_keys) {
   // ---- S^T = Khat . Q'^T --------------------------------------------------
   floatx4 s[2][NT];
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
-    const uint32_t sw = *reinterpret_cast<const uint32_t*>(slot + SLOT_S + (16 * m + r16) * 16 + 4 * g);
+    const uint32_t sw = *reinterpret_cast<const uint32_t*>(slot + SLOT_KS + (16 * m + r16) * 16 + 4 * g);
     const half2_t dlo = as_h2((sw & 0xFFFFu) | (sw << 16));
     const half2_t dhi = as_h2((sw >> 16) | (sw & 0xFFFF0000u));
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) s[m][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const u32x4 w4 = *reinterpret_cast<const u32x4*>(slot + SLOT_K + (m * 4 + j) * 1024 + lane * 16);
+      // bytes 64g + 16j of token 16m + r16: load 4m + r16/4, row r16%4, chunk 4g + j
+      const u32x4 w4 = *reinterpret_cast<const u32x4*>(
+          slot + SLOT_K + kbase(4 * m + (r16 >> 2)) + 16 * kpos(r16 & 3, 4 * g + j));
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int ks = 2 * j + h2;
@@ -111,12 +135,15 @@ __device__ __forceinline__ void compute_tile(State<NT>& st, const uint8_t* slot,
               st.q_lds + (nt * 16 + r16) * Q_LDS_STRIDE + 64 * g + 8 * ks);
           s[m][nt] = mfma16(a, qb, s[m][nt]);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
+  // the key half of the slot has been read: let the caller refill it
+  after_keys();
   // ---- masks: causal rows, tokens past kv_len ------------------------------
   u32x4 vmask = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
-  if (tok0 + 31 > min_limit) {
+  if (__builtin_expect(tok0 + 31 > min_limit, 0)) {
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -173,7 +200,7 @@ __device__ __forceinline__ void compute_tile(State<NT>& st, const uint8_t* slot,
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
     const u32x4 sc =
-        *reinterpret_cast<const u32x4*>(slot + SLOT_S + 512 + (b * 4 + g) * 16) & vmask;
+        *reinterpret_cast<const u32x4*>(slot + SLOT_VS + (b * 4 + g) * 16) & vmask;
     const uint32_t scw[4] = {sc.x, sc.y, sc.z, sc.w};
     half8_t bb[NT];
 #pragma unroll
@@ -194,35 +221,30 @@ __device__ __forceinline__ void compute_tile(State<NT>& st, const uint8_t* slot,
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) st.o[nt][mt] = mfma16(a, bb[nt], st.o[nt][mt]);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-template <int NT>
-__global__ __launch_bounds__(DEC_THREADS, 1) void decode_kernel(DecodeParams p) {
+// NSTAGE: tiles per wave's LDS ring (1: load, wait, compute; the second wave
+// on the SIMD computes meanwhile). WPS: workgroups per CU the kernel is
+// compiled for (registers <= 512 / WPS per lane).
+template <int NT, int NSTAGE, int WPS>
+__global__ __launch_bounds__(DEC_THREADS, WPS) void decode_kernel(DecodeParams p) {
   // LDS: [q' rows | 4 waves x NSTAGE tile slots] during the loop, then the
   // combine buffer [4 waves][NT*16 rows][260] floats.
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
   float* smem = reinterpret_cast<float*>(smem_raw);
   __shared__ float s_m[4][32], s_l[4][32];
   const int h = blockIdx.y, split = blockIdx.x;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, g = lane >> 4;
   const int R = p.n_q_tok * p.gqa;
   const int n_heads = p.n_kv * p.gqa;
   constexpr int Q_BYTES = ((NT * 16 * Q_LDS_STRIDE * 2) + 1023) / 1024 * 1024;
-  uint8_t* slots = smem_raw + Q_BYTES + wave * NSTAGE * SLOT_BYTES;
+  uint8_t* slots = smem_raw + Q_BYTES + wave * NSTAGE * SLOT_BYTES;  // NSTAGE == 1
 
-  // q' rows (f16) into LDS, shared by the four waves; padding rows are zero
   _Float16* q_lds = reinterpret_cast<_Float16*>(smem_raw);
-  for (int i = threadIdx.x; i < NT * 16 * D; i += DEC_THREADS) {
-    const int r = i / D, dim = i % D;
-    float x = 0.f;
-    if (r < R) {
-      const int tq = r / p.gqa, gi = r - tq * p.gqa;
-      x = p.q[((int64_t)tq * n_heads + h * p.gqa + gi) * D + dim] * p.qscale;
-    }
-    q_lds[r * Q_LDS_STRIDE + dim] = (_Float16)x;
-  }
   State<NT> st;
   st.q_lds = q_lds;
 #pragma unroll
@@ -238,7 +260,6 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void decode_kernel(DecodeParams p) 
   const int64_t min_limit = p.kv_len - p.n_q_tok;
   uint32_t nib_mask;  // kept in a VGPR so the nibble unpack fuses into v_and_or
   __asm__ volatile("v_mov_b32 %0, 0x000f000f" : "=v"(nib_mask));
-  __syncthreads();
 
   const int64_t u0 = (int64_t)p.n_units * split / p.n_splits;
   const int64_t u1 = (int64_t)p.n_units * (split + 1) / p.n_splits;
@@ -262,38 +283,72 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void decode_kernel(DecodeParams p) 
     lp_vec = lp;
     ph_vec = ph;
   };
-  auto issue = [&](int i, int64_t& tok, bool& valid) {
+  // Tile i's record; invalid tiles (skipped pages, tokens past kv_len) still
+  // load from record 0 so every wait count below is a constant.
+  auto locate = [&](int i, int64_t& tok, bool& valid, int64_t& rec) {
     if (i % 64 == 0) refill(u0 + i);
     const int lp = __builtin_amdgcn_readlane(lp_vec, i % 64);
     const int ph = __builtin_amdgcn_readlane(ph_vec, i % 64);
     valid = ph >= 0;
     tok = (int64_t)lp * PAGE + c * 32;
-    const int64_t rec = valid ? (int64_t)ph * p.n_kv + h : 0;
-    issue_tile(slots + (i % NSTAGE) * SLOT_BYTES, p.k_pool + rec * K_REC, p.v_pool + rec * V_REC,
-               valid ? c : 0, lane, r16, g);
+    rec = valid ? (int64_t)ph * p.n_kv + h : 0;
   };
 
-  int64_t tok[NSTAGE];
-  bool valid[NSTAGE];
-  if (n_tiles > 0) issue(0, tok[0], valid[0]);
-  for (int i = 0; i < n_tiles; ++i) {
-    const int cur = i % NSTAGE, nxt = (i + 1) % NSTAGE;
-    if (i + 1 < n_tiles) {
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): earlier LDS reads of the slot are done
-      issue(i + 1, tok[nxt], valid[nxt]);
-      wait_loads<LOADS_PER_TILE>();
-    } else {
-      wait_loads<0>();
+  // One LDS slot per wave with separately refilled key and value halves:
+  // keys of tile i+1 load while tile i's softmax and PV run, values of tile
+  // i+1 load while tile i+1's QK runs.
+  uint8_t* slot = slots;
+  int64_t tok = 0, rec = 0, tok_n = 0, rec_n = 0;
+  bool valid = false, valid_n = false;
+  if (n_tiles > 0) {
+    locate(0, tok, valid, rec);
+    issue_keys(slot, p.k_pool + rec * K_REC, valid ? c : 0, lane, r16, g);
+    issue_values(slot, p.v_pool + rec * V_REC, valid ? c : 0, lane, r16, g);
+  }
+  // the first tile is in flight: now stage q' rows (f16) into LDS, shared by
+  // the four waves (padding rows are zero)
+  // q' rows (f16) into LDS, shared by the four waves; padding rows are zero
+  for (int i = threadIdx.x; i < NT * 16 * D; i += DEC_THREADS) {
+    const int r = i / D, dim = i % D;
+    float x = 0.f;
+    if (r < R) {
+      const int tq = r / p.gqa, gi = r - tq * p.gqa;
+      x = p.q[((int64_t)tq * n_heads + h * p.gqa + gi) * D + dim] * p.qscale;
     }
-    if (valid[cur])
-      compute_tile<NT>(st, slots + cur * SLOT_BYTES, tok[cur], p.kv_len, min_limit, lane, r16, g,
-                       nib_mask);
+    q_lds[r * Q_LDS_STRIDE + dim] = (_Float16)x;
+  }
+  __syncthreads();
+  for (int i = 0; i < n_tiles; ++i) {
+    const bool more = i + 1 < n_tiles;
+    if (more) locate(i + 1, tok_n, valid_n, rec_n);
+    wait_loads<V_LOADS>();  // keys of tile i have landed (its values may still fly)
+    auto refill_keys = [&] {
+      if (more) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): key reads of this slot are done
+        issue_keys(slot, p.k_pool + rec_n * K_REC, valid_n ? c : 0, lane, r16, g);
+        wait_loads<K_LOADS>();  // values of tile i have landed
+      } else {
+        wait_loads<0>();
+      }
+    };
+    if (valid) {
+      compute_tile<NT>(st, slot, tok, p.kv_len, min_limit, lane, r16, g, nib_mask, refill_keys);
+    } else {
+      refill_keys();
+    }
+    if (more) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): value reads of this slot are done
+      issue_values(slot, p.v_pool + rec_n * V_REC, valid_n ? c : 0, lane, r16, g);
+    }
+    tok = tok_n;
+    rec = rec_n;
+    valid = valid_n;
   }
 
   // ---- combine the four wavefronts, write this split's partial --------------
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) st.l[nt] = wave_sum_xor_16_32(st.l[nt]);
-  __syncthreads();  // every wave is done with q_lds; smem becomes the combine buffer
+  __syncthreads();  // every wave is done with the LDS ring and q_lds
   if (g == 0) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -303,35 +358,37 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void decode_kernel(DecodeParams p) 
   }
   __syncthreads();
   constexpr int RS = 260;  // padded row stride of the combine buffer
-  float* buf = smem + (size_t)wave * NT * 16 * RS;
+  const int64_t rows_total = (int64_t)p.n_q_tok * n_heads;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int row = nt * 16 + r16;
-    float M = neg_inf();
+    {
+      const int row = nt * 16 + r16;
+      float M = neg_inf();
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][row]);
-    float L = 0.f;
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][row]);
+      float L = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
-      if (s_m[w][row] != neg_inf()) L += s_l[w][row] * __builtin_amdgcn_exp2f(s_m[w][row] - M);
-    const float f =
-        (L > 0.f && st.m[nt] != neg_inf()) ? __builtin_amdgcn_exp2f(st.m[nt] - M) / L : 0.f;
+      for (int w = 0; w < 4; ++w)
+        if (s_m[w][row] != neg_inf()) L += s_l[w][row] * __builtin_amdgcn_exp2f(s_m[w][row] - M);
+      const float f =
+          (L > 0.f && st.m[nt] != neg_inf()) ? __builtin_amdgcn_exp2f(st.m[nt] - M) / L : 0.f;
+      float* buf = smem + (size_t)wave * 16 * RS;
 #pragma unroll
-    for (int mt = 0; mt < 16; ++mt) {
-      const floatx4 v = st.o[nt][mt] * f;
-      *reinterpret_cast<floatx4*>(buf + row * RS + 16 * mt + 4 * g) = v;
+      for (int mt = 0; mt < 16; ++mt)
+        *reinterpret_cast<floatx4*>(buf + r16 * RS + 16 * mt + 4 * g) = st.o[nt][mt] * f;
     }
-  }
-  __syncthreads();
-  const int64_t rows_total = (int64_t)p.n_q_tok * n_heads;
-  const int dim = threadIdx.x;
-  for (int r = 0; r < R; ++r) {
-    const int tq = r / p.gqa, gi = r - tq * p.gqa;
-    const int64_t rowg = (int64_t)tq * n_heads + h * p.gqa + gi;
-    float v = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) v += smem[((size_t)w * NT * 16 + r) * RS + dim];
-    p.o_part[((int64_t)split * rows_total + rowg) * D + dim] = v;
+    __syncthreads();
+    const int dim = threadIdx.x;
+    for (int rr = 0; rr < 16; ++rr) {
+      const int r = nt * 16 + rr;
+      if (r >= R) break;
+      const int tq = r / p.gqa, gi = r - tq * p.gqa;
+      const int64_t rowg = (int64_t)tq * n_heads + h * p.gqa + gi;
+      const float v = (smem[(0 * 16 + rr) * RS + dim] + smem[(1 * 16 + rr) * RS + dim]) +
+                      (smem[(2 * 16 + rr) * RS + dim] + smem[(3 * 16 + rr) * RS + dim]);
+      p.o_part[((int64_t)split * rows_total + rowg) * D + dim] = v;
+    }
+    __syncthreads();
   }
   if (threadIdx.x < R) {
     const int r = threadIdx.x;
@@ -346,21 +403,21 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void decode_kernel(DecodeParams p) 
   }
 }
 
-template <int NT>
+template <int NT, int NSTAGE, int WPS>
 hipError_t launch_nt(const DecodeParams& p, hipStream_t stream) {
-  const size_t combine = sizeof(float) * 4 * NT * 16 * 260;
+  const size_t combine = sizeof(float) * 4 * 16 * 260;
   const size_t qbytes = ((NT * 16 * Q_LDS_STRIDE * 2) + 1023) / 1024 * 1024;
   const size_t loop = qbytes + 4 * NSTAGE * SLOT_BYTES;
   const size_t shmem = combine > loop ? combine : loop;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<NT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<NT, NSTAGE, WPS>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   dim3 grid((unsigned)p.n_splits, (unsigned)p.n_kv);
-  hipLaunchKernelGGL(decode_kernel<NT>, grid, dim3(DEC_THREADS), shmem, stream, p);
+  hipLaunchKernelGGL((decode_kernel<NT, NSTAGE, WPS>), grid, dim3(DEC_THREADS), shmem, stream, p);
   return hipGetLastError();
 }
 
@@ -368,8 +425,8 @@ hipError_t launch_nt(const DecodeParams& p, hipStream_t stream) {
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const int R = p.n_q_tok * p.gqa;
-  if (R <= 16) return launch_nt<1>(p, stream);
-  return launch_nt<2>(p, stream);
+  if (R <= 16) return launch_nt<1, 1, 2>(p, stream);
+  return launch_nt<2, 1, 2>(p, stream);
 }
 
 }  // namespace kvattn

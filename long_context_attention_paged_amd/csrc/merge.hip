@@ -2,7 +2,13 @@
 // announcement on wqu.guru, bullet "Online Log-Sum-Exp prefill & pipelined
 // prefetch": partial results over streamed pages are accumulated by online
 // LSE). Per row: M = max lse_s; L = M + ln sum exp(lse_s - M);
-// out = sum exp(lse_s - L) o_s in ascending s; all-(-inf) rows give 0, -inf.
+// out = sum exp(lse_s - L) o_s; all-(-inf) rows give 0, -inf.
+//
+// Generic head_dim: grid (rows, ceil(head_dim / 64)); 256 threads = 4 waves.
+// Each lane owns one output dim; the four waves take interleaved quarters of
+// the parts and their partial sums are added in a fixed order in LDS, so
+// results are deterministic. Part weights are computed once per workgroup
+// into LDS. head_dim 256 (the decode and prefill partials) uses a float4 path.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -10,11 +16,26 @@ namespace kvattn {
 namespace {
 
 constexpr int MERGE_THREADS = 256;
-constexpr int MERGE_WCHUNK = 1024;  // part weights staged in LDS per pass
+constexpr int MERGE_WCHUNK = 2048;  // part weights staged in LDS per pass
 
-// One workgroup per row; the threads stride over head_dim. Part weights are
-// computed once per row into LDS (in chunks), then every output element is a
-// fixed-order sum over the parts.
+__device__ __forceinline__ float block_max(float x, float* red) {
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  x = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return x;
+}
+
+__device__ __forceinline__ float block_sum(float x, float* red) {
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  x = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return x;
+}
+
 __global__ __launch_bounds__(MERGE_THREADS) void merge_kernel(int32_t n_parts, int64_t rows,
                                                               int32_t head_dim,
                                                               const float* __restrict__ o_parts,
@@ -22,59 +43,102 @@ __global__ __launch_bounds__(MERGE_THREADS) void merge_kernel(int32_t n_parts, i
                                                               float* __restrict__ out,
                                                               float* __restrict__ lse) {
   __shared__ float w[MERGE_WCHUNK];
-  __shared__ float red[MERGE_THREADS / 64];
+  __shared__ float red[4];
+  __shared__ float acc_lds[4][64];
   const int64_t r = blockIdx.x;
-  const int tid = threadIdx.x;
-  // M = max over parts
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int dim = blockIdx.y * 64 + lane;
+
   float m = neg_inf();
   for (int s = tid; s < n_parts; s += MERGE_THREADS) m = fmaxf(m, lse_parts[(int64_t)s * rows + r]);
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((tid & 63) == 0) red[tid >> 6] = m;
+  m = block_max(m, red);
+  if (m == neg_inf()) {  // uniform across the workgroup
+    if (wave == 0 && dim < head_dim) out[r * head_dim + dim] = 0.0f;
+    if (tid == 0 && blockIdx.y == 0) lse[r] = neg_inf();
+    return;
+  }
+  float se = 0.f;
+  for (int s = tid; s < n_parts; s += MERGE_THREADS) se += expf(lse_parts[(int64_t)s * rows + r] - m);
+  const float L = m + logf(block_sum(se, red));
+
+  float acc = 0.f;
+  for (int s0 = 0; s0 < n_parts; s0 += MERGE_WCHUNK) {
+    const int cnt = min(MERGE_WCHUNK, n_parts - s0);
+    for (int i = tid; i < cnt; i += MERGE_THREADS)
+      w[i] = expf(lse_parts[(int64_t)(s0 + i) * rows + r] - L);
+    __syncthreads();
+    if (dim < head_dim) {
+      const float* op = o_parts + ((int64_t)s0 * rows + r) * head_dim + dim;
+      const int64_t stride = rows * head_dim;
+#pragma unroll 4
+      for (int i = wave; i < cnt; i += 4) {
+        const float wi = w[i];
+        if (wi != 0.0f) acc += wi * op[(int64_t)i * stride];  // -inf parts hold no data
+      }
+    }
+    __syncthreads();
+  }
+  acc_lds[wave][lane] = acc;
   __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
+  if (wave == 0 && dim < head_dim)
+    out[r * head_dim + dim] = (acc_lds[0][lane] + acc_lds[1][lane]) + (acc_lds[2][lane] + acc_lds[3][lane]);
+  if (tid == 0 && blockIdx.y == 0) lse[r] = L;
+}
+
+// head_dim == 256: one workgroup per row; lane l owns dims 4l..4l+3 (one
+// float4), so each part's row is one contiguous 1 KB read per wave; waves take
+// parts w, w+4, ... with eight independent loads in flight per lane.
+__global__ __launch_bounds__(MERGE_THREADS) void merge256_kernel(int32_t n_parts, int64_t rows,
+                                                                 const float* __restrict__ o_parts,
+                                                                 const float* __restrict__ lse_parts,
+                                                                 float* __restrict__ out,
+                                                                 float* __restrict__ lse) {
+  __shared__ float w[MERGE_WCHUNK];
+  __shared__ float red[4];
+  __shared__ floatx4 acc_lds[4][64];
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  float m = neg_inf();
+  for (int s = tid; s < n_parts; s += MERGE_THREADS) m = fmaxf(m, lse_parts[(int64_t)s * rows + r]);
+  m = block_max(m, red);
   if (m == neg_inf()) {
-    for (int n = tid; n < head_dim; n += MERGE_THREADS) out[r * head_dim + n] = 0.0f;
+    if (wave == 0) reinterpret_cast<floatx4*>(out + r * 256)[lane] = floatx4{0.f, 0.f, 0.f, 0.f};
     if (tid == 0) lse[r] = neg_inf();
     return;
   }
-  // L = M + ln sum_s exp(lse_s - M), the sum taken in ascending s by thread 0
-  // over per-thread partial sums would reorder it; keep it serial and exact in
-  // order: each thread sums a contiguous run of parts, runs are then combined
-  // in thread order.
-  const int per = (n_parts + MERGE_THREADS - 1) / MERGE_THREADS;
-  float part = 0.0f;
-  for (int s = tid * per; s < n_parts && s < (tid + 1) * per; ++s)
-    part += __expf(lse_parts[(int64_t)s * rows + r] - m);
-  __shared__ float runs[MERGE_THREADS];
-  runs[tid] = part;
-  __syncthreads();
-  __shared__ float s_L;
-  if (tid == 0) {
-    float tot = 0.0f;
-    for (int i = 0; i < MERGE_THREADS; ++i) tot += runs[i];
-    s_L = m + __logf(tot);
-  }
-  __syncthreads();
-  const float L = s_L;
-  for (int n = tid; n < head_dim; n += MERGE_THREADS) out[r * head_dim + n] = 0.0f;
-  // accumulate in chunks of MERGE_WCHUNK parts
+  float se = 0.f;
+  for (int s = tid; s < n_parts; s += MERGE_THREADS) se += expf(lse_parts[(int64_t)s * rows + r] - m);
+  const float L = m + logf(block_sum(se, red));
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int64_t stride = rows * 256;
   for (int s0 = 0; s0 < n_parts; s0 += MERGE_WCHUNK) {
     const int cnt = min(MERGE_WCHUNK, n_parts - s0);
-    __syncthreads();
     for (int i = tid; i < cnt; i += MERGE_THREADS)
-      w[i] = __expf(lse_parts[(int64_t)(s0 + i) * rows + r] - L);
+      w[i] = expf(lse_parts[(int64_t)(s0 + i) * rows + r] - L);
     __syncthreads();
-    for (int n = tid; n < head_dim; n += MERGE_THREADS) {
-      float acc = out[r * head_dim + n];
-      const float* op = o_parts + ((int64_t)s0 * rows + r) * head_dim + n;
-      for (int i = 0; i < cnt; ++i) {
-        const float wi = w[i];
-        if (wi != 0.0f) acc += wi * op[(int64_t)i * rows * head_dim];
+    const floatx4* op = reinterpret_cast<const floatx4*>(o_parts + ((int64_t)s0 * rows + r) * 256) + lane;
+    int i = wave;
+    for (; i + 28 < cnt; i += 32) {
+      floatx4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = op[(int64_t)(i + 4 * u) * (stride / 4)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wu = w[i + 4 * u];
+        if (wu != 0.0f) acc += wu * v[u];  // a -inf part contributes nothing
       }
-      out[r * head_dim + n] = acc;
     }
+    for (; i < cnt; i += 4) {
+      const float wi = w[i];
+      if (wi != 0.0f) acc += wi * op[(int64_t)i * (stride / 4)];
+    }
+    __syncthreads();
   }
+  acc_lds[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0)
+    reinterpret_cast<floatx4*>(out + r * 256)[lane] =
+        (acc_lds[0][lane] + acc_lds[1][lane]) + (acc_lds[2][lane] + acc_lds[3][lane]);
   if (tid == 0) lse[r] = L;
 }
 
@@ -82,8 +146,15 @@ __global__ __launch_bounds__(MERGE_THREADS) void merge_kernel(int32_t n_parts, i
 
 hipError_t launch_merge(int32_t n_parts, int64_t rows, int32_t head_dim, const float* o_parts,
                         const float* lse_parts, float* out, float* lse, hipStream_t stream) {
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)rows), dim3(MERGE_THREADS), 0, stream, n_parts,
-                     rows, head_dim, o_parts, lse_parts, out, lse);
+  if (head_dim == 256 && (reinterpret_cast<uintptr_t>(o_parts) & 15) == 0 &&
+      (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+    hipLaunchKernelGGL(merge256_kernel, dim3((unsigned)rows), dim3(MERGE_THREADS), 0, stream,
+                       n_parts, rows, o_parts, lse_parts, out, lse);
+    return hipGetLastError();
+  }
+  dim3 grid((unsigned)rows, (unsigned)((head_dim + 63) / 64));
+  hipLaunchKernelGGL(merge_kernel, grid, dim3(MERGE_THREADS), 0, stream, n_parts, rows, head_dim,
+                     o_parts, lse_parts, out, lse);
   return hipGetLastError();
 }
 

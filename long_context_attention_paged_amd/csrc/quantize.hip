@@ -15,9 +15,10 @@
 namespace kvattn {
 namespace {
 
-// One workgroup per (32-token group, KV head); thread n owns dim n. A 32-dim
-// quantisation block is one half of a wavefront, so block reductions are
-// five xor-shuffles inside that half.
+// One workgroup per (32-token group, KV head); thread (u, b) = (tid/8, tid%8)
+// quantises the 32-dim block b of token slot u, so all tokens of the group
+// are processed at once and each block's reductions stay in one thread.
+// Value codes go through LDS to be packed into the group's V words.
 __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ k,
                                                        const float* __restrict__ v, int64_t pos0,
                                                        int32_t n_tok, int32_t n_kv,
@@ -27,7 +28,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
   __shared__ uint8_t vcodes[32][D];
   __shared__ uint16_t vscales[32][8];
 
-  const int n = threadIdx.x;
+  const int tid = threadIdx.x;
   const int h = blockIdx.y;
   const int64_t grp = pos0 / 32 + blockIdx.x;  // global 32-token group
   const int64_t gpos = grp * 32;
@@ -37,96 +38,110 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
   if (phys < 0 || phys >= n_phys) return;  // uniform across the workgroup
   uint8_t* krec = k_pool + ((int64_t)phys * n_kv + h) * K_REC;
   uint8_t* vrec = v_pool + ((int64_t)phys * n_kv + h) * V_REC;
-  const int lane = n & 63;
-  const int half_base = lane & 32;  // first lane of this 32-dim block in the wave
-  const int idx_in_block = lane & 31;
-
-  for (int u = 0; u < 32; ++u) {
-    const int64_t pos = gpos + u;
-    if (pos < pos0 || pos >= pos0 + n_tok) continue;  // uniform
-    const int64_t ti = pos - pos0;
-    const int t = c * 32 + u;  // slot in the page
-    const float xk = k[(ti * n_kv + h) * D + n];
-    const float xv = v[(ti * n_kv + h) * D + n];
-
-    // Q8_0: d = RN16(RN32(amax / 127)); codes with inv = RN32(1 / d).
-    float amax = fabsf(xk);
+  uint32_t* vwords = reinterpret_cast<uint32_t*>(vrec) + c * 1024;
+  const int64_t end = pos0 + n_tok;
+  const bool whole = gpos >= pos0 && gpos + 32 <= end;  // uniform
+  uint32_t old[4] = {0u, 0u, 0u, 0u};
+  if (!whole) {
 #pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-    const float d32 = amax / 127.0f;
-    const _Float16 d16 = (_Float16)d32;
+    for (int q = 0; q < 4; ++q) old[q] = vwords[tid + 256 * q];
+  }
+
+  const int u = tid >> 3, b = tid & 7;
+  const int64_t pos = gpos + u;
+  const int t = c * 32 + u;  // slot in the page
+  if (pos >= pos0 && pos < end) {
+    const int64_t row = ((pos - pos0) * n_kv + h) * D + 32 * b;
+    float x[32], y[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 a = reinterpret_cast<const float4*>(k + row)[i];
+      const float4 e = reinterpret_cast<const float4*>(v + row)[i];
+      x[4 * i] = a.x; x[4 * i + 1] = a.y; x[4 * i + 2] = a.z; x[4 * i + 3] = a.w;
+      y[4 * i] = e.x; y[4 * i + 1] = e.y; y[4 * i + 2] = e.z; y[4 * i + 3] = e.w;
+    }
+    // Q8_0: d = RN16(RN32(amax / 127)); codes with inv = RN32(1 / d).
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    const _Float16 d16 = (_Float16)(amax / 127.0f);
     const float d = (float)d16;
-    int8_t code8 = 0;
-    uint16_t bits8 = 0;
+    uint32_t kw[8];
     if (d != 0.0f) {
       const float inv = 1.0f / d;
-      float r = rintf(xk * inv);
-      r = fminf(fmaxf(r, -127.0f), 127.0f);
-      code8 = (int8_t)(int)r;
-      bits8 = __builtin_bit_cast(uint16_t, d16);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t wv = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float r = fminf(fmaxf(rintf(x[4 * i + j] * inv), -127.0f), 127.0f);
+          wv |= ((uint32_t)(int)r & 0xFFu) << (8 * j);
+        }
+        kw[i] = wv;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kw[i] = 0u;
     }
-    krec[t * D + n] = (uint8_t)code8;
-    if (idx_in_block == 0)
-      *reinterpret_cast<uint16_t*>(krec + K_SCALE_OFF + (t * 8 + n / 32) * 2) = bits8;
+    uint4* kdst = reinterpret_cast<uint4*>(krec + t * D + 32 * b);
+    kdst[0] = uint4{kw[0], kw[1], kw[2], kw[3]};
+    kdst[1] = uint4{kw[4], kw[5], kw[6], kw[7]};
+    *reinterpret_cast<uint16_t*>(krec + K_SCALE_OFF + (t * 8 + b) * 2) =
+        d != 0.0f ? __builtin_bit_cast(uint16_t, d16) : (uint16_t)0;
 
     // Q4_0: the lowest-index element of largest magnitude, signed, maps to -8.
-    float a = fabsf(xv);
-    int ai = idx_in_block;
+    float a = fabsf(y[0]), m = y[0];
 #pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) {
-      const float oa = __shfl_xor(a, o);
-      const int oi = __shfl_xor(ai, o);
-      if (oa > a || (oa == a && oi < ai)) {
-        a = oa;
-        ai = oi;
+    for (int i = 1; i < 32; ++i)
+      if (fabsf(y[i]) > a) {
+        a = fabsf(y[i]);
+        m = y[i];
       }
-    }
-    const float m = __shfl(xv, half_base + ai);
-    uint8_t code4 = 8;
     uint16_t bits4 = 0;
-    if (a != 0.0f) {
-      const float dv32 = (-m) / 8.0f;
-      const _Float16 dv16 = (_Float16)dv32;
-      const float dv = (float)dv16;
-      if (dv != 0.0f) {
-        const float inv = 1.0f / dv;
-        float r = rintf(xv * inv);
-        r = fminf(fmaxf(r, -8.0f), 7.0f);
-        code4 = (uint8_t)((int)r + 8);
-        bits4 = __builtin_bit_cast(uint16_t, dv16);
+    const _Float16 dv16 = (_Float16)((-m) / 8.0f);
+    const float dv = (float)dv16;
+    if (a != 0.0f && dv != 0.0f) {
+      const float inv = 1.0f / dv;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const float r = fminf(fmaxf(rintf(y[i] * inv), -8.0f), 7.0f);
+        vcodes[u][32 * b + i] = (uint8_t)((int)r + 8);
       }
+      bits4 = __builtin_bit_cast(uint16_t, dv16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) vcodes[u][32 * b + i] = 8;
     }
-    vcodes[u][n] = code4;
-    if (idx_in_block == 0) vscales[u][n / 32] = bits4;
+    vscales[u][b] = bits4;
   }
   __syncthreads();
 
   // V words of this 32-slot group: word (q, g, d, e) holds dim 16*(4q+e)+d for
   // slots 16*(j/4) + 4g + j%4; slots outside the written range keep their bits.
-  uint32_t* vwords = reinterpret_cast<uint32_t*>(vrec) + c * 1024;
-  for (int i = n; i < 1024; i += 256) {
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    const int i = tid + 256 * qq;
     const int e = i & 3, d = (i >> 2) & 15, g = (i >> 6) & 3, q = i >> 8;
     const int dim = 16 * (4 * q + e) + d;
-    const uint32_t old = vwords[i];
     uint32_t w = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int u = 16 * (j >> 2) + 4 * g + (j & 3);
+      const int uu = 16 * (j >> 2) + 4 * g + (j & 3);
       const int bit = 4 * (j >> 1) + 16 * (j & 1);
-      const int64_t pos = gpos + u;
-      const uint32_t nib = (pos >= pos0 && pos < pos0 + n_tok) ? (uint32_t)vcodes[u][dim]
-                                                                : (old >> bit) & 0xFu;
+      const int64_t p = gpos + uu;
+      const uint32_t nib = (whole || (p >= pos0 && p < end)) ? (uint32_t)vcodes[uu][dim]
+                                                               : (old[qq] >> bit) & 0xFu;
       w |= nib << bit;
     }
     vwords[i] = w;
   }
   {
-    const int i = n;  // 8 blocks x 4 lane groups x 8 slots = 256 scales
-    const int j = i & 7, g = (i >> 3) & 3, b = i >> 5;
-    const int u = 16 * (j >> 2) + 4 * g + (j & 3);
-    const int64_t pos = gpos + u;
-    if (pos >= pos0 && pos < pos0 + n_tok)
-      reinterpret_cast<uint16_t*>(vrec + V_SCALE_OFF)[c * 256 + i] = vscales[u][b];
+    const int i = tid;  // 8 blocks x 4 lane groups x 8 slots = 256 scales
+    const int j = i & 7, g = (i >> 3) & 3, bb = i >> 5;
+    const int uu = 16 * (j >> 2) + 4 * g + (j & 3);
+    const int64_t p = gpos + uu;
+    if (p >= pos0 && p < end)
+      reinterpret_cast<uint16_t*>(vrec + V_SCALE_OFF)[c * 256 + i] = vscales[uu][bb];
   }
 }
 
