@@ -235,6 +235,7 @@ __global__ __launch_bounds__(DEC_THREADS, WPS) void decode_kernel(DecodeParams p
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
   float* smem = reinterpret_cast<float*>(smem_raw);
   __shared__ float s_m[4][32], s_l[4][32];
+  __shared__ int s_rowg[32];
   const int h = blockIdx.y, split = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -305,17 +306,34 @@ __global__ __launch_bounds__(DEC_THREADS, WPS) void decode_kernel(DecodeParams p
     issue_keys(slot, p.k_pool + rec * K_REC, valid ? c : 0, lane, r16, g);
     issue_values(slot, p.v_pool + rec * V_REC, valid ? c : 0, lane, r16, g);
   }
-  // the first tile is in flight: now stage q' rows (f16) into LDS, shared by
-  // the four waves (padding rows are zero)
-  // q' rows (f16) into LDS, shared by the four waves; padding rows are zero
-  for (int i = threadIdx.x; i < NT * 16 * D; i += DEC_THREADS) {
-    const int r = i / D, dim = i % D;
-    float x = 0.f;
-    if (r < R) {
-      const int tq = r / p.gqa, gi = r - tq * p.gqa;
-      x = p.q[((int64_t)tq * n_heads + h * p.gqa + gi) * D + dim] * p.qscale;
+  // The first tile is in flight: stage q' rows (f16) into LDS, shared by the
+  // four waves (padding rows are zero). Row r of this KV head is query token
+  // r / gqa, query head h*gqa + r % gqa; its global row goes to s_rowg.
+  if (threadIdx.x < NT * 16) {
+    const int r = threadIdx.x;
+    const int tq = r / p.gqa, gi = r - tq * p.gqa;
+    s_rowg[r] = r < R ? tq * n_heads + h * p.gqa + gi : -1;
+  }
+  __syncthreads();
+  {
+    constexpr int PER = NT * 16 * (D / 4) / DEC_THREADS;  // float4s per thread
+    float4 qv[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int idx = threadIdx.x + DEC_THREADS * k;
+      const int r = idx >> 6, d4 = idx & 63;
+      const int rowg = s_rowg[r];
+      qv[k] = rowg >= 0 ? reinterpret_cast<const float4*>(p.q + (int64_t)rowg * D)[d4]
+                        : float4{0.f, 0.f, 0.f, 0.f};
     }
-    q_lds[r * Q_LDS_STRIDE + dim] = (_Float16)x;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int idx = threadIdx.x + DEC_THREADS * k;
+      const int r = idx >> 6, d4 = idx & 63;
+      const half2_t lo = {(_Float16)(qv[k].x * p.qscale), (_Float16)(qv[k].y * p.qscale)};
+      const half2_t hi = {(_Float16)(qv[k].z * p.qscale), (_Float16)(qv[k].w * p.qscale)};
+      *reinterpret_cast<uint2*>(q_lds + r * Q_LDS_STRIDE + 4 * d4) = uint2{as_u32(lo), as_u32(hi)};
+    }
   }
   __syncthreads();
   for (int i = 0; i < n_tiles; ++i) {
@@ -378,22 +396,27 @@ __global__ __launch_bounds__(DEC_THREADS, WPS) void decode_kernel(DecodeParams p
         *reinterpret_cast<floatx4*>(buf + r16 * RS + 16 * mt + 4 * g) = st.o[nt][mt] * f;
     }
     __syncthreads();
-    const int dim = threadIdx.x;
-    for (int rr = 0; rr < 16; ++rr) {
-      const int r = nt * 16 + rr;
-      if (r >= R) break;
-      const int tq = r / p.gqa, gi = r - tq * p.gqa;
-      const int64_t rowg = (int64_t)tq * n_heads + h * p.gqa + gi;
-      const float v = (smem[(0 * 16 + rr) * RS + dim] + smem[(1 * 16 + rr) * RS + dim]) +
-                      (smem[(2 * 16 + rr) * RS + dim] + smem[(3 * 16 + rr) * RS + dim]);
-      p.o_part[((int64_t)split * rows_total + rowg) * D + dim] = v;
+    // 16 rows x 64 float4 columns: four per thread, the four waves' values
+    // added in a fixed order
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int idx = threadIdx.x + DEC_THREADS * k;
+      const int rr = idx >> 6, c4 = idx & 63;
+      const int rowg = s_rowg[nt * 16 + rr];
+      if (rowg >= 0) {
+        const floatx4 a = *reinterpret_cast<const floatx4*>(smem + (0 * 16 + rr) * RS + 4 * c4);
+        const floatx4 b = *reinterpret_cast<const floatx4*>(smem + (1 * 16 + rr) * RS + 4 * c4);
+        const floatx4 c2 = *reinterpret_cast<const floatx4*>(smem + (2 * 16 + rr) * RS + 4 * c4);
+        const floatx4 d = *reinterpret_cast<const floatx4*>(smem + (3 * 16 + rr) * RS + 4 * c4);
+        reinterpret_cast<floatx4*>(p.o_part + ((int64_t)split * rows_total + rowg) * D)[c4] =
+            (a + b) + (c2 + d);
+      }
     }
     __syncthreads();
   }
   if (threadIdx.x < R) {
     const int r = threadIdx.x;
-    const int tq = r / p.gqa, gi = r - tq * p.gqa;
-    const int64_t rowg = (int64_t)tq * n_heads + h * p.gqa + gi;
+    const int64_t rowg = s_rowg[r];
     float M = neg_inf();
     for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][r]);
     float L = 0.f;
