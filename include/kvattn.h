@@ -120,7 +120,8 @@ typedef struct kvattn_geom {
   int32_t gqa;          /* query heads per KV head, >= 1 */
   int32_t head_dim;     /* 256 */
   int32_t page_tokens;  /* 128 */
-  int32_t n_phys_pages; /* physical pages in k_pool / v_pool, >= 1 */
+  int32_t n_phys_pages; /* physical pages in k_pool / v_pool, >= 1;
+                          n_phys_pages * n_kv_heads <= INT32_MAX */
 } kvattn_geom;
 
 /* Human-readable name of a status code (static storage, never NULL). */

@@ -15,10 +15,11 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvattn.so")
 SOURCES = ["api.hip", "quantize.hip", "select.hip", "merge.hip", "decode.hip", "prefill.hip"]
-# The decode kernel keeps its 64-128 loop-carried accumulators in VGPRs next
-# to LDS-staged operands; without this the allocator splits them between
-# VGPRs and AGPRs and copies every accumulator on each loop iteration.
-EXTRA_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# The decode and prefill kernels keep their 64-128 loop-carried accumulators
+# in VGPRs next to LDS-staged operands; without this the allocator splits them
+# between VGPRs and AGPRs and copies every accumulator on each loop iteration.
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+EXTRA_FLAGS = {"decode.hip": _VGPR_FORM, "prefill.hip": _VGPR_FORM}
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

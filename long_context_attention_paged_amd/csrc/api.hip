@@ -56,6 +56,7 @@ kvattn_status check_geom(const kvattn_geom* g) {
   if (g->head_dim != KVATTN_HEAD_DIM || g->page_tokens != KVATTN_PAGE_TOKENS)
     return KVATTN_E_UNSUPPORTED;
   if ((int64_t)g->n_kv_heads * g->gqa > (1 << 20)) return KVATTN_E_INVALID;
+  if ((int64_t)g->n_phys_pages * g->n_kv_heads > INT32_MAX) return KVATTN_E_INVALID;  // record index
   return KVATTN_OK;
 }
 

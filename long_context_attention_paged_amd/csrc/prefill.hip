@@ -7,115 +7,234 @@
 // library's.
 //
 // Grid (page groups, query tiles, KV heads); 256 threads = 4 wavefronts; a
-// query tile is 256 rows (row = token * gqa + group member), 64 per wave.
-// Each workgroup walks the pages of its group in 32-token sub-tiles: all 256
-// threads dequantise the sub-tile into LDS as f16 (keys [token][dim], values
-// [dim][slot] in the pool's slot order, value scale applied), then every wave
+// query tile is 128 rows (row = token * gqa + group member), 32 per wave.
+// Each workgroup walks the pages of its group in 32-token sub-tiles. The
+// quantised bytes stream into an LDS ring by direct global->LDS loads, two
+// sub-tiles ahead; each wave loads and dequantises one quarter of a sub-tile
+// (8 key rows, 64 value dims) into an f16 stage (keys [token][dim], values
+// [dim][slot] in the pool's slot order, value scale applied). Every wave
 // computes S^T = Khat . Q'^T and O^T += Vhat^T . P'^T with
-// v_mfma_f32_16x16x32_f16 (rows in the N dimension, four N-tiles), with the
-// online softmax in base 2 in between. Sub-tiles are double-buffered: the
-// global loads of the next sub-tile are in flight while the current one is
-// multiplied. Each group writes normalised partial (o, lse) per row; the LSE
-// merge combines the groups. Group g's workgroups for every query tile share
-// an XCD (group count is kept a multiple of 8 where possible), so the
-// dequantised pages they all read come from the same L2.
+// v_mfma_f32_16x16x32_f16 (rows in the N dimension, two N-tiles), with the
+// online softmax in base 2 in between; the dequantisation of the next
+// sub-tile is placed between the two products, so it overlaps the matrix
+// cores. Each group writes a normalised partial (o, lse) per row; the LSE
+// merge combines the groups.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace kvattn {
 namespace {
 
-constexpr int PF_THREADS = 256;
-constexpr int PF_NT = 2;                        // 16-row N-tiles per wave
-constexpr int PF_ROWS = 4 * 16 * PF_NT;         // rows per workgroup
+constexpr int PF_PRODUCERS = 4;                 // waves that stream and dequantise
+constexpr int PF_CONSUMERS = 4;                 // waves that multiply
+constexpr int PF_THREADS = 64 * (PF_PRODUCERS + PF_CONSUMERS);
+constexpr int PF_NT = 2;                        // 16-row N-tiles per consumer wave
+constexpr int PF_ROWS = PF_CONSUMERS * 16 * PF_NT;  // rows per workgroup
 constexpr int K_LDS_STRIDE = 264;               // halves per key row (256 + pad)
 constexpr int V_LDS_STRIDE = 40;                // halves per value dim row (32 + pad)
 constexpr int K_LDS_HALVES = 32 * K_LDS_STRIDE;
 constexpr int V_LDS_HALVES = D * V_LDS_STRIDE;
-constexpr int STAGE_HALVES = K_LDS_HALVES + V_LDS_HALVES;
+constexpr int STAGE_HALVES = K_LDS_HALVES + V_LDS_HALVES;  // one f16 sub-tile
 constexpr float PF_RESCALE_MARGIN = 8.0f;
+// Raw (quantised) sub-tile share of one producer wave: 8 key rows (2 KB), a
+// quarter of the value words (1 KB), 128 B of key scales, 128 B of value
+// scales. Two slots: sub-tile i+2 refills the slot sub-tile i came from.
+constexpr int RAW_WAVE = 2048 + 1024 + 256;
+constexpr int RAW_STAGE = PF_PRODUCERS * RAW_WAVE;
+constexpr int RAW_DEPTH = 2;
+constexpr int RAW_LOADS = 4;                    // direct loads per producer wave per sub-tile
 
-struct Staged {
-  u32x4 k0, k1;     // 32 key codes: token u = tid/8, block tid%8
-  uint32_t ks;      // that block's scale (low half)
-  u32x4 v;          // four value words: dims 16(4q+e)+d, lane group g
-  u32x4 vs0, vs1;   // value scales of blocks 2q and 2q+1 for the 8 slots of g
-};
+typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ void stage_load(Staged& s, const uint8_t* krec, const uint8_t* vrec,
-                                           int c, int tid) {
-  const int u = tid >> 3, b = tid & 7;
-  const uint8_t* kp = krec + (c * 32 + u) * D + 32 * b;
-  s.k0 = load16_nt(kp);
-  s.k1 = load16_nt(kp + 16);
-  s.ks = *reinterpret_cast<const uint16_t*>(krec + K_SCALE_OFF + ((c * 32 + u) * 8 + b) * 2);
-  s.v = load16_nt(vrec + (c * 1024 + tid * 4) * 4);
-  const int g = (tid >> 4) & 3, q = tid >> 6;
-  s.vs0 = load16_nt(vrec + V_SCALE_OFF + (((c * 8 + 2 * q) * 4 + g) * 8) * 2);
-  s.vs1 = load16_nt(vrec + V_SCALE_OFF + (((c * 8 + 2 * q + 1) * 4 + g) * 8) * 2);
+__device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* lds_dst) {
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (lds_void*)(lds_dst), 16,
+                                   0, 0);
 }
 
-// Dequantise the staged registers into one LDS stage. Slots at or past
-// kv_len (unwritten bytes) are stored as zeros.
-__device__ __forceinline__ void stage_store(const Staged& s, _Float16* stage, int tid,
-                                            int64_t tok0, int64_t kv_len) {
-  const int u = tid >> 3, b = tid & 7;
-  _Float16* krow = stage + u * K_LDS_STRIDE + 32 * b;
-  if (tok0 + u < kv_len) {
-    const half2_t d2 = as_h2(s.ks | (s.ks << 16));
-    *reinterpret_cast<half8_t*>(krow + 0) = k_codes_to_f16(s.k0.x, s.k0.y, d2);
-    *reinterpret_cast<half8_t*>(krow + 8) = k_codes_to_f16(s.k0.z, s.k0.w, d2);
-    *reinterpret_cast<half8_t*>(krow + 16) = k_codes_to_f16(s.k1.x, s.k1.y, d2);
-    *reinterpret_cast<half8_t*>(krow + 24) = k_codes_to_f16(s.k1.z, s.k1.w, d2);
-  } else {
-    const half8_t z = {};
-    *reinterpret_cast<half8_t*>(krow + 0) = z;
-    *reinterpret_cast<half8_t*>(krow + 8) = z;
-    *reinterpret_cast<half8_t*>(krow + 16) = z;
-    *reinterpret_cast<half8_t*>(krow + 24) = z;
+// Workgroup barrier that waits for this wave's LDS traffic only: the raw tile
+// loads still in flight must not be drained (a plain __syncthreads also
+// waits for every outstanding global load).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  __asm__ __volatile__("" ::: "memory");
+}
+
+// Producer wave w's share of sub-tile (group c of a page): key rows
+// 8w..8w+7 of the group, the value words with q = w (dims 16*(4w+e)+d), and
+// the scales both need.
+__device__ __forceinline__ void issue_raw(uint8_t* raw, const uint8_t* krec, const uint8_t* vrec,
+                                          int c, int w, int lane) {
+  const uint8_t* kc = krec + (c * 32 + 8 * w) * D;
+  dma16(kc + lane * 16, raw);
+  dma16(kc + 1024 + lane * 16, raw + 1024);
+  dma16(vrec + (c * 1024 + w * 256) * 4 + lane * 16, raw + 2048);
+  if (lane < 16) {
+    const uint8_t* src = lane < 8 ? krec + K_SCALE_OFF + ((c * 32 + 8 * w) * 8) * 2 + lane * 16
+                                  : vrec + V_SCALE_OFF + ((c * 8 + 2 * w) * 4) * 16 + (lane - 8) * 16;
+    dma16(src, raw + 3072);
   }
-  const int d = tid & 15, g = (tid >> 4) & 3, q = tid >> 6;
-  uint32_t mk[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int j0 = 2 * p, j1 = 2 * p + 1;
-    const int u0 = 16 * (j0 >> 2) + 4 * g + (j0 & 3);
-    const int u1 = 16 * (j1 >> 2) + 4 * g + (j1 & 3);
-    mk[p] = (tok0 + u0 < kv_len ? 0x0000FFFFu : 0u) | (tok0 + u1 < kv_len ? 0xFFFF0000u : 0u);
+}
+
+// Dequantise producer wave w's raw share into an f16 stage. Only the first
+// n_live slots of the sub-tile hold data (later slots are unwritten bytes
+// past kv_len; n_live is 0 for a page the table does not map): their keys
+// and value scales are replaced by zeros.
+// Keys, lane l: row 8w + l/8, block l%8 (32 codes).
+// Values, lane l: word quad l (4 dims, 8 slots each).
+__device__ __forceinline__ void dequant_raw(const uint8_t* raw, _Float16* stage, int w, int lane,
+                                            int n_live) {
+  {
+    const int u = 8 * w + (lane >> 3), b = lane & 7;
+    const u32x4 k0 = *reinterpret_cast<const u32x4*>(raw + (lane >> 3) * D + 32 * b);
+    const u32x4 k1 = *reinterpret_cast<const u32x4*>(raw + (lane >> 3) * D + 32 * b + 16);
+    const uint32_t ks = *reinterpret_cast<const uint16_t*>(raw + 3072 + (lane >> 3) * 16 + 2 * b);
+    const half2_t d2 = as_h2(u < n_live ? (ks | (ks << 16)) : 0u);  // zero scale -> zeros
+    _Float16* krow = stage + u * K_LDS_STRIDE + 32 * b;
+    *reinterpret_cast<half8_t*>(krow + 0) = k_codes_to_f16(k0.x, k0.y, d2);
+    *reinterpret_cast<half8_t*>(krow + 8) = k_codes_to_f16(k0.z, k0.w, d2);
+    *reinterpret_cast<half8_t*>(krow + 16) = k_codes_to_f16(k1.x, k1.y, d2);
+    *reinterpret_cast<half8_t*>(krow + 24) = k_codes_to_f16(k1.z, k1.w, d2);
   }
-  _Float16* vbase = stage + K_LDS_HALVES;
-  const uint32_t words[4] = {s.v.x, s.v.y, s.v.z, s.v.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int dim = 16 * (4 * q + e) + d;
-    const u32x4 sc = (e < 2 ? s.vs0 : s.vs1);
-    const uint32_t scw[4] = {sc.x & mk[0], sc.y & mk[1], sc.z & mk[2], sc.w & mk[3]};
-    half8_t val = v_codes_to_f16(words[e]);
+  {
+    const int d = lane & 15, g = lane >> 4;
+    const u32x4 words = *reinterpret_cast<const u32x4*>(raw + 2048 + lane * 16);
+    uint32_t mk[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const half2_t pr = {val[2 * p], val[2 * p + 1]};
-      const half2_t r = pr * as_h2(scw[p]);
-      val[2 * p] = r[0];
-      val[2 * p + 1] = r[1];
+      const int u0 = 16 * ((2 * p) >> 2) + 4 * g + ((2 * p) & 3);
+      const int u1 = 16 * ((2 * p + 1) >> 2) + 4 * g + ((2 * p + 1) & 3);
+      mk[p] = (u0 < n_live ? 0x0000FFFFu : 0u) | (u1 < n_live ? 0xFFFF0000u : 0u);
     }
-    *reinterpret_cast<half8_t*>(vbase + dim * V_LDS_STRIDE + 8 * g) = val;
+    _Float16* vbase = stage + K_LDS_HALVES;
+    const uint32_t wv[4] = {words.x, words.y, words.z, words.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int dim = 16 * (4 * w + e) + d;
+      // value scales of block 2w + e/2 for lane group g: 16 bytes
+      const u32x4 sc = *reinterpret_cast<const u32x4*>(raw + 3072 + 128 + ((e >> 1) * 4 + g) * 16);
+      const uint32_t scw[4] = {sc.x & mk[0], sc.y & mk[1], sc.z & mk[2], sc.w & mk[3]};
+      half8_t val = v_codes_to_f16(wv[e]);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const half2_t pr = {val[2 * p], val[2 * p + 1]};
+        const half2_t r = pr * as_h2(scw[p]);
+        val[2 * p] = r[0];
+        val[2 * p + 1] = r[1];
+      }
+      *reinterpret_cast<half8_t*>(vbase + dim * V_LDS_STRIDE + 8 * g) = val;
+    }
   }
 }
 
-__global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p) {
-  extern __shared__ _Float16 lds[];  // two stages
+struct SubTiles {
+  int64_t pg0, pg1;  // this group's logical pages [pg0, pg1)
+  int n_sub;         // 32-token sub-tiles to visit
+};
+
+// Page records of a group, 64 pages at a time in one VGPR (lane i holds the
+// record index of page pg0 + first + i, or -1 when the table does not map
+// it), read back with readlane: the loops then issue no page-table loads of
+// their own, whose waits would also drain the raw tile stream.
+struct PageWindow {
+  int64_t first;
+  int32_t rec;
+  __device__ __forceinline__ void load(const PrefillParams& p, const SubTiles& t, int64_t f,
+                                       int h, int lane) {
+    first = f;
+    const int64_t lp = t.pg0 + f + lane;
+    int32_t r = -1;
+    if (lp < t.pg1) {
+      const int32_t ph = p.page_table[lp];
+      if (ph >= 0 && ph < p.n_phys) r = ph * p.n_kv + h;
+    }
+    rec = r;
+  }
+  // record of sub-tile sub's page (-1: unmapped); the page must be in the window
+  __device__ __forceinline__ int32_t record(int sub) const {
+    return __builtin_amdgcn_readlane(rec, (int)((sub >> 2) - first));
+  }
+};
+
+__global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
+  _Float16* lds = reinterpret_cast<_Float16*>(lds_raw);               // two f16 stages
+  uint8_t* raw_ring = lds_raw + 2 * STAGE_HALVES * sizeof(_Float16);  // RAW_DEPTH raw stages
   const int group = blockIdx.x, qtile = blockIdx.y, h = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int r16 = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n_heads = p.n_kv * p.gqa;
   const int64_t rows_head = (int64_t)p.chunk * p.gqa;
   const int64_t kv_len = p.pos0 + p.chunk;
   const int64_t n_pages = (kv_len + PAGE - 1) / PAGE;
-  const int64_t row0 = (int64_t)qtile * PF_ROWS + wave * 16 * PF_NT;  // this wave's first row
 
-  // ---- query operands, row limits ------------------------------------------
+  // ---- this group's sub-tiles (32 tokens each) ------------------------------
+  const int64_t tile_last_row = ((int64_t)qtile + 1) * PF_ROWS - 1 < rows_head
+                                    ? ((int64_t)qtile + 1) * PF_ROWS - 1
+                                    : rows_head - 1;
+  const int64_t wg_max_pos = p.pos0 + tile_last_row / p.gqa;  // last key any row here sees
+  SubTiles t;
+  t.pg0 = n_pages * group / p.n_groups;
+  t.pg1 = n_pages * (group + 1) / p.n_groups;
+  if (t.pg1 > wg_max_pos / PAGE + 1) t.pg1 = wg_max_pos / PAGE + 1;
+  t.n_sub = t.pg1 > t.pg0 ? (int)((t.pg1 - t.pg0) * 4) : 0;
+  if (t.n_sub > 0) {  // drop trailing 32-token groups no row sees
+    const int64_t last_tok0 = t.pg0 * PAGE + (int64_t)(t.n_sub - 1) * 32;
+    if (last_tok0 > wg_max_pos) t.n_sub -= (int)((last_tok0 - wg_max_pos + 31) / 32);
+  }
+  const int n_sub = t.n_sub;
+  PageWindow win;
+  win.load(p, t, 0, h, lane);
+
+  if (wave < PF_PRODUCERS) {
+    // ======== producer: stream raw sub-tiles, dequantise into f16 stages ====
+    const int w = wave;
+    auto slot = [&](int sub) { return raw_ring + (sub % RAW_DEPTH) * RAW_STAGE + w * RAW_WAVE; };
+    auto issue = [&](int sub) {
+      const int32_t r = win.record(sub);
+      const int64_t rec = r >= 0 ? r : 0;  // unmapped pages load record 0, then zero it
+      issue_raw(slot(sub), p.k_pool + rec * K_REC, p.v_pool + rec * V_REC, r >= 0 ? (sub & 3) : 0,
+                w, lane);
+    };
+    auto dequant = [&](int sub) {
+      const int64_t left = kv_len - (t.pg0 * PAGE + (int64_t)sub * 32);
+      const int n_live = win.record(sub) < 0 ? 0 : left >= 32 ? 32 : (int)left;
+      dequant_raw(slot(sub), lds + (sub & 1) * STAGE_HALVES, w, lane, n_live);
+    };
+    if (n_sub > 0) issue(0);
+    if (n_sub > 1) issue(1);
+    if (n_sub > 0) {
+      if (n_sub > 1) wait_loads<RAW_LOADS>(); else wait_loads<0>();
+      dequant(0);
+    }
+    lds_barrier();
+    for (int sub = 0; sub < n_sub; ++sub) {
+      if (((sub + 2) >> 2) >= win.first + 64) {  // sub + 1 and sub + 2 stay in the window
+        wait_loads<0>();
+        win.load(p, t, (sub + 1) >> 2, h, lane);
+      }
+      if (sub + 2 < n_sub) issue(sub + 2);
+      if (sub + 1 < n_sub) {
+        if (sub + 2 < n_sub) wait_loads<RAW_LOADS>(); else wait_loads<0>();
+        dequant(sub + 1);
+      }
+      lds_barrier();
+    }
+    return;
+  }
+
+  // ======== consumer: S^T = Khat . Q'^T, online softmax, O^T += Vhat^T . P'^T
+  const int cw = wave - PF_PRODUCERS;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int64_t row0 = (int64_t)qtile * PF_ROWS + cw * 16 * PF_NT;  // this wave's first row
   half8_t qb[PF_NT][8];
-  int64_t limit[PF_NT];
+  int32_t limit[PF_NT];  // last visible key of the row, relative to pos0
 #pragma unroll
   for (int nt = 0; nt < PF_NT; ++nt) {
     const int64_t r = row0 + nt * 16 + r16;
@@ -132,11 +251,11 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
                              (_Float16)(b.x * p.qscale), (_Float16)(b.y * p.qscale),
                              (_Float16)(b.z * p.qscale), (_Float16)(b.w * p.qscale)};
       }
-      limit[nt] = p.pos0 + tq;
+      limit[nt] = (int32_t)tq;
     } else {
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) qb[nt][ks] = half8_t{};
-      limit[nt] = -1;
+      limit[nt] = -64;  // below every key the mask is applied to
     }
   }
   // wave-uniform visibility bounds of this wave's rows
@@ -145,11 +264,6 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
   const int64_t wave_min_limit = p.pos0 + wr_lo / p.gqa;
   const int64_t wave_max_limit = p.pos0 + wr_hi / p.gqa;
   const bool wave_active = row0 < rows_head;
-  // workgroup-wide last visible position: skip sub-tiles beyond it
-  const int64_t tile_last_row = ((int64_t)qtile + 1) * PF_ROWS - 1 < rows_head
-                                    ? ((int64_t)qtile + 1) * PF_ROWS - 1
-                                    : rows_head - 1;
-  const int64_t wg_max_pos = p.pos0 + tile_last_row / p.gqa;
 
   float mrow[PF_NT], lrow[PF_NT];
   floatx4 o[PF_NT][16];
@@ -160,54 +274,15 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
 #pragma unroll
     for (int mt = 0; mt < 16; ++mt) o[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
+  lds_barrier();
 
-  // ---- this group's sub-tiles -----------------------------------------------
-  const int64_t pg0 = n_pages * group / p.n_groups;
-  int64_t pg1 = n_pages * (group + 1) / p.n_groups;
-  const int64_t last_page = wg_max_pos / PAGE;
-  if (pg1 > last_page + 1) pg1 = last_page + 1;
-  const int64_t n_sub = pg1 > pg0 ? (pg1 - pg0) * 4 : 0;
-
-  auto rec_of = [&](int64_t sub, const uint8_t*& krec, const uint8_t*& vrec, int64_t& tok0,
-                    int& c) -> bool {
-    const int64_t lp = pg0 + (sub >> 2);
-    c = (int)(sub & 3);
-    tok0 = lp * PAGE + c * 32;
-    const int32_t ph = p.page_table[lp];
-    if (ph < 0 || ph >= p.n_phys) return false;
-    krec = p.k_pool + ((int64_t)ph * p.n_kv + h) * K_REC;
-    vrec = p.v_pool + ((int64_t)ph * p.n_kv + h) * V_REC;
-    return true;
-  };
-
-  Staged stg;
-  int64_t cur_tok0 = 0, nxt_tok0 = 0;
-  bool cur_ok = false, nxt_ok = false;
-  if (n_sub > 0) {
-    const uint8_t *kr, *vr;
-    int c;
-    cur_ok = rec_of(0, kr, vr, cur_tok0, c);
-    if (cur_ok) {
-      stage_load(stg, kr, vr, c, tid);
-      stage_store(stg, lds, tid, cur_tok0, kv_len);
-    }
-  }
-  __syncthreads();
-
-  for (int64_t sub = 0; sub < n_sub; ++sub) {
-    _Float16* stage = lds + (sub & 1) * STAGE_HALVES;
-    _Float16* next_stage = lds + ((sub + 1) & 1) * STAGE_HALVES;
-    const bool has_next = sub + 1 < n_sub;
-    if (has_next) {
-      const uint8_t *kr, *vr;
-      int c;
-      nxt_ok = rec_of(sub + 1, kr, vr, nxt_tok0, c);
-      if (nxt_ok && nxt_tok0 <= wg_max_pos) stage_load(stg, kr, vr, c, tid);
-    }
-    // ---- compute on the current stage (waves whose rows see any of it) ----
-    if (cur_ok && wave_active && cur_tok0 <= wave_max_limit) {
-      const _Float16* ks_lds = stage;
-      const _Float16* vs_lds = stage + K_LDS_HALVES;
+  for (int sub = 0; sub < n_sub; ++sub) {
+    if ((sub >> 2) >= win.first + 64) win.load(p, t, sub >> 2, h, lane);
+    const _Float16* ks_lds = lds + (sub & 1) * STAGE_HALVES;
+    const _Float16* vs_lds = ks_lds + K_LDS_HALVES;
+    const int64_t cur_tok0 = t.pg0 * PAGE + (int64_t)sub * 32;
+    const bool compute = win.record(sub) >= 0 && wave_active && cur_tok0 <= wave_max_limit;
+    if (compute) {
       floatx4 s[2][PF_NT];
 #pragma unroll
       for (int m = 0; m < 2; ++m)
@@ -223,14 +298,15 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
           for (int nt = 0; nt < PF_NT; ++nt) s[m][nt] = mfma16(a, qb[nt][ks], s[m][nt]);
         }
       }
-      if (cur_tok0 + 31 > wave_min_limit) {
+      if (cur_tok0 + 31 > wave_min_limit) {  // then cur_tok0 - pos0 > -32
+        const int32_t rel = (int32_t)(cur_tok0 - p.pos0) + 4 * g;
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
           for (int nt = 0; nt < PF_NT; ++nt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              if (cur_tok0 + 16 * m + 4 * g + i > limit[nt]) s[m][nt][i] = neg_inf();
+              if (rel + 16 * m + i > limit[nt]) s[m][nt][i] = neg_inf();
       }
       half8_t pb[PF_NT];
 #pragma unroll
@@ -269,11 +345,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
         for (int nt = 0; nt < PF_NT; ++nt) o[nt][mt] = mfma16(a, pb[nt], o[nt][mt]);
       }
     }
-    if (has_next && nxt_ok && nxt_tok0 <= wg_max_pos)
-      stage_store(stg, next_stage, tid, nxt_tok0, kv_len);
-    cur_ok = has_next && nxt_ok && nxt_tok0 <= wg_max_pos;
-    cur_tok0 = nxt_tok0;
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---- write this group's normalised partial ------------------------------
@@ -303,7 +375,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
 int32_t prefill_rows_per_tile() { return PF_ROWS; }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-  const size_t shmem = sizeof(_Float16) * 2 * STAGE_HALVES;
+  const size_t shmem = sizeof(_Float16) * 2 * STAGE_HALVES + RAW_DEPTH * RAW_STAGE;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel),
