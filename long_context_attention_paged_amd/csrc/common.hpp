@@ -88,15 +88,32 @@ __device__ __forceinline__ uint32_t load4_nt(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
 }
 
+// Reductions over the lanes l, l^16, l^32, l^48 (the four 16-lane rows of a
+// wave), with the gfx950 row-swap permutes. v_permlane16_swap of a value
+// with itself yields rows (0,0,2,2) in one operand and (1,1,3,3) in the
+// other; v_permlane32_swap yields (0,1,0,1) and (2,3,2,3). Combining the two
+// halves each time reduces across rows. (The result elements are copied to
+// scalars before any bit cast: a bit cast applied to an element of the
+// returned pair reads element 0 whatever the index.)
+__device__ __forceinline__ float row_swap_combine16(float x, bool is_max) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const uint32_t a0 = a[0], a1 = a[1];
+  const float p = __builtin_bit_cast(float, a0), q = __builtin_bit_cast(float, a1);
+  return is_max ? fmaxf(p, q) : p + q;
+}
+__device__ __forceinline__ float row_swap_combine32(float x, bool is_max) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const uint32_t a0 = a[0], a1 = a[1];
+  const float p = __builtin_bit_cast(float, a0), q = __builtin_bit_cast(float, a1);
+  return is_max ? fmaxf(p, q) : p + q;
+}
 __device__ __forceinline__ float wave_max_xor_16_32(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  return row_swap_combine32(row_swap_combine16(x, true), true);
 }
 __device__ __forceinline__ float wave_sum_xor_16_32(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  return row_swap_combine32(row_swap_combine16(x, false), false);
 }
 
 }  // namespace kvattn

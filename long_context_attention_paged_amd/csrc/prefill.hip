@@ -68,12 +68,14 @@ __device__ __forceinline__ void wait_loads() {
 
 // Producer wave w's share of sub-tile (group c of a page): key rows
 // 8w..8w+7 of the group, the value words with q = w (dims 16*(4w+e)+d), and
-// the scales both need.
+// the scales both need. Key codes land in LDS as 16-byte chunks ordered
+// (half, block, row): lane i of each load fetches row i%8, block i/8, so the
+// dequantising lanes read and write without bank conflicts.
 __device__ __forceinline__ void issue_raw(uint8_t* raw, const uint8_t* krec, const uint8_t* vrec,
                                           int c, int w, int lane) {
-  const uint8_t* kc = krec + (c * 32 + 8 * w) * D;
-  dma16(kc + lane * 16, raw);
-  dma16(kc + 1024 + lane * 16, raw + 1024);
+  const uint8_t* kc = krec + (c * 32 + 8 * w) * D + (lane & 7) * D + 32 * (lane >> 3);
+  dma16(kc, raw);
+  dma16(kc + 16, raw + 1024);
   dma16(vrec + (c * 1024 + w * 256) * 4 + lane * 16, raw + 2048);
   if (lane < 16) {
     const uint8_t* src = lane < 8 ? krec + K_SCALE_OFF + ((c * 32 + 8 * w) * 8) * 2 + lane * 16
@@ -86,15 +88,15 @@ __device__ __forceinline__ void issue_raw(uint8_t* raw, const uint8_t* krec, con
 // n_live slots of the sub-tile hold data (later slots are unwritten bytes
 // past kv_len; n_live is 0 for a page the table does not map): their keys
 // and value scales are replaced by zeros.
-// Keys, lane l: row 8w + l/8, block l%8 (32 codes).
+// Keys, lane l: row 8w + l%8, block l/8 (32 codes).
 // Values, lane l: word quad l (4 dims, 8 slots each).
 __device__ __forceinline__ void dequant_raw(const uint8_t* raw, _Float16* stage, int w, int lane,
                                             int n_live) {
   {
-    const int u = 8 * w + (lane >> 3), b = lane & 7;
-    const u32x4 k0 = *reinterpret_cast<const u32x4*>(raw + (lane >> 3) * D + 32 * b);
-    const u32x4 k1 = *reinterpret_cast<const u32x4*>(raw + (lane >> 3) * D + 32 * b + 16);
-    const uint32_t ks = *reinterpret_cast<const uint16_t*>(raw + 3072 + (lane >> 3) * 16 + 2 * b);
+    const int u = 8 * w + (lane & 7), b = lane >> 3;
+    const u32x4 k0 = *reinterpret_cast<const u32x4*>(raw + lane * 16);
+    const u32x4 k1 = *reinterpret_cast<const u32x4*>(raw + 1024 + lane * 16);
+    const uint32_t ks = *reinterpret_cast<const uint16_t*>(raw + 3072 + (lane & 7) * 16 + 2 * b);
     const half2_t d2 = as_h2(u < n_live ? (ks | (ks << 16)) : 0u);  // zero scale -> zeros
     _Float16* krow = stage + u * K_LDS_STRIDE + 32 * b;
     *reinterpret_cast<half8_t*>(krow + 0) = k_codes_to_f16(k0.x, k0.y, d2);
