@@ -35,6 +35,7 @@ constexpr int V_LDS_STRIDE = 40;                // halves per value dim row (32 
 constexpr int K_LDS_HALVES = 32 * K_LDS_STRIDE;
 constexpr int V_LDS_HALVES = D * V_LDS_STRIDE;
 constexpr int STAGE_HALVES = K_LDS_HALVES + V_LDS_HALVES;  // one f16 sub-tile
+constexpr int N_STAGES = 3;  // f16 sub-tiles in LDS
 constexpr float PF_RESCALE_MARGIN = 8.0f;
 // Raw (quantised) sub-tile share of one producer wave: 8 key rows (2 KB), a
 // quarter of the value words (1 KB), 128 B of key scales, 128 B of value
@@ -51,13 +52,31 @@ __device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* lds_dst) {
                                    0, 0);
 }
 
-// Workgroup barrier that waits for this wave's LDS traffic only: the raw tile
-// loads still in flight must not be drained (a plain __syncthreads also
-// waits for every outstanding global load).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
+// Wait until an LDS counter reaches target. The counters are raised by other
+// waves of the workgroup, and every wait here is for work those waves do
+// unconditionally: a producer waits for the consumers to release the stage's
+// previous round (three sub-tiles back), a consumer for the producers to
+// fill the current one, so no wait can close a cycle. The spin is capped all
+// the same (2^20 sleeps, tens of milliseconds), so a broken invariant cannot hang the GPU.
+__device__ __forceinline__ void wait_count(const int* c, int target) {
+  for (int spin = 0; spin < (1 << 20); ++spin) {
+    // an LDS read (a generic one would also wait for the raw tile loads)
+    const volatile __attribute__((address_space(3))) int* lc =
+        (const volatile __attribute__((address_space(3))) int*)(c);
+    if (__builtin_amdgcn_readfirstlane(*lc) >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
   __asm__ __volatile__("" ::: "memory");
+}
+
+// Publish this wave's LDS accesses before it: all of them have completed when
+// the count is raised (lane 0 adds). The add is written as an instruction of
+// its own: as an atomic the compiler would first wait for every raw tile load
+// in flight, since those also write LDS.
+__device__ __forceinline__ void signal_count(int* c, int lane) {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  const uint32_t addr = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) int*)(c));
+  if (lane == 0) __asm__ __volatile__("ds_add_u32 %0, %1" ::"v"(addr), "v"(1) : "memory");
 }
 
 template <int N>
@@ -166,8 +185,13 @@ struct PageWindow {
 
 __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
-  _Float16* lds = reinterpret_cast<_Float16*>(lds_raw);               // two f16 stages
-  uint8_t* raw_ring = lds_raw + 2 * STAGE_HALVES * sizeof(_Float16);  // RAW_DEPTH raw stages
+  _Float16* lds = reinterpret_cast<_Float16*>(lds_raw);                      // f16 stages
+  uint8_t* raw_ring = lds_raw + N_STAGES * STAGE_HALVES * sizeof(_Float16);  // raw slots
+  // Per stage: producer waves done writing it, consumer waves done reading
+  // it (both counts only grow; round r of stage s is sub-tile 3r + s).
+  __shared__ int counters[2 * N_STAGES];
+  int* produced = counters;
+  int* consumed = counters + N_STAGES;
   const int group = blockIdx.x, qtile = blockIdx.y, h = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -193,6 +217,8 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
   const int n_sub = t.n_sub;
   PageWindow win;
   win.load(p, t, 0, h, lane);
+  if (tid < 2 * N_STAGES) produced[tid] = 0;  // consumed follows produced
+  __syncthreads();
 
   if (wave < PF_PRODUCERS) {
     // ======== producer: stream raw sub-tiles, dequantise into f16 stages ====
@@ -207,26 +233,21 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
     auto dequant = [&](int sub) {
       const int64_t left = kv_len - (t.pg0 * PAGE + (int64_t)sub * 32);
       const int n_live = win.record(sub) < 0 ? 0 : left >= 32 ? 32 : (int)left;
-      dequant_raw(slot(sub), lds + (sub & 1) * STAGE_HALVES, w, lane, n_live);
+      dequant_raw(slot(sub), lds + (sub % N_STAGES) * STAGE_HALVES, w, lane, n_live);
     };
     if (n_sub > 0) issue(0);
     if (n_sub > 1) issue(1);
-    if (n_sub > 0) {
-      if (n_sub > 1) wait_loads<RAW_LOADS>(); else wait_loads<0>();
-      dequant(0);
-    }
-    lds_barrier();
     for (int sub = 0; sub < n_sub; ++sub) {
-      if (((sub + 2) >> 2) >= win.first + 64) {  // sub + 1 and sub + 2 stay in the window
+      if (((sub + 2) >> 2) >= win.first + 64) {  // sub and sub + 2 stay in the window
         wait_loads<0>();
-        win.load(p, t, (sub + 1) >> 2, h, lane);
+        win.load(p, t, sub >> 2, h, lane);
       }
+      if (sub + 1 < n_sub) wait_loads<RAW_LOADS>(); else wait_loads<0>();  // raw sub-tile sub
+      const int st = sub % N_STAGES, round = sub / N_STAGES;
+      wait_count(consumed + st, PF_CONSUMERS * round);  // previous round read out
+      dequant(sub);
+      signal_count(produced + st, lane);  // also: this raw slot has been read
       if (sub + 2 < n_sub) issue(sub + 2);
-      if (sub + 1 < n_sub) {
-        if (sub + 2 < n_sub) wait_loads<RAW_LOADS>(); else wait_loads<0>();
-        dequant(sub + 1);
-      }
-      lds_barrier();
     }
     return;
   }
@@ -276,29 +297,45 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int mt = 0; mt < 16; ++mt) o[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
-  lds_barrier();
 
   for (int sub = 0; sub < n_sub; ++sub) {
     if ((sub >> 2) >= win.first + 64) win.load(p, t, sub >> 2, h, lane);
-    const _Float16* ks_lds = lds + (sub & 1) * STAGE_HALVES;
+    const int st = sub % N_STAGES;
+    wait_count(produced + st, PF_PRODUCERS * (sub / N_STAGES + 1));
+    const _Float16* ks_lds = lds + st * STAGE_HALVES;
     const _Float16* vs_lds = ks_lds + K_LDS_HALVES;
     const int64_t cur_tok0 = t.pg0 * PAGE + (int64_t)sub * 32;
     const bool compute = win.record(sub) >= 0 && wave_active && cur_tok0 <= wave_max_limit;
     if (compute) {
+      // The sub-tile's 32 operand fragments (16 of keys, then 16 of values)
+      // go through a ring of FR registers, read FR fragments ahead, so LDS
+      // latency is hidden behind the products and, for the first values,
+      // behind the softmax.
+      constexpr int FR = 6;
+      int ln = lane;
+      __asm__ __volatile__("" : "+v"(ln));  // recompute the offsets here, do not hold them
+      const _Float16* kbase = ks_lds + (ln & 15) * K_LDS_STRIDE + 64 * (ln >> 4);
+      const _Float16* vbase = vs_lds + (ln & 15) * V_LDS_STRIDE + 8 * (ln >> 4);
+      auto frag = [&](int f) -> half8_t {
+        return f < 16 ? *reinterpret_cast<const half8_t*>(kbase + 16 * (f & 1) * K_LDS_STRIDE +
+                                                          8 * (f >> 1))
+                      : *reinterpret_cast<const half8_t*>(vbase + 16 * (f - 16) * V_LDS_STRIDE);
+      };
+      half8_t ring[FR];
+#pragma unroll
+      for (int f = 0; f < FR; ++f) ring[f] = frag(f);
       floatx4 s[2][PF_NT];
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int nt = 0; nt < PF_NT; ++nt) s[m][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
+      for (int f = 0; f < 16; ++f) {
+        const int ks = f >> 1, m = f & 1;
+        const half8_t a = ring[f % FR];
+        if (f + FR < 32) ring[f % FR] = frag(f + FR);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const half8_t a = *reinterpret_cast<const half8_t*>(
-              ks_lds + (16 * m + r16) * K_LDS_STRIDE + 64 * g + 8 * ks);
-#pragma unroll
-          for (int nt = 0; nt < PF_NT; ++nt) s[m][nt] = mfma16(a, qb[nt][ks], s[m][nt]);
-        }
+        for (int nt = 0; nt < PF_NT; ++nt) s[m][nt] = mfma16(a, qb[nt][ks], s[m][nt]);
       }
       if (cur_tok0 + 31 > wave_min_limit) {  // then cur_tok0 - pos0 > -32
         const int32_t rel = (int32_t)(cur_tok0 - p.pos0) + 4 * g;
@@ -340,14 +377,15 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
         for (int j = 0; j < 8; ++j) pb[nt][j] = (_Float16)pv[j];
       }
 #pragma unroll
-      for (int mt = 0; mt < 16; ++mt) {
-        const half8_t a =
-            *reinterpret_cast<const half8_t*>(vs_lds + (16 * mt + r16) * V_LDS_STRIDE + 8 * g);
+      for (int f = 16; f < 32; ++f) {
+        const int mt = f - 16;
+        const half8_t a = ring[f % FR];
+        if (f + FR < 32) ring[f % FR] = frag(f + FR);
 #pragma unroll
         for (int nt = 0; nt < PF_NT; ++nt) o[nt][mt] = mfma16(a, pb[nt], o[nt][mt]);
       }
     }
-    lds_barrier();
+    signal_count(consumed + st, lane);
   }
 
   // ---- write this group's normalised partial ------------------------------
@@ -377,7 +415,7 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
 int32_t prefill_rows_per_tile() { return PF_ROWS; }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-  const size_t shmem = sizeof(_Float16) * 2 * STAGE_HALVES + RAW_DEPTH * RAW_STAGE;
+  const size_t shmem = sizeof(_Float16) * N_STAGES * STAGE_HALVES + RAW_DEPTH * RAW_STAGE;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel),
