@@ -6,44 +6,47 @@
 // Streaming guide (alphalab.site, step ④: -ub 512). The kernel design is this
 // library's.
 //
-// Grid (page groups, query tiles, KV heads); 256 threads = 4 wavefronts; a
-// query tile is 128 rows (row = token * gqa + group member), 32 per wave.
-// Each workgroup walks the pages of its group in 32-token sub-tiles. The
-// quantised bytes stream into an LDS ring by direct global->LDS loads, two
-// sub-tiles ahead; each wave loads and dequantises one quarter of a sub-tile
-// (8 key rows, 64 value dims) into an f16 stage (keys [token][dim], values
-// [dim][slot] in the pool's slot order, value scale applied). Every wave
-// computes S^T = Khat . Q'^T and O^T += Vhat^T . P'^T with
-// v_mfma_f32_16x16x32_f16 (rows in the N dimension, two N-tiles), with the
-// online softmax in base 2 in between; the dequantisation of the next
-// sub-tile is placed between the two products, so it overlaps the matrix
-// cores. Each group writes a normalised partial (o, lse) per row; the LSE
-// merge combines the groups.
+// Grid (page groups, query tiles, KV heads); 512 threads = 8 wavefronts, two
+// per SIMD; a query tile is 256 rows (row = token * gqa + group member), 32
+// per wave. Each workgroup walks the pages of its group in 32-token
+// sub-tiles. Every wave does two jobs per sub-tile:
+//  - it streams one eighth of the quantised bytes of a later sub-tile into a
+//    private LDS slot by direct global->LDS loads, and dequantises its eighth
+//    (4 key rows; 64 value dims x 16 slots) into an f16 stage: keys
+//    [token][dim], values [dim][slot] in the pool's slot order with the value
+//    scale applied;
+//  - it computes S^T = Khat . Q'^T and O^T += Vhat^T . P'^T for its 32 rows
+//    with v_mfma_f32_16x16x32_f16 (rows in the N dimension, two N-tiles) and
+//    the online softmax in base 2 in between.
+// Three f16 stages rotate; waves synchronise through per-stage LDS counters
+// (eighths written, waves done reading) rather than workgroup barriers, so
+// the two waves of a SIMD drift apart and one's products overlap the other's
+// LDS reads and vector work. Each group writes a normalised partial (o, lse)
+// per row; the LSE merge combines the groups.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace kvattn {
 namespace {
 
-constexpr int PF_PRODUCERS = 4;                 // waves that stream and dequantise
-constexpr int PF_CONSUMERS = 4;                 // waves that multiply
-constexpr int PF_THREADS = 64 * (PF_PRODUCERS + PF_CONSUMERS);
-constexpr int PF_NT = 2;                        // 16-row N-tiles per consumer wave
-constexpr int PF_ROWS = PF_CONSUMERS * 16 * PF_NT;  // rows per workgroup
+constexpr int PF_WAVES = 8;
+constexpr int PF_THREADS = 64 * PF_WAVES;
+constexpr int PF_NT = 2;                        // 16-row N-tiles per wave
+constexpr int PF_ROWS = PF_WAVES * 16 * PF_NT;  // rows per workgroup
 constexpr int K_LDS_STRIDE = 264;               // halves per key row (256 + pad)
 constexpr int V_LDS_STRIDE = 40;                // halves per value dim row (32 + pad)
 constexpr int K_LDS_HALVES = 32 * K_LDS_STRIDE;
 constexpr int V_LDS_HALVES = D * V_LDS_STRIDE;
 constexpr int STAGE_HALVES = K_LDS_HALVES + V_LDS_HALVES;  // one f16 sub-tile
-constexpr int N_STAGES = 3;  // f16 sub-tiles in LDS
+constexpr int N_STAGES = 3;
 constexpr float PF_RESCALE_MARGIN = 8.0f;
-// Raw (quantised) sub-tile share of one producer wave: 8 key rows (2 KB), a
-// quarter of the value words (1 KB), 128 B of key scales, 128 B of value
-// scales. Two slots: sub-tile i+2 refills the slot sub-tile i came from.
-constexpr int RAW_WAVE = 2048 + 1024 + 256;
-constexpr int RAW_STAGE = PF_PRODUCERS * RAW_WAVE;
-constexpr int RAW_DEPTH = 2;
-constexpr int RAW_LOADS = 4;                    // direct loads per producer wave per sub-tile
+// Raw (quantised) share of one wave per sub-tile: 4 key rows (1 KB), 128
+// value words (512 B), 4 x 16 B of key scales, 4 x 16 B of value scales.
+constexpr int RAW_K = 0, RAW_V = 1024, RAW_KS = 1536, RAW_VS = 1600;
+constexpr int RAW_WAVE = 1664;
+constexpr int RAW_STAGE = PF_WAVES * RAW_WAVE;
+constexpr int RAW_DEPTH = 2;                    // sub-tile i+2 refills sub-tile i's slot
+constexpr int RAW_LOADS = 3;                    // direct loads per wave per sub-tile
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -52,12 +55,17 @@ __device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* lds_dst) {
                                    0, 0);
 }
 
-// Wait until an LDS counter reaches target. The counters are raised by other
-// waves of the workgroup, and every wait here is for work those waves do
-// unconditionally: a producer waits for the consumers to release the stage's
-// previous round (three sub-tiles back), a consumer for the producers to
-// fill the current one, so no wait can close a cycle. The spin is capped all
-// the same (2^20 sleeps, tens of milliseconds), so a broken invariant cannot hang the GPU.
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  __asm__ __volatile__("" ::: "memory");
+}
+
+// Wait until an LDS counter reaches target. The counters only grow, and each
+// wait is for work that the awaited waves reach without waiting on the
+// waiter (see the loop in prefill_kernel), so it ends. The spin is capped all
+// the same (2^20 sleeps, tens of milliseconds), so a broken invariant cannot
+// hang the GPU.
 __device__ __forceinline__ void wait_count(const int* c, int target) {
   for (int spin = 0; spin < (1 << 20); ++spin) {
     // an LDS read (a generic one would also wait for the raw tile loads)
@@ -79,69 +87,92 @@ __device__ __forceinline__ void signal_count(int* c, int lane) {
   if (lane == 0) __asm__ __volatile__("ds_add_u32 %0, %1" ::"v"(addr), "v"(1) : "memory");
 }
 
-template <int N>
-__device__ __forceinline__ void wait_loads() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-  __asm__ __volatile__("" ::: "memory");
-}
-
-// Producer wave w's share of sub-tile (group c of a page): key rows
-// 8w..8w+7 of the group, the value words with q = w (dims 16*(4w+e)+d), and
-// the scales both need. Key codes land in LDS as 16-byte chunks ordered
-// (half, block, row): lane i of each load fetches row i%8, block i/8, so the
-// dequantising lanes read and write without bank conflicts.
+// Wave w's raw share of sub-tile (group c of a page), placed so that its
+// dequantisation reads and writes LDS without bank conflicts:
+//  - key codes: lane i fetches row 4w + i%4, block (i/4)%8, half i/32 (16 B);
+//  - value words: q = w/2, lane groups g = 2(w%2), 2(w%2)+1: 128 consecutive
+//    words (lanes 0-31);
+//  - scales (lanes 0-7): key rows 4w..4w+3 (16 B each), then value blocks
+//    2q, 2q+1 for the two lane groups (16 B each).
 __device__ __forceinline__ void issue_raw(uint8_t* raw, const uint8_t* krec, const uint8_t* vrec,
                                           int c, int w, int lane) {
-  const uint8_t* kc = krec + (c * 32 + 8 * w) * D + (lane & 7) * D + 32 * (lane >> 3);
-  dma16(kc, raw);
-  dma16(kc + 16, raw + 1024);
-  dma16(vrec + (c * 1024 + w * 256) * 4 + lane * 16, raw + 2048);
-  if (lane < 16) {
-    const uint8_t* src = lane < 8 ? krec + K_SCALE_OFF + ((c * 32 + 8 * w) * 8) * 2 + lane * 16
-                                  : vrec + V_SCALE_OFF + ((c * 8 + 2 * w) * 4) * 16 + (lane - 8) * 16;
-    dma16(src, raw + 3072);
+  const int q = w >> 1, gh = w & 1;
+  dma16(krec + (c * 32 + 4 * w + (lane & 3)) * D + 32 * ((lane >> 2) & 7) + 16 * (lane >> 5),
+        raw + RAW_K);
+  if (lane < 32) dma16(vrec + (((c * 4 + q) * 4 + 2 * gh) * 64) * 4 + lane * 16, raw + RAW_V);
+  if (lane < 8) {
+    const uint8_t* src =
+        lane < 4 ? krec + K_SCALE_OFF + (c * 32 + 4 * w + lane) * 16
+                 : vrec + V_SCALE_OFF + ((c * 8 + 2 * q + ((lane - 4) >> 1)) * 4 + 2 * gh + (lane & 1)) * 16;
+    dma16(src, raw + RAW_KS);
   }
 }
 
-// Dequantise producer wave w's raw share into an f16 stage. Only the first
-// n_live slots of the sub-tile hold data (later slots are unwritten bytes
-// past kv_len; n_live is 0 for a page the table does not map): their keys
-// and value scales are replaced by zeros.
-// Keys, lane l: row 8w + l%8, block l/8 (32 codes).
-// Values, lane l: word quad l (4 dims, 8 slots each).
-__device__ __forceinline__ void dequant_raw(const uint8_t* raw, _Float16* stage, int w, int lane,
+// The raw share's bytes a lane needs, read in one block that also waits for
+// them. Written as instructions of their own: as plain loads the compiler
+// would first wait for every raw tile load in flight (those write LDS too),
+// including the next sub-tile's, which is still meant to be in flight.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+struct RawIn {
+  u32x4 k;      // 16 key codes
+  u32x2 v;      // 2 value words
+  u32x4 vs;     // 8 value scales
+  uint32_t ks;  // key scale (low 16 bits)
+};
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint8_t*)(p));
+}
+__device__ __forceinline__ RawIn read_raw(const uint8_t* k, const uint8_t* v, const uint8_t* vs,
+                                          const uint8_t* ks) {
+  RawIn r;
+  __asm__ __volatile__(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b64 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_u16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r.k), "=&v"(r.v), "=&v"(r.vs), "=&v"(r.ks)
+      : "v"(lds_addr(k)), "v"(lds_addr(v)), "v"(lds_addr(vs)), "v"(lds_addr(ks))
+      : "memory");
+  return r;
+}
+
+// Dequantise wave w's raw share into an f16 stage. Only the first n_live
+// slots of the sub-tile hold data (later slots are unwritten bytes past
+// kv_len; n_live is 0 for a page the table does not map): their keys and
+// value scales are replaced by zeros. ln is the lane index.
+// Keys, lane (u, b, hh) = (l%4, (l/4)%8, l/32): 16 codes of row 4w + u.
+// Values, lane (d, ep, gl) = (l%16, (l/16)%2, l/32): words e = 2ep, 2ep+1 of
+// dim group q = w/2, lane group g = 2(w%2) + gl.
+__device__ __forceinline__ void dequant_raw(const uint8_t* raw, _Float16* stage, int w, int ln,
                                             int n_live) {
+  const int u = ln & 3, b = (ln >> 2) & 7, hh = ln >> 5;
+  const int q = w >> 1, d = ln & 15, ep = (ln >> 4) & 1, gl = ln >> 5;
+  const int g = 2 * (w & 1) + gl;
+  const RawIn in = read_raw(raw + RAW_K + ln * 16, raw + RAW_V + ((gl * 16 + d) * 4 + 2 * ep) * 4,
+                            raw + RAW_VS + (ep * 2 + gl) * 16, raw + RAW_KS + u * 16 + 2 * b);
   {
-    const int u = 8 * w + (lane & 7), b = lane >> 3;
-    const u32x4 k0 = *reinterpret_cast<const u32x4*>(raw + lane * 16);
-    const u32x4 k1 = *reinterpret_cast<const u32x4*>(raw + 1024 + lane * 16);
-    const uint32_t ks = *reinterpret_cast<const uint16_t*>(raw + 3072 + (lane & 7) * 16 + 2 * b);
-    const half2_t d2 = as_h2(u < n_live ? (ks | (ks << 16)) : 0u);  // zero scale -> zeros
-    _Float16* krow = stage + u * K_LDS_STRIDE + 32 * b;
-    *reinterpret_cast<half8_t*>(krow + 0) = k_codes_to_f16(k0.x, k0.y, d2);
-    *reinterpret_cast<half8_t*>(krow + 8) = k_codes_to_f16(k0.z, k0.w, d2);
-    *reinterpret_cast<half8_t*>(krow + 16) = k_codes_to_f16(k1.x, k1.y, d2);
-    *reinterpret_cast<half8_t*>(krow + 24) = k_codes_to_f16(k1.z, k1.w, d2);
+    const uint32_t ks = in.ks & 0xFFFFu;
+    const half2_t d2 = as_h2(4 * w + u < n_live ? (ks | (ks << 16)) : 0u);  // zero scale -> zeros
+    _Float16* krow = stage + (4 * w + u) * K_LDS_STRIDE + 32 * b + 16 * hh;
+    *reinterpret_cast<half8_t*>(krow + 0) = k_codes_to_f16(in.k.x, in.k.y, d2);
+    *reinterpret_cast<half8_t*>(krow + 8) = k_codes_to_f16(in.k.z, in.k.w, d2);
   }
   {
-    const int d = lane & 15, g = lane >> 4;
-    const u32x4 words = *reinterpret_cast<const u32x4*>(raw + 2048 + lane * 16);
-    uint32_t mk[4];
+    // scales of block 2q + ep for lane group g (in.vs), masked past n_live
+    uint32_t scw[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int u0 = 16 * ((2 * p) >> 2) + 4 * g + ((2 * p) & 3);
       const int u1 = 16 * ((2 * p + 1) >> 2) + 4 * g + ((2 * p + 1) & 3);
-      mk[p] = (u0 < n_live ? 0x0000FFFFu : 0u) | (u1 < n_live ? 0xFFFF0000u : 0u);
+      const uint32_t mk = (u0 < n_live ? 0x0000FFFFu : 0u) | (u1 < n_live ? 0xFFFF0000u : 0u);
+      scw[p] = in.vs[p] & mk;
     }
     _Float16* vbase = stage + K_LDS_HALVES;
-    const uint32_t wv[4] = {words.x, words.y, words.z, words.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int dim = 16 * (4 * w + e) + d;
-      // value scales of block 2w + e/2 for lane group g: 16 bytes
-      const u32x4 sc = *reinterpret_cast<const u32x4*>(raw + 3072 + 128 + ((e >> 1) * 4 + g) * 16);
-      const uint32_t scw[4] = {sc.x & mk[0], sc.y & mk[1], sc.z & mk[2], sc.w & mk[3]};
-      half8_t val = v_codes_to_f16(wv[e]);
+    for (int i = 0; i < 2; ++i) {
+      const int dim = 16 * (4 * q + 2 * ep + i) + d;
+      half8_t val = v_codes_to_f16(in.v[i]);
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const half2_t pr = {val[2 * p], val[2 * p + 1]};
@@ -161,8 +192,8 @@ struct SubTiles {
 
 // Page records of a group, 64 pages at a time in one VGPR (lane i holds the
 // record index of page pg0 + first + i, or -1 when the table does not map
-// it), read back with readlane: the loops then issue no page-table loads of
-// their own, whose waits would also drain the raw tile stream.
+// it), read back with readlane: the loop then issues no page-table loads of
+// its own, whose waits would also drain the raw tile stream.
 struct PageWindow {
   int64_t first;
   int32_t rec;
@@ -187,14 +218,16 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
   _Float16* lds = reinterpret_cast<_Float16*>(lds_raw);                      // f16 stages
   uint8_t* raw_ring = lds_raw + N_STAGES * STAGE_HALVES * sizeof(_Float16);  // raw slots
-  // Per stage: producer waves done writing it, consumer waves done reading
-  // it (both counts only grow; round r of stage s is sub-tile 3r + s).
+  // Per stage: eighths written, waves done reading (both only grow; round r
+  // of stage s is sub-tile 3r + s).
   __shared__ int counters[2 * N_STAGES];
   int* produced = counters;
   int* consumed = counters + N_STAGES;
+
   const int group = blockIdx.x, qtile = blockIdx.y, h = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
   const int n_heads = p.n_kv * p.gqa;
   const int64_t rows_head = (int64_t)p.chunk * p.gqa;
   const int64_t kv_len = p.pos0 + p.chunk;
@@ -217,45 +250,31 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
   const int n_sub = t.n_sub;
   PageWindow win;
   win.load(p, t, 0, h, lane);
-  if (tid < 2 * N_STAGES) produced[tid] = 0;  // consumed follows produced
-  __syncthreads();
+  if (tid < 2 * N_STAGES) counters[tid] = 0;
 
-  if (wave < PF_PRODUCERS) {
-    // ======== producer: stream raw sub-tiles, dequantise into f16 stages ====
-    const int w = wave;
-    auto slot = [&](int sub) { return raw_ring + (sub % RAW_DEPTH) * RAW_STAGE + w * RAW_WAVE; };
-    auto issue = [&](int sub) {
-      const int32_t r = win.record(sub);
-      const int64_t rec = r >= 0 ? r : 0;  // unmapped pages load record 0, then zero it
-      issue_raw(slot(sub), p.k_pool + rec * K_REC, p.v_pool + rec * V_REC, r >= 0 ? (sub & 3) : 0,
-                w, lane);
-    };
-    auto dequant = [&](int sub) {
-      const int64_t left = kv_len - (t.pg0 * PAGE + (int64_t)sub * 32);
-      const int n_live = win.record(sub) < 0 ? 0 : left >= 32 ? 32 : (int)left;
-      dequant_raw(slot(sub), lds + (sub % N_STAGES) * STAGE_HALVES, w, lane, n_live);
-    };
-    if (n_sub > 0) issue(0);
-    if (n_sub > 1) issue(1);
-    for (int sub = 0; sub < n_sub; ++sub) {
-      if (((sub + 2) >> 2) >= win.first + 64) {  // sub and sub + 2 stay in the window
-        wait_loads<0>();
-        win.load(p, t, sub >> 2, h, lane);
-      }
-      if (sub + 1 < n_sub) wait_loads<RAW_LOADS>(); else wait_loads<0>();  // raw sub-tile sub
-      const int st = sub % N_STAGES, round = sub / N_STAGES;
-      wait_count(consumed + st, PF_CONSUMERS * round);  // previous round read out
-      dequant(sub);
-      signal_count(produced + st, lane);  // also: this raw slot has been read
-      if (sub + 2 < n_sub) issue(sub + 2);
-    }
-    return;
-  }
+  uint8_t* const my_raw = raw_ring + wave * RAW_WAVE;
+  auto issue = [&](int sub) {
+    const int32_t r = win.record(sub);
+    const int64_t rec = r >= 0 ? r : 0;  // unmapped pages load record 0, then zero it
+    int ln = lane;
+    __asm__ __volatile__("" : "+v"(ln));  // recompute lane offsets here, do not hold them
+    issue_raw(my_raw + (sub % RAW_DEPTH) * RAW_STAGE, p.k_pool + rec * K_REC,
+              p.v_pool + rec * V_REC, r >= 0 ? (sub & 3) : 0, wave, ln);
+  };
+  auto dequant = [&](int sub) {
+    const int64_t left = kv_len - (t.pg0 * PAGE + (int64_t)sub * 32);
+    const int n_live = win.record(sub) < 0 ? 0 : left >= 32 ? 32 : (int)left;
+    int ln = lane;
+    __asm__ __volatile__("" : "+v"(ln));  // recompute lane offsets here, do not hold them
+    dequant_raw(my_raw + (sub % RAW_DEPTH) * RAW_STAGE, lds + (sub % N_STAGES) * STAGE_HALVES,
+                wave, ln, n_live);
+  };
+  // start the raw stream before anything else
+  if (n_sub > 0) issue(0);
+  if (n_sub > 1) issue(1);
 
-  // ======== consumer: S^T = Khat . Q'^T, online softmax, O^T += Vhat^T . P'^T
-  const int cw = wave - PF_PRODUCERS;
-  const int r16 = lane & 15, g = lane >> 4;
-  const int64_t row0 = (int64_t)qtile * PF_ROWS + cw * 16 * PF_NT;  // this wave's first row
+  // ---- query operands, row limits ------------------------------------------
+  const int64_t row0 = (int64_t)qtile * PF_ROWS + wave * 16 * PF_NT;  // this wave's first row
   half8_t qb[PF_NT][8];
   int32_t limit[PF_NT];  // last visible key of the row, relative to pos0
 #pragma unroll
@@ -297,13 +316,35 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int mt = 0; mt < 16; ++mt) o[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
+  __syncthreads();  // counters cleared
 
+  // Step i: dequantise this wave's eighth of sub-tile i+1 (stage (i+1)%3,
+  // once every wave has read sub-tile i-2 from it), refill the raw slot with
+  // sub-tile i+3, then multiply sub-tile i once all eighths of it are in.
+  // The slowest wave never waits on a faster one: what it needs (sub-tile i-2
+  // read, sub-tile i written) every other wave finished before step i.
+  if (n_sub > 0) {
+    if (n_sub > 1) wait_loads<RAW_LOADS>(); else wait_loads<0>();
+    dequant(0);
+    signal_count(produced + 0, lane);
+    if (n_sub > 2) issue(2);
+  }
   for (int sub = 0; sub < n_sub; ++sub) {
-    if ((sub >> 2) >= win.first + 64) win.load(p, t, sub >> 2, h, lane);
+    if (((sub + 3) >> 2) >= win.first + 64) {  // sub .. sub + 3 stay in the window
+      wait_loads<0>();
+      win.load(p, t, sub >> 2, h, lane);
+    }
+    const int nx = sub + 1;
+    if (nx < n_sub) {
+      if (nx + 1 < n_sub) wait_loads<RAW_LOADS>(); else wait_loads<0>();  // raw sub-tile nx in
+      if (nx >= N_STAGES) wait_count(consumed + nx % N_STAGES, PF_WAVES * (nx / N_STAGES));
+      dequant(nx);
+      signal_count(produced + nx % N_STAGES, lane);  // also: raw slot of nx has been read
+      if (nx + 2 < n_sub) issue(nx + 2);
+    }
+
     const int st = sub % N_STAGES;
-    wait_count(produced + st, PF_PRODUCERS * (sub / N_STAGES + 1));
-    const _Float16* ks_lds = lds + st * STAGE_HALVES;
-    const _Float16* vs_lds = ks_lds + K_LDS_HALVES;
+    wait_count(produced + st, PF_WAVES * (sub / N_STAGES + 1));
     const int64_t cur_tok0 = t.pg0 * PAGE + (int64_t)sub * 32;
     const bool compute = win.record(sub) >= 0 && wave_active && cur_tok0 <= wave_max_limit;
     if (compute) {
@@ -311,11 +352,12 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
       // go through a ring of FR registers, read FR fragments ahead, so LDS
       // latency is hidden behind the products and, for the first values,
       // behind the softmax.
-      constexpr int FR = 6;
+      constexpr int FR = 4;
       int ln = lane;
-      __asm__ __volatile__("" : "+v"(ln));  // recompute the offsets here, do not hold them
-      const _Float16* kbase = ks_lds + (ln & 15) * K_LDS_STRIDE + 64 * (ln >> 4);
-      const _Float16* vbase = vs_lds + (ln & 15) * V_LDS_STRIDE + 8 * (ln >> 4);
+      __asm__ __volatile__("" : "+v"(ln));  // recompute lane offsets here, do not hold them
+      const _Float16* kbase = lds + st * STAGE_HALVES + (ln & 15) * K_LDS_STRIDE + 64 * (ln >> 4);
+      const _Float16* vbase =
+          lds + st * STAGE_HALVES + K_LDS_HALVES + (ln & 15) * V_LDS_STRIDE + 8 * (ln >> 4);
       auto frag = [&](int f) -> half8_t {
         return f < 16 ? *reinterpret_cast<const half8_t*>(kbase + 16 * (f & 1) * K_LDS_STRIDE +
                                                           8 * (f >> 1))
