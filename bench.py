@@ -102,31 +102,28 @@ def time_graph(step_fn, steps, warmup):
 
 
 def time_launches(call_fn, n_layers, reps):
-    """Average duration of one call (one kernel launch group) with HIP events on
-    the stream the work is launched on: each layer's call is captured in its own
-    graph, and events bracket every replay."""
+    """Average duration of one call with HIP events on the stream the work is
+    launched on: the n_layers calls (one per layer, so every call reads its own
+    pool) are captured back to back in one graph, and a pair of events brackets
+    reps replays of it; the figure is the bracketed time over reps * n_layers
+    (it includes the short gaps between consecutive launches)."""
     import torch
-    graphs = []
     for layer in range(n_layers):
         call_fn(layer)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            call_fn(layer)
-        graphs.append(g)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps * n_layers)]
-    i = 0
-    for _ in range(reps):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
         for layer in range(n_layers):
-            ev[i][0].record()
-            graphs[layer].replay()
-            ev[i][1].record()
-            i += 1
+            call_fn(layer)
+    g.replay()
     torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in ev]
-    return sum(ms) / len(ms)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / (reps * n_layers)
 
 
 def bench_decode(w, dev, steps, warmup, sparse=False):
@@ -164,8 +161,23 @@ def bench_decode(w, dev, steps, warmup, sparse=False):
                                         out_blocks=blocks[layer], workspace=sel_ws)
             decode_call(layer)
 
+    # the decode kernel alone: the same split-K partials kvattn_decode makes,
+    # without its merge
+    n_units = blocks[0].shape[1] if sparse else w.n_pages
+    n_splits = kv.kvattn_decode_splits(pools.geom, n_units)
+    rows = w.n_q_tok * w.n_heads
+    o_part = torch.empty((n_splits, rows, 256), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((n_splits, rows), dtype=torch.float32, device=dev)
+
+    def kernel_call(layer):
+        kv.kvattn_decode_partials(pools.geom, pools.q[layer], pools.kp[layer], pools.vp[layer],
+                                  pools.table, w.kv_len, 1.0 / 16.0, n_splits,
+                                  blocks=blocks[layer] if sparse else None, o_part=o_part,
+                                  lse_part=lse_part)
+
     ms, _ = time_graph(step, steps, warmup)
     launch_ms = time_launches(decode_call, w.n_layers, max(steps, 3))
+    kernel_ms = time_launches(kernel_call, w.n_layers, max(steps, 3))
     tokens = (w.k_top + w.n_recent) * 128 if sparse else w.kv_len
     bytes_per_launch = tokens * w.n_kv * (272 + 144)
     res = {
@@ -174,6 +186,9 @@ def bench_decode(w, dev, steps, warmup, sparse=False):
         "gbs": bytes_per_launch * w.n_layers / (ms * 1e-3) / 1e9,
         "launch_ms": launch_ms,
         "launch_gbs": bytes_per_launch / (launch_ms * 1e-3) / 1e9,
+        "kernel_ms": kernel_ms,
+        "kernel_gbs": bytes_per_launch / (kernel_ms * 1e-3) / 1e9,
+        "n_splits": n_splits,
         "bytes_per_launch": bytes_per_launch,
     }
     if sparse:
@@ -217,8 +232,21 @@ def bench_prefill(w, dev, steps, warmup):
                                      pools.table, pools.kp[layer], pools.vp[layer])
             prefill_call(layer)
 
+    # the prefill kernel alone: kvattn_prefill_chunk's per-group partials
+    n_groups = kv.kvattn_prefill_groups(pools.geom, w.chunk, w.pos0)
+    rows = w.chunk * w.n_heads
+    o_part = torch.empty((n_groups, rows, 256), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((n_groups, rows), dtype=torch.float32, device=dev)
+
+    def kernel_call(layer):
+        kv.kvattn_prefill_partials(pools.geom, pools.q[layer], pools.kp[layer], pools.vp[layer],
+                                   pools.table, w.pos0, 1.0 / 16.0, n_groups, o_part=o_part,
+                                   lse_part=lse_part)
+
     ms, _ = time_graph(step, steps, warmup)
-    launch_ms = time_launches(prefill_call, w.n_layers, max(2, min(steps, 3)))
+    reps = max(2, min(steps, 3))
+    launch_ms = time_launches(prefill_call, w.n_layers, reps)
+    kernel_ms = time_launches(kernel_call, w.n_layers, reps)
     fl = prefill_flops_per_layer(w)
     return {
         "ms_per_step": ms,
@@ -228,6 +256,9 @@ def bench_prefill(w, dev, steps, warmup):
         "launch_ms": launch_ms,
         "flops_per_launch": fl,
         "launch_tflops": fl / (launch_ms * 1e-3) / 1e12,
+        "kernel_ms": kernel_ms,
+        "kernel_tflops": fl / (kernel_ms * 1e-3) / 1e12,
+        "n_groups": n_groups,
     }, pools
 
 
@@ -362,15 +393,18 @@ def main():
     }
     if decode_res:
         line["roofline"] = {
-            "kernel": "decode_kernel<2> + merge_kernel (one kvattn_decode call)",
+            "kernel": "decode_kernel<2,1,2> (kvattn_decode_partials: split-K partials, "
+                      f"{decode_res['n_splits']} splits per KV head)",
             "bound": "hbm",
-            "achieved": round(decode_res["launch_gbs"], 2),
+            "achieved": round(decode_res["kernel_gbs"], 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(decode_res["launch_gbs"] / HBM_PEAK_GBS, 4),
+            "frac": round(decode_res["kernel_gbs"] / HBM_PEAK_GBS, 4),
             "traffic": None,
-            "launch_us": round(decode_res["launch_ms"] * 1e3, 2),
+            "kernel_us": round(decode_res["kernel_ms"] * 1e3, 2),
             "bytes_per_launch": decode_res["bytes_per_launch"],
+            "call_us": round(decode_res["launch_ms"] * 1e3, 2),
+            "call_gbs": round(decode_res["launch_gbs"], 2),
         }
     if prefill_res:
         line["prefill"] = {
@@ -381,14 +415,16 @@ def main():
             "ms_per_step": round(prefill_res["ms_per_step"], 3),
             "tokens_per_s": round(prefill_res["tokens_per_s"], 1),
             "roofline": {
-                "kernel": "prefill_kernel + merge_kernel (one kvattn_prefill_chunk call)",
+                "kernel": "prefill_kernel (kvattn_prefill_partials: "
+                          f"{prefill_res['n_groups']} page groups)",
                 "bound": "mfma",
-                "achieved": round(prefill_res["launch_tflops"], 2),
+                "achieved": round(prefill_res["kernel_tflops"], 2),
                 "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s",
-                "frac": round(prefill_res["launch_tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
+                "frac": round(prefill_res["kernel_tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
                 "traffic": None,
-                "launch_ms": round(prefill_res["launch_ms"], 4),
+                "kernel_ms": round(prefill_res["kernel_ms"], 4),
+                "call_ms": round(prefill_res["launch_ms"], 4),
             },
         }
         if "cpu_baseline" in prefill_res:

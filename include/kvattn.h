@@ -215,6 +215,36 @@ kvattn_status kvattn_decode(const kvattn_geom *geom, const float *q,
                             void *workspace, size_t *workspace_bytes,
                             void *stream);
 
+/* a3 alone — the split-K partials of kvattn_decode, without the merge, for
+ * callers that combine them with partials computed elsewhere (other pages,
+ * another device) through kvattn_merge_lse ([RDNA4] "Online Log-Sum-Exp":
+ * partial results over streamed pages combined by online LSE). Arguments as
+ * kvattn_decode, except:
+ *  n_splits  >= 1. Split s covers units [n_units*s/n_splits,
+ *            n_units*(s+1)/n_splits) of the unit list, where the units are
+ *            logical pages 0 .. ceil(kv_len/128)-1 (dense) or blocks[h][..]
+ *            (sparse), n_units their count.
+ *  o_part    fp32 [n_splits][n_q_tok*n_kv_heads*gqa][256], 16-byte aligned;
+ *            lse_part fp32 [n_splits][n_q_tok*n_kv_heads*gqa]. For split s
+ *            and row r over the split's key set J_s: lse_part = ln sum
+ *            exp(s_j), o_part = sum exp(s_j - lse_part) Vhat_j; an empty J_s
+ *            gives o_part = 0, lse_part = -inf. kvattn_merge_lse of all
+ *            splits is kvattn_decode's result.
+ * No workspace; nothing but o_part and lse_part is written. */
+kvattn_status kvattn_decode_partials(const kvattn_geom *geom, const float *q,
+                                     int32_t n_q_tok, const uint8_t *k_pool,
+                                     const uint8_t *v_pool,
+                                     const int32_t *page_table,
+                                     int32_t n_logical_pages,
+                                     const int32_t *blocks, int32_t n_blk,
+                                     int64_t kv_len, float scale,
+                                     int32_t n_splits, float *o_part,
+                                     float *lse_part, void *stream);
+
+/* The split count kvattn_decode chooses (n_splits = 0) for n_units units on
+ * the current device; 0 if geom is invalid or n_units < 1. */
+int32_t kvattn_decode_splits(const kvattn_geom *geom, int32_t n_units);
+
 /* a6 — chunked prefill attention ([RDNA4] "Online Log-Sum-Exp prefill":
  * chunked prefill across pages with online LSE accumulation; [STREAM] step ④
  * -ub 512). Query token t (0 <= t < chunk) sits at position pos0 + t and sees
@@ -236,6 +266,28 @@ kvattn_status kvattn_prefill_chunk(const kvattn_geom *geom, const float *q,
                                    float scale, float *out, float *lse,
                                    int32_t n_groups, void *workspace,
                                    size_t *workspace_bytes, void *stream);
+
+/* a6 alone — the per-group partials of kvattn_prefill_chunk, without the
+ * merge. Arguments as kvattn_prefill_chunk, except:
+ *  n_groups  >= 1. Group gi covers logical pages [n_pages*gi/n_groups,
+ *            n_pages*(gi+1)/n_groups), n_pages = ceil((pos0+chunk)/128).
+ *  o_part    fp32 [n_groups][chunk*n_kv_heads*gqa][256], 16-byte aligned;
+ *            lse_part fp32 [n_groups][chunk*n_kv_heads*gqa]; per group and
+ *            row as kvattn_decode_partials (row order as out).
+ * No workspace; nothing but o_part and lse_part is written. */
+kvattn_status kvattn_prefill_partials(const kvattn_geom *geom, const float *q,
+                                      int32_t chunk, const uint8_t *k_pool,
+                                      const uint8_t *v_pool,
+                                      const int32_t *page_table,
+                                      int32_t n_logical_pages, int64_t pos0,
+                                      float scale, int32_t n_groups,
+                                      float *o_part, float *lse_part,
+                                      void *stream);
+
+/* The group count kvattn_prefill_chunk chooses (n_groups = 0) on the current
+ * device; 0 if geom is invalid, chunk < 1 or pos0 < 0. */
+int32_t kvattn_prefill_groups(const kvattn_geom *geom, int32_t chunk,
+                              int64_t pos0);
 
 /* a4 — merge partial attention results by log-sum-exp ([RDNA4] "Online
  * Log-Sum-Exp prefill"). For each row r:

@@ -13,7 +13,9 @@ import os
 __all__ = [
     "Geom", "KvattnError", "library_path", "load_library",
     "kvattn_quantize_pages", "kvattn_select_blocks", "kvattn_decode",
-    "kvattn_prefill_chunk", "kvattn_merge_lse", "kvattn_select_count",
+    "kvattn_decode_partials", "kvattn_decode_splits", "kvattn_prefill_chunk",
+    "kvattn_prefill_partials", "kvattn_prefill_groups", "kvattn_merge_lse",
+    "kvattn_select_count",
     "K_RECORD_BYTES", "V_RECORD_BYTES", "HEAD_DIM", "PAGE_TOKENS",
 ]
 
@@ -64,7 +66,11 @@ def load_library():
         "kvattn_quantize_pages": ([G, P, P, I64, I32, P, I32, P, P, P, P], I32),
         "kvattn_select_blocks": ([G, P, P, I32, I32, I32, I32, P, P, SZP, P], I32),
         "kvattn_decode": ([G, P, I32, P, P, P, I32, P, I32, I64, F32, P, P, I32, P, SZP, P], I32),
+        "kvattn_decode_partials": ([G, P, I32, P, P, P, I32, P, I32, I64, F32, I32, P, P, P], I32),
+        "kvattn_decode_splits": ([G, I32], I32),
         "kvattn_prefill_chunk": ([G, P, I32, P, P, P, I32, I64, F32, P, P, I32, P, SZP, P], I32),
+        "kvattn_prefill_partials": ([G, P, I32, P, P, P, I32, I64, F32, I32, P, P, P], I32),
+        "kvattn_prefill_groups": ([G, I32, I64], I32),
         "kvattn_merge_lse": ([I32, I64, I32, P, P, P, P, P], I32),
     }
     for name, (args, res) in sigs.items():
@@ -233,6 +239,55 @@ def kvattn_decode(geom, q, k_pool, v_pool, page_table, kv_len, scale, blocks=Non
     return out, lse
 
 
+def _decode_args(geom, q, k_pool, v_pool, page_table, blocks):
+    torch = _torch()
+    _need(q, "q", torch.float32)
+    for name, t, dt in (("k_pool", k_pool, torch.uint8), ("v_pool", v_pool, torch.uint8),
+                        ("page_table", page_table, torch.int32)):
+        _need(t, name, dt)
+    n_heads = geom.n_kv_heads * geom.gqa
+    if q.dim() != 3 or q.shape[1] != n_heads or q.shape[2] != HEAD_DIM:
+        raise ValueError(f"q must be [n_q_tok, {n_heads}, {HEAD_DIM}]")
+    _pools(geom, k_pool, v_pool)
+    n_blk = 0
+    if blocks is not None:
+        _need(blocks, "blocks", torch.int32)
+        if blocks.dim() != 2 or blocks.shape[0] != geom.n_kv_heads:
+            raise ValueError("blocks must be [n_kv_heads, n_blk]")
+        n_blk = blocks.shape[1]
+    return n_blk
+
+
+def kvattn_decode_splits(geom, n_units):
+    """Split count kvattn_decode picks by itself for n_units pages or blocks."""
+    return load_library().kvattn_decode_splits(ctypes.byref(geom), int(n_units))
+
+
+def kvattn_decode_partials(geom, q, k_pool, v_pool, page_table, kv_len, scale, n_splits,
+                           blocks=None, o_part=None, lse_part=None, stream=None):
+    """Split-K partials of decode (a3) without the merge:
+    q [n_q_tok, n_heads, 256] -> (o_part [n_splits, n_q_tok*n_heads, 256], lse_part)."""
+    torch = _torch()
+    lib = load_library()
+    n_blk = _decode_args(geom, q, k_pool, v_pool, page_table, blocks)
+    rows = q.shape[0] * q.shape[1]
+    if o_part is None:
+        o_part = torch.empty((n_splits, rows, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((n_splits, rows), dtype=torch.float32, device=q.device)
+    _need(o_part, "o_part", torch.float32)
+    _need(lse_part, "lse_part", torch.float32)
+    _size(o_part, "o_part", n_splits * rows * HEAD_DIM)
+    _size(lse_part, "lse_part", n_splits * rows)
+    _check("kvattn_decode_partials",
+           lib.kvattn_decode_partials(ctypes.byref(geom), _ptr(q), q.shape[0], _ptr(k_pool),
+                                      _ptr(v_pool), _ptr(page_table), page_table.numel(),
+                                      _ptr(blocks), n_blk, int(kv_len), float(scale),
+                                      int(n_splits), _ptr(o_part), _ptr(lse_part),
+                                      _stream(stream)))
+    return o_part, lse_part
+
+
 def kvattn_prefill_chunk(geom, q, k_pool, v_pool, page_table, pos0, scale, out=None, lse=None,
                          n_groups=0, workspace=None, stream=None):
     """Chunked prefill attention (a6); q [chunk, n_heads, 256] -> (out, lse)."""
@@ -264,6 +319,35 @@ def kvattn_prefill_chunk(geom, q, k_pool, v_pool, page_table, pos0, scale, out=N
     workspace, nbytes = _workspace(call, workspace, q.device)
     _check("kvattn_prefill_chunk", call(_ptr(workspace), ctypes.byref(nbytes)))
     return out, lse
+
+
+def kvattn_prefill_groups(geom, chunk, pos0):
+    """Page-group count kvattn_prefill_chunk picks by itself."""
+    return load_library().kvattn_prefill_groups(ctypes.byref(geom), int(chunk), int(pos0))
+
+
+def kvattn_prefill_partials(geom, q, k_pool, v_pool, page_table, pos0, scale, n_groups,
+                            o_part=None, lse_part=None, stream=None):
+    """Per-group partials of chunked prefill (a6) without the merge:
+    q [chunk, n_heads, 256] -> (o_part [n_groups, chunk*n_heads, 256], lse_part)."""
+    torch = _torch()
+    lib = load_library()
+    _decode_args(geom, q, k_pool, v_pool, page_table, None)
+    rows = q.shape[0] * q.shape[1]
+    if o_part is None:
+        o_part = torch.empty((n_groups, rows, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((n_groups, rows), dtype=torch.float32, device=q.device)
+    _need(o_part, "o_part", torch.float32)
+    _need(lse_part, "lse_part", torch.float32)
+    _size(o_part, "o_part", n_groups * rows * HEAD_DIM)
+    _size(lse_part, "lse_part", n_groups * rows)
+    _check("kvattn_prefill_partials",
+           lib.kvattn_prefill_partials(ctypes.byref(geom), _ptr(q), q.shape[0], _ptr(k_pool),
+                                       _ptr(v_pool), _ptr(page_table), page_table.numel(),
+                                       int(pos0), float(scale), int(n_groups), _ptr(o_part),
+                                       _ptr(lse_part), _stream(stream)))
+    return o_part, lse_part
 
 
 def kvattn_merge_lse(o_parts, lse_parts, out=None, lse=None, stream=None):

@@ -166,56 +166,60 @@ kvattn_status kvattn_select_blocks(const kvattn_geom* geom, const float* q,
                               n_cand, k_sel, r, n_out, out_blocks, s));
 }
 
-kvattn_status kvattn_decode(const kvattn_geom* geom, const float* q, int32_t n_q_tok,
-                            const uint8_t* k_pool, const uint8_t* v_pool,
-                            const int32_t* page_table, int32_t n_logical_pages,
-                            const int32_t* blocks, int32_t n_blk, int64_t kv_len, float scale,
-                            float* out, float* lse, int32_t n_splits, void* workspace,
-                            size_t* workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+kvattn_status check_scale(float scale) {
+  if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+    return KVATTN_E_INVALID;
+  return KVATTN_OK;
+}
+
+// Validation shared by kvattn_decode and kvattn_decode_partials; n_units is
+// the number of pages (dense) or listed blocks (sparse) the splits divide.
+kvattn_status check_decode(const kvattn_geom* geom, const float* q, int32_t n_q_tok,
+                           const uint8_t* k_pool, const uint8_t* v_pool,
+                           const int32_t* page_table, int32_t n_logical_pages,
+                           const int32_t* blocks, int32_t n_blk, int64_t kv_len, float scale,
+                           int32_t* n_units) {
   kvattn_status st = check_geom(geom);
   if (st) return st;
   if ((st = check_pools(geom, k_pool, v_pool))) return st;
-  if (!q || !page_table || !out || !lse || !aligned(q, 16) || !aligned(out, 16))
-    return KVATTN_E_INVALID;
-  if (n_q_tok < 1 || n_logical_pages < 1 || n_splits < 0) return KVATTN_E_INVALID;
+  if (!q || !page_table || !aligned(q, 16)) return KVATTN_E_INVALID;
+  if (n_q_tok < 1 || n_logical_pages < 1) return KVATTN_E_INVALID;
   if ((int64_t)n_q_tok * geom->gqa > KVATTN_MAX_QUERY_ROWS) return KVATTN_E_UNSUPPORTED;
   if (kv_len < n_q_tok || kv_len > (int64_t)n_logical_pages * KVATTN_PAGE_TOKENS)
     return KVATTN_E_INVALID;
   if (blocks && n_blk < 1) return KVATTN_E_INVALID;
-  if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
-    return KVATTN_E_INVALID;
-  const int32_t n_units =
-      blocks ? n_blk : (int32_t)((kv_len + KVATTN_PAGE_TOKENS - 1) / KVATTN_PAGE_TOKENS);
-  int n_cu = 256;
-  int32_t splits = n_splits;
-  if (splits == 0) {
-    // With a workspace query on a machine without a device, size for the
-    // default CU count; the launch below recomputes with the real count, so
-    // query and launch must run on the same device.
-    if (workspace && (st = current_device(&n_cu))) return st;
-    if (!workspace && current_device(&n_cu) != KVATTN_OK) n_cu = 256;
-    // two resident workgroups per CU (the decode kernel is built for two
-    // waves per SIMD), so that many splits over the KV heads
-    splits = (2 * n_cu + geom->n_kv_heads - 1) / geom->n_kv_heads;
-  }
+  if ((st = check_scale(scale))) return st;
+  *n_units = blocks ? n_blk : (int32_t)((kv_len + KVATTN_PAGE_TOKENS - 1) / KVATTN_PAGE_TOKENS);
+  return KVATTN_OK;
+}
+
+// Splits per KV head chosen by the library: two resident workgroups per CU
+// (the decode kernel is built for two waves per SIMD), spread over the KV
+// heads, at most one per unit.
+int32_t auto_decode_splits(int32_t n_kv, int32_t n_units, int n_cu) {
+  int32_t splits = (2 * n_cu + n_kv - 1) / n_kv;
   if (splits > n_units) splits = n_units;
-  if (splits < 1) splits = 1;
-  const int64_t rows = (int64_t)n_q_tok * geom->n_kv_heads * geom->gqa;
-  const size_t o_bytes = round_up(sizeof(float) * (size_t)splits * rows * KVATTN_HEAD_DIM);
-  const size_t need = o_bytes + round_up(sizeof(float) * (size_t)splits * rows);
-  bool query_only = false;
-  if ((st = workspace_check(workspace, workspace_bytes, need, &query_only))) return st;
-  if (query_only) return KVATTN_OK;
-  if ((st = current_device(nullptr))) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  return splits < 1 ? 1 : splits;
+}
+
+kvattn_status launch_decode_partials(const kvattn_geom* geom, const float* q, int32_t n_q_tok,
+                                     const uint8_t* k_pool, const uint8_t* v_pool,
+                                     const int32_t* page_table, int32_t n_logical_pages,
+                                     const int32_t* blocks, int32_t n_blk, int64_t kv_len,
+                                     float scale, int32_t n_units, int32_t splits, float* o_part,
+                                     float* lse_part, hipStream_t s) {
   DecodeParams p;
   p.q = q;
   p.k_pool = k_pool;
   p.v_pool = v_pool;
   p.page_table = page_table;
   p.blocks = blocks;
-  p.o_part = static_cast<float*>(workspace);
-  p.lse_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + o_bytes);
+  p.o_part = o_part;
+  p.lse_part = lse_part;
   p.kv_len = kv_len;
   p.n_units = n_units;
   p.n_splits = splits;
@@ -226,56 +230,46 @@ kvattn_status kvattn_decode(const kvattn_geom* geom, const float* q, int32_t n_q
   p.n_phys = geom->n_phys_pages;
   p.n_blk = blocks ? n_blk : 0;
   p.qscale = scale * kLog2e;
-  if ((st = launched(launch_decode(p, s)))) return st;
-  return launched(launch_merge(splits, rows, KVATTN_HEAD_DIM, p.o_part, p.lse_part, out, lse, s));
+  return launched(launch_decode(p, s));
 }
 
-kvattn_status kvattn_prefill_chunk(const kvattn_geom* geom, const float* q, int32_t chunk,
-                                   const uint8_t* k_pool, const uint8_t* v_pool,
-                                   const int32_t* page_table, int32_t n_logical_pages,
-                                   int64_t pos0, float scale, float* out, float* lse,
-                                   int32_t n_groups, void* workspace, size_t* workspace_bytes,
-                                   void* stream) {
+kvattn_status check_prefill(const kvattn_geom* geom, const float* q, int32_t chunk,
+                            const uint8_t* k_pool, const uint8_t* v_pool,
+                            const int32_t* page_table, int32_t n_logical_pages, int64_t pos0,
+                            float scale) {
   kvattn_status st = check_geom(geom);
   if (st) return st;
   if ((st = check_pools(geom, k_pool, v_pool))) return st;
-  if (!q || !page_table || !out || !lse || !aligned(q, 16) || !aligned(out, 16))
-    return KVATTN_E_INVALID;
-  if (chunk < 1 || pos0 < 0 || n_logical_pages < 1 || n_groups < 0) return KVATTN_E_INVALID;
+  if (!q || !page_table || !aligned(q, 16)) return KVATTN_E_INVALID;
+  if (chunk < 1 || pos0 < 0 || n_logical_pages < 1) return KVATTN_E_INVALID;
   if (pos0 + chunk > (int64_t)n_logical_pages * KVATTN_PAGE_TOKENS) return KVATTN_E_INVALID;
-  if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
-    return KVATTN_E_INVALID;
-  const int64_t kv_len = pos0 + chunk;
-  const int32_t n_pages = (int32_t)((kv_len + KVATTN_PAGE_TOKENS - 1) / KVATTN_PAGE_TOKENS);
-  const int64_t rows = (int64_t)chunk * geom->n_kv_heads * geom->gqa;
-  int32_t groups = n_groups;
-  if (groups == 0) {
-    int n_cu = 256;
-    if (workspace && (st = current_device(&n_cu))) return st;
-    if (!workspace && current_device(&n_cu) != KVATTN_OK) n_cu = 256;
-    const int64_t rows_per_head = (int64_t)chunk * geom->gqa;
-    const int64_t tiles = geom->n_kv_heads * ((rows_per_head + prefill_rows_per_tile() - 1) /
-                                              prefill_rows_per_tile());
-    int64_t gr = (3 * (int64_t)n_cu + tiles - 1) / tiles;  // about three rounds of the grid
-    if (gr < 1) gr = 1;
-    groups = (int32_t)gr;
-  }
-  if (groups > n_pages) groups = n_pages;
-  if (groups < 1) groups = 1;
-  const size_t o_bytes = round_up(sizeof(float) * (size_t)groups * rows * KVATTN_HEAD_DIM);
-  const size_t need = o_bytes + round_up(sizeof(float) * (size_t)groups * rows);
-  bool query_only = false;
-  if ((st = workspace_check(workspace, workspace_bytes, need, &query_only))) return st;
-  if (query_only) return KVATTN_OK;
-  if ((st = current_device(nullptr))) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  return check_scale(scale);
+}
+
+// Page groups chosen by the library: about three rounds of the grid, at most
+// one group per page.
+int32_t auto_prefill_groups(const kvattn_geom* geom, int32_t chunk, int64_t pos0, int n_cu) {
+  const int64_t n_pages = (pos0 + chunk + KVATTN_PAGE_TOKENS - 1) / KVATTN_PAGE_TOKENS;
+  const int64_t rows_per_head = (int64_t)chunk * geom->gqa;
+  const int64_t tiles =
+      geom->n_kv_heads * ((rows_per_head + prefill_rows_per_tile() - 1) / prefill_rows_per_tile());
+  int64_t gr = (3 * (int64_t)n_cu + tiles - 1) / tiles;
+  if (gr > n_pages) gr = n_pages;
+  return gr < 1 ? 1 : (int32_t)gr;
+}
+
+kvattn_status launch_prefill_partials(const kvattn_geom* geom, const float* q, int32_t chunk,
+                                      const uint8_t* k_pool, const uint8_t* v_pool,
+                                      const int32_t* page_table, int32_t n_logical_pages,
+                                      int64_t pos0, float scale, int32_t groups, float* o_part,
+                                      float* lse_part, hipStream_t s) {
   PrefillParams p;
   p.q = q;
   p.k_pool = k_pool;
   p.v_pool = v_pool;
   p.page_table = page_table;
-  p.o_part = static_cast<float*>(workspace);
-  p.lse_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + o_bytes);
+  p.o_part = o_part;
+  p.lse_part = lse_part;
   p.pos0 = pos0;
   p.chunk = chunk;
   p.n_groups = groups;
@@ -284,8 +278,131 @@ kvattn_status kvattn_prefill_chunk(const kvattn_geom* geom, const float* q, int3
   p.n_logical = n_logical_pages;
   p.n_phys = geom->n_phys_pages;
   p.qscale = scale * kLog2e;
-  if ((st = launched(launch_prefill(p, s)))) return st;
-  return launched(launch_merge(groups, rows, KVATTN_HEAD_DIM, p.o_part, p.lse_part, out, lse, s));
+  return launched(launch_prefill(p, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvattn_decode_splits(const kvattn_geom* geom, int32_t n_units) {
+  if (check_geom(geom) != KVATTN_OK || n_units < 1) return 0;
+  int n_cu = 256;
+  if (current_device(&n_cu) != KVATTN_OK) n_cu = 256;
+  return auto_decode_splits(geom->n_kv_heads, n_units, n_cu);
+}
+
+kvattn_status kvattn_decode(const kvattn_geom* geom, const float* q, int32_t n_q_tok,
+                            const uint8_t* k_pool, const uint8_t* v_pool,
+                            const int32_t* page_table, int32_t n_logical_pages,
+                            const int32_t* blocks, int32_t n_blk, int64_t kv_len, float scale,
+                            float* out, float* lse, int32_t n_splits, void* workspace,
+                            size_t* workspace_bytes, void* stream) {
+  int32_t n_units = 0;
+  kvattn_status st = check_decode(geom, q, n_q_tok, k_pool, v_pool, page_table, n_logical_pages,
+                                  blocks, n_blk, kv_len, scale, &n_units);
+  if (st) return st;
+  if (!out || !lse || !aligned(out, 16) || n_splits < 0) return KVATTN_E_INVALID;
+  int32_t splits = n_splits;
+  if (splits == 0) {
+    // With a workspace query on a machine without a device, size for the
+    // default CU count; the launch below recomputes with the real count, so
+    // query and launch must run on the same device.
+    int n_cu = 256;
+    if (workspace && (st = current_device(&n_cu))) return st;
+    if (!workspace && current_device(&n_cu) != KVATTN_OK) n_cu = 256;
+    splits = auto_decode_splits(geom->n_kv_heads, n_units, n_cu);
+  }
+  if (splits > n_units) splits = n_units;
+  const int64_t rows = (int64_t)n_q_tok * geom->n_kv_heads * geom->gqa;
+  const size_t o_bytes = round_up(sizeof(float) * (size_t)splits * rows * KVATTN_HEAD_DIM);
+  const size_t need = o_bytes + round_up(sizeof(float) * (size_t)splits * rows);
+  bool query_only = false;
+  if ((st = workspace_check(workspace, workspace_bytes, need, &query_only))) return st;
+  if (query_only) return KVATTN_OK;
+  if ((st = current_device(nullptr))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* o_part = static_cast<float*>(workspace);
+  float* lse_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + o_bytes);
+  if ((st = launch_decode_partials(geom, q, n_q_tok, k_pool, v_pool, page_table, n_logical_pages,
+                                   blocks, n_blk, kv_len, scale, n_units, splits, o_part, lse_part,
+                                   s)))
+    return st;
+  return launched(launch_merge(splits, rows, KVATTN_HEAD_DIM, o_part, lse_part, out, lse, s));
+}
+
+kvattn_status kvattn_decode_partials(const kvattn_geom* geom, const float* q, int32_t n_q_tok,
+                                     const uint8_t* k_pool, const uint8_t* v_pool,
+                                     const int32_t* page_table, int32_t n_logical_pages,
+                                     const int32_t* blocks, int32_t n_blk, int64_t kv_len,
+                                     float scale, int32_t n_splits, float* o_part,
+                                     float* lse_part, void* stream) {
+  int32_t n_units = 0;
+  kvattn_status st = check_decode(geom, q, n_q_tok, k_pool, v_pool, page_table, n_logical_pages,
+                                  blocks, n_blk, kv_len, scale, &n_units);
+  if (st) return st;
+  if (!o_part || !lse_part || !aligned(o_part, 16) || n_splits < 1) return KVATTN_E_INVALID;
+  if ((st = current_device(nullptr))) return st;
+  return launch_decode_partials(geom, q, n_q_tok, k_pool, v_pool, page_table, n_logical_pages,
+                                blocks, n_blk, kv_len, scale, n_units, n_splits, o_part, lse_part,
+                                static_cast<hipStream_t>(stream));
+}
+
+int32_t kvattn_prefill_groups(const kvattn_geom* geom, int32_t chunk, int64_t pos0) {
+  if (check_geom(geom) != KVATTN_OK || chunk < 1 || pos0 < 0) return 0;
+  int n_cu = 256;
+  if (current_device(&n_cu) != KVATTN_OK) n_cu = 256;
+  return auto_prefill_groups(geom, chunk, pos0, n_cu);
+}
+
+kvattn_status kvattn_prefill_chunk(const kvattn_geom* geom, const float* q, int32_t chunk,
+                                   const uint8_t* k_pool, const uint8_t* v_pool,
+                                   const int32_t* page_table, int32_t n_logical_pages,
+                                   int64_t pos0, float scale, float* out, float* lse,
+                                   int32_t n_groups, void* workspace, size_t* workspace_bytes,
+                                   void* stream) {
+  kvattn_status st =
+      check_prefill(geom, q, chunk, k_pool, v_pool, page_table, n_logical_pages, pos0, scale);
+  if (st) return st;
+  if (!out || !lse || !aligned(out, 16) || n_groups < 0) return KVATTN_E_INVALID;
+  const int32_t n_pages = (int32_t)((pos0 + chunk + KVATTN_PAGE_TOKENS - 1) / KVATTN_PAGE_TOKENS);
+  const int64_t rows = (int64_t)chunk * geom->n_kv_heads * geom->gqa;
+  int32_t groups = n_groups;
+  if (groups == 0) {
+    int n_cu = 256;
+    if (workspace && (st = current_device(&n_cu))) return st;
+    if (!workspace && current_device(&n_cu) != KVATTN_OK) n_cu = 256;
+    groups = auto_prefill_groups(geom, chunk, pos0, n_cu);
+  }
+  if (groups > n_pages) groups = n_pages;
+  const size_t o_bytes = round_up(sizeof(float) * (size_t)groups * rows * KVATTN_HEAD_DIM);
+  const size_t need = o_bytes + round_up(sizeof(float) * (size_t)groups * rows);
+  bool query_only = false;
+  if ((st = workspace_check(workspace, workspace_bytes, need, &query_only))) return st;
+  if (query_only) return KVATTN_OK;
+  if ((st = current_device(nullptr))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* o_part = static_cast<float*>(workspace);
+  float* lse_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + o_bytes);
+  if ((st = launch_prefill_partials(geom, q, chunk, k_pool, v_pool, page_table, n_logical_pages,
+                                    pos0, scale, groups, o_part, lse_part, s)))
+    return st;
+  return launched(launch_merge(groups, rows, KVATTN_HEAD_DIM, o_part, lse_part, out, lse, s));
+}
+
+kvattn_status kvattn_prefill_partials(const kvattn_geom* geom, const float* q, int32_t chunk,
+                                      const uint8_t* k_pool, const uint8_t* v_pool,
+                                      const int32_t* page_table, int32_t n_logical_pages,
+                                      int64_t pos0, float scale, int32_t n_groups, float* o_part,
+                                      float* lse_part, void* stream) {
+  kvattn_status st =
+      check_prefill(geom, q, chunk, k_pool, v_pool, page_table, n_logical_pages, pos0, scale);
+  if (st) return st;
+  if (!o_part || !lse_part || !aligned(o_part, 16) || n_groups < 1) return KVATTN_E_INVALID;
+  if ((st = current_device(nullptr))) return st;
+  return launch_prefill_partials(geom, q, chunk, k_pool, v_pool, page_table, n_logical_pages, pos0,
+                                 scale, n_groups, o_part, lse_part,
+                                 static_cast<hipStream_t>(stream));
 }
 
 kvattn_status kvattn_merge_lse(int32_t n_parts, int64_t rows, int32_t head_dim,

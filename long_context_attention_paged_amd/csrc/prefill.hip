@@ -318,23 +318,20 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
   }
   __syncthreads();  // counters cleared
 
-  // Step i: dequantise this wave's eighth of sub-tile i+1 (stage (i+1)%3,
-  // once every wave has read sub-tile i-2 from it), refill the raw slot with
-  // sub-tile i+3, then multiply sub-tile i once all eighths of it are in.
-  // The slowest wave never waits on a faster one: what it needs (sub-tile i-2
-  // read, sub-tile i written) every other wave finished before step i.
+  // Step i: dequantise this wave's eighth of sub-tile i+1 and multiply
+  // sub-tile i once all eighths of it are in. The slowest wave never waits on
+  // a faster one: what it needs (sub-tile i-2 read, sub-tile i written) every
+  // other wave finished before step i, whichever order it takes the jobs in.
   if (n_sub > 0) {
     if (n_sub > 1) wait_loads<RAW_LOADS>(); else wait_loads<0>();
     dequant(0);
     signal_count(produced + 0, lane);
     if (n_sub > 2) issue(2);
   }
-  for (int sub = 0; sub < n_sub; ++sub) {
-    if (((sub + 3) >> 2) >= win.first + 64) {  // sub .. sub + 3 stay in the window
-      wait_loads<0>();
-      win.load(p, t, sub >> 2, h, lane);
-    }
-    const int nx = sub + 1;
+  // Dequantise this wave's eighth of sub-tile nx into stage nx%3 (once every
+  // wave has read sub-tile nx-3 from it), then refill the raw slot with
+  // sub-tile nx+2.
+  auto produce = [&](int nx) {
     if (nx < n_sub) {
       if (nx + 1 < n_sub) wait_loads<RAW_LOADS>(); else wait_loads<0>();  // raw sub-tile nx in
       if (nx >= N_STAGES) wait_count(consumed + nx % N_STAGES, PF_WAVES * (nx / N_STAGES));
@@ -342,7 +339,16 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
       signal_count(produced + nx % N_STAGES, lane);  // also: raw slot of nx has been read
       if (nx + 2 < n_sub) issue(nx + 2);
     }
-
+  };
+  // The two waves of a SIMD (w and w+4) take the two jobs of a step in
+  // opposite orders, so one's dequantisation overlaps the other's products.
+  const bool deq_first = (wave & 4) == 0;
+  for (int sub = 0; sub < n_sub; ++sub) {
+    if (((sub + 3) >> 2) >= win.first + 64) {  // sub .. sub + 3 stay in the window
+      wait_loads<0>();
+      win.load(p, t, sub >> 2, h, lane);
+    }
+    if (deq_first) produce(sub + 1);
     const int st = sub % N_STAGES;
     wait_count(produced + st, PF_WAVES * (sub / N_STAGES + 1));
     const int64_t cur_tok0 = t.pg0 * PAGE + (int64_t)sub * 32;
@@ -428,6 +434,7 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
       }
     }
     signal_count(consumed + st, lane);
+    if (!deq_first) produce(sub + 1);
   }
 
   // ---- write this group's normalised partial ------------------------------

@@ -153,3 +153,38 @@ def test_python_binding_requires_gpu_tensors():
     import torch
     with pytest.raises((ValueError, TypeError)):
         kv.kvattn_merge_lse(torch.zeros(2, 4, 256), torch.zeros(2, 4))
+
+
+def test_partials_entry_points_validate_before_device():
+    import torch
+    lib = kv.load_library()
+    g = geom()
+    d = lib.kvattn_decode_partials
+    args = [ctypes.byref(g), P(FAKE), 1, P(FAKE), P(FAKE), P(FAKE), 16, None, 0, 1000, 0.0625]
+    assert d(*args, 0, P(FAKE), P(FAKE), None) == E_INVALID             # n_splits 0
+    assert d(*args, 4, P(FAKE + 4), P(FAKE), None) == E_INVALID         # misaligned o_part
+    assert d(*args, 4, P(FAKE), None, None) == E_INVALID                # no lse_part
+    assert d(ctypes.byref(geom(head_dim=128)), *args[1:], 4, P(FAKE), P(FAKE),
+             None) == E_UNSUPPORTED
+    p = lib.kvattn_prefill_partials
+    pargs = [ctypes.byref(g), P(FAKE), 100, P(FAKE), P(FAKE), P(FAKE), 16, 1000, 0.0625]
+    assert p(*pargs, 0, P(FAKE), P(FAKE), None) == E_INVALID            # n_groups 0
+    assert p(ctypes.byref(g), P(FAKE), 100, P(FAKE), P(FAKE), P(FAKE), 16, 2000, 0.0625, 4,
+             P(FAKE), P(FAKE), None) == E_INVALID                       # past the table
+    if not torch.cuda.is_available():
+        assert d(*args, 4, P(FAKE), P(FAKE), None) in (E_DEVICE, E_UNSUPPORTED)
+        assert p(*pargs, 4, P(FAKE), P(FAKE), None) in (E_DEVICE, E_UNSUPPORTED)
+
+
+def test_split_and_group_counts():
+    import torch
+    g = geom()
+    assert kv.kvattn_decode_splits(geom(head_dim=64), 100) == 0
+    assert kv.kvattn_decode_splits(g, 0) == 0
+    assert kv.kvattn_decode_splits(g, 3) == 3                            # at most one per unit
+    assert kv.kvattn_prefill_groups(g, 0, 0) == 0
+    assert kv.kvattn_prefill_groups(g, 100, 0) == 1                      # one page
+    if not torch.cuda.is_available():                                    # 256 CUs assumed
+        assert kv.kvattn_decode_splits(g, 2048) == 128                   # 2 x 256 / 4 heads
+        # 512 x 6 rows per head in 256-row tiles: 48 tiles, about three rounds
+        assert kv.kvattn_prefill_groups(g, 512, 262144) == 16

@@ -288,3 +288,72 @@ def test_prefill_indicator_causal_exact():
         counts = np.bincount(np.arange(n) // 128, minlength=256)[:256].astype(float)
         for gg in range(gqa):
             np.testing.assert_allclose(o[t, gg], counts / n, rtol=0, atol=2e-7)
+
+
+@pytest.mark.gpu
+def test_decode_partials_merge_to_decode():
+    """kvattn_decode_partials + kvattn_merge_lse is kvattn_decode, bit for bit;
+    each split's partial is attention over its own pages."""
+    n_kv, gqa, kv_len, S = 2, 6, 5000, 7
+    pools, table, _, _ = fill(n_kv, gqa, kv_len, seed=31, init_seed=9)
+    n_pages = len(table)
+    for n_q_tok in (1, 4):
+        q = np.random.default_rng(32 + n_q_tok).standard_normal(
+            (n_q_tok, n_kv * gqa, 256)).astype(np.float32)
+        qd, td = gpu(q), gpu(table, torch.int32)
+        out, lse = kv.kvattn_decode(pools.geom, qd, pools.gk, pools.gv, td, kv_len, 1 / 16,
+                                    n_splits=S)
+        op, lp = kv.kvattn_decode_partials(pools.geom, qd, pools.gk, pools.gv, td, kv_len, 1 / 16,
+                                           S)
+        o2, l2 = kv.kvattn_merge_lse(op, lp)
+        torch.cuda.synchronize()
+        assert torch.equal(out.reshape(-1, 256), o2.reshape(-1, 256))
+        assert torch.equal(lse.reshape(-1), l2.reshape(-1))
+    # n_q_tok = 1: split s against the oracle over pages [n*s/S, n*(s+1)/S)
+    q1 = np.random.default_rng(33).standard_normal((1, n_kv * gqa, 256)).astype(np.float32)
+    op, lp = kv.kvattn_decode_partials(pools.geom, gpu(q1), pools.gk, pools.gv,
+                                       gpu(table, torch.int32), kv_len, 1 / 16, S)
+    opn, lpn = host(op), host(lp)
+    for s in range(S):
+        pages = np.arange(n_pages * s // S, n_pages * (s + 1) // S)
+        blocks = np.stack([pages] * n_kv)
+        ref_o, ref_l = oracle.decode(q1, gqa, pools.ok, pools.ov, table, n_pages, kv_len, 1 / 16,
+                                     blocks=blocks)
+        assert np.abs(opn[s] - ref_o.reshape(-1, 256)).max() <= DEC_TOL
+        assert np.abs(lpn[s] - ref_l.reshape(-1)).max() <= 1e-3
+
+
+@pytest.mark.gpu
+def test_decode_partials_more_splits_than_pages():
+    """Splits past the unit count are empty: o = 0, lse = -inf, and the merge
+    still gives the oracle's result."""
+    n_kv, gqa, kv_len, S = 1, 6, 700, 9          # 6 pages, 9 splits
+    pools, table, _, _ = fill(n_kv, gqa, kv_len, seed=34, init_seed=10)
+    q = np.random.default_rng(35).standard_normal((1, gqa, 256)).astype(np.float32)
+    op, lp = kv.kvattn_decode_partials(pools.geom, gpu(q), pools.gk, pools.gv,
+                                       gpu(table, torch.int32), kv_len, 1 / 16, S)
+    lpn = host(lp)
+    empty = [s for s in range(S) if 6 * s // S == 6 * (s + 1) // S]
+    assert empty and all(np.isneginf(lpn[s]).all() for s in empty)
+    assert all((host(op)[s] == 0).all() for s in empty)
+    o2, l2 = kv.kvattn_merge_lse(op, lp)
+    ref_o, ref_l = oracle.decode(q, gqa, pools.ok, pools.ov, table, len(table), kv_len, 1 / 16)
+    eo, el, _ = compare(o2.reshape(1, gqa, 256), l2.reshape(1, gqa), ref_o.reshape(1, gqa, 256),
+                        ref_l.reshape(1, gqa))
+    assert eo <= DEC_TOL and el <= 1e-3
+
+
+@pytest.mark.gpu
+def test_prefill_partials_merge_to_prefill():
+    chunk, pos0, gqa, n_kv, G = 130, 1000, 6, 2, 3
+    kv_len = pos0 + chunk
+    pools, table, _, _ = fill(n_kv, gqa, kv_len, seed=36, init_seed=11)
+    q = np.random.default_rng(37).standard_normal((chunk, n_kv * gqa, 256)).astype(np.float32)
+    qd, td = gpu(q), gpu(table, torch.int32)
+    out, lse = kv.kvattn_prefill_chunk(pools.geom, qd, pools.gk, pools.gv, td, pos0, 1 / 16,
+                                       n_groups=G)
+    op, lp = kv.kvattn_prefill_partials(pools.geom, qd, pools.gk, pools.gv, td, pos0, 1 / 16, G)
+    o2, l2 = kv.kvattn_merge_lse(op, lp)
+    torch.cuda.synchronize()
+    assert torch.equal(out.reshape(-1, 256), o2.reshape(-1, 256))
+    assert torch.equal(lse.reshape(-1), l2.reshape(-1))
