@@ -33,6 +33,34 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16/bf16 matrix peak, published
 K_REC, V_REC = 34816, 18432
 METRIC = "decode-attn KV GB/s (% HBM peak) @262K; prefill-chunk TFLOP/s (% MFMA peak)"
 
+# HBM traffic per launch from rocprofv3 counter runs (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch) of `bench.py --profile-kernels`, scaled by what
+# the same counters read for a 1 GiB device copy in the same run (FETCH_SIZE
+# reads half of the copied bytes, WRITE_SIZE all of them). Valid only for the
+# kernel sources they were taken on: the sha256 prefixes below are checked at
+# run time and the traffic is reported as null once a source has changed.
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+TRAFFIC = {
+    "decode": {"sources": {"decode.hip": "69cb578be001d6c2", "common.hpp": "ed6f88ee167a235a"},
+               "fetch_kib": 213514.0, "write_kib": 12354.9},
+    "prefill": {"sources": {"prefill.hip": "638c01faea331a9f", "common.hpp": "ed6f88ee167a235a"},
+                "fetch_kib": 370403.0, "write_kib": 199156.0},
+}
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the counter runs, or None if its
+    sources changed since."""
+    import hashlib
+    t = TRAFFIC[kernel]
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "long_context_attention_paged_amd", "csrc")
+    for name, prefix in t["sources"].items():
+        with open(os.path.join(csrc, name), "rb") as f:
+            if not hashlib.sha256(f.read()).hexdigest().startswith(prefix):
+                return None
+    return int(round((t["fetch_kib"] * FETCH_SCALE + t["write_kib"] * WRITE_SCALE) * 1024))
+
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -317,6 +345,51 @@ def cpu_model():
     return platform.processor()
 
 
+def profile_kernels(dev, layers, reps):
+    """A short fixed sequence for counter runs (rocprofv3 --pmc): a device copy
+    of 1 GiB (the calibration kernel: reads and writes exactly 1 GiB), then the
+    decode kernel on verify-262k and the prefill kernel on prefill-512-after-262k,
+    each over `layers` per-layer pools, `reps` times."""
+    import torch
+    import long_context_attention_paged_amd as kv
+    from dataclasses import replace
+    from long_context_attention_paged_amd import synth
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    log(f"profile: copied {n} bytes x {reps}")
+    w = replace(synth.WORKLOADS[3], n_layers=layers)
+    pools = LayerPools(w, dev)
+    S = kv.kvattn_decode_splits(pools.geom, w.n_pages)
+    o_part = torch.empty((S, w.n_q_tok * w.n_heads, 256), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((S, w.n_q_tok * w.n_heads), dtype=torch.float32, device=dev)
+    for _ in range(reps):
+        for layer in range(layers):
+            kv.kvattn_decode_partials(pools.geom, pools.q[layer], pools.kp[layer],
+                                      pools.vp[layer], pools.table, w.kv_len, 1.0 / 16.0, S,
+                                      o_part=o_part, lse_part=lse_part)
+    torch.cuda.synchronize()
+    log(f"profile: decode_kernel x {reps * layers}, {w.kv_len * w.n_kv * 416} KV bytes each")
+    del pools, o_part, lse_part
+    torch.cuda.empty_cache()
+    w = replace(synth.WORKLOADS[4], n_layers=layers)
+    pools = LayerPools(w, dev)
+    G = kv.kvattn_prefill_groups(pools.geom, w.chunk, w.pos0)
+    o_part = torch.empty((G, w.chunk * w.n_heads, 256), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((G, w.chunk * w.n_heads), dtype=torch.float32, device=dev)
+    for _ in range(reps):
+        for layer in range(layers):
+            kv.kvattn_prefill_partials(pools.geom, pools.q[layer], pools.kp[layer],
+                                       pools.vp[layer], pools.table, w.pos0, 1.0 / 16.0, G,
+                                       o_part=o_part, lse_part=lse_part)
+    torch.cuda.synchronize()
+    log(f"profile: prefill_kernel x {reps * layers}, {prefill_flops_per_layer(w)} flop each")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -325,6 +398,9 @@ def main():
     ap.add_argument("--configs", default="3,4",
                     help="workloads to run: 2 decode-131k, 3 verify-262k, 4 prefill, 5 kvmem")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-kernels", action="store_true",
+                    help="run only a short fixed kernel sequence for counter runs (no JSON line)")
+    ap.add_argument("--layers", type=int, default=2, help="pools per workload in --profile-kernels")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -340,6 +416,9 @@ def main():
     kv.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.profile_kernels:
+        profile_kernels(dev, args.layers, max(1, args.steps))
+        return
     cfgs = [int(c) for c in args.configs.split(",") if c]
     extra = {}
     decode_res = prefill_res = None
@@ -400,7 +479,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(decode_res["kernel_gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("decode"),
             "kernel_us": round(decode_res["kernel_ms"] * 1e3, 2),
             "bytes_per_launch": decode_res["bytes_per_launch"],
             "call_us": round(decode_res["launch_ms"] * 1e3, 2),
@@ -422,7 +501,7 @@ def main():
                 "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s",
                 "frac": round(prefill_res["kernel_tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
-                "traffic": None,
+                "traffic": measured_traffic("prefill"),
                 "kernel_ms": round(prefill_res["kernel_ms"], 4),
                 "call_ms": round(prefill_res["launch_ms"], 4),
             },
