@@ -290,6 +290,72 @@ def bench_prefill(w, dev, steps, warmup):
     }, pools
 
 
+def bench_prefill_host_pool(w, dev, steps, warmup):
+    """Prefill with the page pool resident in pinned host memory (a7): while
+    layer L computes from one device staging pool, a copy stream fills the
+    other with layer L+1's pages; events order the two streams. The rate is
+    bound by the host link, not by the GPU."""
+    import torch
+    import long_context_attention_paged_amd as kv
+    pools = LayerPools(w, dev)
+    hk, hv = [], []
+    for layer in range(w.n_layers):  # move every layer's pool to pinned host memory
+        hk.append(torch.empty(pools.kp[layer].numel(), dtype=torch.uint8, pin_memory=True))
+        hv.append(torch.empty(pools.vp[layer].numel(), dtype=torch.uint8, pin_memory=True))
+        hk[layer].copy_(pools.kp[layer])
+        hv[layer].copy_(pools.vp[layer])
+    torch.cuda.synchronize()
+    pools.kp = pools.vp = None
+    torch.cuda.empty_cache()
+    stage_k = [torch.empty(hk[0].numel(), dtype=torch.uint8, device=dev) for _ in range(2)]
+    stage_v = [torch.empty(hv[0].numel(), dtype=torch.uint8, device=dev) for _ in range(2)]
+    pages = list(range(pools.n_phys))
+    outs = [torch.empty_like(q) for q in pools.q]
+    lses = [torch.empty(q.shape[:2], dtype=torch.float32, device=dev) for q in pools.q]
+    ws = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    copy = torch.cuda.Stream()
+    compute = torch.cuda.current_stream()
+
+    def step():
+        copied = [torch.cuda.Event() for _ in range(w.n_layers)]
+        done = [torch.cuda.Event() for _ in range(w.n_layers)]
+        for layer in range(w.n_layers + 1):
+            if layer < w.n_layers:  # copy layer `layer` once its staging slot is free
+                if layer >= 2:
+                    copy.wait_event(done[layer - 2])
+                kv.kvattn_prefetch_pages(pools.geom, hk[layer], hv[layer], stage_k[layer % 2],
+                                         stage_v[layer % 2], pages, stream=copy)
+                copied[layer].record(copy)
+            c = layer - 1           # compute the previous layer meanwhile
+            if c >= 0:
+                compute.wait_event(copied[c])
+                kv.kvattn_quantize_pages(pools.geom, pools.new_k[c], pools.new_v[c], w.pos0,
+                                         pools.table, stage_k[c % 2], stage_v[c % 2])
+                kv.kvattn_prefill_chunk(pools.geom, pools.q[c], stage_k[c % 2], stage_v[c % 2],
+                                        pools.table, w.pos0, 1.0 / 16.0, out=outs[c],
+                                        lse=lses[c], workspace=ws)
+                done[c].record(compute)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    fl = prefill_flops_per_layer(w)
+    pool_bytes = (hk[0].numel() + hv[0].numel()) * w.n_layers
+    return {
+        "ms_per_step": ms,
+        "tokens_per_s": w.chunk / (ms * 1e-3),
+        "tflops": fl * w.n_layers / (ms * 1e-3) / 1e12,
+        "host_to_device_bytes_per_step": pool_bytes,
+        "host_to_device_gbs": pool_bytes / (ms * 1e-3) / 1e9,
+        "note": "pool in pinned host memory, layer-ahead page prefetch on a copy stream",
+    }, pools
+
+
 def cpu_baseline_decode(w, pools):
     """The oracle, as it stands, on one (layer, KV head) of the workload."""
     import numpy as np
@@ -396,7 +462,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--configs", default="3,4",
-                    help="workloads to run: 2 decode-131k, 3 verify-262k, 4 prefill, 5 kvmem")
+                    help="workloads to run: 2 decode-131k, 3 verify-262k, 4 prefill, 5 kvmem, "
+                         "4h prefill with the pool in pinned host memory")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="run only a short fixed kernel sequence for counter runs (no JSON line)")
@@ -419,11 +486,21 @@ def main():
     if args.profile_kernels:
         profile_kernels(dev, args.layers, max(1, args.steps))
         return
-    cfgs = [int(c) for c in args.configs.split(",") if c]
+    cfgs = [c.strip() for c in args.configs.split(",") if c.strip()]
     extra = {}
     decode_res = prefill_res = None
     cpu = None
     for c in cfgs:
+        if c == "4h":
+            w = synth.WORKLOADS[4]
+            log(f"workload {w.name} (host pool)")
+            res, pools = bench_prefill_host_pool(w, dev, max(2, min(args.steps, 5)), 1)
+            extra[w.name + "-host-pool"] = res
+            del pools
+            torch.cuda.empty_cache()
+            log(f"{w.name} host pool: {json.dumps(res)}")
+            continue
+        c = int(c)
         w = synth.WORKLOADS[c]
         log(f"workload {w.name}")
         if c in (1, 2, 3):

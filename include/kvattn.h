@@ -303,6 +303,32 @@ kvattn_status kvattn_merge_lse(int32_t n_parts, int64_t rows, int32_t head_dim,
                                const float *o_parts, const float *lse_parts,
                                float *out, float *lse, void *stream);
 
+/* a7 — page prefetch for a host-resident pool ([RDNA4] "Online Log-Sum-Exp
+ * prefill & pipelined prefetch": pages stream in ahead of the layer that
+ * needs them; [STREAM] the Adaptive KV Streaming path keeps history in host
+ * memory). Copies the records of physical pages pages[0 .. n_pages-1] (all
+ * KV heads of each page) from the src pools to the same physical slots of the
+ * dst pools, asynchronously on `stream` (hipMemcpyAsync; runs of consecutive
+ * page indices go as one copy per pool). The typical use keeps the src pools
+ * in pinned host memory (hipHostMalloc) and the dst pools on the device, and
+ * issues layer L+1's pages on a copy stream while layer L computes; the
+ * caller orders the streams with events.
+ *  src_k_pool, src_v_pool, dst_k_pool, dst_v_pool: pools of geom's size
+ *    (host or device memory, any combination hipMemcpyAsync accepts;
+ *    pinned host memory for the copy to be asynchronous).
+ *  pages  HOST array of n_pages physical page indices in [0, n_phys_pages);
+ *         read before the call returns. n_pages >= 0 (0: nothing is done).
+ * Errors: E_INVALID for a null pool, n_pages < 0, pages NULL with
+ * n_pages > 0, or an index out of range (checked before any copy is
+ * enqueued); E_DEVICE if a copy cannot be enqueued (copies enqueued before it
+ * stay enqueued). */
+kvattn_status kvattn_prefetch_pages(const kvattn_geom *geom,
+                                    const uint8_t *src_k_pool,
+                                    const uint8_t *src_v_pool,
+                                    uint8_t *dst_k_pool, uint8_t *dst_v_pool,
+                                    const int32_t *pages, int32_t n_pages,
+                                    void *stream);
+
 #ifdef __cplusplus
 }
 #endif

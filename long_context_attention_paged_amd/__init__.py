@@ -15,7 +15,7 @@ __all__ = [
     "kvattn_quantize_pages", "kvattn_select_blocks", "kvattn_decode",
     "kvattn_decode_partials", "kvattn_decode_splits", "kvattn_prefill_chunk",
     "kvattn_prefill_partials", "kvattn_prefill_groups", "kvattn_merge_lse",
-    "kvattn_select_count",
+    "kvattn_prefetch_pages", "kvattn_select_count",
     "K_RECORD_BYTES", "V_RECORD_BYTES", "HEAD_DIM", "PAGE_TOKENS",
 ]
 
@@ -72,6 +72,7 @@ def load_library():
         "kvattn_prefill_partials": ([G, P, I32, P, P, P, I32, I64, F32, I32, P, P, P], I32),
         "kvattn_prefill_groups": ([G, I32, I64], I32),
         "kvattn_merge_lse": ([I32, I64, I32, P, P, P, P, P], I32),
+        "kvattn_prefetch_pages": ([G, P, P, P, P, P, I32, P], I32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -370,3 +371,28 @@ def kvattn_merge_lse(o_parts, lse_parts, out=None, lse=None, stream=None):
                                 _stream(stream))
     _check("kvattn_merge_lse", code)
     return out, lse
+
+
+def kvattn_prefetch_pages(geom, src_k_pool, src_v_pool, dst_k_pool, dst_v_pool, pages,
+                          stream=None):
+    """Page prefetch (a7): copy the records of physical `pages` (a host
+    sequence of ints) from the src pools (typically pinned host tensors) to the
+    dst pools (device tensors), asynchronously on `stream`."""
+    import numpy as np
+    torch = _torch()
+    lib = load_library()
+    for name, t in (("src_k_pool", src_k_pool), ("src_v_pool", src_v_pool)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous uint8 torch tensor")
+        if not t.is_cuda and not t.is_pinned():
+            raise ValueError(f"{name} must be on the GPU or in pinned host memory")
+    _need(dst_k_pool, "dst_k_pool", torch.uint8)
+    _need(dst_v_pool, "dst_v_pool", torch.uint8)
+    _pools(geom, dst_k_pool, dst_v_pool)
+    _pools(geom, src_k_pool, src_v_pool)
+    idx = np.ascontiguousarray(np.asarray(pages, dtype=np.int32))
+    _check("kvattn_prefetch_pages",
+           lib.kvattn_prefetch_pages(ctypes.byref(geom), _ptr(src_k_pool), _ptr(src_v_pool),
+                                     _ptr(dst_k_pool), _ptr(dst_v_pool),
+                                     idx.ctypes.data_as(ctypes.c_void_p), int(idx.size),
+                                     _stream(stream)))

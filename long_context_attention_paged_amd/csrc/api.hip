@@ -419,4 +419,38 @@ kvattn_status kvattn_merge_lse(int32_t n_parts, int64_t rows, int32_t head_dim,
                                static_cast<hipStream_t>(stream)));
 }
 
+
+kvattn_status kvattn_prefetch_pages(const kvattn_geom* geom, const uint8_t* src_k_pool,
+                                    const uint8_t* src_v_pool, uint8_t* dst_k_pool,
+                                    uint8_t* dst_v_pool, const int32_t* pages, int32_t n_pages,
+                                    void* stream) {
+  kvattn_status st = check_geom(geom);
+  if (st) return st;
+  if (!src_k_pool || !src_v_pool || !dst_k_pool || !dst_v_pool || n_pages < 0)
+    return KVATTN_E_INVALID;
+  if (n_pages > 0 && !pages) return KVATTN_E_INVALID;
+  for (int32_t i = 0; i < n_pages; ++i)
+    if (pages[i] < 0 || pages[i] >= geom->n_phys_pages) return KVATTN_E_INVALID;
+  if (n_pages == 0) return KVATTN_OK;
+  if ((st = current_device(nullptr))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // a physical page's records for all KV heads are contiguous in each pool;
+  // runs of consecutive page indices go as one copy per pool
+  const size_t k_page = (size_t)geom->n_kv_heads * KVATTN_K_RECORD_BYTES;
+  const size_t v_page = (size_t)geom->n_kv_heads * KVATTN_V_RECORD_BYTES;
+  int32_t i = 0;
+  while (i < n_pages) {
+    int32_t j = i + 1;
+    while (j < n_pages && pages[j] == pages[j - 1] + 1) ++j;
+    const size_t first = (size_t)pages[i], count = (size_t)(j - i);
+    if (hipMemcpyAsync(dst_k_pool + first * k_page, src_k_pool + first * k_page, count * k_page,
+                       hipMemcpyDefault, s) != hipSuccess ||
+        hipMemcpyAsync(dst_v_pool + first * v_page, src_v_pool + first * v_page, count * v_page,
+                       hipMemcpyDefault, s) != hipSuccess)
+      return KVATTN_E_DEVICE;
+    i = j;
+  }
+  return KVATTN_OK;
+}
+
 }  // extern "C"

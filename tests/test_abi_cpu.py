@@ -188,3 +188,25 @@ def test_split_and_group_counts():
         assert kv.kvattn_decode_splits(g, 2048) == 128                   # 2 x 256 / 4 heads
         # 512 x 6 rows per head in 256-row tiles: 48 tiles, about three rounds
         assert kv.kvattn_prefill_groups(g, 512, 262144) == 16
+
+
+def test_prefetch_validation_before_device():
+    import numpy as np
+    import torch
+    lib = kv.load_library()
+    g = geom(n_phys=16)
+    f = lib.kvattn_prefetch_pages
+    pages = np.array([0, 1, 2, 15], np.int32)
+    pp = pages.ctypes.data_as(ctypes.c_void_p)
+    assert f(ctypes.byref(g), P(FAKE), P(FAKE), P(FAKE), P(FAKE), pp, 4, None) in \
+        ((E_DEVICE, E_UNSUPPORTED) if not torch.cuda.is_available() else (OK,))
+    bad = np.array([0, 16], np.int32)                                   # 16 is out of range
+    assert f(ctypes.byref(g), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+             bad.ctypes.data_as(ctypes.c_void_p), 2, None) == E_INVALID
+    neg = np.array([-1], np.int32)
+    assert f(ctypes.byref(g), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+             neg.ctypes.data_as(ctypes.c_void_p), 1, None) == E_INVALID
+    assert f(ctypes.byref(g), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, 3, None) == E_INVALID
+    assert f(ctypes.byref(g), P(FAKE), P(FAKE), P(FAKE), P(FAKE), pp, -1, None) == E_INVALID
+    assert f(ctypes.byref(g), None, P(FAKE), P(FAKE), P(FAKE), pp, 4, None) == E_INVALID
+    assert f(ctypes.byref(g), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, 0, None) == OK  # no-op

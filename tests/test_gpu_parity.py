@@ -357,3 +357,58 @@ def test_prefill_partials_merge_to_prefill():
     torch.cuda.synchronize()
     assert torch.equal(out.reshape(-1, 256), o2.reshape(-1, 256))
     assert torch.equal(lse.reshape(-1), l2.reshape(-1))
+
+
+@pytest.mark.gpu
+def test_prefetch_pages_from_pinned_host():
+    """a7: records of the listed physical pages arrive bit for bit in the
+    device pool; other pages are untouched."""
+    n_kv, n_phys = 2, 12
+    g = kv.Geom(n_kv, 6, n_phys)
+    rng = np.random.default_rng(40)
+    hk = torch.from_numpy(rng.integers(0, 256, n_phys * n_kv * quant.K_RECORD_BYTES,
+                                       dtype=np.uint8)).pin_memory()
+    hv = torch.from_numpy(rng.integers(0, 256, n_phys * n_kv * quant.V_RECORD_BYTES,
+                                       dtype=np.uint8)).pin_memory()
+    dk = torch.zeros(hk.numel(), dtype=torch.uint8, device=DEV)
+    dv = torch.zeros(hv.numel(), dtype=torch.uint8, device=DEV)
+    pages = [3, 4, 5, 9, 0, 11]
+    copy = torch.cuda.Stream()
+    kv.kvattn_prefetch_pages(g, hk, hv, dk, dv, pages, stream=copy)
+    copy.synchronize()
+    K = host(dk).reshape(n_phys, -1)
+    V = host(dv).reshape(n_phys, -1)
+    HK, HV = hk.numpy().reshape(n_phys, -1), hv.numpy().reshape(n_phys, -1)
+    for p_ in range(n_phys):
+        if p_ in pages:
+            assert (K[p_] == HK[p_]).all() and (V[p_] == HV[p_]).all(), p_
+        else:
+            assert not K[p_].any() and not V[p_].any(), p_
+
+
+@pytest.mark.gpu
+def test_decode_over_prefetched_staging_pool():
+    """Layer-ahead streaming: the pool lives in pinned host memory, a copy
+    stream fills a device staging pool, an event gates the decode; the result
+    is the one decode gives on the device-resident pool, bit for bit."""
+    n_kv, gqa, kv_len = 2, 6, 3000
+    pools, table, _, _ = fill(n_kv, gqa, kv_len, seed=41, init_seed=12)
+    hk = torch.empty(pools.gk.numel(), dtype=torch.uint8, pin_memory=True)
+    hv = torch.empty(pools.gv.numel(), dtype=torch.uint8, pin_memory=True)
+    hk.copy_(pools.gk)
+    hv.copy_(pools.gv)
+    torch.cuda.synchronize()
+    sk = torch.zeros_like(pools.gk)
+    sv = torch.zeros_like(pools.gv)
+    q = np.random.default_rng(42).standard_normal((4, n_kv * gqa, 256)).astype(np.float32)
+    qd, td = gpu(q), gpu(table, torch.int32)
+    copy = torch.cuda.Stream()
+    ready = torch.cuda.Event()
+    kv.kvattn_prefetch_pages(pools.geom, hk, hv, sk, sv, sorted(set(table.tolist())),
+                             stream=copy)
+    ready.record(copy)
+    torch.cuda.current_stream().wait_event(ready)
+    o1, l1 = kv.kvattn_decode(pools.geom, qd, sk, sv, td, kv_len, 1 / 16, n_splits=8)
+    o2, l2 = kv.kvattn_decode(pools.geom, qd, pools.gk, pools.gv, td, kv_len, 1 / 16, n_splits=8)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
