@@ -461,7 +461,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--configs", default="3,4",
+    ap.add_argument("--configs", default="3,4,2,5",
                     help="workloads to run: 2 decode-131k, 3 verify-262k, 4 prefill, 5 kvmem, "
                          "4h prefill with the pool in pinned host memory")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -146,23 +146,40 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
 }
 
 // summary[h][p][n] = RN32(binary64 sum over slots t = 0..127 ascending of
-// d(t, n/32) * code(t, n), divided by 128). One workgroup per (page, head).
+// d(t, n/32) * code(t, n), divided by 128). One workgroup per (page, head):
+// the record's codes and scales are staged in LDS with 16-byte loads, then
+// thread n sums its column in order.
 __global__ __launch_bounds__(256) void summarize_kernel(const uint8_t* __restrict__ k_pool,
                                                         const int32_t* __restrict__ page_table,
                                                         int32_t n_kv, int32_t n_phys,
                                                         int32_t n_logical, int32_t first_page,
                                                         float* __restrict__ k_summary) {
+  __shared__ __attribute__((aligned(16))) uint8_t rec[K_REC];
   const int n = threadIdx.x;
   const int h = blockIdx.y;
   const int32_t lp = first_page + blockIdx.x;
   const int32_t phys = page_table[lp];
-  if (phys < 0 || phys >= n_phys) return;
+  if (phys < 0 || phys >= n_phys) return;  // uniform across the workgroup
   const uint8_t* krec = k_pool + ((int64_t)phys * n_kv + h) * K_REC;
-  const uint16_t* sc = reinterpret_cast<const uint16_t*>(krec + K_SCALE_OFF);
+  {  // 2176 16-byte pieces: 9 per thread (the last for threads < 128), issued together
+    uint4 v[9];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+      const int i = n + 256 * k;
+      v[k] = reinterpret_cast<const uint4*>(krec)[i < K_REC / 16 ? i : K_REC / 16 - 1];
+    }
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+      const int i = n + 256 * k;
+      if (i < K_REC / 16) reinterpret_cast<uint4*>(rec)[i] = v[k];
+    }
+  }
+  __syncthreads();
+  const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec + K_SCALE_OFF);
   double acc = 0.0;
   for (int t = 0; t < PAGE; ++t) {
     const float d = f16_value(sc[t * 8 + n / 32]);
-    const float kh = d * (float)(int8_t)krec[t * D + n];  // exact in binary32
+    const float kh = d * (float)(int8_t)rec[t * D + n];  // exact in binary32
     acc = acc + (double)kh;
   }
   k_summary[((int64_t)h * n_logical + lp) * D + n] = (float)(acc / 128.0);

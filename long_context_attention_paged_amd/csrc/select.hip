@@ -16,36 +16,80 @@
 namespace kvattn {
 namespace {
 
-constexpr int SCORE_BLOCKS = 64;  // candidate blocks scored per workgroup
+constexpr int SCORE_BLOCKS = 64;   // candidate blocks scored per workgroup
+constexpr int SCORE_THREADS = 256;  // all four waves stage, wave 0 sums
+constexpr int SCORE_LD = SCORE_BLOCKS + 1;
 
-// grid (ceil(n_cand / 64), n_kv), 256 threads. The 64 summaries are staged
-// through LDS with coalesced loads (row stride 257 words: conflict-free column
-// walks); lanes 0..63 then each run one block's fixed-order binary64 sum.
-__global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ q,
-                                                    const float* __restrict__ k_summary,
-                                                    int32_t gqa, int32_t n_logical,
-                                                    int32_t n_cand, double* __restrict__ scores) {
+// grid (ceil(n_cand / 64), n_kv), 256 threads. The 64 summaries (64 KB) are
+// staged in LDS, transposed to [dim][block] (row stride 65 words), by all four
+// waves with coalesced 16-byte loads (16 rows per wave, issued together);
+// then lane t of wave 0 reads its column 32 dims at a time (independent,
+// conflict-free reads) and runs block b0 + t's fixed-order binary64 sum over
+// ascending dims.
+__global__ __launch_bounds__(SCORE_THREADS) void score_kernel(const float* __restrict__ q,
+                                                              const float* __restrict__ k_summary,
+                                                              int32_t gqa, int32_t n_logical,
+                                                              int32_t n_cand,
+                                                              double* __restrict__ scores) {
   __shared__ float qs[D];
-  __shared__ float sm[SCORE_BLOCKS][D + 1];
-  const int tid = threadIdx.x;
+  __shared__ float sm[D * SCORE_LD];
+  const int tid = threadIdx.x, t = tid & 63, wave = tid >> 6;
   const int h = blockIdx.y;
   const int b0 = blockIdx.x * SCORE_BLOCKS;
+  const float* base = k_summary + ((int64_t)h * n_logical + b0) * D;
   {
+    // Row r is one coalesced 1 KB read (lane t: float4 t). Rows past the
+    // candidates re-read the last candidate's row (a valid address, so the
+    // loads need no branch) and store zeros.
+    const int last = n_cand - 1 - b0;
+    float4 v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int row = 16 * wave + k;
+      v[k] = *reinterpret_cast<const float4*>(base + (int64_t)(row < last ? row : last) * D + 4 * t);
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int row = 16 * wave + k;
+      const float4 w = row <= last ? v[k] : float4{0.f, 0.f, 0.f, 0.f};
+      sm[(4 * t + 0) * SCORE_LD + row] = w.x;
+      sm[(4 * t + 1) * SCORE_LD + row] = w.y;
+      sm[(4 * t + 2) * SCORE_LD + row] = w.z;
+      sm[(4 * t + 3) * SCORE_LD + row] = w.w;
+    }
+  }
+  {
+    // q_sel[n], n = tid: the group's query vectors summed in ascending order;
+    // the loads of eight members are issued together, the additions stay in
+    // order (members past gqa re-read the last one and are not added)
     double acc = 0.0;
-    for (int g = 0; g < gqa; ++g) acc = acc + (double)q[((int64_t)h * gqa + g) * D + tid];
+    for (int g0 = 0; g0 < gqa; g0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int gg = g0 + j < gqa ? g0 + j : gqa - 1;
+        v[j] = q[((int64_t)h * gqa + gg) * D + tid];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (g0 + j < gqa) acc = acc + (double)v[j];
+    }
     qs[tid] = (float)acc;
   }
-  const float* base = k_summary + ((int64_t)h * n_logical + b0) * D;
-  for (int i = tid; i < SCORE_BLOCKS * D; i += 256) {
-    const int row = i / D, col = i % D;
-    sm[row][col] = (b0 + row < n_cand) ? base[(int64_t)row * D + col] : 0.0f;
-  }
   __syncthreads();
-  if (tid < SCORE_BLOCKS && b0 + tid < n_cand) {
-    double acc = 0.0;
-    for (int n = 0; n < D; ++n) acc = acc + (double)qs[n] * (double)sm[tid][n];
-    scores[(int64_t)h * n_cand + b0 + tid] = acc;
+  if (wave != 0) return;
+  double acc = 0.0;
+  for (int c0 = 0; c0 < D; c0 += 32) {
+    float v[32];
+#pragma unroll
+    for (int n = 0; n < 32; ++n) v[n] = sm[(c0 + n) * SCORE_LD + t];
+    // all 32 reads are in flight before the first is used
+#pragma unroll
+    for (int n = 0; n < 32; ++n) __asm__ __volatile__("" : "+v"(v[n]));
+#pragma unroll
+    for (int n = 0; n < 32; ++n) acc = acc + (double)qs[c0 + n] * (double)v[n];
   }
+  if (b0 + t < n_cand) scores[(int64_t)h * n_cand + b0 + t] = acc;
 }
 
 // Order-preserving 64-bit key of a binary64 score (-0 is mapped to +0 first):
@@ -77,10 +121,14 @@ __device__ int block_exclusive_scan(int flag, int* warp_sums, int* total) {
   return off + before;
 }
 
+constexpr int TOPK_LDS_KEYS = 6144;  // keys held in LDS (48 KB); more are re-read from scores
+
 // One workgroup per KV head. Finds the k-th largest key by an 8-bit radix
-// select over the 64-bit keys, then marks keys above it plus, among keys equal
-// to it, the lowest block indices, and compacts the marked blocks in ascending
-// block order; the recent window follows.
+// select over the 64-bit keys (held in LDS when they fit), stopping early once
+// the digit bucket holding the k-th key is taken whole. Then marks the keys
+// above it plus, among keys equal to it, the lowest block indices, and
+// compacts the marked blocks in ascending block order; the recent window
+// follows.
 __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(const double* __restrict__ scores,
                                                             int32_t n_cand, int32_t k_sel,
                                                             int32_t n_recent, int32_t n_out,
@@ -88,7 +136,8 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(const double* __rest
   __shared__ int hist[256];
   __shared__ int warp_sums[TOPK_THREADS / 64];
   __shared__ uint64_t s_prefix;
-  __shared__ int s_krem;
+  __shared__ int s_krem, s_whole;
+  __shared__ uint64_t skeys[TOPK_LDS_KEYS];
   const int tid = threadIdx.x;
   const int h = blockIdx.x;
   int32_t* out = out_blocks + (int64_t)h * n_out;
@@ -98,13 +147,30 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(const double* __rest
     return;
   }
   const double* sc = scores + (int64_t)h * n_cand;
+  const bool cached = n_cand <= TOPK_LDS_KEYS;  // uniform
+  if (cached) {  // TOPK_LDS_KEYS / 1024 = 6 loads per thread, issued together
+    double v[TOPK_LDS_KEYS / TOPK_THREADS];
+#pragma unroll
+    for (int k = 0; k < TOPK_LDS_KEYS / TOPK_THREADS; ++k) {
+      const int i = tid + TOPK_THREADS * k;
+      v[k] = sc[i < n_cand ? i : n_cand - 1];
+    }
+#pragma unroll
+    for (int k = 0; k < TOPK_LDS_KEYS / TOPK_THREADS; ++k) {
+      const int i = tid + TOPK_THREADS * k;
+      if (i < n_cand) skeys[i] = score_key(v[k]);
+    }
+    __syncthreads();
+  }
+  auto key_at = [&](int i) -> uint64_t { return cached ? skeys[i] : score_key(sc[i]); };
   uint64_t prefix = 0, pmask = 0;
   int krem = k_sel;
+  bool whole = false;
   for (int shift = 56; shift >= 0; shift -= 8) {
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
     for (int i = tid; i < n_cand; i += TOPK_THREADS) {
-      const uint64_t key = score_key(sc[i]);
+      const uint64_t key = key_at(i);
       if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
     }
     __syncthreads();
@@ -122,42 +188,51 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(const double* __rest
       }
       int cum = incl - s;
       if (cum < krem && cum + s >= krem) {
-        int digit;
+        int digit, cnt;
         if (cum + c3 >= krem) {
-          digit = 4 * tid + 3;
+          digit = 4 * tid + 3, cnt = c3;
         } else if ((cum += c3) + c2 >= krem) {
-          digit = 4 * tid + 2;
+          digit = 4 * tid + 2, cnt = c2;
         } else if ((cum += c2) + c1 >= krem) {
-          digit = 4 * tid + 1;
+          digit = 4 * tid + 1, cnt = c1;
         } else {
           cum += c1;
-          digit = 4 * tid;
+          digit = 4 * tid, cnt = c0;
         }
         s_krem = krem - cum;
         s_prefix = prefix | ((uint64_t)digit << shift);
+        s_whole = cnt == krem - cum;  // the whole bucket is selected
       }
     }
     __syncthreads();
     prefix = s_prefix;
     pmask |= (uint64_t)255 << shift;
     krem = s_krem;
+    whole = s_whole != 0;
     __syncthreads();
+    if (whole) break;  // uniform
   }
-  // prefix is now the exact k-th largest key; krem of the equal keys are kept
+  // Selected: keys whose digits so far are above the chosen ones, and every
+  // key of the chosen bucket when it is taken whole; otherwise (prefix is the
+  // exact k-th key) the first krem keys equal to it by block index.
   const uint64_t thr = prefix;
   int eq_seen = 0, written = 0;
   for (int base = 0; base < n_cand; base += TOPK_THREADS) {
     const int i = base + tid;
-    uint64_t key = 0;
-    if (i < n_cand) key = score_key(sc[i]);
-    const int is_eq = (i < n_cand && key == thr) ? 1 : 0;
-    int eq_total;
-    const int eq_rank = eq_seen + block_exclusive_scan(is_eq, warp_sums, &eq_total);
-    const int keep = (i < n_cand) && (key > thr || (is_eq && eq_rank < krem));
+    const uint64_t key = i < n_cand ? key_at(i) : 0;
+    int keep;
+    if (whole) {
+      keep = (i < n_cand) && (key & pmask) >= thr;
+    } else {
+      const int is_eq = (i < n_cand && key == thr) ? 1 : 0;
+      int eq_total;
+      const int eq_rank = eq_seen + block_exclusive_scan(is_eq, warp_sums, &eq_total);
+      keep = (i < n_cand) && (key > thr || (is_eq && eq_rank < krem));
+      eq_seen += eq_total;
+    }
     int keep_total;
     const int pos = written + block_exclusive_scan(keep, warp_sums, &keep_total);
     if (keep) out[pos] = i;
-    eq_seen += eq_total;
     written += keep_total;
   }
 }
@@ -167,7 +242,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(const double* __rest
 hipError_t launch_score(const float* q, const float* k_summary, int32_t n_kv, int32_t gqa,
                         int32_t n_logical, int32_t n_cand, double* scores, hipStream_t stream) {
   dim3 grid((unsigned)((n_cand + SCORE_BLOCKS - 1) / SCORE_BLOCKS), (unsigned)n_kv);
-  hipLaunchKernelGGL(score_kernel, grid, dim3(256), 0, stream, q, k_summary, gqa, n_logical,
+  hipLaunchKernelGGL(score_kernel, grid, dim3(SCORE_THREADS), 0, stream, q, k_summary, gqa, n_logical,
                      n_cand, scores);
   return hipGetLastError();
 }
