@@ -201,7 +201,7 @@ kvattn_status check_decode(const kvattn_geom* geom, const float* q, int32_t n_q_
 // (the decode kernel is built for two waves per SIMD), spread over the KV
 // heads, at most one per unit.
 int32_t auto_decode_splits(int32_t n_kv, int32_t n_units, int n_cu) {
-  int32_t splits = (2 * n_cu + n_kv - 1) / n_kv;
+  int32_t splits = (DECODE_WGS_PER_CU * n_cu + n_kv - 1) / n_kv;
   if (splits > n_units) splits = n_units;
   return splits < 1 ? 1 : splits;
 }

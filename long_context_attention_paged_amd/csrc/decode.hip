@@ -7,10 +7,14 @@
 // the Adaptive KV Streaming guide (alphalab.site), step ④: flash attention
 // over Q8_0 K / Q4_0 V. The kernel design below is this library's.
 //
-// Work decomposition. Grid (splits, KV heads); 256 threads = 4 wavefronts.
-// A split owns a contiguous run of pages (or block-list entries); wavefront w
-// handles 32-token group w of every page in the run, so the four waves stream
-// the four quarters of one page together. Per 32-token group a wave computes
+// Work decomposition. Grid (splits, KV heads); 512 threads = 8 wavefronts,
+// one workgroup per CU. A split owns a contiguous run of pages (or block-list
+// entries); wavefront w handles 32-token group w % 4 of every other page of
+// the run (waves 0-3 the even ones, 4-7 the odd ones), so four waves stream
+// the four quarters of one page together. A CU-sized split halves the partials
+// written per layer against two 4-wave workgroups per CU. Every page-record
+// load is a buffer load straight into LDS whose base sits in scalar registers.
+// Per 32-token group a wave computes
 //   S^T (32 tokens x R rows) = Khat (32 x 256) . Q'^T      (16 mfma per N-tile)
 //   O^T (256 dims x R rows) += Vhat^T (256 x 32) . P'^T    (16 mfma per N-tile)
 // with v_mfma_f32_16x16x32_f16, R = query rows (n_q_tok * gqa) padded to 16
@@ -31,7 +35,6 @@
 namespace kvattn {
 namespace {
 
-constexpr int DEC_THREADS = 256;
 constexpr float RESCALE_MARGIN = 8.0f;  // log2 units
 // One 32-token tile of one KV head in LDS:
 //   [0, 8320)      key codes: 8 loads of 4 whole token rows (1 KB contiguous in
@@ -51,9 +54,23 @@ constexpr int Q_LDS_STRIDE = 264;       // halves per query row in LDS (256 + pa
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* lds_dst) {
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                   (lds_void*)(lds_dst), 16, 0, 0);
+// 16 bytes per lane from a buffer (one page record) straight into LDS: the
+// record base lives in scalar registers, the lane part is a 32-bit offset.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rec, int lane_off, int wave_off,
+                                      uint8_t* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rec, (lds_void*)(lds_dst), 16, lane_off, wave_off, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t record(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, 0x00020000);
+}
+
+// A copy of the lane id the compiler cannot see through, so per-lane offsets
+// derived from it are recomputed where used rather than held across the loop.
+__device__ __forceinline__ int opaque_lane() {
+  int ln = __lane_id();
+  __asm__ volatile("" : "+v"(ln));
+  return ln;
 }
 
 // Wait until at most n direct-to-LDS loads of this wave are outstanding
@@ -80,22 +97,23 @@ __device__ __forceinline__ int kbase(int i) { return i * 1024 + 16 * (i & 3) + 6
 // Position (16-byte unit) inside a key load of chunk s (0..15) of row a (0..3).
 __device__ __forceinline__ int kpos(int a, int s) { return 16 * a + ((s + 4 * a) & 15); }
 
-__device__ __forceinline__ void issue_keys(uint8_t* slot, const uint8_t* krec, int c, int lane,
-                                           int r16, int g) {
+__device__ __forceinline__ void issue_keys(uint8_t* slot, const uint8_t* krec, int c) {
+  const __amdgpu_buffer_rsrc_t r = record(krec, K_REC);
   // lane p of load i brings chunk s = (p%16 - 4a) & 15 of row a = p/16
+  const int lane = opaque_lane();
   const int a = lane >> 4, s = ((lane & 15) - 4 * a) & 15;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    dma16(krec + (c * 32 + 4 * i + a) * D + 16 * s, slot + SLOT_K + kbase(i));
-  if (lane < 32) dma16(krec + K_SCALE_OFF + (c * 32 + lane) * 16, slot + SLOT_KS);
+  for (int i = 0; i < 8; ++i) dma16(r, a * D + 16 * s, (c * 32 + 4 * i) * D, slot + SLOT_K + kbase(i));
+  if (lane < 32) dma16(r, lane * 16, K_SCALE_OFF + c * 512, slot + SLOT_KS);
 }
 
-__device__ __forceinline__ void issue_values(uint8_t* slot, const uint8_t* vrec, int c, int lane,
-                                             int r16, int g) {
+__device__ __forceinline__ void issue_values(uint8_t* slot, const uint8_t* vrec, int c) {
+  const __amdgpu_buffer_rsrc_t r = record(vrec, V_REC);
+  // value words are stored lane-ordered: load q of group c is 1 KB at (4c + q) KB
+  const int lane = opaque_lane();
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    dma16(vrec + ((((c * 4 + q) * 4 + g) * 16 + r16) * 4) * 4, slot + SLOT_V + q * 1024);
-  if (lane < 32) dma16(vrec + V_SCALE_OFF + c * 512 + lane * 16, slot + SLOT_VS);
+  for (int q = 0; q < 4; ++q) dma16(r, lane * 16, (c * 4 + q) * 1024, slot + SLOT_V + q * 1024);
+  if (lane < 32) dma16(r, lane * 16, V_SCALE_OFF + c * 512, slot + SLOT_VS);
 }
 
 template <int NT>
@@ -112,31 +130,46 @@ __device__ __forceinline__ void compute_tile(State<NT>& st, const uint8_t* slot,
                                              int64_t kv_len, int64_t min_limit, int lane, int r16,
                                              int g, uint32_t nib_mask, MidFn&& after_keys) {
   // ---- S^T = Khat . Q'^T --------------------------------------------------
+  // Both 16-token halves (m) share each q' operand read.
   floatx4 s[2][NT];
+  half2_t dlo[2], dhi[2];
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     const uint32_t sw = *reinterpret_cast<const uint32_t*>(slot + SLOT_KS + (16 * m + r16) * 16 + 4 * g);
-    const half2_t dlo = as_h2((sw & 0xFFFFu) | (sw << 16));
-    const half2_t dhi = as_h2((sw >> 16) | (sw & 0xFFFF0000u));
+    dlo[m] = as_h2((sw & 0xFFFFu) | (sw << 16));
+    dhi[m] = as_h2((sw >> 16) | (sw & 0xFFFF0000u));
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) s[m][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  // lane offsets recomputed per tile from an opaque copy of the lane id, so
+  // they are not kept live across the loop
+  int ln = lane;
+  __asm__ volatile("" : "+v"(ln));
+  const int kr16 = ln & 15, kg = ln >> 4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // bytes 64g + 16j of token 16m + r16: load 4m + r16/4, row r16%4, chunk 4g + j
-      const u32x4 w4 = *reinterpret_cast<const u32x4*>(
-          slot + SLOT_K + kbase(4 * m + (r16 >> 2)) + 16 * kpos(r16 & 3, 4 * g + j));
+  for (int j = 0; j < 4; ++j) {
+    // bytes 64g + 16j of token 16m + r16: load 4m + r16/4, row r16%4, chunk 4g + j
+    u32x4 w4[2];
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int ks = 2 * j + h2;
-        const half8_t a = k_codes_to_f16(h2 ? w4.z : w4.x, h2 ? w4.w : w4.y, ks < 4 ? dlo : dhi);
+    for (int m = 0; m < 2; ++m)
+      w4[m] = *reinterpret_cast<const u32x4*>(
+          slot + SLOT_K + kbase(4 * m + (kr16 >> 2)) + 16 * kpos(kr16 & 3, 4 * kg + j));
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const half8_t qb = *reinterpret_cast<const half8_t*>(
-              st.q_lds + (nt * 16 + r16) * Q_LDS_STRIDE + 64 * g + 8 * ks);
-          s[m][nt] = mfma16(a, qb, s[m][nt]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int ks = 2 * j + h2;
+      half8_t a[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        a[m] = k_codes_to_f16(h2 ? w4[m].z : w4[m].x, h2 ? w4[m].w : w4[m].y,
+                              ks < 4 ? dlo[m] : dhi[m]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const half8_t qb = *reinterpret_cast<const half8_t*>(
+            st.q_lds + (nt * 16 + r16) * Q_LDS_STRIDE + 64 * g + 8 * ks);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) s[m][nt] = mfma16(a[m], qb, s[m][nt]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   // the key half of the slot has been read: let the caller refill it
@@ -225,16 +258,19 @@ __device__ __forceinline__ void compute_tile(State<NT>& st, const uint8_t* slot,
   }
 }
 
-// NSTAGE: tiles per wave's LDS ring (1: load, wait, compute; the second wave
-// on the SIMD computes meanwhile). WPS: workgroups per CU the kernel is
-// compiled for (registers <= 512 / WPS per lane).
-template <int NT, int NSTAGE, int WPS>
-__global__ __launch_bounds__(DEC_THREADS, WPS) void decode_kernel(DecodeParams p) {
-  // LDS: [q' rows | 4 waves x NSTAGE tile slots] during the loop, then the
-  // combine buffer [4 waves][NT*16 rows][260] floats.
+// WAVES: wavefronts per workgroup (4 or 8); either way two wavefronts share
+// a SIMD (two 4-wave workgroups or one 8-wave workgroup per CU), so every
+// lane may hold up to 256 VGPRs. With 8 waves, waves 0-3 stream the even
+// units of the split and waves 4-7 the odd ones.
+template <int NT, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
+  constexpr int THREADS = 64 * WAVES;
+  constexpr int NH = WAVES / 4;  // units in flight per split
+  // LDS: [q' rows | one tile slot per wave] during the loop, then the
+  // combine buffer [WAVES][16 rows][260] floats.
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
   float* smem = reinterpret_cast<float*>(smem_raw);
-  __shared__ float s_m[4][32], s_l[4][32];
+  __shared__ float s_m[WAVES][32], s_l[WAVES][32];
   __shared__ int s_rowg[32];
   const int h = blockIdx.y, split = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -243,7 +279,7 @@ __global__ __launch_bounds__(DEC_THREADS, WPS) void decode_kernel(DecodeParams p
   const int R = p.n_q_tok * p.gqa;
   const int n_heads = p.n_kv * p.gqa;
   constexpr int Q_BYTES = ((NT * 16 * Q_LDS_STRIDE * 2) + 1023) / 1024 * 1024;
-  uint8_t* slots = smem_raw + Q_BYTES + wave * NSTAGE * SLOT_BYTES;  // NSTAGE == 1
+  uint8_t* slots = smem_raw + Q_BYTES + wave * SLOT_BYTES;
 
   _Float16* q_lds = reinterpret_cast<_Float16*>(smem_raw);
   State<NT> st;
@@ -264,15 +300,17 @@ __global__ __launch_bounds__(DEC_THREADS, WPS) void decode_kernel(DecodeParams p
 
   const int64_t u0 = (int64_t)p.n_units * split / p.n_splits;
   const int64_t u1 = (int64_t)p.n_units * (split + 1) / p.n_splits;
-  const int n_tiles = (int)(u1 - u0);
-  const int c = wave;  // 32-token group of every page handled by this wave
+  const int half = wave >> 2;  // this wave's units: u0 + half + NH * i
+  const int n_span = (int)(u1 - u0) - half;
+  const int n_tiles = n_span > 0 ? (n_span + NH - 1) / NH : 0;
+  const int c = wave & 3;  // 32-token group of every page handled by this wave
 
   // Page lookups for 64 upcoming units at a time, one per lane, read back
   // with readlane so every address is wavefront-uniform. Invalid tiles still
   // issue their 13 loads (from record 0) so the wait counts stay constant.
   int lp_vec = -1, ph_vec = -1;
-  auto refill = [&](int64_t ub) {
-    const int64_t u = ub + lane;
+  auto refill = [&](int i0) {
+    const int64_t u = u0 + half + (int64_t)NH * (i0 + lane);
     int lp = -1, ph = -1;
     if (u < u1) {
       lp = p.blocks ? p.blocks[(int64_t)h * p.n_blk + u] : (int)u;
@@ -287,7 +325,7 @@ __global__ __launch_bounds__(DEC_THREADS, WPS) void decode_kernel(DecodeParams p
   // Tile i's record; invalid tiles (skipped pages, tokens past kv_len) still
   // load from record 0 so every wait count below is a constant.
   auto locate = [&](int i, int64_t& tok, bool& valid, int64_t& rec) {
-    if (i % 64 == 0) refill(u0 + i);
+    if (i % 64 == 0) refill(i);
     const int lp = __builtin_amdgcn_readlane(lp_vec, i % 64);
     const int ph = __builtin_amdgcn_readlane(ph_vec, i % 64);
     valid = ph >= 0;
@@ -303,11 +341,11 @@ __global__ __launch_bounds__(DEC_THREADS, WPS) void decode_kernel(DecodeParams p
   bool valid = false, valid_n = false;
   if (n_tiles > 0) {
     locate(0, tok, valid, rec);
-    issue_keys(slot, p.k_pool + rec * K_REC, valid ? c : 0, lane, r16, g);
-    issue_values(slot, p.v_pool + rec * V_REC, valid ? c : 0, lane, r16, g);
+    issue_keys(slot, p.k_pool + rec * K_REC, valid ? c : 0);
+    issue_values(slot, p.v_pool + rec * V_REC, valid ? c : 0);
   }
-  // The first tile is in flight: stage q' rows (f16) into LDS, shared by the
-  // four waves (padding rows are zero). Row r of this KV head is query token
+  // The first tile is in flight: stage q' rows (f16) into LDS, shared by all
+  // waves (padding rows are zero). Row r of this KV head is query token
   // r / gqa, query head h*gqa + r % gqa; its global row goes to s_rowg.
   if (threadIdx.x < NT * 16) {
     const int r = threadIdx.x;
@@ -316,11 +354,11 @@ __global__ __launch_bounds__(DEC_THREADS, WPS) void decode_kernel(DecodeParams p
   }
   __syncthreads();
   {
-    constexpr int PER = NT * 16 * (D / 4) / DEC_THREADS;  // float4s per thread
+    constexpr int PER = NT * 16 * (D / 4) / THREADS;  // float4s per thread
     float4 qv[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int idx = threadIdx.x + DEC_THREADS * k;
+      const int idx = threadIdx.x + THREADS * k;
       const int r = idx >> 6, d4 = idx & 63;
       const int rowg = s_rowg[r];
       qv[k] = rowg >= 0 ? reinterpret_cast<const float4*>(p.q + (int64_t)rowg * D)[d4]
@@ -328,7 +366,7 @@ __global__ __launch_bounds__(DEC_THREADS, WPS) void decode_kernel(DecodeParams p
     }
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int idx = threadIdx.x + DEC_THREADS * k;
+      const int idx = threadIdx.x + THREADS * k;
       const int r = idx >> 6, d4 = idx & 63;
       const half2_t lo = {(_Float16)(qv[k].x * p.qscale), (_Float16)(qv[k].y * p.qscale)};
       const half2_t hi = {(_Float16)(qv[k].z * p.qscale), (_Float16)(qv[k].w * p.qscale)};
@@ -343,7 +381,7 @@ __global__ __launch_bounds__(DEC_THREADS, WPS) void decode_kernel(DecodeParams p
     auto refill_keys = [&] {
       if (more) {
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): key reads of this slot are done
-        issue_keys(slot, p.k_pool + rec_n * K_REC, valid_n ? c : 0, lane, r16, g);
+        issue_keys(slot, p.k_pool + rec_n * K_REC, valid_n ? c : 0);
         wait_loads<K_LOADS>();  // values of tile i have landed
       } else {
         wait_loads<0>();
@@ -356,14 +394,14 @@ __global__ __launch_bounds__(DEC_THREADS, WPS) void decode_kernel(DecodeParams p
     }
     if (more) {
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): value reads of this slot are done
-      issue_values(slot, p.v_pool + rec_n * V_REC, valid_n ? c : 0, lane, r16, g);
+      issue_values(slot, p.v_pool + rec_n * V_REC, valid_n ? c : 0);
     }
     tok = tok_n;
     rec = rec_n;
     valid = valid_n;
   }
 
-  // ---- combine the four wavefronts, write this split's partial --------------
+  // ---- combine the wavefronts, write this split's partial --------------------
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) st.l[nt] = wave_sum_xor_16_32(st.l[nt]);
   __syncthreads();  // every wave is done with the LDS ring and q_lds
@@ -383,10 +421,10 @@ __global__ __launch_bounds__(DEC_THREADS, WPS) void decode_kernel(DecodeParams p
       const int row = nt * 16 + r16;
       float M = neg_inf();
 #pragma unroll
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][row]);
+      for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][row]);
       float L = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
+      for (int w = 0; w < WAVES; ++w)
         if (s_m[w][row] != neg_inf()) L += s_l[w][row] * __builtin_amdgcn_exp2f(s_m[w][row] - M);
       const float f =
           (L > 0.f && st.m[nt] != neg_inf()) ? __builtin_amdgcn_exp2f(st.m[nt] - M) / L : 0.f;
@@ -396,20 +434,23 @@ __global__ __launch_bounds__(DEC_THREADS, WPS) void decode_kernel(DecodeParams p
         *reinterpret_cast<floatx4*>(buf + r16 * RS + 16 * mt + 4 * g) = st.o[nt][mt] * f;
     }
     __syncthreads();
-    // 16 rows x 64 float4 columns: four per thread, the four waves' values
-    // added in a fixed order
+    // 16 rows x 64 float4 columns, the waves' values added pairwise in a
+    // fixed order
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int idx = threadIdx.x + DEC_THREADS * k;
+    for (int k = 0; k < 16 * 64 / THREADS; ++k) {
+      const int idx = threadIdx.x + THREADS * k;
       const int rr = idx >> 6, c4 = idx & 63;
       const int rowg = s_rowg[nt * 16 + rr];
       if (rowg >= 0) {
-        const floatx4 a = *reinterpret_cast<const floatx4*>(smem + (0 * 16 + rr) * RS + 4 * c4);
-        const floatx4 b = *reinterpret_cast<const floatx4*>(smem + (1 * 16 + rr) * RS + 4 * c4);
-        const floatx4 c2 = *reinterpret_cast<const floatx4*>(smem + (2 * 16 + rr) * RS + 4 * c4);
-        const floatx4 d = *reinterpret_cast<const floatx4*>(smem + (3 * 16 + rr) * RS + 4 * c4);
-        reinterpret_cast<floatx4*>(p.o_part + ((int64_t)split * rows_total + rowg) * D)[c4] =
-            (a + b) + (c2 + d);
+        floatx4 v[WAVES];
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w)
+          v[w] = *reinterpret_cast<const floatx4*>(smem + (w * 16 + rr) * RS + 4 * c4);
+#pragma unroll
+        for (int step = 1; step < WAVES; step *= 2)
+#pragma unroll
+          for (int w = 0; w < WAVES; w += 2 * step) v[w] = v[w] + v[w + step];
+        reinterpret_cast<floatx4*>(p.o_part + ((int64_t)split * rows_total + rowg) * D)[c4] = v[0];
       }
     }
     __syncthreads();
@@ -418,29 +459,29 @@ __global__ __launch_bounds__(DEC_THREADS, WPS) void decode_kernel(DecodeParams p
     const int r = threadIdx.x;
     const int64_t rowg = s_rowg[r];
     float M = neg_inf();
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][r]);
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][r]);
     float L = 0.f;
-    for (int w = 0; w < 4; ++w)
+    for (int w = 0; w < WAVES; ++w)
       if (s_m[w][r] != neg_inf()) L += s_l[w][r] * __builtin_amdgcn_exp2f(s_m[w][r] - M);
     p.lse_part[(int64_t)split * rows_total + rowg] = (L > 0.f) ? (M + __log2f(L)) * LN2 : neg_inf();
   }
 }
 
-template <int NT, int NSTAGE, int WPS>
+template <int NT>
 hipError_t launch_nt(const DecodeParams& p, hipStream_t stream) {
-  const size_t combine = sizeof(float) * 4 * 16 * 260;
+  const size_t combine = sizeof(float) * DECODE_WAVES * 16 * 260;
   const size_t qbytes = ((NT * 16 * Q_LDS_STRIDE * 2) + 1023) / 1024 * 1024;
-  const size_t loop = qbytes + 4 * NSTAGE * SLOT_BYTES;
+  const size_t loop = qbytes + DECODE_WAVES * SLOT_BYTES;
   const size_t shmem = combine > loop ? combine : loop;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<NT, NSTAGE, WPS>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<NT, DECODE_WAVES>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   dim3 grid((unsigned)p.n_splits, (unsigned)p.n_kv);
-  hipLaunchKernelGGL((decode_kernel<NT, NSTAGE, WPS>), grid, dim3(DEC_THREADS), shmem, stream, p);
+  hipLaunchKernelGGL((decode_kernel<NT, DECODE_WAVES>), grid, dim3(64 * DECODE_WAVES), shmem, stream, p);
   return hipGetLastError();
 }
 
@@ -448,8 +489,8 @@ hipError_t launch_nt(const DecodeParams& p, hipStream_t stream) {
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const int R = p.n_q_tok * p.gqa;
-  if (R <= 16) return launch_nt<1, 1, 2>(p, stream);
-  return launch_nt<2, 1, 2>(p, stream);
+  if (R <= 16) return launch_nt<1>(p, stream);
+  return launch_nt<2>(p, stream);
 }
 
 }  // namespace kvattn

@@ -44,6 +44,11 @@ struct DecodeParams {
   float qscale;              // softmax scale * log2(e)
 };
 
+// Wavefronts per decode workgroup. The kernel is sized for one workgroup of
+// 8 (or two of 4) per CU; the default split count fills every CU once.
+constexpr int DECODE_WAVES = 8;
+constexpr int DECODE_WGS_PER_CU = 8 / DECODE_WAVES;
+
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
 struct PrefillParams {

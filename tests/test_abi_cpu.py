@@ -185,7 +185,7 @@ def test_split_and_group_counts():
     assert kv.kvattn_prefill_groups(g, 0, 0) == 0
     assert kv.kvattn_prefill_groups(g, 100, 0) == 1                      # one page
     if not torch.cuda.is_available():                                    # 256 CUs assumed
-        assert kv.kvattn_decode_splits(g, 2048) == 128                   # 2 x 256 / 4 heads
+        assert kv.kvattn_decode_splits(g, 2048) == 64                    # 256 CUs / 4 heads
         # 512 x 6 rows per head in 256-row tiles: 48 tiles, about three rounds
         assert kv.kvattn_prefill_groups(g, 512, 262144) == 16
 
