@@ -41,8 +41,9 @@ METRIC = "decode-attn KV GB/s (% HBM peak) @262K; prefill-chunk TFLOP/s (% MFMA 
 # run time and the traffic is reported as null once a source has changed.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
-    "decode": {"sources": {"decode.hip": "69cb578be001d6c2", "common.hpp": "ed6f88ee167a235a"},
-               "fetch_kib": 213514.0, "write_kib": 12354.9},
+    "decode": {"sources": {"decode.hip": "ffed503c19b6d031", "common.hpp": "ed6f88ee167a235a",
+                           "launch.hpp": "cac19bd41199d061"},
+               "fetch_kib": 213512.0, "write_kib": 6168.0},
     "prefill": {"sources": {"prefill.hip": "638c01faea331a9f", "common.hpp": "ed6f88ee167a235a"},
                 "fetch_kib": 370403.0, "write_kib": 199156.0},
 }
@@ -549,7 +550,7 @@ def main():
     }
     if decode_res:
         line["roofline"] = {
-            "kernel": "decode_kernel<2,1,2> (kvattn_decode_partials: split-K partials, "
+            "kernel": "decode_kernel<2,8> (kvattn_decode_partials: split-K partials, "
                       f"{decode_res['n_splits']} splits per KV head)",
             "bound": "hbm",
             "achieved": round(decode_res["kernel_gbs"], 2),
