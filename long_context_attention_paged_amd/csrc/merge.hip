@@ -87,9 +87,16 @@ __global__ __launch_bounds__(MERGE_THREADS) void merge_kernel(int32_t n_parts, i
 
 // head_dim == 256: one workgroup of 16 waves per row; lane l owns dims
 // 4l..4l+3 (one float4), so each part's row is one contiguous 1 KB read per
-// wave. Wave w takes parts w, w+16, ... with up to eight loads in flight per
-// lane; the 16 partial sums are added in a fixed order.
+// wave. Wave w takes parts w, w+16, ... in passes of M256_DEPTH parts per
+// wave; the 16 partial sums are added in a fixed order, so results are
+// deterministic. Every load is unconditional (indices clamped, weights of
+// absent or -inf parts zero, the select after the load), and the first
+// pass's partial rows are requested before the lse reductions, so a row
+// costs about one memory round trip when n_parts <= 16 * M256_DEPTH.
 constexpr int M256_WAVES = 16;
+constexpr int M256_THREADS = 64 * M256_WAVES;
+constexpr int M256_DEPTH = 8;
+constexpr int M256_PASS = M256_WAVES * M256_DEPTH;  // parts per pass
 
 __device__ __forceinline__ float block_reduce16(float x, float* red, bool is_max) {
   for (int o = 32; o >= 1; o >>= 1) {
@@ -104,49 +111,63 @@ __device__ __forceinline__ float block_reduce16(float x, float* red, bool is_max
   return t;
 }
 
-__global__ __launch_bounds__(64 * M256_WAVES) void merge256_kernel(int32_t n_parts, int64_t rows,
-                                                                   const float* __restrict__ o_parts,
-                                                                   const float* __restrict__ lse_parts,
-                                                                   float* __restrict__ out,
-                                                                   float* __restrict__ lse) {
-  constexpr int NT_ = 64 * M256_WAVES;
-  __shared__ float w[MERGE_WCHUNK];
+__global__ __launch_bounds__(M256_THREADS) void merge256_kernel(int32_t n_parts, int64_t rows,
+                                                                const float* __restrict__ o_parts,
+                                                                const float* __restrict__ lse_parts,
+                                                                float* __restrict__ out,
+                                                                float* __restrict__ lse) {
+  __shared__ float w[M256_PASS];
   __shared__ float red[M256_WAVES];
   __shared__ floatx4 acc_lds[M256_WAVES][64];
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  float m = neg_inf();
-  for (int s = tid; s < n_parts; s += NT_) m = fmaxf(m, lse_parts[(int64_t)s * rows + r]);
-  m = block_reduce16(m, red, true);
-  if (m == neg_inf()) {
-    if (wave == 0) reinterpret_cast<floatx4*>(out + r * 256)[lane] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (tid == 0) lse[r] = neg_inf();
-    return;
-  }
-  float se = 0.f;
-  for (int s = tid; s < n_parts; s += NT_) se += expf(lse_parts[(int64_t)s * rows + r] - m);
-  const float L = m + logf(block_reduce16(se, red, false));
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int last = n_parts - 1;
   const int64_t stride4 = rows * 64;  // float4s between consecutive parts
-  for (int s0 = 0; s0 < n_parts; s0 += MERGE_WCHUNK) {
-    const int cnt = min(MERGE_WCHUNK, n_parts - s0);
-    for (int i = tid; i < cnt; i += NT_) w[i] = expf(lse_parts[(int64_t)(s0 + i) * rows + r] - L);
-    __syncthreads();
-    const floatx4* op = reinterpret_cast<const floatx4*>(o_parts + ((int64_t)s0 * rows + r) * 256) + lane;
-    int i = wave;
-    for (; i + 7 * M256_WAVES < cnt; i += 8 * M256_WAVES) {
-      floatx4 v[8];
+  const floatx4* op = reinterpret_cast<const floatx4*>(o_parts + r * 256) + lane;
+  auto load_pass = [&](int s0, floatx4 (&v)[M256_DEPTH]) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = op[(int64_t)(i + M256_WAVES * u) * stride4];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float wu = w[i + M256_WAVES * u];
-        if (wu != 0.0f) acc += wu * v[u];  // a -inf part contributes nothing
-      }
+    for (int u = 0; u < M256_DEPTH; ++u) {
+      const int i = min(s0 + wave + M256_WAVES * u, last);
+      v[u] = op[(int64_t)i * stride4];
     }
-    for (; i < cnt; i += M256_WAVES) {
-      const float wi = w[i];
-      if (wi != 0.0f) acc += wi * op[(int64_t)i * stride4];
+  };
+  floatx4 v[M256_DEPTH];
+  load_pass(0, v);  // in flight during the reductions below
+
+  // this thread's first lse (part tid), later ones re-read (only when
+  // n_parts exceeds the workgroup)
+  const float my = lse_parts[(int64_t)min(tid, last) * rows + r];
+  float m = tid < n_parts ? my : neg_inf();
+  for (int s = tid + M256_THREADS; s < n_parts; s += M256_THREADS)
+    m = fmaxf(m, lse_parts[(int64_t)s * rows + r]);
+  m = block_reduce16(m, red, true);
+  const bool empty = m == neg_inf();  // uniform: every part is -inf
+  float se = 0.f;
+  if (!empty) {
+    se = tid < n_parts ? expf(my - m) : 0.f;
+    for (int s = tid + M256_THREADS; s < n_parts; s += M256_THREADS)
+      se += expf(lse_parts[(int64_t)s * rows + r] - m);
+  }
+  const float L = empty ? neg_inf() : m + logf(block_reduce16(se, red, false));
+
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < n_parts; s0 += M256_PASS) {
+    if (s0 > 0) load_pass(s0, v);
+    if (tid < M256_PASS) {  // weights of this pass; absent and -inf parts weigh 0
+      const int s = s0 + tid;
+      const float ls = s0 == 0 ? my : lse_parts[(int64_t)min(s, last) * rows + r];
+      w[tid] = (s < n_parts && !empty && ls != neg_inf()) ? expf(ls - L) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < M256_DEPTH; ++u) {
+      const float wu = w[wave + M256_WAVES * u];
+      const floatx4 t = wu * v[u];
+      // a zero weight contributes nothing, whatever the (unwritten) row holds
+      acc[0] += wu != 0.f ? t[0] : 0.f;
+      acc[1] += wu != 0.f ? t[1] : 0.f;
+      acc[2] += wu != 0.f ? t[2] : 0.f;
+      acc[3] += wu != 0.f ? t[3] : 0.f;
     }
     __syncthreads();
   }
@@ -167,7 +188,7 @@ hipError_t launch_merge(int32_t n_parts, int64_t rows, int32_t head_dim, const f
                         const float* lse_parts, float* out, float* lse, hipStream_t stream) {
   if (head_dim == 256 && (reinterpret_cast<uintptr_t>(o_parts) & 15) == 0 &&
       (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
-    hipLaunchKernelGGL(merge256_kernel, dim3((unsigned)rows), dim3(64 * M256_WAVES), 0, stream,
+    hipLaunchKernelGGL(merge256_kernel, dim3((unsigned)rows), dim3(M256_THREADS), 0, stream,
                        n_parts, rows, o_parts, lse_parts, out, lse);
     return hipGetLastError();
   }
