@@ -41,10 +41,10 @@ METRIC = "decode-attn KV GB/s (% HBM peak) @262K; prefill-chunk TFLOP/s (% MFMA 
 # run time and the traffic is reported as null once a source has changed.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
-    "decode": {"sources": {"decode.hip": "ffed503c19b6d031", "common.hpp": "ed6f88ee167a235a",
-                           "launch.hpp": "cac19bd41199d061"},
+    "decode": {"sources": {"decode.hip": "5fc7ace9330413eb", "common.hpp": "ed6f88ee167a235a",
+                           "launch.hpp": "2d81fda5089689a9"},
                "fetch_kib": 213512.0, "write_kib": 6168.0},
-    "prefill": {"sources": {"prefill.hip": "638c01faea331a9f", "common.hpp": "ed6f88ee167a235a"},
+    "prefill": {"sources": {"prefill.hip": "ef66795c3dfe19ab", "common.hpp": "ed6f88ee167a235a"},
                 "fetch_kib": 370403.0, "write_kib": 199156.0},
 }
 

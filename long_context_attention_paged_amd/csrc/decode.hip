@@ -473,13 +473,10 @@ hipError_t launch_nt(const DecodeParams& p, hipStream_t stream) {
   const size_t qbytes = ((NT * 16 * Q_LDS_STRIDE * 2) + 1023) / 1024 * 1024;
   const size_t loop = qbytes + DECODE_WAVES * SLOT_BYTES;
   const size_t shmem = combine > loop ? combine : loop;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<NT, DECODE_WAVES>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = set_lds_limit(
+      lds_set, reinterpret_cast<const void*>(&decode_kernel<NT, DECODE_WAVES>), shmem);
+  if (e != hipSuccess) return e;
   dim3 grid((unsigned)p.n_splits, (unsigned)p.n_kv);
   hipLaunchKernelGGL((decode_kernel<NT, DECODE_WAVES>), grid, dim3(64 * DECODE_WAVES), shmem, stream, p);
   return hipGetLastError();

@@ -6,7 +6,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace kvattn {
+
+// Raises a kernel's dynamic LDS limit to `bytes` on the current device, once
+// per device (the attribute is per device). `done` is the caller's
+// per-kernel set of devices already configured; thread-safe and idempotent.
+inline hipError_t set_lds_limit(std::atomic<uint64_t>& done, const void* kernel, size_t bytes) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  const uint64_t bit = uint64_t(1) << dev;
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  const hipError_t e =
+      hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 hipError_t launch_quantize(const float* k, const float* v, int64_t pos0, int32_t n_tok,
                            int32_t n_kv, const int32_t* page_table, int32_t n_phys,

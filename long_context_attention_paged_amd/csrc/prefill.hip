@@ -465,13 +465,10 @@ int32_t prefill_rows_per_tile() { return PF_ROWS; }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   const size_t shmem = sizeof(_Float16) * N_STAGES * STAGE_HALVES + RAW_DEPTH * RAW_STAGE;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e =
+      set_lds_limit(lds_set, reinterpret_cast<const void*>(&prefill_kernel), shmem);
+  if (e != hipSuccess) return e;
   const int64_t rows_head = (int64_t)p.chunk * p.gqa;
   const unsigned n_qtiles = (unsigned)((rows_head + PF_ROWS - 1) / PF_ROWS);
   dim3 grid((unsigned)p.n_groups, n_qtiles, (unsigned)p.n_kv);
