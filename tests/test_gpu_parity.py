@@ -123,6 +123,9 @@ DECODE_CASES = [
     (3, 5, 2, 777, 0),
     (4, 8, 1, 4, 0),
     (1, 1, 3, 130, 64),
+    (1, 6, 1, 1100, 2),       # 9 pages over 2 splits: 4 and 5 (odd) per split
+    (2, 16, 1, 2500, 0),      # 32 rows
+    (4, 6, 2, 64 * 128 * 3 + 5, 0),  # several pages per wave, partial last page
 ]
 
 
