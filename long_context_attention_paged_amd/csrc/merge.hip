@@ -8,7 +8,9 @@
 // Each lane owns one output dim; the four waves take interleaved quarters of
 // the parts and their partial sums are added in a fixed order in LDS, so
 // results are deterministic. Part weights are computed once per workgroup
-// into LDS. head_dim 256 (the decode and prefill partials) uses a float4 path.
+// into LDS. head_dim 256 (the decode and prefill partials) uses float4 paths:
+// a 16-wave workgroup per row when there are many parts (decode splits), one
+// wavefront per row when there are few parts and many rows (prefill groups).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -182,12 +184,89 @@ __global__ __launch_bounds__(M256_THREADS) void merge256_kernel(int32_t n_parts,
   if (tid == 0) lse[r] = L;
 }
 
+// head_dim == 256 with many rows and few parts (the prefill page groups):
+// one wavefront per row, four rows per workgroup, no LDS and no barrier.
+// Lane l owns dims 4l..4l+3; lane s holds lse of part s (passes of 64) for
+// the max and the sum; the parts' rows are then added in ascending part
+// order, MR_DEPTH rows in flight per lane.
+constexpr int MR_DEPTH = 16;
+
+__device__ __forceinline__ float wave_reduce(float x, bool is_max) {
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float y = __shfl_xor(x, o);
+    x = is_max ? fmaxf(x, y) : x + y;
+  }
+  return x;
+}
+
+__global__ __launch_bounds__(256) void merge_rows256_kernel(int32_t n_parts, int64_t rows,
+                                                            const float* __restrict__ o_parts,
+                                                            const float* __restrict__ lse_parts,
+                                                            float* __restrict__ out,
+                                                            float* __restrict__ lse) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;  // uniform across the wavefront
+  const int last = n_parts - 1;
+  const int64_t stride4 = rows * 64;  // float4s between consecutive parts
+  const floatx4* op = reinterpret_cast<const floatx4*>(o_parts + r * 256) + lane;
+  floatx4 v[MR_DEPTH];
+  auto load_pass = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < MR_DEPTH; ++u) v[u] = op[(int64_t)min(s0 + u, last) * stride4];
+  };
+  load_pass(0);  // in flight during the reductions below
+
+  const float my = lse_parts[(int64_t)min(lane, last) * rows + r];  // part `lane`
+  float m = lane < n_parts ? my : neg_inf();
+  for (int s = lane + 64; s < n_parts; s += 64) m = fmaxf(m, lse_parts[(int64_t)s * rows + r]);
+  m = wave_reduce(m, true);
+  const bool empty = m == neg_inf();  // every part is -inf
+  float se = 0.f;
+  if (!empty) {
+    se = lane < n_parts ? expf(my - m) : 0.f;
+    for (int s = lane + 64; s < n_parts; s += 64) se += expf(lse_parts[(int64_t)s * rows + r] - m);
+  }
+  const float L = empty ? neg_inf() : m + logf(wave_reduce(se, false));
+
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < n_parts; s0 += MR_DEPTH) {
+    if (s0 > 0) load_pass(s0);
+    // weight of part s0 + j sits in lane (s0 + j) % 64: this pass's weights
+    float wl = 0.f;
+    if (!empty) {
+      const int s = (s0 & ~63) + lane;
+      const float ls = s0 < 64 ? my : lse_parts[(int64_t)min(s, last) * rows + r];
+      wl = (s < n_parts && ls != neg_inf()) ? expf(ls - L) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < MR_DEPTH; ++u) {
+      const float wu = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), (s0 + u) & 63));
+      const floatx4 t = wu * v[u];
+      // a zero weight (absent or -inf part) contributes nothing, whatever the row holds
+      acc[0] += wu != 0.f ? t[0] : 0.f;
+      acc[1] += wu != 0.f ? t[1] : 0.f;
+      acc[2] += wu != 0.f ? t[2] : 0.f;
+      acc[3] += wu != 0.f ? t[3] : 0.f;
+    }
+  }
+  reinterpret_cast<floatx4*>(out + r * 256)[lane] = acc;
+  if (lane == 0) lse[r] = L;
+}
+
 }  // namespace
 
 hipError_t launch_merge(int32_t n_parts, int64_t rows, int32_t head_dim, const float* o_parts,
                         const float* lse_parts, float* out, float* lse, hipStream_t stream) {
-  if (head_dim == 256 && (reinterpret_cast<uintptr_t>(o_parts) & 15) == 0 &&
-      (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+  const bool vec4 = head_dim == 256 && (reinterpret_cast<uintptr_t>(o_parts) & 15) == 0 &&
+                    (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+  if (vec4 && n_parts <= 2 * MR_DEPTH && rows >= 1024) {
+    hipLaunchKernelGGL(merge_rows256_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
+                       n_parts, rows, o_parts, lse_parts, out, lse);
+    return hipGetLastError();
+  }
+  if (vec4) {
     hipLaunchKernelGGL(merge256_kernel, dim3((unsigned)rows), dim3(M256_THREADS), 0, stream,
                        n_parts, rows, o_parts, lse_parts, out, lse);
     return hipGetLastError();

@@ -242,7 +242,8 @@ def test_merge_parity():
     (NaN here for the GPU; zeros for the oracle). Part counts cover one pass,
     several passes and more parts than threads."""
     g = np.random.default_rng(40)
-    for S, rows, D in ((1, 5, 256), (7, 33, 256), (130, 7, 256), (300, 4, 100), (1100, 3, 256)):
+    for S, rows, D in ((1, 5, 256), (7, 33, 256), (130, 7, 256), (300, 4, 100), (1100, 3, 256),
+                       (16, 1501, 256), (3, 1024, 256), (32, 1100, 256)):  # last three: many rows
         o = g.standard_normal((S, rows, D)).astype(np.float32)
         ls = (g.standard_normal((S, rows)) * 3).astype(np.float32)
         ls[g.random((S, rows)) < 0.2] = -np.inf
