@@ -335,8 +335,13 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
     if (nx < n_sub) {
       if (nx + 1 < n_sub) wait_loads<RAW_LOADS>(); else wait_loads<0>();  // raw sub-tile nx in
       if (nx >= N_STAGES) wait_count(consumed + nx % N_STAGES, PF_WAVES * (nx / N_STAGES));
+      // Every wave waits for all eighths of a stage, so a dequantising wave
+      // holds up the workgroup: it outranks its SIMD partner's products
+      // until its eighth is published.
+      __builtin_amdgcn_s_setprio(2);
       dequant(nx);
       signal_count(produced + nx % N_STAGES, lane);  // also: raw slot of nx has been read
+      __builtin_amdgcn_s_setprio(0);
       if (nx + 2 < n_sub) issue(nx + 2);
     }
   };
