@@ -63,16 +63,16 @@ __device__ __forceinline__ void wait_loads() {
 
 // Wait until an LDS counter reaches target. The counters only grow, and each
 // wait is for work that the awaited waves reach without waiting on the
-// waiter (see the loop in prefill_kernel), so it ends. The spin is capped all
-// the same (2^20 sleeps, tens of milliseconds), so a broken invariant cannot
-// hang the GPU.
+// waiter (see the loop in prefill_kernel), so it ends. The poll has no sleep
+// (each round trip to LDS paces it, and a sleeping wave wakes late); it is
+// capped all the same (2^20 polls, tens of milliseconds), so a broken
+// invariant cannot hang the GPU.
 __device__ __forceinline__ void wait_count(const int* c, int target) {
   for (int spin = 0; spin < (1 << 20); ++spin) {
     // an LDS read (a generic one would also wait for the raw tile loads)
     const volatile __attribute__((address_space(3))) int* lc =
         (const volatile __attribute__((address_space(3))) int*)(c);
     if (__builtin_amdgcn_readfirstlane(*lc) >= target) break;
-    __builtin_amdgcn_s_sleep(1);
   }
   __asm__ __volatile__("" ::: "memory");
 }
@@ -318,10 +318,10 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
   }
   __syncthreads();  // counters cleared
 
-  // Step i: dequantise this wave's eighth of sub-tile i+1 and multiply
-  // sub-tile i once all eighths of it are in. The slowest wave never waits on
-  // a faster one: what it needs (sub-tile i-2 read, sub-tile i written) every
-  // other wave finished before step i, whichever order it takes the jobs in.
+  // Step i: multiply sub-tile i once all eighths of it are in, then
+  // dequantise this wave's eighth of sub-tile i+1. The slowest wave never
+  // waits on a faster one: what it needs (sub-tile i-2 read, sub-tile i
+  // written) every other wave finished before step i.
   if (n_sub > 0) {
     if (n_sub > 1) wait_loads<RAW_LOADS>(); else wait_loads<0>();
     dequant(0);
@@ -345,15 +345,15 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
       if (nx + 2 < n_sub) issue(nx + 2);
     }
   };
-  // The two waves of a SIMD (w and w+4) take the two jobs of a step in
-  // opposite orders, so one's dequantisation overlaps the other's products.
-  const bool deq_first = (wave & 4) == 0;
+  // Every wave multiplies first and dequantises after; the waves of a SIMD
+  // still drift apart, so one's dequantisation overlaps the other's
+  // products. (Measured: taking the jobs in opposite orders on the two waves
+  // of a SIMD, or dequantising first everywhere, is slower.)
   for (int sub = 0; sub < n_sub; ++sub) {
     if (((sub + 3) >> 2) >= win.first + 64) {  // sub .. sub + 3 stay in the window
       wait_loads<0>();
       win.load(p, t, sub >> 2, h, lane);
     }
-    if (deq_first) produce(sub + 1);
     const int st = sub % N_STAGES;
     wait_count(produced + st, PF_WAVES * (sub / N_STAGES + 1));
     const int64_t cur_tok0 = t.pg0 * PAGE + (int64_t)sub * 32;
@@ -439,7 +439,7 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
       }
     }
     signal_count(consumed + st, lane);
-    if (!deq_first) produce(sub + 1);
+    produce(sub + 1);
   }
 
   // ---- write this group's normalised partial ------------------------------
