@@ -151,22 +151,28 @@ __device__ __forceinline__ void dequant_raw(const uint8_t* raw, _Float16* stage,
   const int g = 2 * (w & 1) + gl;
   const RawIn in = read_raw(raw + RAW_K + ln * 16, raw + RAW_V + ((gl * 16 + d) * 4 + 2 * ep) * 4,
                             raw + RAW_VS + (ep * 2 + gl) * 16, raw + RAW_KS + u * 16 + 2 * b);
+  // n_live is wave-uniform and 32 on every sub-tile but a ragged last one
+  const bool full = n_live >= 32;
   {
     const uint32_t ks = in.ks & 0xFFFFu;
-    const half2_t d2 = as_h2(4 * w + u < n_live ? (ks | (ks << 16)) : 0u);  // zero scale -> zeros
+    uint32_t dw = ks | (ks << 16);
+    if (!full && 4 * w + u >= n_live) dw = 0u;  // zero scale -> zeros
+    const half2_t d2 = as_h2(dw);
     _Float16* krow = stage + (4 * w + u) * K_LDS_STRIDE + 32 * b + 16 * hh;
     *reinterpret_cast<half8_t*>(krow + 0) = k_codes_to_f16(in.k.x, in.k.y, d2);
     *reinterpret_cast<half8_t*>(krow + 8) = k_codes_to_f16(in.k.z, in.k.w, d2);
   }
   {
     // scales of block 2q + ep for lane group g (in.vs), masked past n_live
-    uint32_t scw[4];
+    uint32_t scw[4] = {in.vs[0], in.vs[1], in.vs[2], in.vs[3]};
+    if (!full) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int u0 = 16 * ((2 * p) >> 2) + 4 * g + ((2 * p) & 3);
-      const int u1 = 16 * ((2 * p + 1) >> 2) + 4 * g + ((2 * p + 1) & 3);
-      const uint32_t mk = (u0 < n_live ? 0x0000FFFFu : 0u) | (u1 < n_live ? 0xFFFF0000u : 0u);
-      scw[p] = in.vs[p] & mk;
+      for (int p = 0; p < 4; ++p) {
+        const int u0 = 16 * ((2 * p) >> 2) + 4 * g + ((2 * p) & 3);
+        const int u1 = 16 * ((2 * p + 1) >> 2) + 4 * g + ((2 * p + 1) & 3);
+        const uint32_t mk = (u0 < n_live ? 0x0000FFFFu : 0u) | (u1 < n_live ? 0xFFFF0000u : 0u);
+        scw[p] &= mk;
+      }
     }
     _Float16* vbase = stage + K_LDS_HALVES;
 #pragma unroll
