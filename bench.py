@@ -44,9 +44,9 @@ TRAFFIC = {
     "decode": {"sources": {"decode.hip": "5fc7ace9330413eb", "common.hpp": "ed6f88ee167a235a",
                            "launch.hpp": "2d81fda5089689a9"},
                "fetch_kib": 213512.0, "write_kib": 6168.0},
-    "prefill": {"sources": {"prefill.hip": "cc8ed514966d39ce", "common.hpp": "ed6f88ee167a235a",
+    "prefill": {"sources": {"prefill.hip": "231dfa6bd3338761", "common.hpp": "ed6f88ee167a235a",
                             "launch.hpp": "2d81fda5089689a9"},
-                "fetch_kib": 369384.0, "write_kib": 199505.0},
+                "fetch_kib": 369374.0, "write_kib": 199494.0},
 }
 
 
