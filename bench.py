@@ -37,24 +37,30 @@ METRIC = "decode-attn KV GB/s (% HBM peak) @262K; prefill-chunk TFLOP/s (% MFMA 
 # WRITE_SIZE, KiB per dispatch) of `bench.py --profile-kernels`, scaled by what
 # the same counters read for a 1 GiB device copy in the same run (FETCH_SIZE
 # reads half of the copied bytes, WRITE_SIZE all of them). Valid only for the
-# kernel sources they were taken on: the sha256 prefixes below are checked at
-# run time and the traffic is reported as null once a source has changed.
+# kernel sources and compile flags they were taken on: the sha256 prefixes and
+# the flags below are checked at run time and the traffic is reported as null
+# once either has changed.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
     "decode": {"sources": {"decode.hip": "5fc7ace9330413eb", "common.hpp": "ed6f88ee167a235a",
                            "launch.hpp": "2d81fda5089689a9"},
+               "flags": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
                "fetch_kib": 213512.0, "write_kib": 6168.0},
     "prefill": {"sources": {"prefill.hip": "231dfa6bd3338761", "common.hpp": "ed6f88ee167a235a",
                             "launch.hpp": "2d81fda5089689a9"},
+                "flags": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
                 "fetch_kib": 369374.0, "write_kib": 199494.0},
 }
 
 
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from the counter runs, or None if its
-    sources changed since."""
+    sources or compile flags changed since."""
     import hashlib
+    from long_context_attention_paged_amd import build
     t = TRAFFIC[kernel]
+    if build.EXTRA_FLAGS.get(f"{kernel}.hip", []) != t["flags"]:
+        return None
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                         "long_context_attention_paged_amd", "csrc")
     for name, prefix in t["sources"].items():

@@ -257,7 +257,9 @@ int32_t kvattn_decode_splits(const kvattn_geom *geom, int32_t n_units);
  *  n_groups page groups per (KV head, query tile) merged by LSE; 0 = chosen
  *           by the library.
  * Arithmetic: K/V tiles dequantised to f16 in LDS, f16 matrix-core products,
- * fp32 accumulation; within 1e-2 (max-abs) of exact attention. */
+ * fp32 accumulation; within 1e-2 (max-abs) of exact attention. q and the
+ * pool's scales must be finite: the kernel is compiled assuming no NaN
+ * operands, so a NaN input gives unspecified (not necessarily NaN) output. */
 kvattn_status kvattn_prefill_chunk(const kvattn_geom *geom, const float *q,
                                    int32_t chunk, const uint8_t *k_pool,
                                    const uint8_t *v_pool,
