@@ -111,6 +111,7 @@ typedef int32_t kvattn_status;
 #define KVATTN_K_RECORD_BYTES 34816
 #define KVATTN_V_RECORD_BYTES 18432
 #define KVATTN_MAX_QUERY_ROWS 32 /* n_q_tok * gqa per KV head in decode */
+#define KVATTN_MAX_APPEND_TOKENS 32 /* n_new of kvattn_append_decode */
 
 /* Geometry of one layer's pool. head_dim must be 256 and page_tokens 128
  * (the pages' shape: [VULKAN] "模型結構"; [KVMEM] --kvmem-block-tokens 128).
@@ -214,6 +215,41 @@ kvattn_status kvattn_decode(const kvattn_geom *geom, const float *q,
                             float *out, float *lse, int32_t n_splits,
                             void *workspace, size_t *workspace_bytes,
                             void *stream);
+
+/* a1 + a3/a5 in one launch — append, then decode: the step of a decode or
+ * verify pass that first writes the new tokens' keys and values into the
+ * cache ([STREAM] step ④ quantised KV cache; [RDNA4] verify batches through
+ * paged decode) and then attends over it. Equivalent to
+ *   kvattn_quantize_pages(geom, k_new, v_new, kv_len - n_new, n_new,
+ *                         page_table, n_logical_pages, k_pool, v_pool,
+ *                         k_summary, stream)
+ * followed by kvattn_decode with the other arguments: the pool bytes,
+ * summaries, out and lse are identical bit for bit. The decode kernel itself
+ * quantises the tokens: the wavefront that streams the tile holding them
+ * writes them before it reads that tile, so no separate quantisation launch
+ * is made (the summary of a page the append completes, when k_summary is not
+ * NULL, is one more launch after the merge).
+ *  k_new, v_new  fp32 [n_new][n_kv_heads][256], finite; the keys and values
+ *                of positions kv_len - n_new .. kv_len - 1.
+ *  n_new         1 <= n_new <= min(KVATTN_MAX_APPEND_TOKENS, kv_len).
+ *  k_pool, v_pool  written (the new tokens' slots) and read.
+ *  Sparse form: every logical page that holds a new token must appear in
+ *                blocks[h] of every KV head h (kvattn_select_blocks' recent
+ *                window does); the tokens of a page that is not listed are
+ *                not written.
+ * Other arguments, the workspace protocol and errors as kvattn_decode
+ * (KVATTN_E_INVALID also for bad k_new, v_new or n_new). */
+kvattn_status kvattn_append_decode(const kvattn_geom *geom, const float *k_new,
+                                   const float *v_new, int32_t n_new,
+                                   const float *q, int32_t n_q_tok,
+                                   uint8_t *k_pool, uint8_t *v_pool,
+                                   const int32_t *page_table,
+                                   int32_t n_logical_pages,
+                                   const int32_t *blocks, int32_t n_blk,
+                                   int64_t kv_len, float scale,
+                                   float *k_summary, float *out, float *lse,
+                                   int32_t n_splits, void *workspace,
+                                   size_t *workspace_bytes, void *stream);
 
 /* a3 alone — the split-K partials of kvattn_decode, without the merge, for
  * callers that combine them with partials computed elsewhere (other pages,

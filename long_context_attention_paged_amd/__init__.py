@@ -67,6 +67,8 @@ def load_library():
         "kvattn_select_blocks": ([G, P, P, I32, I32, I32, I32, P, P, SZP, P], I32),
         "kvattn_decode": ([G, P, I32, P, P, P, I32, P, I32, I64, F32, P, P, I32, P, SZP, P], I32),
         "kvattn_decode_partials": ([G, P, I32, P, P, P, I32, P, I32, I64, F32, I32, P, P, P], I32),
+        "kvattn_append_decode": ([G, P, P, I32, P, I32, P, P, P, I32, P, I32, I64, F32, P, P, P,
+                                  I32, P, SZP, P], I32),
         "kvattn_decode_splits": ([G, I32], I32),
         "kvattn_prefill_chunk": ([G, P, I32, P, P, P, I32, I64, F32, P, P, I32, P, SZP, P], I32),
         "kvattn_prefill_partials": ([G, P, I32, P, P, P, I32, I64, F32, I32, P, P, P], I32),
@@ -237,6 +239,44 @@ def kvattn_decode(geom, q, k_pool, v_pool, page_table, kv_len, scale, blocks=Non
 
     workspace, nbytes = _workspace(call, workspace, q.device)
     _check("kvattn_decode", call(_ptr(workspace), ctypes.byref(nbytes)))
+    return out, lse
+
+
+def kvattn_append_decode(geom, k_new, v_new, q, k_pool, v_pool, page_table, kv_len, scale,
+                         blocks=None, k_summary=None, out=None, lse=None, n_splits=0,
+                         workspace=None, stream=None):
+    """Append then decode in one launch (a1 + a3/a5): k_new, v_new [n_new, n_kv, 256]
+    are the keys and values of positions kv_len - n_new .. kv_len - 1; -> (out, lse)."""
+    torch = _torch()
+    lib = load_library()
+    n_blk = _decode_args(geom, q, k_pool, v_pool, page_table, blocks)
+    n_new = k_new.shape[0]
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _need(t, name, torch.float32)
+        _size(t, name, n_new * geom.n_kv_heads * HEAD_DIM)
+    if k_summary is not None:
+        _need(k_summary, "k_summary", torch.float32)
+        _size(k_summary, "k_summary", geom.n_kv_heads * page_table.numel() * HEAD_DIM)
+    n_q_tok = q.shape[0]
+    n_heads = geom.n_kv_heads * geom.gqa
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32)
+    _need(lse, "lse", torch.float32)
+    _size(out, "out", q.numel())
+    _size(lse, "lse", n_q_tok * n_heads)
+
+    def call(ws, nbytes):
+        return lib.kvattn_append_decode(ctypes.byref(geom), _ptr(k_new), _ptr(v_new), n_new,
+                                        _ptr(q), n_q_tok, _ptr(k_pool), _ptr(v_pool),
+                                        _ptr(page_table), page_table.numel(), _ptr(blocks), n_blk,
+                                        int(kv_len), float(scale), _ptr(k_summary), _ptr(out),
+                                        _ptr(lse), int(n_splits), ws, nbytes, _stream(stream))
+
+    workspace, nbytes = _workspace(call, workspace, q.device)
+    _check("kvattn_append_decode", call(_ptr(workspace), ctypes.byref(nbytes)))
     return out, lse
 
 

@@ -206,12 +206,22 @@ int32_t auto_decode_splits(int32_t n_kv, int32_t n_units, int n_cu) {
   return splits < 1 ? 1 : splits;
 }
 
+// The tokens kvattn_append_decode quantises inside the decode launch.
+struct AppendArgs {
+  const float* k_new;
+  const float* v_new;
+  uint8_t* k_pool;
+  uint8_t* v_pool;
+  int32_t n_new;
+};
+
 kvattn_status launch_decode_partials(const kvattn_geom* geom, const float* q, int32_t n_q_tok,
                                      const uint8_t* k_pool, const uint8_t* v_pool,
                                      const int32_t* page_table, int32_t n_logical_pages,
                                      const int32_t* blocks, int32_t n_blk, int64_t kv_len,
                                      float scale, int32_t n_units, int32_t splits, float* o_part,
-                                     float* lse_part, hipStream_t s) {
+                                     float* lse_part, hipStream_t s,
+                                     const AppendArgs* app = nullptr) {
   DecodeParams p;
   p.q = q;
   p.k_pool = k_pool;
@@ -230,6 +240,11 @@ kvattn_status launch_decode_partials(const kvattn_geom* geom, const float* q, in
   p.n_phys = geom->n_phys_pages;
   p.n_blk = blocks ? n_blk : 0;
   p.qscale = scale * kLog2e;
+  p.k_new = app ? app->k_new : nullptr;
+  p.v_new = app ? app->v_new : nullptr;
+  p.k_pool_w = app ? app->k_pool : nullptr;
+  p.v_pool_w = app ? app->v_pool : nullptr;
+  p.n_new = app ? app->n_new : 0;
   return launched(launch_decode(p, s));
 }
 
@@ -292,12 +307,17 @@ int32_t kvattn_decode_splits(const kvattn_geom* geom, int32_t n_units) {
   return auto_decode_splits(geom->n_kv_heads, n_units, n_cu);
 }
 
-kvattn_status kvattn_decode(const kvattn_geom* geom, const float* q, int32_t n_q_tok,
-                            const uint8_t* k_pool, const uint8_t* v_pool,
-                            const int32_t* page_table, int32_t n_logical_pages,
-                            const int32_t* blocks, int32_t n_blk, int64_t kv_len, float scale,
-                            float* out, float* lse, int32_t n_splits, void* workspace,
-                            size_t* workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// kvattn_decode, with the fused append when `app` is given.
+kvattn_status decode_impl(const kvattn_geom* geom, const float* q, int32_t n_q_tok,
+                          const uint8_t* k_pool, const uint8_t* v_pool,
+                          const int32_t* page_table, int32_t n_logical_pages,
+                          const int32_t* blocks, int32_t n_blk, int64_t kv_len, float scale,
+                          float* out, float* lse, int32_t n_splits, void* workspace,
+                          size_t* workspace_bytes, void* stream, const AppendArgs* app) {
   int32_t n_units = 0;
   kvattn_status st = check_decode(geom, q, n_q_tok, k_pool, v_pool, page_table, n_logical_pages,
                                   blocks, n_blk, kv_len, scale, &n_units);
@@ -326,9 +346,49 @@ kvattn_status kvattn_decode(const kvattn_geom* geom, const float* q, int32_t n_q
   float* lse_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + o_bytes);
   if ((st = launch_decode_partials(geom, q, n_q_tok, k_pool, v_pool, page_table, n_logical_pages,
                                    blocks, n_blk, kv_len, scale, n_units, splits, o_part, lse_part,
-                                   s)))
+                                   s, app)))
     return st;
   return launched(launch_merge(splits, rows, KVATTN_HEAD_DIM, o_part, lse_part, out, lse, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+kvattn_status kvattn_decode(const kvattn_geom* geom, const float* q, int32_t n_q_tok,
+                            const uint8_t* k_pool, const uint8_t* v_pool,
+                            const int32_t* page_table, int32_t n_logical_pages,
+                            const int32_t* blocks, int32_t n_blk, int64_t kv_len, float scale,
+                            float* out, float* lse, int32_t n_splits, void* workspace,
+                            size_t* workspace_bytes, void* stream) {
+  return decode_impl(geom, q, n_q_tok, k_pool, v_pool, page_table, n_logical_pages, blocks, n_blk,
+                     kv_len, scale, out, lse, n_splits, workspace, workspace_bytes, stream, nullptr);
+}
+
+kvattn_status kvattn_append_decode(const kvattn_geom* geom, const float* k_new, const float* v_new,
+                                   int32_t n_new, const float* q, int32_t n_q_tok,
+                                   uint8_t* k_pool, uint8_t* v_pool, const int32_t* page_table,
+                                   int32_t n_logical_pages, const int32_t* blocks, int32_t n_blk,
+                                   int64_t kv_len, float scale, float* k_summary, float* out,
+                                   float* lse, int32_t n_splits, void* workspace,
+                                   size_t* workspace_bytes, void* stream) {
+  if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16)) return KVATTN_E_INVALID;
+  if (n_new < 1 || n_new > KVATTN_MAX_APPEND_TOKENS || n_new > kv_len) return KVATTN_E_INVALID;
+  if (k_summary && !aligned(k_summary, 16)) return KVATTN_E_INVALID;
+  const AppendArgs app{k_new, v_new, k_pool, v_pool, n_new};
+  const kvattn_status st =
+      decode_impl(geom, q, n_q_tok, k_pool, v_pool, page_table, n_logical_pages, blocks, n_blk,
+                  kv_len, scale, out, lse, n_splits, workspace, workspace_bytes, stream, &app);
+  if (st || !workspace || !k_summary) return st;
+  // the summaries of the pages this append completes, from the updated pool
+  const int64_t pos0 = kv_len - n_new;
+  const int64_t first = pos0 / KVATTN_PAGE_TOKENS;
+  const int64_t last_full = kv_len / KVATTN_PAGE_TOKENS - 1;
+  if (last_full < first) return KVATTN_OK;
+  return launched(launch_summarize(k_pool, page_table, geom->n_kv_heads, geom->n_phys_pages,
+                                   n_logical_pages, (int32_t)first,
+                                   (int32_t)(last_full - first + 1), k_summary,
+                                   static_cast<hipStream_t>(stream)));
 }
 
 kvattn_status kvattn_decode_partials(const kvattn_geom* geom, const float* q, int32_t n_q_tok,

@@ -31,6 +31,7 @@
 // P' <= 256 fits f16 and the O accumulators are rarely touched.
 #include "common.hpp"
 #include "launch.hpp"
+#include "qround.hpp"
 
 namespace kvattn {
 namespace {
@@ -49,7 +50,6 @@ constexpr int SLOT_KS = 8320;
 constexpr int SLOT_V = 8832;
 constexpr int SLOT_VS = 12928;
 constexpr int SLOT_BYTES = 13440;
-constexpr int LOADS_PER_TILE = 13;      // 1 KB direct-to-LDS loads per tile
 constexpr int Q_LDS_STRIDE = 264;       // halves per query row in LDS (256 + pad)
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -258,6 +258,163 @@ __device__ __forceinline__ void compute_tile(State<NT>& st, const uint8_t* slot,
   }
 }
 
+// ---- fused append ------------------------------------------------------------
+// The newest n_new tokens are quantised into the pools by the wavefront that
+// streams the tile holding them, before it loads that tile (it waits for its
+// own stores first), so no other wavefront or workgroup depends on them. One
+// wavefront handles one slot at a time: lane (b, s) = (lane / 8, lane % 8)
+// takes elements 4s..4s+3 of 32-dim block b, and the block's largest
+// magnitude (keys) and lowest-index element of largest magnitude (values)
+// are reduced over its eight lanes. The lane's value dims n0..n0+3
+// (n0 = 32b + 4s) share (q, e) and take d = n0 % 16 .. +3, so each slot group
+// g gives the lane four words to merge.
+struct AppendTile {
+  int64_t tok;        // first position of the tile (32-token group c of its page)
+  int64_t rec;        // record index of the page and KV head
+  int ub, ue;         // new slots [ub, ue) of the tile
+  uint32_t newmask[4];  // per slot group g: bit j set when slot t(c, g, j) is new
+  uint32_t old[4][4];   // words (g, i) whose other slots keep their codes
+  float4 x[4], y[4];    // inputs of up to four slots in flight
+};
+
+__device__ __forceinline__ uint32_t slots_mask(uint32_t newmask) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (newmask & (1u << j)) m |= 0xFu << v_slot_bit(j);
+  return m;
+}
+
+// Word index (within the V record) of the lane's dim n0 + i in slot group g.
+__device__ __forceinline__ int append_word(int c, int g, int lane, int i) {
+  const int b = lane >> 3, s = lane & 7;
+  const int q = b >> 1, e = (2 * b + (s >> 2)) & 3, d = 4 * (s & 3) + i;
+  return c * 1024 + (((q * 4 + g) * 16 + d) * 4 + e);
+}
+
+__device__ __forceinline__ void append_load(const DecodeParams& p, const AppendTile& a, int h,
+                                            int64_t first_new, int u0, int lane, float4 (&x)[4],
+                                            float4 (&y)[4]) {
+  const int b = lane >> 3, s = lane & 7;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (u0 + k < a.ue) {  // uniform
+      const int64_t row = ((a.tok + u0 + k - first_new) * p.n_kv + h) * D + 32 * b + 4 * s;
+      x[k] = *reinterpret_cast<const float4*>(p.k_new + row);
+      y[k] = *reinterpret_cast<const float4*>(p.v_new + row);
+    }
+  }
+}
+
+// Requests the first slots' inputs and the old words of partly new V words.
+__device__ __forceinline__ void append_issue(const DecodeParams& p, AppendTile& a, int h, int c,
+                                             int64_t first_new, int lane) {
+  a.ub = (int)(first_new > a.tok ? first_new - a.tok : 0);
+  a.ue = (int)(p.kv_len - a.tok < 32 ? p.kv_len - a.tok : 32);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int u_lo = 4 * g + k, u_hi = 16 + 4 * g + k;  // slots j = k and j = 4 + k
+      if (u_lo >= a.ub && u_lo < a.ue) m |= 1u << k;
+      if (u_hi >= a.ub && u_hi < a.ue) m |= 1u << (4 + k);
+    }
+    a.newmask[g] = m;
+  }
+  append_load(p, a, h, first_new, a.ub, lane, a.x, a.y);
+  const uint32_t* vw = reinterpret_cast<const uint32_t*>(p.v_pool_w + a.rec * V_REC);
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      a.old[g][i] = (a.newmask[g] != 0 && a.newmask[g] != 0xFFu) ? vw[append_word(c, g, lane, i)] : 0u;
+}
+
+// Quantises every new slot of the tile and writes codes, scales and words.
+__device__ __forceinline__ void append_finish(const DecodeParams& p, AppendTile& a, int h, int c,
+                                              int64_t first_new, int lane) {
+  const int b = lane >> 3, s = lane & 7;
+  uint8_t* krec = p.k_pool_w + a.rec * K_REC;
+  uint8_t* vrec = p.v_pool_w + a.rec * V_REC;
+  uint32_t acc[4][4] = {};
+  for (int u0 = a.ub; u0 < a.ue; u0 += 4) {
+    if (u0 != a.ub) append_load(p, a, h, first_new, u0, lane, a.x, a.y);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int u = u0 + k;
+      if (u >= a.ue) break;  // uniform
+      const int t = c * 32 + u;
+      const float xe[4] = {a.x[k].x, a.x[k].y, a.x[k].z, a.x[k].w};
+      const float ye[4] = {a.y[k].x, a.y[k].y, a.y[k].z, a.y[k].w};
+      // keys: Q8_0
+      float amax = fmaxf(fmaxf(fabsf(xe[0]), fabsf(xe[1])), fmaxf(fabsf(xe[2]), fabsf(xe[3])));
+      amax = fmaxf(amax, __shfl_xor(amax, 1));
+      amax = fmaxf(amax, __shfl_xor(amax, 2));
+      amax = fmaxf(amax, __shfl_xor(amax, 4));
+      const _Float16 d16 = q8_scale(amax);
+      const float d = (float)d16;
+      uint32_t kw = 0u;
+      if (d != 0.0f) {
+        const float inv = 1.0f / d;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kw |= q8_code(xe[j], inv) << (8 * j);
+      }
+      *reinterpret_cast<uint32_t*>(krec + t * D + 32 * b + 4 * s) = kw;
+      if (s == 0)
+        *reinterpret_cast<uint16_t*>(krec + K_SCALE_OFF + (t * 8 + b) * 2) =
+            d != 0.0f ? __builtin_bit_cast(uint16_t, d16) : (uint16_t)0;
+      // values: Q4_0, the lowest-index element of largest magnitude sets the scale
+      float am = fabsf(ye[0]), m = ye[0];
+      int idx = 4 * s;
+#pragma unroll
+      for (int j = 1; j < 4; ++j)
+        if (fabsf(ye[j]) > am) {
+          am = fabsf(ye[j]);
+          m = ye[j];
+          idx = 4 * s + j;
+        }
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        const float am2 = __shfl_xor(am, o), m2 = __shfl_xor(m, o);
+        const int idx2 = __shfl_xor(idx, o);
+        if (am2 > am || (am2 == am && idx2 < idx)) {
+          am = am2;
+          m = m2;
+          idx = idx2;
+        }
+      }
+      const _Float16 dv16 = q4_scale(m);
+      const float dv = (float)dv16;
+      uint32_t code[4] = {8u, 8u, 8u, 8u};
+      uint16_t bits4 = 0;
+      if (am != 0.0f && dv != 0.0f) {
+        const float inv = 1.0f / dv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) code[j] = q4_code(ye[j], inv);
+        bits4 = __builtin_bit_cast(uint16_t, dv16);
+      }
+      const int g = (u & 15) >> 2, j = 4 * (u >> 4) + (u & 3);
+      if (s == 0)
+        *reinterpret_cast<uint16_t*>(vrec + V_SCALE_OFF + 2 * (((c * 8 + b) * 4 + g) * 8 + j)) = bits4;
+      const int bit = v_slot_bit(j);
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+        if (gg == g)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[gg][i] |= code[i] << bit;
+    }
+  }
+  uint32_t* vw = reinterpret_cast<uint32_t*>(vrec);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    if (a.newmask[g] == 0) continue;  // uniform
+    const uint32_t keep = a.newmask[g] == 0xFFu ? 0u : ~slots_mask(a.newmask[g]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vw[append_word(c, g, lane, i)] = (a.old[g][i] & keep) | acc[g][i];
+  }
+}
+
 // WAVES: wavefronts per workgroup (4 or 8); either way two wavefronts share
 // a SIMD (two 4-wave workgroups or one 8-wave workgroup per CU), so every
 // lane may hold up to 256 VGPRs. With 8 waves, waves 0-3 stream the even
@@ -339,10 +496,44 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
   uint8_t* slot = slots;
   int64_t tok = 0, rec = 0, tok_n = 0, rec_n = 0;
   bool valid = false, valid_n = false;
+  // Fused append: the one tile of this wave that holds new tokens, if any
+  // (n_new <= 32, and a wave keeps one 32-token group c of every page). Its
+  // inputs and old words are requested before the first tile's loads, the
+  // codes computed and stored while those loads fly; the tile itself is
+  // loaded only after this wave's stores have completed.
+  const int64_t first_new = p.kv_len - p.n_new;
+  bool app = false;
+  AppendTile at;
   if (n_tiles > 0) {
     locate(0, tok, valid, rec);
-    issue_keys(slot, p.k_pool + rec * K_REC, valid ? c : 0);
-    issue_values(slot, p.v_pool + rec * V_REC, valid ? c : 0);
+    if (p.n_new > 0) {
+      int i0 = 0;
+      for (; i0 < n_tiles; i0 += 64) {
+        if (i0 > 0) refill(i0);
+        const bool hit = ph_vec >= 0 && (int64_t)lp_vec * PAGE + c * 32 + 32 > first_new;
+        const uint64_t m = __ballot(hit);
+        if (m) {
+          const int l = (int)__builtin_ctzll(m);
+          at.tok = (int64_t)__builtin_amdgcn_readlane(lp_vec, l) * PAGE + c * 32;
+          at.rec = (int64_t)__builtin_amdgcn_readlane(ph_vec, l) * p.n_kv + h;
+          app = true;
+          break;
+        }
+      }
+      if (n_tiles > 64 && i0 > 0) refill(0);  // the loop starts from the first 64 units
+      if (app) append_issue(p, at, h, c, first_new, lane);
+    }
+    const bool first_new_tile = app && valid && tok + 32 > first_new;
+    if (!first_new_tile) {
+      issue_keys(slot, p.k_pool + rec * K_REC, valid ? c : 0);
+      issue_values(slot, p.v_pool + rec * V_REC, valid ? c : 0);
+    }
+    if (app) append_finish(p, at, h, c, first_new, lane);
+    if (first_new_tile) {
+      wait_loads<0>();  // this wave's stores have completed
+      issue_keys(slot, p.k_pool + rec * K_REC, c);
+      issue_values(slot, p.v_pool + rec * V_REC, c);
+    }
   }
   // The first tile is in flight: stage q' rows (f16) into LDS, shared by all
   // waves (padding rows are zero). Row r of this KV head is query token
@@ -381,6 +572,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
     auto refill_keys = [&] {
       if (more) {
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): key reads of this slot are done
+        if (app && valid_n && tok_n + 32 > first_new) wait_loads<0>();  // appended tile: stores done
         issue_keys(slot, p.k_pool + rec_n * K_REC, valid_n ? c : 0);
         wait_loads<K_LOADS>();  // values of tile i have landed
       } else {

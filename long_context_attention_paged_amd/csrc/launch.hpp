@@ -58,6 +58,13 @@ struct DecodeParams {
   int32_t n_phys;
   int32_t n_blk;
   float qscale;              // softmax scale * log2(e)
+  // Fused append (n_new > 0): positions kv_len - n_new .. kv_len - 1 are
+  // quantised from k_new / v_new ([n_new][n_kv][256]) into the pools first.
+  const float* k_new;
+  const float* v_new;
+  uint8_t* k_pool_w;         // k_pool / v_pool, writable
+  uint8_t* v_pool_w;
+  int32_t n_new;
 };
 
 // Wavefronts per decode workgroup. The kernel is sized for one workgroup of

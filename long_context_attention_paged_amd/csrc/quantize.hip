@@ -9,6 +9,7 @@
 // are reproducible bit for bit; nothing here may be contracted or reordered.
 #include "common.hpp"
 #include "launch.hpp"
+#include "qround.hpp"
 
 #pragma clang fp contract(off)
 
@@ -64,7 +65,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
-    const _Float16 d16 = (_Float16)(amax / 127.0f);
+    const _Float16 d16 = q8_scale(amax);
     const float d = (float)d16;
     uint32_t kw[8];
     if (d != 0.0f) {
@@ -73,10 +74,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
       for (int i = 0; i < 8; ++i) {
         uint32_t wv = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float r = fminf(fmaxf(rintf(x[4 * i + j] * inv), -127.0f), 127.0f);
-          wv |= ((uint32_t)(int)r & 0xFFu) << (8 * j);
-        }
+        for (int j = 0; j < 4; ++j) wv |= q8_code(x[4 * i + j], inv) << (8 * j);
         kw[i] = wv;
       }
     } else {
@@ -98,15 +96,12 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
         m = y[i];
       }
     uint16_t bits4 = 0;
-    const _Float16 dv16 = (_Float16)((-m) / 8.0f);
+    const _Float16 dv16 = q4_scale(m);
     const float dv = (float)dv16;
     if (a != 0.0f && dv != 0.0f) {
       const float inv = 1.0f / dv;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const float r = fminf(fmaxf(rintf(y[i] * inv), -8.0f), 7.0f);
-        vcodes[u][32 * b + i] = (uint8_t)((int)r + 8);
-      }
+      for (int i = 0; i < 32; ++i) vcodes[u][32 * b + i] = (uint8_t)q4_code(y[i], inv);
       bits4 = __builtin_bit_cast(uint16_t, dv16);
     } else {
 #pragma unroll
@@ -127,7 +122,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int uu = 16 * (j >> 2) + 4 * g + (j & 3);
-      const int bit = 4 * (j >> 1) + 16 * (j & 1);
+      const int bit = v_slot_bit(j);
       const int64_t p = gpos + uu;
       const uint32_t nib = (whole || (p >= pos0 && p < end)) ? (uint32_t)vcodes[uu][dim]
                                                                : (old[qq] >> bit) & 0xFu;

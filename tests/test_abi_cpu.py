@@ -93,6 +93,36 @@ def test_decode_workspace_protocol():
     assert code == OK and need1 > 0
 
 
+def append_decode(g, **kw):
+    a = dict(k_new=FAKE, v_new=FAKE, n_new=4, q=FAKE, n_q_tok=4, k_pool=FAKE, v_pool=FAKE,
+             table=FAKE, n_logical=16, blocks=None, n_blk=0, kv_len=1000, scale=0.0625,
+             summ=None, out=FAKE, lse=FAKE, n_splits=0, ws=FAKE, nbytes=1 << 30)
+    a.update(kw)
+    nb = ctypes.c_size_t(a["nbytes"])
+    code = kv.load_library().kvattn_append_decode(
+        ctypes.byref(g), P(a["k_new"]), P(a["v_new"]), a["n_new"], P(a["q"]), a["n_q_tok"],
+        P(a["k_pool"]), P(a["v_pool"]), P(a["table"]), a["n_logical"], P(a["blocks"]), a["n_blk"],
+        a["kv_len"], a["scale"], P(a["summ"]), P(a["out"]), P(a["lse"]), a["n_splits"],
+        P(a["ws"]), ctypes.byref(nb), None)
+    return code, nb.value
+
+
+def test_append_decode_validation_and_workspace():
+    g = geom()
+    assert append_decode(g, k_new=0)[0] == E_INVALID
+    assert append_decode(g, v_new=FAKE + 4)[0] == E_INVALID      # misaligned
+    assert append_decode(g, n_new=0)[0] == E_INVALID
+    assert append_decode(g, n_new=33)[0] == E_INVALID             # more than 32 new tokens
+    assert append_decode(g, n_new=5, n_q_tok=1, kv_len=4)[0] == E_INVALID  # n_new > kv_len
+    assert append_decode(g, summ=FAKE + 4)[0] == E_INVALID
+    assert append_decode(g, n_q_tok=6)[0] == E_UNSUPPORTED       # decode's own checks apply
+    assert append_decode(g, kv_len=16 * 128 + 1)[0] == E_INVALID
+    # the workspace is kvattn_decode's
+    code, need = append_decode(g, ws=None, nbytes=0, n_splits=8)
+    assert code == OK and need == decode(g, ws=None, nbytes=0, n_splits=8, n_q_tok=4)[1]
+    assert append_decode(g, n_splits=8, nbytes=need - 1)[0] == E_WORKSPACE
+
+
 def test_prefill_and_select_validation():
     lib = kv.load_library()
     g = geom()

@@ -33,6 +33,10 @@ def special_blocks(K, V):
     V[3, 0, 96 + 5] = 1e-9                               # scale underflows in binary16
     K[4, 0, 128:160] *= 50.0                             # outlier block
     V[5, 0, :32] = ((np.arange(32) % 16 - 8) * 2.0 ** -5).astype(np.float32)  # exact grid
+    V[6, 0, 160:192] = 0.25
+    V[6, 0, 160 + 30], V[6, 0, 160 + 9], V[6, 0, 160 + 17] = 3.0, -3.0, 3.0  # tie over far-apart indices
+    V[7, 0, 192:224] = -0.5
+    V[7, 0, 192 + 1], V[7, 0, 192 + 2] = -4.0, 4.0       # tie inside one group of four
 
 
 def test_quantize_bitexact_incremental():
