@@ -6,8 +6,9 @@ query tokens causal among themselves) and chunked-prefill TFLOP/s (512-token
 chunk after 262144 prior tokens), both against the chip's peaks.
 
 A step is one pass over all 16 layers of one workload:
-  verify-262k : per layer, quantise the 4 new tokens into their pages, then
-                decode attention over 2048 pages with the LSE merge;
+  verify-262k : per layer, one launch that quantises the 4 new tokens into
+                their pages and runs decode attention over 2048 pages, then
+                the LSE merge;
   prefill-262k: per layer, quantise the 512-token chunk into pages, then
                 chunked-prefill attention over 2052 pages with the LSE merge;
   (optional) decode-131k, kvmem-523k (selection + sparse decode).
@@ -32,6 +33,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16/bf16 matrix peak, published
 K_REC, V_REC = 34816, 18432
 METRIC = "decode-attn KV GB/s (% HBM peak) @262K; prefill-chunk TFLOP/s (% MFMA peak)"
+WARM_SECONDS = 0.3             # untimed graph replays before each timed region
 
 # HBM traffic per launch from rocprofv3 counter runs (FETCH_SIZE, then
 # WRITE_SIZE, KiB per dispatch) of `bench.py --profile-kernels`, scaled by what
@@ -43,7 +45,7 @@ METRIC = "decode-attn KV GB/s (% HBM peak) @262K; prefill-chunk TFLOP/s (% MFMA 
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
     "decode": {"sources": {"decode.hip": "5fc7ace9330413eb", "common.hpp": "ed6f88ee167a235a",
-                           "launch.hpp": "2d81fda5089689a9"},
+                           "launch.hpp": "2d81fda5089689a9", "qround.hpp": "0"},
                "flags": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
                "fetch_kib": 213512.0, "write_kib": 6168.0},
     "prefill": {"sources": {"prefill.hip": "231dfa6bd3338761", "common.hpp": "ed6f88ee167a235a",
@@ -113,7 +115,8 @@ class LayerPools:
 
 
 def time_graph(step_fn, steps, warmup):
-    """Warm up eagerly, capture one step in a HIP graph, replay: returns ms/step."""
+    """Warm up eagerly (warmup steps), capture one step in a HIP graph, replay it
+    untimed for WARM_SECONDS, then time `steps` replays: returns ms/step."""
     import torch
     for _ in range(warmup):
         step_fn()
@@ -127,9 +130,14 @@ def time_graph(step_fn, steps, warmup):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         step_fn()
-    for _ in range(2):
+    # untimed replays until the clocks have settled (at least 0.3 s of
+    # back-to-back work): a cold GPU runs the first ~30 ms some 4% slower
+    t_w = time.perf_counter()
+    n = 0
+    while n < 2 or time.perf_counter() - t_w < WARM_SECONDS:
         g.replay()
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        n += 1
     t0 = time.perf_counter()
     for _ in range(steps):
         g.replay()
@@ -163,7 +171,7 @@ def time_launches(call_fn, n_layers, reps):
 
 
 def bench_decode(w, dev, steps, warmup, sparse=False):
-    """Decode / verify workload: quantise the new tokens, attend, merge (x16)."""
+    """Decode / verify workload: append the new tokens and attend (one launch), merge (x16)."""
     import torch
     import long_context_attention_paged_amd as kv
     pools = LayerPools(w, dev, with_summary=sparse)
@@ -173,7 +181,6 @@ def bench_decode(w, dev, steps, warmup, sparse=False):
     blocks = [torch.empty((w.n_kv, max(n_out, 1)), dtype=torch.int32, device=dev)
               for _ in range(w.n_layers)]
     ws = None
-    pos_new = w.kv_len - w.n_q_tok
 
     def decode_call(layer):
         nonlocal ws
@@ -185,17 +192,22 @@ def bench_decode(w, dev, steps, warmup, sparse=False):
                          lse=lses[layer], workspace=ws)
 
     sel_ws = torch.empty(8 << 20, dtype=torch.uint8, device=dev) if sparse else None
+    step_ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
 
     def step():
+        # per layer: [select the blocks (kvmem)], then one launch that appends
+        # the new tokens to the pool and attends, and the merge (plus the
+        # summary of a page the append completes)
         for layer in range(w.n_layers):
-            kv.kvattn_quantize_pages(pools.geom, pools.new_k[layer], pools.new_v[layer],
-                                     pos_new, pools.table, pools.kp[layer], pools.vp[layer],
-                                     pools.summ[layer])
             if sparse:
                 kv.kvattn_select_blocks(pools.geom, pools.q[layer][-1], pools.summ[layer],
                                         w.n_pages, w.n_pages, w.n_recent, w.k_top,
                                         out_blocks=blocks[layer], workspace=sel_ws)
-            decode_call(layer)
+            kv.kvattn_append_decode(pools.geom, pools.new_k[layer], pools.new_v[layer],
+                                    pools.q[layer], pools.kp[layer], pools.vp[layer], pools.table,
+                                    w.kv_len, 1.0 / 16.0, blocks=blocks[layer] if sparse else None,
+                                    k_summary=pools.summ[layer], out=outs[layer], lse=lses[layer],
+                                    workspace=step_ws)
 
     # the decode kernel alone: the same split-K partials kvattn_decode makes,
     # without its merge

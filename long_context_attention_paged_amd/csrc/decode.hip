@@ -10,10 +10,11 @@
 // Work decomposition. Grid (splits, KV heads); 512 threads = 8 wavefronts,
 // one workgroup per CU. A split owns a contiguous run of pages (or block-list
 // entries); wavefront w handles 32-token group w % 4 of every other page of
-// the run (waves 0-3 the even ones, 4-7 the odd ones), so four waves stream
-// the four quarters of one page together. A CU-sized split halves the partials
-// written per layer against two 4-wave workgroups per CU. Every page-record
-// load is a buffer load straight into LDS whose base sits in scalar registers.
+// the run (waves 0-3 the pages of the last page's parity, 4-7 the others),
+// so four waves stream the four quarters of one page together. A CU-sized
+// split halves the partials written per layer against two 4-wave workgroups
+// per CU. Every page-record load is a buffer load straight into LDS whose
+// base sits in scalar registers.
 // Per 32-token group a wave computes
 //   S^T (32 tokens x R rows) = Khat (32 x 256) . Q'^T      (16 mfma per N-tile)
 //   O^T (256 dims x R rows) += Vhat^T (256 x 32) . P'^T    (16 mfma per N-tile)
@@ -417,8 +418,8 @@ __device__ __forceinline__ void append_finish(const DecodeParams& p, AppendTile&
 
 // WAVES: wavefronts per workgroup (4 or 8); either way two wavefronts share
 // a SIMD (two 4-wave workgroups or one 8-wave workgroup per CU), so every
-// lane may hold up to 256 VGPRs. With 8 waves, waves 0-3 stream the even
-// units of the split and waves 4-7 the odd ones.
+// lane may hold up to 256 VGPRs. With 8 waves, waves 0-3 stream every other
+// unit of the split, ending with its last, and waves 4-7 the others.
 template <int NT, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
   constexpr int THREADS = 64 * WAVES;
@@ -457,8 +458,11 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
 
   const int64_t u0 = (int64_t)p.n_units * split / p.n_splits;
   const int64_t u1 = (int64_t)p.n_units * (split + 1) / p.n_splits;
-  const int half = wave >> 2;  // this wave's units: u0 + half + NH * i
-  const int n_span = (int)(u1 - u0) - half;
+  // This wave's units are u0 + first + NH * i. With two halves, the half of
+  // waves 0-3 (the older waves, which the SIMDs favour and which finish
+  // first) takes the split's last unit: the page that an append writes.
+  const int first = NH == 1 ? 0 : (int)(((u1 - u0 - 1) & 1) ^ (wave >> 2));
+  const int n_span = (int)(u1 - u0) - first;
   const int n_tiles = n_span > 0 ? (n_span + NH - 1) / NH : 0;
   const int c = wave & 3;  // 32-token group of every page handled by this wave
 
@@ -467,7 +471,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
   // issue their 13 loads (from record 0) so the wait counts stay constant.
   int lp_vec = -1, ph_vec = -1;
   auto refill = [&](int i0) {
-    const int64_t u = u0 + half + (int64_t)NH * (i0 + lane);
+    const int64_t u = u0 + first + (int64_t)NH * (i0 + lane);
     int lp = -1, ph = -1;
     if (u < u1) {
       lp = p.blocks ? p.blocks[(int64_t)h * p.n_blk + u] : (int)u;
@@ -498,11 +502,13 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
   bool valid = false, valid_n = false;
   // Fused append: the one tile of this wave that holds new tokens, if any
   // (n_new <= 32, and a wave keeps one 32-token group c of every page). Its
-  // inputs and old words are requested before the first tile's loads, the
-  // codes computed and stored while those loads fly; the tile itself is
-  // loaded only after this wave's stores have completed.
+  // inputs and old words are requested before the first tile's loads; the
+  // codes are computed and stored after the q' staging, while the first
+  // tile's loads fly, and the first wait of the loop covers those stores
+  // (vmcnt counts them), so every later tile load sees them. When the first
+  // tile is the appended one, it is loaded only after the stores complete.
   const int64_t first_new = p.kv_len - p.n_new;
-  bool app = false;
+  bool app = false, app_pending = false;
   AppendTile at;
   if (n_tiles > 0) {
     locate(0, tok, valid, rec);
@@ -528,12 +534,13 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
       issue_keys(slot, p.k_pool + rec * K_REC, valid ? c : 0);
       issue_values(slot, p.v_pool + rec * V_REC, valid ? c : 0);
     }
-    if (app) append_finish(p, at, h, c, first_new, lane);
     if (first_new_tile) {
+      append_finish(p, at, h, c, first_new, lane);
       wait_loads<0>();  // this wave's stores have completed
       issue_keys(slot, p.k_pool + rec * K_REC, c);
       issue_values(slot, p.v_pool + rec * V_REC, c);
     }
+    app_pending = app && !first_new_tile;
   }
   // The first tile is in flight: stage q' rows (f16) into LDS, shared by all
   // waves (padding rows are zero). Row r of this KV head is query token
@@ -565,14 +572,18 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
     }
   }
   __syncthreads();
+  if (app_pending) append_finish(p, at, h, c, first_new, lane);
   for (int i = 0; i < n_tiles; ++i) {
     const bool more = i + 1 < n_tiles;
     if (more) locate(i + 1, tok_n, valid_n, rec_n);
-    wait_loads<V_LOADS>();  // keys of tile i have landed (its values may still fly)
+    if (app_pending && i == 0) {
+      wait_loads<0>();  // the appended tokens' stores (and all of tile 0) have completed
+    } else {
+      wait_loads<V_LOADS>();  // keys of tile i have landed (its values may still fly)
+    }
     auto refill_keys = [&] {
       if (more) {
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): key reads of this slot are done
-        if (app && valid_n && tok_n + 32 > first_new) wait_loads<0>();  // appended tile: stores done
         issue_keys(slot, p.k_pool + rec_n * K_REC, valid_n ? c : 0);
         wait_loads<K_LOADS>();  // values of tile i have landed
       } else {
