@@ -8,9 +8,10 @@
 // Each lane owns one output dim; the four waves take interleaved quarters of
 // the parts and their partial sums are added in a fixed order in LDS, so
 // results are deterministic. Part weights are computed once per workgroup
-// into LDS. head_dim 256 (the decode and prefill partials) uses float4 paths:
-// a 16-wave workgroup per row when there are many parts (decode splits), one
-// wavefront per row when there are few parts and many rows (prefill groups).
+// into LDS. head_dim 256 (the decode and prefill partials) has its own paths:
+// one wavefront per row when there are few parts and many rows (prefill
+// groups), one wavefront per 64 dims when there are at most 64 parts (decode
+// splits), a 16-wave workgroup per row when there are more.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -255,6 +256,45 @@ __global__ __launch_bounds__(256) void merge_rows256_kernel(int32_t n_parts, int
   if (lane == 0) lse[r] = L;
 }
 
+// head_dim == 256 with at most 64 parts (the decode splits): one workgroup per
+// row, wavefront qd owns dims 64qd..64qd+63 (lane l: dim 64qd + l). Every
+// part's 256-byte slice is requested at once (one float per lane per part),
+// lane s holds lse of part s, and the weights are broadcast with readlane:
+// no LDS, no barrier, about one memory round trip per row. Parts are added
+// in ascending order.
+constexpr int MP_PARTS = 64;
+
+__global__ __launch_bounds__(256) void merge_parts64_kernel(int32_t n_parts, int64_t rows,
+                                                            const float* __restrict__ o_parts,
+                                                            const float* __restrict__ lse_parts,
+                                                            float* __restrict__ out,
+                                                            float* __restrict__ lse) {
+  const int lane = threadIdx.x & 63, qd = threadIdx.x >> 6;
+  const int64_t r = blockIdx.x;
+  const int last = n_parts - 1;
+  const float* op = o_parts + r * 256 + 64 * qd + lane;
+  const int64_t stride = rows * 256;  // floats between consecutive parts
+  float v[MP_PARTS];
+#pragma unroll
+  for (int s = 0; s < MP_PARTS; ++s) v[s] = op[(int64_t)(s < last ? s : last) * stride];
+
+  const float my = lse_parts[(int64_t)(lane < last ? lane : last) * rows + r];  // part `lane`
+  const float m = wave_reduce(lane < n_parts ? my : neg_inf(), true);
+  const bool empty = m == neg_inf();  // every part is -inf
+  const float se = (!empty && lane < n_parts) ? expf(my - m) : 0.f;
+  const float L = empty ? neg_inf() : m + logf(wave_reduce(se, false));
+  const float wl = (!empty && lane < n_parts && my != neg_inf()) ? expf(my - L) : 0.f;
+  float acc = 0.f;
+#pragma unroll
+  for (int s = 0; s < MP_PARTS; ++s) {
+    const float ws = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s));
+    // a zero weight (absent or -inf part) contributes nothing, whatever the row holds
+    acc += ws != 0.f ? ws * v[s] : 0.f;
+  }
+  out[r * 256 + 64 * qd + lane] = acc;
+  if (threadIdx.x == 0) lse[r] = L;
+}
+
 }  // namespace
 
 hipError_t launch_merge(int32_t n_parts, int64_t rows, int32_t head_dim, const float* o_parts,
@@ -264,6 +304,11 @@ hipError_t launch_merge(int32_t n_parts, int64_t rows, int32_t head_dim, const f
   if (vec4 && n_parts <= 2 * MR_DEPTH && rows >= 1024) {
     hipLaunchKernelGGL(merge_rows256_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
                        n_parts, rows, o_parts, lse_parts, out, lse);
+    return hipGetLastError();
+  }
+  if (head_dim == 256 && n_parts <= MP_PARTS) {
+    hipLaunchKernelGGL(merge_parts64_kernel, dim3((unsigned)rows), dim3(256), 0, stream, n_parts,
+                       rows, o_parts, lse_parts, out, lse);
     return hipGetLastError();
   }
   if (vec4) {

@@ -243,10 +243,12 @@ def test_decode_deterministic_and_page_permutation_invariant():
 
 def test_merge_parity():
     """Partials with lse = -inf contribute nothing, whatever their rows hold
-    (NaN here for the GPU; zeros for the oracle). Part counts cover one pass,
-    several passes and more parts than threads."""
+    (NaN here for the GPU; zeros for the oracle). Part counts cover every
+    merge path: up to 64 parts (decode splits), one and several passes of the
+    16-wave path, more parts than threads, and many rows with few parts."""
     g = np.random.default_rng(40)
-    for S, rows, D in ((1, 5, 256), (7, 33, 256), (130, 7, 256), (300, 4, 100), (1100, 3, 256),
+    for S, rows, D in ((1, 5, 256), (7, 33, 256), (64, 96, 256), (63, 24, 256), (65, 6, 256),
+                       (130, 7, 256), (300, 4, 100), (1100, 3, 256),
                        (16, 1501, 256), (3, 1024, 256), (32, 1100, 256)):  # last three: many rows
         o = g.standard_normal((S, rows, D)).astype(np.float32)
         ls = (g.standard_normal((S, rows)) * 3).astype(np.float32)
