@@ -232,6 +232,8 @@ def bench_decode(w, dev, steps, warmup, sparse=False):
         "ms_per_step": ms,
         "kv_bytes_per_step": bytes_per_launch * w.n_layers,
         "gbs": bytes_per_launch * w.n_layers / (ms * 1e-3) / 1e9,
+        "tokens_per_s": 1e3 / ms,                 # attention-only: one step per token
+        "query_tokens_per_s": w.n_q_tok * 1e3 / ms,
         "launch_ms": launch_ms,
         "launch_gbs": bytes_per_launch / (launch_ms * 1e-3) / 1e9,
         "kernel_ms": kernel_ms,
@@ -413,6 +415,64 @@ def cpu_baseline_prefill(w, pools, n_tok=24):
                       f"({n_tok * w.gqa} rows over {w.kv_len} keys), binary64, numpy + OpenBLAS"}
 
 
+def cpu_baseline_tiny_one_thread():
+    """The oracle on the tiny decode workload (one layer, one KV head, 4096
+    tokens, identity table, one query) with one BLAS thread; its pages are
+    quantised by the oracle too, so no device is involved."""
+    import numpy as np
+    import oracle
+    from oracle import quant
+    from threadpoolctl import threadpool_limits
+    from long_context_attention_paged_amd import synth
+    w = synth.WORKLOADS[1]
+    q = synth.queries(w, 0)
+    K, V = synth.kv_layer(w, 0, q, threads=1)
+    table = synth.page_table(w)
+    kp = np.zeros((w.n_pages, w.n_kv, K_REC), np.uint8)
+    vp = np.zeros((w.n_pages, w.n_kv, V_REC), np.uint8)
+    quant.quantize_into_pool(K, V, 0, table, kp, vp)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        reps = 0
+        while reps < 3 or time.perf_counter() - t0 < 1.0:
+            oracle.decode(q, w.gqa, kp, vp, table, w.n_pages, w.kv_len, 1.0 / 16.0)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+    nbytes = w.kv_len * w.n_kv * (272 + 144)
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds_per_call": dt,
+            "sample": f"{w.name}: the whole workload ({w.kv_len} tokens x {w.gqa} query rows), "
+                      "binary64, numpy + OpenBLAS, one thread"}
+
+
+def gemm_probe(dev, n=8192, reps=20):
+    """Dense f16 matrix-core rate of the vendor library on this GPU: torch.mm of
+    two contiguous n x n f16 matrices (hipBLASLt), fp32 accumulate inside."""
+    import torch
+    a = torch.randn(n, n, dtype=torch.float16, device=dev)
+    b = torch.randn(n, n, dtype=torch.float16, device=dev)
+    c = torch.empty(n, n, dtype=torch.float16, device=dev)
+    for _ in range(3):
+        torch.mm(a, b, out=c)
+    torch.cuda.synchronize()
+    t_w = time.perf_counter()
+    while time.perf_counter() - t_w < WARM_SECONDS:
+        torch.mm(a, b, out=c)
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.mm(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"tflops": round(tflops, 1), "frac_of_published_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+            "what": f"torch.mm f16 {n}x{n}x{n} (hipBLASLt), {reps} calls"}
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -566,6 +626,8 @@ def main():
             "head_dim": 256, "context": w3.kv_len, "query_tokens": w3.n_q_tok,
         },
         "hbm_frac": round(head.get("gbs", 0.0) / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(head.get("tokens_per_s", 0.0), 1),
+        "query_tokens_per_s": round(head.get("query_tokens_per_s", 0.0), 1),
     }
     if decode_res:
         line["roofline"] = {
@@ -605,8 +667,12 @@ def main():
         }
         if "cpu_baseline" in prefill_res:
             line["prefill"]["cpu_baseline"] = prefill_res["cpu_baseline"]
+        line["prefill"]["gemm_probe"] = gemm_probe(dev)
+        log(f"gemm probe: {json.dumps(line['prefill']['gemm_probe'])}")
     if cpu:
         cpu["cpu_model"] = cpu_model()
+        cpu["nproc"] = os.cpu_count()
+        cpu["one_thread"] = cpu_baseline_tiny_one_thread()
         line["cpu_baseline"] = cpu
     others = {k: v for k, v in extra.items() if k not in (w3.name, synth.WORKLOADS[4].name)}
     if others:
