@@ -11,7 +11,9 @@ A step is one pass over all 16 layers of one workload:
                 the LSE merge;
   prefill-262k: per layer, quantise the 512-token chunk into pages, then
                 chunked-prefill attention over 2052 pages with the LSE merge;
-  (optional) decode-131k, kvmem-523k (selection + sparse decode).
+  also decode-131k, kvmem-523k (selection + sparse decode), and verify-262k
+  with the history streamed from pinned host memory into a 2100 MiB device
+  working set (PCIe-bound; never `value`).
 Inputs are seeded synthetic tensors (long_context_attention_paged_amd.synth),
 resident in HBM before timing; every layer has its own pool so repeated steps
 stream from HBM, not from the 256 MB last-level cache. Steps are captured
@@ -378,6 +380,56 @@ def bench_prefill_host_pool(w, dev, steps, warmup):
     }, pools
 
 
+def bench_verify_streamed(w, dev, steps, warmup, budget=2100 << 20):
+    """Verify with adaptive host-resident KV streaming: a device working set of
+    `budget` bytes (the pages' decode figure, 2100 MiB) holds each layer's
+    newest pages plus two staging pools; every step streams each layer's older
+    history from pinned host memory over PCIe while the previous layer
+    computes, appends the 4 new tokens to the resident pages, attends over
+    both tiers and merges them. Bound by the host link, not by the GPU."""
+    import torch
+    from long_context_attention_paged_amd import streaming
+    pools = LayerPools(w, dev)
+    n_res = streaming.resident_pages_for_budget(budget, w.n_layers, w.n_pages, w.n_kv)
+    n_hist = w.n_pages - n_res
+    layers = []
+    for layer in range(w.n_layers):  # full device pool -> host history + resident pages
+        layers.append(streaming.StreamedLayer(pools.geom, pools.kp[layer], pools.vp[layer],
+                                              pools.table, w.n_pages, n_hist))
+        pools.kp[layer] = pools.vp[layer] = None
+    torch.cuda.empty_cache()
+    sd = streaming.StreamedDecode(pools.geom, layers, w.n_pages, w.n_q_tok, dev)
+    outs = [torch.empty_like(q) for q in pools.q]
+    lses = [torch.empty(q.shape[:2], dtype=torch.float32, device=dev) for q in pools.q]
+
+    def step():
+        sd.step(pools.q, pools.new_k, pools.new_v, w.kv_len, 1.0 / 16.0, outs, lses)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    h2d = sd.host_to_device_bytes_per_step()
+    kv_bytes = w.kv_len * w.n_kv * (272 + 144) * w.n_layers
+    return {
+        "ms_per_step": ms,
+        "tokens_per_s": 1e3 / ms,
+        "query_tokens_per_s": w.n_q_tok * 1e3 / ms,
+        "gbs": kv_bytes / (ms * 1e-3) / 1e9,
+        "device_budget_bytes": budget,
+        "device_pool_bytes": sd.device_bytes(),
+        "resident_pages_per_layer": n_res,
+        "streamed_pages_per_layer": n_hist,
+        "host_to_device_bytes_per_step": h2d,
+        "host_to_device_gbs": h2d / (ms * 1e-3) / 1e9,
+        "note": "history in pinned host memory, newest pages resident, layer-ahead staging",
+    }, pools
+
+
 def cpu_baseline_decode(w, pools):
     """The oracle, as it stands, on one (layer, KV head) of the workload."""
     import numpy as np
@@ -541,9 +593,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--configs", default="3,4,2,5",
+    ap.add_argument("--configs", default="3,4,2,5,3s",
                     help="workloads to run: 2 decode-131k, 3 verify-262k, 4 prefill, 5 kvmem, "
-                         "4h prefill with the pool in pinned host memory")
+                         "4h prefill with the pool in pinned host memory, 3s verify with the "
+                         "history streamed from host memory (2100 MiB device working set)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="run only a short fixed kernel sequence for counter runs (no JSON line)")
@@ -571,6 +624,15 @@ def main():
     decode_res = prefill_res = None
     cpu = None
     for c in cfgs:
+        if c == "3s":
+            w = synth.WORKLOADS[3]
+            log(f"workload {w.name} (streamed history)")
+            res, pools = bench_verify_streamed(w, dev, max(2, min(args.steps, 5)), 1)
+            extra[w.name + "-streamed"] = res
+            del pools
+            torch.cuda.empty_cache()
+            log(f"{w.name} streamed: {json.dumps(res)}")
+            continue
         if c == "4h":
             w = synth.WORKLOADS[4]
             log(f"workload {w.name} (host pool)")
