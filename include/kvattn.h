@@ -341,6 +341,41 @@ kvattn_status kvattn_merge_lse(int32_t n_parts, int64_t rows, int32_t head_dim,
                                const float *o_parts, const float *lse_parts,
                                float *out, float *lse, void *stream);
 
+/* KVMem host tier — the GPU pulls the blocks a selection kept from a pool
+ * that may live in pinned host memory ([KVMEM] 測試口徑 and "Recall 測試":
+ * history blocks in host RAM, budget/128 of them brought to the GPU next to a
+ * reserved recent window). For every KV head h and rank i < n_sel, copies
+ * the key and value records of logical page blocks[h][i] (physical page
+ * page_table[blocks[h][i]]) into record (i * n_kv_heads + h) of the dst pools
+ * and sets dst_blocks[h][i] = i; an entry outside [0, n_logical_pages), or
+ * mapping to a physical page outside [0, n_phys_pages), copies nothing and
+ * sets dst_blocks[h][i] = -1. A kernel does the copy, reading the block list
+ * on the device, so a selection (kvattn_select_blocks, whose first k_top
+ * entries per head are the kept history) feeds it with no host round trip.
+ * kvattn_decode_partials over the dst pools with page_table = identity on
+ * [0, n_sel) (and -1 beyond), blocks = dst_blocks attends exactly the
+ * gathered blocks.
+ *  geom        geometry of the src pools (n_phys_pages, n_kv_heads).
+ *  src_k_pool, src_v_pool  device memory or pinned host memory
+ *              (hipHostMalloc); the kernel reads host memory over the host
+ *              link through its device mapping. Other host memory is
+ *              rejected (E_INVALID).
+ *  page_table  DEVICE int32 [n_logical_pages].
+ *  blocks      DEVICE int32 [n_kv_heads][n_blk]; the first n_sel entries of
+ *              each row are gathered; 0 <= n_sel <= n_blk.
+ *  dst_k_pool, dst_v_pool  DEVICE pools of n_sel * n_kv_heads records.
+ *  dst_blocks  DEVICE int32 [n_kv_heads][n_sel].
+ * Pools 256-byte aligned. */
+kvattn_status kvattn_gather_blocks(const kvattn_geom *geom,
+                                   const uint8_t *src_k_pool,
+                                   const uint8_t *src_v_pool,
+                                   const int32_t *page_table,
+                                   int32_t n_logical_pages,
+                                   const int32_t *blocks, int32_t n_blk,
+                                   int32_t n_sel, uint8_t *dst_k_pool,
+                                   uint8_t *dst_v_pool, int32_t *dst_blocks,
+                                   void *stream);
+
 /* a7 — page prefetch for a host-resident pool ([RDNA4] "Online Log-Sum-Exp
  * prefill & pipelined prefetch": pages stream in ahead of the layer that
  * needs them; [STREAM] the Adaptive KV Streaming path keeps history in host

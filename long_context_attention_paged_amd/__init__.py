@@ -75,6 +75,7 @@ def load_library():
         "kvattn_prefill_groups": ([G, I32, I64], I32),
         "kvattn_merge_lse": ([I32, I64, I32, P, P, P, P, P], I32),
         "kvattn_prefetch_pages": ([G, P, P, P, P, P, I32, P], I32),
+        "kvattn_gather_blocks": ([G, P, P, P, I32, P, I32, I32, P, P, P, P], I32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -411,6 +412,41 @@ def kvattn_merge_lse(o_parts, lse_parts, out=None, lse=None, stream=None):
                                 _stream(stream))
     _check("kvattn_merge_lse", code)
     return out, lse
+
+
+def kvattn_gather_blocks(geom, src_k_pool, src_v_pool, page_table, blocks, n_sel, dst_k_pool,
+                         dst_v_pool, dst_blocks=None, stream=None):
+    """KVMem host tier: copy the first n_sel blocks of each head's row of
+    `blocks` (device [n_kv, n_blk]) from the src pools (device, or pinned host
+    tensors) into ranks 0..n_sel-1 of the dst pools -> dst_blocks [n_kv, n_sel]."""
+    torch = _torch()
+    lib = load_library()
+    for name, t in (("src_k_pool", src_k_pool), ("src_v_pool", src_v_pool)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous uint8 torch tensor")
+        if not t.is_cuda and not t.is_pinned():
+            raise ValueError(f"{name} must be on the GPU or in pinned host memory")
+    _pools(geom, src_k_pool, src_v_pool)
+    _need(page_table, "page_table", torch.int32)
+    _need(blocks, "blocks", torch.int32)
+    if blocks.dim() != 2 or blocks.shape[0] != geom.n_kv_heads:
+        raise ValueError("blocks must be [n_kv_heads, n_blk]")
+    n_sel = int(n_sel)
+    _need(dst_k_pool, "dst_k_pool", torch.uint8)
+    _need(dst_v_pool, "dst_v_pool", torch.uint8)
+    _size(dst_k_pool, "dst_k_pool", n_sel * geom.n_kv_heads * K_RECORD_BYTES)
+    _size(dst_v_pool, "dst_v_pool", n_sel * geom.n_kv_heads * V_RECORD_BYTES)
+    if dst_blocks is None:
+        dst_blocks = torch.empty((geom.n_kv_heads, max(n_sel, 1)), dtype=torch.int32,
+                                 device=blocks.device)
+    _need(dst_blocks, "dst_blocks", torch.int32)
+    _size(dst_blocks, "dst_blocks", geom.n_kv_heads * n_sel)
+    _check("kvattn_gather_blocks",
+           lib.kvattn_gather_blocks(ctypes.byref(geom), _ptr(src_k_pool), _ptr(src_v_pool),
+                                    _ptr(page_table), page_table.numel(), _ptr(blocks),
+                                    blocks.shape[1], n_sel, _ptr(dst_k_pool), _ptr(dst_v_pool),
+                                    _ptr(dst_blocks), _stream(stream)))
+    return dst_blocks
 
 
 def kvattn_prefetch_pages(geom, src_k_pool, src_v_pool, dst_k_pool, dst_v_pool, pages,

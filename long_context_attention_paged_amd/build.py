@@ -14,7 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvattn.so")
-SOURCES = ["api.hip", "quantize.hip", "select.hip", "merge.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.hip", "quantize.hip", "select.hip", "merge.hip", "decode.hip", "prefill.hip",
+           "gather.hip"]
 # The decode and prefill kernels keep their 64-128 loop-carried accumulators
 # in VGPRs next to LDS-staged operands; without this the allocator splits them
 # between VGPRs and AGPRs and copies every accumulator on each loop iteration.

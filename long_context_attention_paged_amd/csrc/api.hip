@@ -50,6 +50,31 @@ kvattn_status current_device(int* n_cu) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// The address a kernel reads `p` through: device memory as is, pinned host
+// memory (hipHostMalloc) through its device mapping. Pageable host memory and
+// unknown pointers are rejected, so a kernel never dereferences them.
+kvattn_status device_view(const void* p, const void** out) {
+  hipPointerAttribute_t a{};
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return KVATTN_E_INVALID;
+  }
+  if (a.type == hipMemoryTypeDevice) {
+    *out = p;
+    return KVATTN_OK;
+  }
+  if (a.type == hipMemoryTypeHost) {
+    void* d = nullptr;
+    if (hipHostGetDevicePointer(&d, const_cast<void*>(p), 0) != hipSuccess || !d) {
+      (void)hipGetLastError();
+      return KVATTN_E_INVALID;
+    }
+    *out = d;
+    return KVATTN_OK;
+  }
+  return KVATTN_E_INVALID;
+}
+
 kvattn_status check_geom(const kvattn_geom* g) {
   if (!g) return KVATTN_E_INVALID;
   if (g->n_kv_heads < 1 || g->gqa < 1 || g->n_phys_pages < 1) return KVATTN_E_INVALID;
@@ -479,6 +504,30 @@ kvattn_status kvattn_merge_lse(int32_t n_parts, int64_t rows, int32_t head_dim,
                                static_cast<hipStream_t>(stream)));
 }
 
+
+kvattn_status kvattn_gather_blocks(const kvattn_geom* geom, const uint8_t* src_k_pool,
+                                   const uint8_t* src_v_pool, const int32_t* page_table,
+                                   int32_t n_logical_pages, const int32_t* blocks, int32_t n_blk,
+                                   int32_t n_sel, uint8_t* dst_k_pool, uint8_t* dst_v_pool,
+                                   int32_t* dst_blocks, void* stream) {
+  kvattn_status st = check_geom(geom);
+  if (st) return st;
+  if (!src_k_pool || !src_v_pool || !dst_k_pool || !dst_v_pool || !page_table || !blocks ||
+      !dst_blocks)
+    return KVATTN_E_INVALID;
+  if (n_logical_pages < 1 || n_blk < 1 || n_sel < 0 || n_sel > n_blk) return KVATTN_E_INVALID;
+  if (!aligned(src_k_pool, 256) || !aligned(src_v_pool, 256) || !aligned(dst_k_pool, 256) ||
+      !aligned(dst_v_pool, 256))
+    return KVATTN_E_INVALID;
+  if ((st = current_device(nullptr))) return st;
+  if (n_sel == 0) return KVATTN_OK;
+  const void *sk = nullptr, *sv = nullptr;
+  if ((st = device_view(src_k_pool, &sk)) || (st = device_view(src_v_pool, &sv))) return st;
+  return launched(launch_gather(static_cast<const uint8_t*>(sk), static_cast<const uint8_t*>(sv),
+                                page_table, n_logical_pages, geom->n_phys_pages, blocks, n_blk,
+                                n_sel, geom->n_kv_heads, dst_k_pool, dst_v_pool, dst_blocks,
+                                static_cast<hipStream_t>(stream)));
+}
 
 kvattn_status kvattn_prefetch_pages(const kvattn_geom* geom, const uint8_t* src_k_pool,
                                     const uint8_t* src_v_pool, uint8_t* dst_k_pool,

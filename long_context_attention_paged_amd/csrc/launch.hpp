@@ -94,6 +94,11 @@ struct PrefillParams {
 int32_t prefill_rows_per_tile();
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 
+hipError_t launch_gather(const uint8_t* src_k, const uint8_t* src_v, const int32_t* page_table,
+                         int32_t n_logical, int32_t n_phys, const int32_t* blocks, int32_t n_blk,
+                         int32_t n_sel, int32_t n_kv, uint8_t* dst_k, uint8_t* dst_v,
+                         int32_t* dst_blocks, hipStream_t stream);
+
 hipError_t launch_merge(int32_t n_parts, int64_t rows, int32_t head_dim, const float* o_parts,
                         const float* lse_parts, float* out, float* lse, hipStream_t stream);
 

@@ -39,10 +39,10 @@ def resident_pages_for_budget(budget_bytes, n_layers, n_pages, n_kv):
 class StreamedLayer:
     """One layer's two tiers, built from a full device pool (k_pool, v_pool,
     page_table over n_pages logical pages): history pages [0, n_hist) go to
-    pinned host memory in logical order, pages [n_hist, n_pages) to a compact
-    device pool."""
+    pinned host memory in logical order (unless keep_history is False), pages
+    [n_hist, n_pages) to a compact device pool."""
 
-    def __init__(self, geom, k_pool, v_pool, page_table, n_pages, n_hist):
+    def __init__(self, geom, k_pool, v_pool, page_table, n_pages, n_hist, keep_history=True):
         import torch
         dev = k_pool.device
         n_kv = geom.n_kv_heads
@@ -51,11 +51,13 @@ class StreamedLayer:
         vview = v_pool.view(-1, n_kv * V_REC)
         hist, res = table[:n_hist], table[n_hist:n_pages]
         self.n_hist, self.n_res = n_hist, n_pages - n_hist
-        self.host_k = torch.empty(max(n_hist, 1) * n_kv * K_REC, dtype=torch.uint8,
-                                  pin_memory=True)
-        self.host_v = torch.empty(max(n_hist, 1) * n_kv * V_REC, dtype=torch.uint8,
-                                  pin_memory=True)
-        if n_hist:
+        self.host_k = self.host_v = None
+        if keep_history:
+            self.host_k = torch.empty(max(n_hist, 1) * n_kv * K_REC, dtype=torch.uint8,
+                                      pin_memory=True)
+            self.host_v = torch.empty(max(n_hist, 1) * n_kv * V_REC, dtype=torch.uint8,
+                                      pin_memory=True)
+        if n_hist and keep_history:
             self.host_k[:n_hist * n_kv * K_REC].copy_(kview[hist].reshape(-1))
             self.host_v[:n_hist * n_kv * V_REC].copy_(vview[hist].reshape(-1))
         self.res_k = kview[res].reshape(-1).contiguous()
@@ -142,5 +144,96 @@ class StreamedDecode:
                                       self.splits, blocks=self.hist_blocks,
                                       o_part=self.parts[1:], lse_part=self.lparts[1:])
             done[c].record(compute)
+            kv.kvattn_merge_lse(self.parts, self.lparts, out=outs[c].view(-1, kv.HEAD_DIM),
+                                lse=lses[c].view(-1))
+
+
+class KVMemHostLayer:
+    """One layer of KVMem with its history in pinned host memory ([KVMEM]
+    測試口徑, "Recall 測試": budget/128 history blocks plus a reserved recent
+    window on the GPU, the rest in host RAM). Built from a full device pool:
+    every page goes to a pinned host pool (same physical layout), the newest
+    n_recent pages stay resident in a compact device pool, and the block
+    summaries stay on the device for the selection."""
+
+    def __init__(self, geom, k_pool, v_pool, page_table, n_pages, n_recent, summary):
+        import torch
+        dev = k_pool.device
+        n_kv = geom.n_kv_heads
+        self.host_k = torch.empty(k_pool.numel(), dtype=torch.uint8, pin_memory=True)
+        self.host_v = torch.empty(v_pool.numel(), dtype=torch.uint8, pin_memory=True)
+        self.host_k.copy_(k_pool)
+        self.host_v.copy_(v_pool)
+        self.recent = StreamedLayer(geom, k_pool, v_pool, page_table, n_pages,
+                                    n_pages - min(n_recent, n_pages), keep_history=False)
+        self.summary = summary
+        torch.cuda.synchronize()
+
+
+class KVMemHostDecode:
+    """Per step and layer: select (kvattn_select_blocks, on the device), pull
+    the kept history blocks from host memory (kvattn_gather_blocks: a kernel
+    reads the block list on the device and the pages over the host link),
+    append + attend over the resident recent window (kvattn_append_decode,
+    which also refreshes the summary of a page the append completes), attend
+    over the gathered blocks (kvattn_decode_partials) and merge."""
+
+    def __init__(self, geom, layers, page_table, n_pages, n_recent, k_top, n_q_tok, dev,
+                 workspace_bytes=64 << 20):
+        import torch
+        self.geom, self.layers, self.table = geom, layers, page_table
+        self.n_pages, self.n_recent, self.k_top = n_pages, n_recent, k_top
+        n_kv = geom.n_kv_heads
+        r = min(n_recent, n_pages)
+        self.k_sel = min(k_top, n_pages - r)
+        self.n_out = kv.kvattn_select_count(n_pages, n_recent, k_top)
+        self.blocks = torch.empty((n_kv, self.n_out), dtype=torch.int32, device=dev)
+        self.sel_ws = torch.empty(8 * n_kv * max(n_pages, 1) + 4096, dtype=torch.uint8, device=dev)
+        n_st = max(self.k_sel, 1)
+        self.stage_geom = kv.Geom(n_kv, geom.gqa, n_st)
+        self.stage_k = torch.empty(n_st * n_kv * K_REC, dtype=torch.uint8, device=dev)
+        self.stage_v = torch.empty(n_st * n_kv * V_REC, dtype=torch.uint8, device=dev)
+        self.stage_blocks = torch.empty((n_kv, n_st), dtype=torch.int32, device=dev)
+        st = np.full(n_pages, -1, np.int32)
+        st[:self.k_sel] = np.arange(self.k_sel, dtype=np.int32)
+        self.stage_table = torch.from_numpy(st).to(dev)
+        self.splits = kv.kvattn_decode_splits(self.stage_geom, n_st)
+        rows = n_q_tok * n_kv * geom.gqa
+        self.parts = torch.empty((1 + self.splits, rows, kv.HEAD_DIM), dtype=torch.float32,
+                                 device=dev)
+        self.lparts = torch.empty((1 + self.splits, rows), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(workspace_bytes, dtype=torch.uint8, device=dev)
+        self.kept = [torch.empty((n_kv, self.n_out), dtype=torch.int32, device=dev)
+                     for _ in layers]
+
+    def host_to_device_bytes_per_step(self):
+        return len(self.layers) * self.k_sel * self.geom.n_kv_heads * (K_REC + V_REC)
+
+    def device_bytes(self):
+        res = sum(L.recent.res_k.numel() + L.recent.res_v.numel() + L.summary.numel() * 4
+                  for L in self.layers)
+        return res + self.stage_k.numel() + self.stage_v.numel()
+
+    def step(self, q, k_new, v_new, kv_len, scale, outs, lses):
+        for c, L in enumerate(self.layers):
+            kv.kvattn_select_blocks(self.geom, q[c][-1], L.summary, self.n_pages, self.n_pages,
+                                    self.n_recent, self.k_top, out_blocks=self.kept[c],
+                                    workspace=self.sel_ws)
+            R = L.recent
+            kv.kvattn_append_decode(R.res_geom, k_new[c], v_new[c], q[c], R.res_k, R.res_v,
+                                    R.res_table, kv_len, scale, blocks=R.res_blocks,
+                                    k_summary=L.summary, out=self.parts[0], lse=self.lparts[0],
+                                    workspace=self.ws)
+            if not self.k_sel:
+                outs[c].copy_(self.parts[0].view_as(outs[c]))
+                lses[c].copy_(self.lparts[0].view_as(lses[c]))
+                continue
+            kv.kvattn_gather_blocks(self.geom, L.host_k, L.host_v, self.table, self.kept[c],
+                                    self.k_sel, self.stage_k, self.stage_v,
+                                    dst_blocks=self.stage_blocks)
+            kv.kvattn_decode_partials(self.stage_geom, q[c], self.stage_k, self.stage_v,
+                                      self.stage_table, kv_len, scale, self.splits,
+                                      blocks=self.stage_blocks, o_part=self.parts[1:],
+                                      lse_part=self.lparts[1:])
             kv.kvattn_merge_lse(self.parts, self.lparts, out=outs[c].view(-1, kv.HEAD_DIM),
                                 lse=lses[c].view(-1))

@@ -240,3 +240,28 @@ def test_prefetch_validation_before_device():
     assert f(ctypes.byref(g), P(FAKE), P(FAKE), P(FAKE), P(FAKE), pp, -1, None) == E_INVALID
     assert f(ctypes.byref(g), None, P(FAKE), P(FAKE), P(FAKE), pp, 4, None) == E_INVALID
     assert f(ctypes.byref(g), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, 0, None) == OK  # no-op
+
+
+def test_gather_validation_before_device():
+    import torch
+    lib = kv.load_library()
+    g = geom(n_phys=16)
+    f = lib.kvattn_gather_blocks
+
+    def call(src=FAKE, table=FAKE, n_logical=16, blocks=FAKE, n_blk=8, n_sel=4, dst=FAKE,
+             dst_blocks=FAKE):
+        return f(ctypes.byref(g), P(src), P(src), P(table), n_logical, P(blocks), n_blk, n_sel,
+                 P(dst), P(dst), P(dst_blocks), None)
+
+    if not torch.cuda.is_available():
+        assert call() in (E_DEVICE, E_UNSUPPORTED)
+    assert call(src=0) == E_INVALID
+    assert call(table=0) == E_INVALID
+    assert call(blocks=0) == E_INVALID
+    assert call(dst_blocks=0) == E_INVALID
+    assert call(n_sel=9) == E_INVALID                 # more than a row holds
+    assert call(n_sel=-1) == E_INVALID
+    assert call(n_blk=0, n_sel=0) == E_INVALID
+    assert call(n_logical=0) == E_INVALID
+    assert call(src=FAKE + 16) == E_INVALID           # pools need 256-byte alignment
+    assert call(dst=FAKE + 64) == E_INVALID

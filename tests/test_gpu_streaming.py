@@ -65,3 +65,87 @@ def test_streamed_decode_matches_oracle(n_kv, gqa, n_q_tok, kv_len, n_hist, n_la
         assert eo <= DEC_TOL and el <= 1e-3 and rr <= 2e-3, (c, eo, el, rr)
     assert sd.host_to_device_bytes_per_step() == n_layers * n_hist * n_kv * 53248
 
+
+
+@pytest.mark.parametrize("src_on_host", [True, False])
+def test_gather_blocks_bitexact(src_on_host):
+    """kvattn_gather_blocks copies each kept block's records to its rank slot
+    bit for bit, from pinned host memory or from the device, marks entries
+    outside the table or the pool -1 and leaves their slots untouched."""
+    n_kv, n_phys, n_logical, n_blk, n_sel = 3, 20, 18, 10, 8
+    g = np.random.default_rng(5 + src_on_host)
+    pools = Pools(n_phys, n_kv, 6, init_seed=9)
+    table = g.permutation(n_phys)[:n_logical].astype(np.int32)
+    table[5] = 99                                      # maps outside the pool
+    blocks = np.stack([g.permutation(n_logical)[:n_blk] for _ in range(n_kv)]).astype(np.int32)
+    blocks[0, 1], blocks[1, 2], blocks[2, 0] = -1, 30, 5   # invalid entries
+    if src_on_host:
+        sk = torch.empty(pools.gk.numel(), dtype=torch.uint8, pin_memory=True)
+        sv = torch.empty(pools.gv.numel(), dtype=torch.uint8, pin_memory=True)
+        sk.copy_(pools.gk)
+        sv.copy_(pools.gv)
+    else:
+        sk, sv = pools.gk, pools.gv
+    dk = torch.full((n_sel * n_kv * quant.K_RECORD_BYTES,), 0xAB, dtype=torch.uint8, device=DEV)
+    dv = torch.full((n_sel * n_kv * quant.V_RECORD_BYTES,), 0xAB, dtype=torch.uint8, device=DEV)
+    db = kv.kvattn_gather_blocks(pools.geom, sk, sv, gpu(table, torch.int32),
+                                 gpu(blocks, torch.int32), n_sel, dk, dv)
+    torch.cuda.synchronize()
+    got_k = host(dk).reshape(n_sel, n_kv, -1)
+    got_v = host(dv).reshape(n_sel, n_kv, -1)
+    got_b = host(db)
+    for h in range(n_kv):
+        for i in range(n_sel):
+            lp = blocks[h, i]
+            ok = 0 <= lp < n_logical and 0 <= table[lp] < n_phys
+            assert got_b[h, i] == (i if ok else -1)
+            if ok:
+                assert (got_k[i, h] == pools.ok[table[lp], h]).all()
+                assert (got_v[i, h] == pools.ov[table[lp], h]).all()
+            else:
+                assert (got_k[i, h] == 0xAB).all() and (got_v[i, h] == 0xAB).all()
+
+
+def test_kvmem_host_tier_matches_oracle():
+    """KVMem with the history in pinned host memory: per layer the kept blocks
+    (selected on the device, bit-exact with the oracle's selection) are pulled
+    over the host link and attended with the resident recent window; the
+    result equals the oracle's attention over the selection."""
+    n_kv, gqa, n_pages, n_recent, k_top = 2, 6, 40, 8, 10
+    kv_len = n_pages * 128                           # the new token completes the last page
+    n_phys = n_pages + 2
+    g = np.random.default_rng(123)
+    geom = kv.Geom(n_kv, gqa, n_phys)
+    table = g.permutation(n_phys)[:n_pages].astype(np.int32)
+    pools = Pools(n_phys, n_kv, gqa, init_seed=7)
+    summ = torch.zeros((n_kv, n_pages, 256), dtype=torch.float32, device=DEV)
+    pools.write(g.standard_normal((kv_len - 1, n_kv, 256)).astype(np.float32),
+                g.standard_normal((kv_len - 1, n_kv, 256)).astype(np.float32), 0, table, summ)
+    table_d = gpu(table, torch.int32)
+    layer = streaming.KVMemHostLayer(geom, pools.gk, pools.gv, table_d, n_pages, n_recent, summ)
+    kd = streaming.KVMemHostDecode(geom, [layer], table_d, n_pages, n_recent, k_top, 1, DEV)
+    q = g.standard_normal((1, n_kv * gqa, 256)).astype(np.float32)
+    kn = g.standard_normal((1, n_kv, 256)).astype(np.float32)
+    vn = g.standard_normal((1, n_kv, 256)).astype(np.float32)
+    out = torch.empty((1, n_kv * gqa, 256), dtype=torch.float32, device=DEV)
+    lse = torch.empty((1, n_kv * gqa), dtype=torch.float32, device=DEV)
+    kd.step([gpu(q)], [gpu(kn)], [gpu(vn)], kv_len, 1 / 16, [out], [lse])
+    torch.cuda.synchronize()
+    kept = host(kd.kept[0])
+    # the selection ran on the summaries before this step's append (the last
+    # page is in the recent window, not a candidate)
+    qs = oracle.query_sum(q[0], gqa)
+    summ_ref = quant.summaries_from_pool(pools.ok, table, n_pages - 1, n_kv)
+    for h in range(n_kv):
+        sc = oracle.block_scores(qs[h], summ_ref[h, :n_pages - n_recent])
+        ref = oracle.select_blocks(np.r_[sc, np.zeros(n_recent)], n_pages, n_recent, k_top)
+        assert (kept[h] == ref).all(), (h, kept[h], ref)
+    quant.quantize_into_pool(kn, vn, kv_len - 1, table, pools.ok, pools.ov)
+    ref_o, ref_l = oracle.decode(q, gqa, pools.ok, pools.ov, table, n_pages, kv_len, 1 / 16,
+                                 blocks=kept)
+    eo, el, rr = compare(out, lse, ref_o, ref_l)
+    assert eo <= DEC_TOL and el <= 1e-3 and rr <= 2e-3, (eo, el, rr)
+    # the append completed the last page: its summary now matches the oracle's
+    full = quant.summaries_from_pool(pools.ok, table, n_pages, n_kv)
+    got = host(summ)
+    assert (got[:, n_pages - 1].view(np.uint32) == full[:, n_pages - 1].view(np.uint32)).all()
