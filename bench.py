@@ -430,6 +430,75 @@ def bench_verify_streamed(w, dev, steps, warmup, budget=2100 << 20):
     }, pools
 
 
+def bench_kvmem_host(w, dev, steps, warmup, budgets=(32768, 65536, 98304)):
+    """KVMem with the history in pinned host memory: per step and layer the
+    blocks selected on the device are pulled over the host link by a kernel
+    (kvattn_gather_blocks) and attended with the resident recent window. For
+    each token budget (k_top = budget / 128 history blocks): step time, the
+    needle recall of the selection, and the share of full attention's softmax
+    mass the kept blocks carry (exp(lse_sparse - lse_full) per row)."""
+    import numpy as np
+    import torch
+    import long_context_attention_paged_amd as kv
+    from long_context_attention_paged_amd import streaming
+    pools = LayerPools(w, dev, with_summary=True)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+    lse_full = []
+    for layer in range(w.n_layers):  # full attention (with this step's append) for the coverage
+        o = torch.empty_like(pools.q[layer])
+        l_ = torch.empty(pools.q[layer].shape[:2], dtype=torch.float32, device=dev)
+        kv.kvattn_append_decode(pools.geom, pools.new_k[layer], pools.new_v[layer],
+                                pools.q[layer], pools.kp[layer], pools.vp[layer], pools.table,
+                                w.kv_len, 1.0 / 16.0, out=o, lse=l_, workspace=ws)
+        lse_full.append(l_)
+    layers = []
+    for layer in range(w.n_layers):
+        layers.append(streaming.KVMemHostLayer(pools.geom, pools.kp[layer], pools.vp[layer],
+                                               pools.table, w.n_pages, w.n_recent,
+                                               pools.summ[layer]))
+        pools.kp[layer] = pools.vp[layer] = None
+    torch.cuda.empty_cache()
+    outs = [torch.empty_like(q) for q in pools.q]
+    lses = [torch.empty(q.shape[:2], dtype=torch.float32, device=dev) for q in pools.q]
+    res = {"note": "history in pinned host memory, kept blocks gathered by kernel over the host "
+                   "link, recent window resident", "budgets": {}}
+    for budget in budgets:
+        k_top = budget // 128
+        kd = streaming.KVMemHostDecode(pools.geom, layers, pools.table, w.n_pages, w.n_recent,
+                                       k_top, w.n_q_tok, dev)
+
+        def step():
+            kd.step(pools.q, pools.new_k, pools.new_v, w.kv_len, 1.0 / 16.0, outs, lses)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / steps * 1e3
+        cover = torch.cat([torch.exp(lses[c] - lse_full[c]).reshape(-1)
+                           for c in range(w.n_layers)])
+        h2d = kd.host_to_device_bytes_per_step()
+        tokens = (kd.k_sel + min(w.n_recent, w.n_pages)) * 128
+        res["budgets"][str(budget)] = {
+            "k_top": k_top,
+            "ms_per_step": ms,
+            "tokens_per_s": 1e3 / ms,
+            "attended_tokens": tokens,
+            "kv_gbs": tokens * w.n_kv * (272 + 144) * w.n_layers / (ms * 1e-3) / 1e9,
+            "host_to_device_bytes_per_step": h2d,
+            "host_to_device_gbs": h2d / (ms * 1e-3) / 1e9,
+            "device_pool_bytes": kd.device_bytes(),
+            "recall": needle_recall(w, pools, kd.kept),
+            "mass_covered": {"mean": float(cover.mean()), "min": float(cover.min())},
+        }
+        log(f"{w.name} host tier, budget {budget}: {json.dumps(res['budgets'][str(budget)])}")
+        del kd
+    return res, pools
+
+
 def cpu_baseline_decode(w, pools):
     """The oracle, as it stands, on one (layer, KV head) of the workload."""
     import numpy as np
@@ -593,10 +662,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--configs", default="3,4,2,5,3s",
+    ap.add_argument("--configs", default="3,4,2,5,3s,5h",
                     help="workloads to run: 2 decode-131k, 3 verify-262k, 4 prefill, 5 kvmem, "
                          "4h prefill with the pool in pinned host memory, 3s verify with the "
-                         "history streamed from host memory (2100 MiB device working set)")
+                         "history streamed from host memory (2100 MiB device working set), "
+                         "5h kvmem with its history in host memory (budget sweep)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="run only a short fixed kernel sequence for counter runs (no JSON line)")
@@ -624,6 +694,14 @@ def main():
     decode_res = prefill_res = None
     cpu = None
     for c in cfgs:
+        if c == "5h":
+            w = synth.WORKLOADS[5]
+            log(f"workload {w.name} (host tier)")
+            res, pools = bench_kvmem_host(w, dev, max(2, min(args.steps, 5)), 1)
+            extra[w.name + "-host-tier"] = res
+            del pools
+            torch.cuda.empty_cache()
+            continue
         if c == "3s":
             w = synth.WORKLOADS[3]
             log(f"workload {w.name} (streamed history)")
@@ -665,7 +743,8 @@ def main():
         torch.cuda.empty_cache()
         log(f"{w.name}: {json.dumps(res)}")
 
-    head = decode_res or next(iter(extra.values()))
+    head = decode_res or next((v for v in extra.values() if "ms_per_step" in v),
+                              {"ms_per_step": 0.0})
     w3 = synth.WORKLOADS[3]
     line = {
         "metric": METRIC,
