@@ -341,6 +341,23 @@ kvattn_status kvattn_merge_lse(int32_t n_parts, int64_t rows, int32_t head_dim,
                                const float *o_parts, const float *lse_parts,
                                float *out, float *lse, void *stream);
 
+/* Hadamard rotation of 256-dim rows, in place ([VULKAN] section
+ * "沒踩到的坑：注意力旋轉": the attention rotation raises the precision of a
+ * quantised KV cache and stays on with q8_0 / q5_1 / q4_0 caches). Each row
+ * x[r][0..255] becomes H_256 x / 16, H the Sylvester-ordered Hadamard matrix
+ * (orthonormal after the 1/16), computed in binary32 by the fast
+ * Walsh-Hadamard butterflies with half-widths 1, 2, 4, ..., 128 in that
+ * order (pair (i, i + h), bit h of i clear, becomes x[i] + x[i+h],
+ * x[i] - x[i+h], each rounded), then the exact multiplication by 1/16; the
+ * result is reproducible bit for bit. Rotating the key rows before
+ * kvattn_quantize_pages / kvattn_append_decode and the query rows before
+ * attention or selection leaves q . k unchanged in exact arithmetic and
+ * spreads a key's outlier channels over all dims, which lowers the Q8_0
+ * error where a few channels dominate. Values are not rotated.
+ *  x       fp32 [n_rows][256], device, 16-byte aligned; n_rows >= 0
+ *          (0: nothing is done). */
+kvattn_status kvattn_rotate_rows(float *x, int64_t n_rows, void *stream);
+
 /* KVMem host tier — the GPU pulls the blocks a selection kept from a pool
  * that may live in pinned host memory ([KVMEM] 測試口徑 and "Recall 測試":
  * history blocks in host RAM, budget/128 of them brought to the GPU next to a

@@ -76,6 +76,7 @@ def load_library():
         "kvattn_merge_lse": ([I32, I64, I32, P, P, P, P, P], I32),
         "kvattn_prefetch_pages": ([G, P, P, P, P, P, I32, P], I32),
         "kvattn_gather_blocks": ([G, P, P, P, I32, P, I32, I32, P, P, P, P], I32),
+        "kvattn_rotate_rows": ([P, I64, P], I32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -412,6 +413,19 @@ def kvattn_merge_lse(o_parts, lse_parts, out=None, lse=None, stream=None):
                                 _stream(stream))
     _check("kvattn_merge_lse", code)
     return out, lse
+
+
+def kvattn_rotate_rows(x, stream=None):
+    """In-place Hadamard rotation H_256 / 16 of every 256-element row of the
+    fp32 device tensor x (keys before quantisation, queries before attention)."""
+    torch = _torch()
+    lib = load_library()
+    _need(x, "x", torch.float32)
+    if x.numel() % HEAD_DIM:
+        raise ValueError(f"x must hold whole rows of {HEAD_DIM} elements")
+    _check("kvattn_rotate_rows",
+           lib.kvattn_rotate_rows(_ptr(x), x.numel() // HEAD_DIM, _stream(stream)))
+    return x
 
 
 def kvattn_gather_blocks(geom, src_k_pool, src_v_pool, page_table, blocks, n_sel, dst_k_pool,

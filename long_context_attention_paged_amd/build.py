@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvattn.so")
 SOURCES = ["api.hip", "quantize.hip", "select.hip", "merge.hip", "decode.hip", "prefill.hip",
-           "gather.hip"]
+           "gather.hip", "rotate.hip"]
 # The decode and prefill kernels keep their 64-128 loop-carried accumulators
 # in VGPRs next to LDS-staged operands; without this the allocator splits them
 # between VGPRs and AGPRs and copies every accumulator on each loop iteration.

@@ -505,6 +505,15 @@ kvattn_status kvattn_merge_lse(int32_t n_parts, int64_t rows, int32_t head_dim,
 }
 
 
+kvattn_status kvattn_rotate_rows(float* x, int64_t n_rows, void* stream) {
+  if (n_rows < 0 || (n_rows > 0 && (!x || !aligned(x, 16)))) return KVATTN_E_INVALID;
+  if (n_rows > ((int64_t)1 << 33)) return KVATTN_E_INVALID;  // grid limit
+  kvattn_status st = current_device(nullptr);
+  if (st) return st;
+  if (n_rows == 0) return KVATTN_OK;
+  return launched(launch_rotate(x, n_rows, static_cast<hipStream_t>(stream)));
+}
+
 kvattn_status kvattn_gather_blocks(const kvattn_geom* geom, const uint8_t* src_k_pool,
                                    const uint8_t* src_v_pool, const int32_t* page_table,
                                    int32_t n_logical_pages, const int32_t* blocks, int32_t n_blk,

@@ -99,6 +99,8 @@ hipError_t launch_gather(const uint8_t* src_k, const uint8_t* src_v, const int32
                          int32_t n_sel, int32_t n_kv, uint8_t* dst_k, uint8_t* dst_v,
                          int32_t* dst_blocks, hipStream_t stream);
 
+hipError_t launch_rotate(float* x, int64_t n_rows, hipStream_t stream);
+
 hipError_t launch_merge(int32_t n_parts, int64_t rows, int32_t head_dim, const float* o_parts,
                         const float* lse_parts, float* out, float* lse, hipStream_t stream);
 

@@ -265,3 +265,14 @@ def test_gather_validation_before_device():
     assert call(n_logical=0) == E_INVALID
     assert call(src=FAKE + 16) == E_INVALID           # pools need 256-byte alignment
     assert call(dst=FAKE + 64) == E_INVALID
+
+
+def test_rotate_validation_before_device():
+    import torch
+    f = kv.load_library().kvattn_rotate_rows
+    assert f(P(FAKE), -1, None) == E_INVALID
+    assert f(None, 4, None) == E_INVALID
+    assert f(P(FAKE + 4), 4, None) == E_INVALID        # misaligned
+    if not torch.cuda.is_available():
+        assert f(P(FAKE), 4, None) in (E_DEVICE, E_UNSUPPORTED)
+        assert f(None, 0, None) in (E_DEVICE, E_UNSUPPORTED)
