@@ -248,6 +248,66 @@ def bench_decode(w, dev, steps, warmup, sparse=False):
     return res, pools
 
 
+def rotation_quality(w, pools, dev):
+    """Key rotation on the decode workload's outlier channels: layer 0's cache
+    rebuilt from Hadamard-rotated keys (kvattn_rotate_rows before
+    kvattn_quantize_pages, the query rotated too) against the plain cache, both
+    compared with exact binary64 attention over the unquantised keys and values
+    for the 6 query rows of KV head 0 (numpy here, not the oracle)."""
+    import numpy as np
+    import torch
+    import long_context_attention_paged_amd as kv
+    from long_context_attention_paged_amd import synth
+    q_np = synth.queries(w, 0)
+    K, V = synth.kv_layer(w, 0, q_np, threads=16)
+    Kd, Vd = torch.from_numpy(K).to(dev), torch.from_numpy(V).to(dev)
+    kv.kvattn_rotate_rows(Kd)
+    kr = torch.zeros_like(pools.kp[0])
+    vr = torch.zeros_like(pools.vp[0])
+    kv.kvattn_quantize_pages(pools.geom, Kd, Vd, 0, pools.table, kr, vr)
+    qr = pools.q[0].clone()
+    kv.kvattn_rotate_rows(qr)
+    out_r, _ = kv.kvattn_decode(pools.geom, qr, kr, vr, pools.table, w.kv_len, 1.0 / 16.0)
+    out_p, _ = kv.kvattn_decode(pools.geom, pools.q[0], pools.kp[0], pools.vp[0], pools.table,
+                                w.kv_len, 1.0 / 16.0)
+    # values rotated too: H/16 is symmetric and orthonormal, so rotating the
+    # output rows once more undoes it (o = R sum p R v)
+    kv.kvattn_rotate_rows(Vd)
+    kvv = torch.zeros_like(pools.kp[0])
+    vvv = torch.zeros_like(pools.vp[0])
+    kv.kvattn_quantize_pages(pools.geom, Kd, Vd, 0, pools.table, kvv, vvv)
+    out_kv, _ = kv.kvattn_decode(pools.geom, qr, kvv, vvv, pools.table, w.kv_len, 1.0 / 16.0)
+    kv.kvattn_rotate_rows(out_kv)
+    rows = q_np[0, :w.gqa].astype(np.float64)            # query heads of KV head 0
+    s = rows @ K[:, 0].astype(np.float64).T / 16.0
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    exact = (p @ V[:, 0].astype(np.float64)) / p.sum(axis=1, keepdims=True)
+    res = {"sample": "decode-131k layer 0, KV head 0, 6 query rows, 4 channels x8 (keys and "
+                     "values); scores isolate the key error, outputs include the values'"}
+
+    def head0_keys(pool):
+        # dequantised keys of KV head 0 in token order, from the pool's layout
+        rec = pool.view(-1, w.n_kv, K_REC)[pools.table.long(), 0].cpu().numpy()
+        codes = rec[:, :32768].view(np.int8).reshape(-1, 128, 8, 32).astype(np.float64)
+        d = rec[:, 32768:].view(np.float16).reshape(-1, 128, 8, 1).astype(np.float64)
+        return (codes * d).reshape(-1, 256)[:w.kv_len]
+
+    qrot = qr[0, :w.gqa].double().cpu().numpy()
+    for name, out, pool, qrows in (("plain", out_p, pools.kp[0], rows),
+                                   ("rotated_k", out_r, kr, qrot),
+                                   ("rotated_kv", out_kv, None, None)):
+        o = out[0, :w.gqa].double().cpu().numpy()
+        res[f"out_max_abs_err_{name}"] = float(np.abs(o - exact).max())
+        res[f"out_rel_rms_err_{name}"] = float(np.sqrt(((o - exact) ** 2).sum() / (exact ** 2).sum()))
+        if pool is not None:
+            s_hat = qrows @ head0_keys(pool).T / 16.0
+            res[f"score_rel_rms_err_{name}"] = float(
+                np.sqrt(((s_hat - s) ** 2).sum() / (s ** 2).sum()))
+    del Kd, Vd, kr, vr, kvv, vvv
+    torch.cuda.empty_cache()
+    return res
+
+
 def needle_recall(w, pools, blocks):
     from long_context_attention_paged_amd import synth
     needles = set(int(b) for b in synth.needle_blocks(w))
@@ -725,6 +785,8 @@ def main():
         log(f"workload {w.name}")
         if c in (1, 2, 3):
             res, pools = bench_decode(w, dev, args.steps, args.warmup)
+            if c == 2:
+                res["key_rotation"] = rotation_quality(w, pools, dev)
             if c == 3:
                 decode_res = res
                 if not args.no_cpu_baseline:

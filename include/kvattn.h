@@ -353,7 +353,10 @@ kvattn_status kvattn_merge_lse(int32_t n_parts, int64_t rows, int32_t head_dim,
  * kvattn_quantize_pages / kvattn_append_decode and the query rows before
  * attention or selection leaves q . k unchanged in exact arithmetic and
  * spreads a key's outlier channels over all dims, which lowers the Q8_0
- * error where a few channels dominate. Values are not rotated.
+ * error where a few channels dominate. Values may be rotated as well before
+ * quantisation: H / 16 is symmetric and orthonormal, so rotating the
+ * attention output rows once more returns the attention over the unrotated
+ * values (this lowers the Q4_0 error in the same way).
  *  x       fp32 [n_rows][256], device, 16-byte aligned; n_rows >= 0
  *          (0: nothing is done). */
 kvattn_status kvattn_rotate_rows(float *x, int64_t n_rows, void *stream);

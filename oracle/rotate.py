@@ -8,7 +8,8 @@ The pages do not spell the transform out. Reading taken here: the rotation is
 the orthonormal Sylvester-Hadamard matrix H_256 / 16 applied to each 256-dim
 key row before Q8_0 quantisation and to each query row before attention, so
 q . k = (H q / 16) . (H k / 16) exactly in real arithmetic and the attention
-is unchanged apart from quantisation error. Values are not rotated.
+is unchanged apart from quantisation error. Values may be rotated too, the
+output then rotated once more (H / 16 is its own inverse).
 
 For the quantised bytes to be reproducible bit for bit the binary32
 arithmetic is fixed: the fast Walsh-Hadamard butterflies with half-widths

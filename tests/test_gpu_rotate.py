@@ -82,3 +82,33 @@ def test_rotated_cache_parity_and_error():
     err_r = np.abs(host(out_r) - exact).max()
     err_p = np.abs(host(out_p) - exact).max()
     assert err_r < err_p, (err_r, err_p)
+
+
+def test_rotated_values_round_trip_through_the_output():
+    """Values rotated before quantisation too: H/16 is symmetric and
+    orthonormal, so rotating the attention output rows once more gives the
+    attention over the unrotated values; matches the oracle's same pipeline."""
+    n_kv, gqa, kv_len, n_q_tok = 1, 6, 2000, 1
+    g = np.random.default_rng(78)
+    n_pages = (kv_len + 127) // 128
+    table = np.arange(n_pages, dtype=np.int32)
+    K, V = outlier_kv(g, kv_len, n_kv)
+    V[:, 0, g.choice(256, 4, replace=False)] *= 8.0
+    q = g.standard_normal((n_q_tok, gqa, 256)).astype(np.float32)
+    Kd, Vd, qd = gpu(K), gpu(V), gpu(q)
+    for t in (Kd, Vd, qd):
+        kv.kvattn_rotate_rows(t)
+    pools = Pools(n_pages, n_kv, gqa)
+    kv.kvattn_quantize_pages(pools.geom, Kd, Vd, 0, gpu(table, torch.int32), pools.gk, pools.gv)
+    out, lse = kv.kvattn_decode(pools.geom, qd, pools.gk, pools.gv, gpu(table, torch.int32),
+                                kv_len, 1 / 16)
+    kv.kvattn_rotate_rows(out)
+    quant.quantize_into_pool(rotate.rotate_rows_f32(K), rotate.rotate_rows_f32(V), 0, table,
+                             pools.ok, pools.ov)
+    gk, gv = pools.gpu_bytes()
+    assert (gk == pools.ok).all() and (gv == pools.ov).all()
+    ref_o, ref_l = oracle.decode(rotate.rotate_rows_f32(q), gqa, pools.ok, pools.ov, table,
+                                 n_pages, kv_len, 1 / 16)
+    ref_o = rotate.rotate_rows_f64(ref_o)
+    eo, el, rr = compare(out, lse, ref_o, ref_l)
+    assert eo <= DEC_TOL and el <= 1e-3 and rr <= 2e-3, (eo, el, rr)
