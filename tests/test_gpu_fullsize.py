@@ -9,7 +9,9 @@ itself (nothing the GPU produced is fed to it):
   - decode / verify outputs of one KV head (all its query rows);
   - prefill outputs of one KV head at sampled chunk positions;
   - KVMem summaries and selected blocks of two KV heads, bit for bit, the
-    sparse decode of one head, and needle recall.
+    sparse decode of one head, and needle recall;
+  - the verify step's fused append + decode: whole pools and outputs against
+    quantise + decode bit for bit, one head against the oracle.
 """
 import numpy as np
 import pytest
@@ -153,3 +155,35 @@ def test_kvmem_full_size_selection_and_sparse_decode():
                                          w.kv_len, 1 / 16, blocks=sel[None, :])
             eo, el, rr = compare(out[:, rows], lse[:, rows], ref_o, ref_l)
             assert eo <= DEC_TOL and el <= 1e-3 and rr <= 2e-3, (eo, el, rr)
+
+
+def test_verify_full_size_append_decode():
+    """verify-262k as the benchmark step runs it: one launch appends the 4 new
+    tokens (fresh values, so the append changes the pool) and attends. Whole
+    pools and outputs equal kvattn_quantize_pages + kvattn_decode bit for bit;
+    KV head 1 matches the oracle over its own pool with the new tokens."""
+    w = synth.WORKLOADS[3]
+    head = 1
+    L = FullLayer(w)
+    g = np.random.default_rng(33)
+    n_new = w.n_q_tok
+    pos0 = w.kv_len - n_new
+    Kn = g.standard_normal((n_new, w.n_kv, 256)).astype(np.float32)
+    Vn = g.standard_normal((n_new, w.n_kv, 256)).astype(np.float32)
+    kp2, vp2 = L.kp.clone(), L.vp.clone()
+    kv.kvattn_quantize_pages(L.geom, gpu(Kn), gpu(Vn), pos0, L.td, kp2, vp2)
+    o2, l2 = kv.kvattn_decode(L.geom, gpu(L.q), kp2, vp2, L.td, w.kv_len, 1 / 16)
+    out, lse = kv.kvattn_append_decode(L.geom, gpu(Kn), gpu(Vn), gpu(L.q), L.kp, L.vp, L.td,
+                                       w.kv_len, 1 / 16)
+    torch.cuda.synchronize()
+    assert torch.equal(L.kp, kp2) and torch.equal(L.vp, vp2), "pools differ"
+    assert torch.equal(out, o2) and torch.equal(lse, l2), "outputs differ"
+    K, V = L.K.copy(), L.V.copy()
+    K[pos0:], V[pos0:] = Kn, Vn
+    ok = np.zeros((w.n_pages, 1, quant.K_RECORD_BYTES), np.uint8)
+    ov = np.zeros((w.n_pages, 1, quant.V_RECORD_BYTES), np.uint8)
+    quant.quantize_into_pool(K[:, head:head + 1], V[:, head:head + 1], 0, L.table, ok, ov)
+    rows = slice(head * w.gqa, (head + 1) * w.gqa)
+    ref_o, ref_l = oracle.decode(L.q[:, rows], w.gqa, ok, ov, L.table, w.n_pages, w.kv_len, 1 / 16)
+    eo, el, rr = compare(out[:, rows], lse[:, rows], ref_o, ref_l)
+    assert eo <= DEC_TOL and el <= 1e-3 and rr <= 2e-3, (eo, el, rr)
