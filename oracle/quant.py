@@ -23,6 +23,10 @@ K_CODES_BYTES = PAGE_TOKENS * HEAD_DIM          # 32768
 K_RECORD_BYTES = K_CODES_BYTES + PAGE_TOKENS * N_BLOCKS * 2   # 34816
 V_CODES_BYTES = PAGE_TOKENS * HEAD_DIM // 2     # 16384
 V_RECORD_BYTES = V_CODES_BYTES + PAGE_TOKENS * N_BLOCKS * 2   # 18432
+# Q8_0 values (the q8_0/q8_0 pair, [KVMEM] 測試口徑 --kv-dtype q8_0): a value
+# record of the key record's size, selected by the record size of the pool.
+V8_CODES_BYTES = PAGE_TOKENS * HEAD_DIM         # 32768
+V8_RECORD_BYTES = V8_CODES_BYTES + PAGE_TOKENS * N_BLOCKS * 2  # 34816
 
 
 def rn16(x):
@@ -139,6 +143,25 @@ _V_DIM, _V_TOK, _V_BIT = _v_word_index_tables()
 _VS_TOK, _VS_BLK = _v_scale_index_tables()
 
 
+def _v8_byte_index_tables():
+    """For each of the 32768 code bytes of a Q8_0 value record: the token slot
+    and dim it holds. Byte c*8192 + q*1024 + (16*g + r16)*16 + 8*half + j holds
+    dim 32q + 16*half + r16 of slot 32c + 16*(j/4) + 4g + j%4 (include/kvattn.h)."""
+    i = np.arange(V8_CODES_BYTES)
+    j = i % 8
+    half = (i // 8) % 2
+    r16 = (i // 16) % 16
+    g = (i // 256) % 4
+    q = (i // 1024) % 8
+    c = i // 8192
+    tok = 32 * c + 16 * (j // 4) + 4 * g + (j % 4)
+    dim = 32 * q + 16 * half + r16
+    return tok, dim
+
+
+_V8_TOK, _V8_DIM = _v8_byte_index_tables()
+
+
 def pack_k_record(codes, scale_bits):
     """K record bytes from Q8_0 codes int8 [..., 128, 256] and scales uint16
     [..., 128, 8]; returns uint8 [..., 34816]."""
@@ -189,11 +212,43 @@ def unpack_v_record(rec):
     return codes, bits
 
 
+def pack_v8_record(codes, scale_bits):
+    """Q8_0 value record bytes from codes int8 [..., 128, 256] and scales uint16
+    [..., 128, 8]; returns uint8 [..., 34816]. Scales sit after the codes in the
+    Q4_0 value record's scale order."""
+    codes = np.asarray(codes, np.int8)
+    lead = codes.shape[:-2]
+    rec = np.zeros(lead + (V8_RECORD_BYTES,), np.uint8)
+    rec[..., :V8_CODES_BYTES] = np.ascontiguousarray(codes[..., _V8_TOK, _V8_DIM]).view(np.uint8)
+    sc = np.asarray(scale_bits, np.uint16)[..., _VS_TOK, _VS_BLK]
+    rec[..., V8_CODES_BYTES:] = np.ascontiguousarray(sc.astype('<u2')).view(np.uint8)
+    return rec
+
+
+def unpack_v8_record(rec):
+    """(codes int8 [..., 128, 256], scale_bits uint16 [..., 128, 8]) of Q8_0 value records."""
+    rec = np.ascontiguousarray(np.asarray(rec, np.uint8))
+    lead = rec.shape[:-1]
+    codes = np.zeros(lead + (PAGE_TOKENS, HEAD_DIM), np.int8)
+    codes[..., _V8_TOK, _V8_DIM] = rec[..., :V8_CODES_BYTES].view(np.int8)
+    bits = np.zeros(lead + (PAGE_TOKENS, N_BLOCKS), np.uint16)
+    bits[..., _VS_TOK, _VS_BLK] = np.ascontiguousarray(rec[..., V8_CODES_BYTES:]).view('<u2')
+    return codes, bits
+
+
+def values_are_q8(v_pool):
+    """True when a value pool (uint8 [..., record bytes]) holds Q8_0 records."""
+    n = np.asarray(v_pool).shape[-1]
+    assert n in (V_RECORD_BYTES, V8_RECORD_BYTES), n
+    return n == V8_RECORD_BYTES
+
+
 def quantize_into_pool(k, v, pos0, page_table, k_pool, v_pool):
     """Write positions pos0 .. pos0+n_tok-1 into the pools (kvattn_quantize_pages
     semantics without summaries). k, v: float32 [n_tok, n_kv, 256].
-    k_pool: uint8 [n_phys, n_kv, 34816]; v_pool: uint8 [n_phys, n_kv, 18432],
-    both modified in place. Slots outside the written range keep their bytes.
+    k_pool: uint8 [n_phys, n_kv, 34816]; v_pool: uint8 [n_phys, n_kv, 18432]
+    (Q4_0 values) or [n_phys, n_kv, 34816] (Q8_0 values), both modified in
+    place. Slots outside the written range keep their bytes.
     A page-table entry outside [0, n_phys) skips that page.
 
     [KVMEM] 測試口徑 (--kvmem-block-tokens 128: history held in 128-token
@@ -205,8 +260,10 @@ def quantize_into_pool(k, v, pos0, page_table, k_pool, v_pool):
     n_tok, n_kv, D = k.shape
     assert D == HEAD_DIM and v.shape == k.shape
     n_phys = k_pool.shape[0]
+    v8 = values_are_q8(v_pool)
     kc, ks = q8_0_quantize(k.reshape(n_tok, n_kv, N_BLOCKS, BLOCK))
-    vc, vs = q4_0_quantize(v.reshape(n_tok, n_kv, N_BLOCKS, BLOCK))
+    vq = q8_0_quantize if v8 else q4_0_quantize
+    vc, vs = vq(v.reshape(n_tok, n_kv, N_BLOCKS, BLOCK))
     kc = kc.reshape(n_tok, n_kv, HEAD_DIM)
     vc = vc.reshape(n_tok, n_kv, HEAD_DIM)
     pos = pos0 + np.arange(n_tok)
@@ -223,14 +280,14 @@ def quantize_into_pool(k, v, pos0, page_table, k_pool, v_pool):
     tsel = np.nonzero(ok)[0]
     pidx, slot = where[tsel], pos[tsel] % PAGE_TOKENS
     kcodes, kbits = unpack_k_record(k_pool[phys])                # [P, n_kv, 128, ...]
-    vcodes, vbits = unpack_v_record(v_pool[phys])
+    vcodes, vbits = (unpack_v8_record if v8 else unpack_v_record)(v_pool[phys])
     for h in range(n_kv):
         kcodes[pidx, h, slot] = kc[tsel, h]
         kbits[pidx, h, slot] = ks[tsel, h]
         vcodes[pidx, h, slot] = vc[tsel, h]
         vbits[pidx, h, slot] = vs[tsel, h]
     k_pool[phys] = pack_k_record(kcodes, kbits)
-    v_pool[phys] = pack_v_record(vcodes, vbits)
+    v_pool[phys] = (pack_v8_record if v8 else pack_v_record)(vcodes, vbits)
 
 
 def page_summaries(k_records):

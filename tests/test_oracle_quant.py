@@ -247,3 +247,48 @@ def test_page_summary_closed_forms():
     codes[17, 3] = 64
     s = quant.page_summary(quant.pack_k_record(codes, bits))
     assert s[3] == 0.5 and (np.delete(s, 3) == 0).all()
+
+
+def test_q8_value_record_layout_positions():
+    """Q8_0 value records: bytes at hand-computed positions of the layout in
+    include/kvattn.h (byte c*8192 + q*1024 + (16g + r16)*16 + 8*half + j holds
+    dim 32q + 16*half + r16 of slot 32c + 16*(j//4) + 4g + j%4), 272 bytes per
+    token and head (8.5 bits per element, as for keys), and a round trip."""
+    assert quant.V8_RECORD_BYTES == 34816 and quant.V8_RECORD_BYTES // 128 == 272
+    codes = np.zeros((128, 256), np.int8)
+    bits = np.zeros((128, 8), np.uint16)
+    marks = {  # (slot, dim) -> expected byte offset
+        (0, 0): 0, (1, 0): 1, (16, 0): 4, (4, 0): 256, (0, 16): 8, (0, 1): 16,
+        (0, 32): 1024, (32, 0): 8192, (127, 255): 3 * 8192 + 7 * 1024 + (16 * 3 + 15) * 16 + 8 + 7,
+    }
+    for n, (t, d) in enumerate(marks):
+        codes[t, d] = n + 1
+    rec = quant.pack_v8_record(codes, bits)
+    for n, ((t, d), off) in enumerate(marks.items()):
+        assert rec[off] == n + 1, (t, d, off)
+    assert int((rec[:32768] != 0).sum()) == len(marks)
+    g = np.random.default_rng(8)
+    c2 = g.integers(-127, 128, (3, 128, 256)).astype(np.int8)
+    b2 = g.integers(0, 1 << 16, (3, 128, 8)).astype(np.uint16)
+    c3, b3 = quant.unpack_v8_record(quant.pack_v8_record(c2, b2))
+    assert (c3 == c2).all() and (b3 == b2).all()
+    # scales follow the Q4_0 value record's scale order
+    r4 = quant.pack_v_record(np.zeros((128, 256), np.uint8), b2[0])
+    r8 = quant.pack_v8_record(np.zeros((128, 256), np.int8), b2[0])
+    assert (r4[16384:] == r8[32768:]).all()
+
+
+def test_q8_values_quantise_like_keys():
+    """With a Q8_0 value pool the values go through the key rule: the pool's
+    dequantised values equal the dequantised keys of the same numbers."""
+    g = np.random.default_rng(9)
+    n_tok, n_kv = 300, 2
+    x = g.standard_normal((n_tok, n_kv, 256)).astype(np.float32)
+    x[5, 0, :32] = 0.0
+    table = np.array([2, 0, 3], np.int32)
+    kp = np.zeros((4, n_kv, quant.K_RECORD_BYTES), np.uint8)
+    vp = np.zeros((4, n_kv, quant.V8_RECORD_BYTES), np.uint8)
+    quant.quantize_into_pool(x, x, 0, table, kp, vp)
+    kh, vh = oracle.dequant_page(kp[table], vp[table])
+    assert (kh == vh).all()
+    assert not (vh == 0).all()
