@@ -71,6 +71,15 @@
  *  The V word order places, for each group of 32 slots, the eight slots that
  *  one lane of a 16x16x32 matrix-core tile consumes in one 32-bit word, so a
  *  lane turns a word into four f16 pairs with one shift and one mask each.
+ *  Q8_0 V record (v_type KVATTN_V_Q8_0), KVATTN_V8_RECORD_BYTES = 34816:
+ *   [0, 32768)      int8 codes. For c in [0,4), q in [0,8), g in [0,4),
+ *                   r in [0,16), half in [0,2), j in [0,8), byte
+ *                   c*8192 + q*1024 + (16*g + r)*16 + 8*half + j holds the
+ *                   code of dim n = 32*q + 16*half + r for slot t(c,g,j)
+ *                   (t as above): each 16 bytes are what one lane of a
+ *                   16x16x32 tile reads for two 16-dim tiles of one block.
+ *   [32768, 34816)  binary16 scale of (slot t(c,g,j), block b) at byte
+ *                   32768 + 2*(((c*8 + b)*4 + g)*8 + j).
  *
  * Quantisation (per token, per KV head, per 32-dim block x[0..31]; RN32 and
  * RN16 are IEEE round-to-nearest-even to binary32 / binary16, rint rounds
@@ -79,6 +88,7 @@
  *   code is 0 and the stored scale is +0. Otherwise inv = RN32(1 / d) and
  *   code_i = clamp(rint(RN32(x_i * inv)), -127, 127). Dequantised: d * code.
  *   34 bytes per 32 elements = 8.5 bits per element ([VULKAN] closing remark).
+ *  Q8_0 values (v_type KVATTN_V_Q8_0) follow the key rule above.
  *  Q4_0 (values): j* = lowest index with |x_j*| = amax; m = x_j* (signed);
  *   d = RN16(RN32(-m / 8)). If amax == 0 or d == 0, the stored scale is +0
  *   and every code is 8. Otherwise inv = RN32(1 / d) and
@@ -110,12 +120,18 @@ typedef int32_t kvattn_status;
 #define KVATTN_PAGE_TOKENS 128
 #define KVATTN_K_RECORD_BYTES 34816
 #define KVATTN_V_RECORD_BYTES 18432
+#define KVATTN_V8_RECORD_BYTES 34816 /* Q8_0 values (v_type KVATTN_V_Q8_0) */
+#define KVATTN_V_Q4_0 0 /* value cache type: Q4_0 (the default) */
+#define KVATTN_V_Q8_0 1 /* value cache type: Q8_0 (the q8_0/q8_0 pair) */
 #define KVATTN_MAX_QUERY_ROWS 32 /* n_q_tok * gqa per KV head in decode */
 #define KVATTN_MAX_APPEND_TOKENS 32 /* n_new of kvattn_append_decode */
 
 /* Geometry of one layer's pool. head_dim must be 256 and page_tokens 128
  * (the pages' shape: [VULKAN] "模型結構"; [KVMEM] --kvmem-block-tokens 128).
- * Query head hq uses KV head hq / gqa (grouped-query attention). */
+ * Query head hq uses KV head hq / gqa (grouped-query attention). Keys are
+ * always Q8_0; v_type picks the value type: KVATTN_V_Q4_0 (the [STREAM]
+ * -ctk q8_0 -ctv q4_0 pair) or KVATTN_V_Q8_0 (KVMem's q8_0/q8_0, [KVMEM]
+ * 測試口徑 --kv-dtype q8_0), which sets the value record size. */
 typedef struct kvattn_geom {
   int32_t n_kv_heads;   /* >= 1 */
   int32_t gqa;          /* query heads per KV head, >= 1 */
@@ -123,6 +139,7 @@ typedef struct kvattn_geom {
   int32_t page_tokens;  /* 128 */
   int32_t n_phys_pages; /* physical pages in k_pool / v_pool, >= 1;
                           n_phys_pages * n_kv_heads <= INT32_MAX */
+  int32_t v_type;       /* KVATTN_V_Q4_0 or KVATTN_V_Q8_0 */
 } kvattn_geom;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -146,7 +163,8 @@ int32_t kvattn_select_count(int32_t n_blocks, int32_t n_recent, int32_t k_top);
  *              Requires pos0 >= 0, n_tok >= 1 and
  *              pos0 + n_tok <= n_logical_pages * 128.
  *  k_pool      n_phys_pages * n_kv_heads * 34816 bytes.
- *  v_pool      n_phys_pages * n_kv_heads * 18432 bytes.
+ *  v_pool      n_phys_pages * n_kv_heads * the value record size (18432 bytes
+ *              for Q4_0 values, 34816 for Q8_0).
  *  k_summary   fp32 [n_kv_heads][n_logical_pages][256] or NULL.
  * Logical pages that map to the same physical page race. A page-table entry
  * outside [0, n_phys_pages) makes the kernel skip that page's writes. */

@@ -82,7 +82,13 @@ kvattn_status check_geom(const kvattn_geom* g) {
     return KVATTN_E_UNSUPPORTED;
   if ((int64_t)g->n_kv_heads * g->gqa > (1 << 20)) return KVATTN_E_INVALID;
   if ((int64_t)g->n_phys_pages * g->n_kv_heads > INT32_MAX) return KVATTN_E_INVALID;  // record index
+  if (g->v_type != KVATTN_V_Q4_0 && g->v_type != KVATTN_V_Q8_0) return KVATTN_E_UNSUPPORTED;
   return KVATTN_OK;
+}
+
+// Bytes of one (page, KV head) value record for the geometry's value type.
+size_t v_record_bytes(const kvattn_geom* g) {
+  return g->v_type == KVATTN_V_Q8_0 ? KVATTN_V8_RECORD_BYTES : KVATTN_V_RECORD_BYTES;
 }
 
 kvattn_status check_pools(const kvattn_geom* g, const uint8_t* k_pool, const uint8_t* v_pool) {
@@ -150,7 +156,8 @@ kvattn_status kvattn_quantize_pages(const kvattn_geom* geom, const float* k, con
   if ((st = current_device(nullptr))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = launched(launch_quantize(k, v, pos0, n_tok, geom->n_kv_heads, page_table,
-                                geom->n_phys_pages, k_pool, v_pool, s));
+                                geom->n_phys_pages, k_pool, v_pool,
+                                geom->v_type == KVATTN_V_Q8_0, s));
   if (st || !k_summary) return st;
   const int64_t first = pos0 / KVATTN_PAGE_TOKENS;
   const int64_t last_full = (pos0 + n_tok) / KVATTN_PAGE_TOKENS - 1;
@@ -270,6 +277,7 @@ kvattn_status launch_decode_partials(const kvattn_geom* geom, const float* q, in
   p.k_pool_w = app ? app->k_pool : nullptr;
   p.v_pool_w = app ? app->v_pool : nullptr;
   p.n_new = app ? app->n_new : 0;
+  p.v_q8 = geom->v_type == KVATTN_V_Q8_0;
   return launched(launch_decode(p, s));
 }
 
@@ -279,6 +287,7 @@ kvattn_status check_prefill(const kvattn_geom* geom, const float* q, int32_t chu
                             float scale) {
   kvattn_status st = check_geom(geom);
   if (st) return st;
+  if (geom->v_type != KVATTN_V_Q4_0) return KVATTN_E_UNSUPPORTED;  // prefill reads Q4_0 values only
   if ((st = check_pools(geom, k_pool, v_pool))) return st;
   if (!q || !page_table || !aligned(q, 16)) return KVATTN_E_INVALID;
   if (chunk < 1 || pos0 < 0 || n_logical_pages < 1) return KVATTN_E_INVALID;
@@ -535,7 +544,7 @@ kvattn_status kvattn_gather_blocks(const kvattn_geom* geom, const uint8_t* src_k
   return launched(launch_gather(static_cast<const uint8_t*>(sk), static_cast<const uint8_t*>(sv),
                                 page_table, n_logical_pages, geom->n_phys_pages, blocks, n_blk,
                                 n_sel, geom->n_kv_heads, dst_k_pool, dst_v_pool, dst_blocks,
-                                static_cast<hipStream_t>(stream)));
+                                geom->v_type == KVATTN_V_Q8_0, static_cast<hipStream_t>(stream)));
 }
 
 kvattn_status kvattn_prefetch_pages(const kvattn_geom* geom, const uint8_t* src_k_pool,
@@ -555,7 +564,7 @@ kvattn_status kvattn_prefetch_pages(const kvattn_geom* geom, const uint8_t* src_
   // a physical page's records for all KV heads are contiguous in each pool;
   // runs of consecutive page indices go as one copy per pool
   const size_t k_page = (size_t)geom->n_kv_heads * KVATTN_K_RECORD_BYTES;
-  const size_t v_page = (size_t)geom->n_kv_heads * KVATTN_V_RECORD_BYTES;
+  const size_t v_page = (size_t)geom->n_kv_heads * v_record_bytes(geom);
   int32_t i = 0;
   while (i < n_pages) {
     int32_t j = i + 1;

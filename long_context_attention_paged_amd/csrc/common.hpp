@@ -9,7 +9,8 @@ namespace kvattn {
 constexpr int D = 256;            // head_dim
 constexpr int PAGE = 128;         // tokens per page
 constexpr int K_REC = 34816;      // bytes per (page, KV head) key record
-constexpr int V_REC = 18432;      // bytes per (page, KV head) value record
+constexpr int V_REC = 18432;      // bytes per (page, KV head) value record, Q4_0 values
+constexpr int V8_REC = 34816;     // the same with Q8_0 values (laid out like a key record)
 constexpr int K_SCALE_OFF = 32768;
 constexpr int V_SCALE_OFF = 16384;
 constexpr float LOG2E = 1.4426950408889634f;

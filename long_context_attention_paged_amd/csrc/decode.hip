@@ -47,11 +47,13 @@ constexpr int SLOW_SHARE = 12;          // 32nds of a split's units for waves 4-
 //   [8320, 8832)   key scales;
 //   [8832, 12928)  value words (4 x 1 KB, lane-ordered: each lane reads its own);
 //   [12928, 13440) value scales.
+// With Q8_0 values the value codes take 8 x 1 KB (lane-ordered the same way),
+// the scales follow at 17024 and a slot is 17536 bytes.
 constexpr int SLOT_K = 0;
 constexpr int SLOT_KS = 8320;
 constexpr int SLOT_V = 8832;
-constexpr int SLOT_VS = 12928;
-constexpr int SLOT_BYTES = 13440;
+template <bool V8> constexpr int SLOT_VS = V8 ? 17024 : 12928;
+template <bool V8> constexpr int SLOT_BYTES = V8 ? 17536 : 13440;
 constexpr int Q_LDS_STRIDE = 264;       // halves per query row in LDS (256 + pad)
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -87,11 +89,12 @@ __device__ __forceinline__ void wait_loads() {
 // Direct loads of one tile (32-token group c of a page record) into an LDS
 // slot, in two parts so each can be refilled as soon as it is consumed:
 //   keys   (9 loads): 8 x 1 KB codes + 512 B scales (lanes 0..31);
-//   values (5 loads): 4 x 1 KB words + 512 B scales (lanes 0..31).
+//   values (5 loads): 4 x 1 KB words + 512 B scales (lanes 0..31);
+//            9 loads with Q8_0 values (8 x 1 KB codes + scales).
 // Lane (r16, g) brings exactly the 16-byte code chunks it will feed to the
 // matrix cores, so those LDS reads are lane-local and conflict-free.
 constexpr int K_LOADS = 9;
-constexpr int V_LOADS = 5;
+template <bool V8> constexpr int V_LOADS = V8 ? 9 : 5;
 
 // LDS base of key load i (4 token rows): 1 KB apart plus a 16-byte shift per
 // row quad (i % 4) and 64 bytes per M-tile (i / 4), so loads never overlap.
@@ -109,13 +112,28 @@ __device__ __forceinline__ void issue_keys(uint8_t* slot, const uint8_t* krec, i
   if (lane < 32) dma16(r, lane * 16, K_SCALE_OFF + c * 512, slot + SLOT_KS);
 }
 
+template <bool V8>
 __device__ __forceinline__ void issue_values(uint8_t* slot, const uint8_t* vrec, int c) {
-  const __amdgpu_buffer_rsrc_t r = record(vrec, V_REC);
-  // value words are stored lane-ordered: load q of group c is 1 KB at (4c + q) KB
+  constexpr int NQ = V8 ? 8 : 4;
+  const __amdgpu_buffer_rsrc_t r = record(vrec, V8 ? V8_REC : V_REC);
+  // value codes are stored lane-ordered: load q of group c is 1 KB at (NQ*c + q) KB
   const int lane = opaque_lane();
 #pragma unroll
-  for (int q = 0; q < 4; ++q) dma16(r, lane * 16, (c * 4 + q) * 1024, slot + SLOT_V + q * 1024);
-  if (lane < 32) dma16(r, lane * 16, V_SCALE_OFF + c * 512, slot + SLOT_VS);
+  for (int q = 0; q < NQ; ++q) dma16(r, lane * 16, (c * NQ + q) * 1024, slot + SLOT_V + q * 1024);
+  if (lane < 32)
+    dma16(r, lane * 16, (V8 ? K_SCALE_OFF : V_SCALE_OFF) + c * 512, slot + SLOT_VS<V8>);
+}
+
+// Eight int8 codes (two words, byte order) -> eight exact f16 values.
+__device__ __forceinline__ half8_t v8_codes_to_f16(uint32_t w0, uint32_t w1) {
+  const half2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const uint32_t y0 = w0 ^ 0x80808080u, y1 = w1 ^ 0x80808080u;
+  const half2_t a = as_h2(__builtin_amdgcn_perm(0x64646464u, y0, 0x04010400u)) - off;
+  const half2_t b = as_h2(__builtin_amdgcn_perm(0x64646464u, y0, 0x04030402u)) - off;
+  const half2_t c = as_h2(__builtin_amdgcn_perm(0x64646464u, y1, 0x04010400u)) - off;
+  const half2_t e = as_h2(__builtin_amdgcn_perm(0x64646464u, y1, 0x04030402u)) - off;
+  half8_t r = {a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
+  return r;
 }
 
 template <int NT>
@@ -127,7 +145,7 @@ struct State {
   floatx4 o[NT][16];      // O^T accumulators: dims 16mt + 4g + i, row nt*16 + r16
 };
 
-template <int NT, typename MidFn>
+template <int NT, bool V8, typename MidFn>
 __device__ __forceinline__ void compute_tile(State<NT>& st, const uint8_t* slot, int64_t tok0,
                                              int64_t kv_len, int64_t min_limit, int lane, int r16,
                                              int g, uint32_t nib_mask, MidFn&& after_keys) {
@@ -228,14 +246,25 @@ __device__ __forceinline__ void compute_tile(State<NT>& st, const uint8_t* slot,
     for (int j = 0; j < 8; ++j) pb[nt][j] = (_Float16)p[j];
   }
   // ---- O^T += Vhat^T . (P' * d_V)^T ----------------------------------------
+  // Q4_0: four words per lane hold all 16 dim tiles; Q8_0: 16 bytes per
+  // block b (two dim tiles), read one block ahead.
   u32x4 vw[4];
+  if constexpr (V8) {
+    vw[0] = *reinterpret_cast<const u32x4*>(slot + SLOT_V + lane * 16);
+  } else {
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    vw[q] = *reinterpret_cast<const u32x4*>(slot + SLOT_V + q * 1024 + lane * 16);
+    for (int q = 0; q < 4; ++q)
+      vw[q] = *reinterpret_cast<const u32x4*>(slot + SLOT_V + q * 1024 + lane * 16);
+  }
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
+    u32x4 v8cur;
+    if constexpr (V8) {
+      v8cur = vw[0];
+      if (b < 7) vw[0] = *reinterpret_cast<const u32x4*>(slot + SLOT_V + (b + 1) * 1024 + lane * 16);
+    }
     const u32x4 sc =
-        *reinterpret_cast<const u32x4*>(slot + SLOT_VS + (b * 4 + g) * 16) & vmask;
+        *reinterpret_cast<const u32x4*>(slot + SLOT_VS<V8> + (b * 4 + g) * 16) & vmask;
     const uint32_t scw[4] = {sc.x, sc.y, sc.z, sc.w};
     half8_t bb[NT];
 #pragma unroll
@@ -250,9 +279,14 @@ __device__ __forceinline__ void compute_tile(State<NT>& st, const uint8_t* slot,
 #pragma unroll
     for (int e2 = 0; e2 < 2; ++e2) {
       const int mt = 2 * b + e2;
-      const u32x4 vq = vw[mt >> 2];
-      const uint32_t w = (mt & 3) == 0 ? vq.x : (mt & 3) == 1 ? vq.y : (mt & 3) == 2 ? vq.z : vq.w;
-      const half8_t a = v_codes_to_f16_m(w, nib_mask);
+      half8_t a;
+      if constexpr (V8) {
+        a = v8_codes_to_f16(e2 ? v8cur.z : v8cur.x, e2 ? v8cur.w : v8cur.y);
+      } else {
+        const u32x4 vq = vw[mt >> 2];
+        const uint32_t w = (mt & 3) == 0 ? vq.x : (mt & 3) == 1 ? vq.y : (mt & 3) == 2 ? vq.z : vq.w;
+        a = v_codes_to_f16_m(w, nib_mask);
+      }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) st.o[nt][mt] = mfma16(a, bb[nt], st.o[nt][mt]);
     }
@@ -269,7 +303,8 @@ __device__ __forceinline__ void compute_tile(State<NT>& st, const uint8_t* slot,
 // magnitude (keys) and lowest-index element of largest magnitude (values)
 // are reduced over its eight lanes. The lane's value dims n0..n0+3
 // (n0 = 32b + 4s) share (q, e) and take d = n0 % 16 .. +3, so each slot group
-// g gives the lane four words to merge.
+// g gives the lane four words to merge. Q8_0 values are plain bytes: the
+// lane stores its four codes where the value record places them.
 struct AppendTile {
   int64_t tok;        // first position of the tile (32-token group c of its page)
   int64_t rec;        // record index of the page and KV head
@@ -309,6 +344,7 @@ __device__ __forceinline__ void append_load(const DecodeParams& p, const AppendT
 }
 
 // Requests the first slots' inputs and the old words of partly new V words.
+template <bool V8>
 __device__ __forceinline__ void append_issue(const DecodeParams& p, AppendTile& a, int h, int c,
                                              int64_t first_new, int lane) {
   a.ub = (int)(first_new > a.tok ? first_new - a.tok : 0);
@@ -325,6 +361,7 @@ __device__ __forceinline__ void append_issue(const DecodeParams& p, AppendTile& 
     a.newmask[g] = m;
   }
   append_load(p, a, h, first_new, a.ub, lane, a.x, a.y);
+  if constexpr (V8) return;
   const uint32_t* vw = reinterpret_cast<const uint32_t*>(p.v_pool_w + a.rec * V_REC);
 #pragma unroll
   for (int g = 0; g < 4; ++g)
@@ -334,11 +371,12 @@ __device__ __forceinline__ void append_issue(const DecodeParams& p, AppendTile& 
 }
 
 // Quantises every new slot of the tile and writes codes, scales and words.
+template <bool V8>
 __device__ __forceinline__ void append_finish(const DecodeParams& p, AppendTile& a, int h, int c,
                                               int64_t first_new, int lane) {
   const int b = lane >> 3, s = lane & 7;
   uint8_t* krec = p.k_pool_w + a.rec * K_REC;
-  uint8_t* vrec = p.v_pool_w + a.rec * V_REC;
+  uint8_t* vrec = p.v_pool_w + a.rec * (V8 ? V8_REC : V_REC);
   uint32_t acc[4][4] = {};
   for (int u0 = a.ub; u0 < a.ue; u0 += 4) {
     if (u0 != a.ub) append_load(p, a, h, first_new, u0, lane, a.x, a.y);
@@ -366,6 +404,24 @@ __device__ __forceinline__ void append_finish(const DecodeParams& p, AppendTile&
       if (s == 0)
         *reinterpret_cast<uint16_t*>(krec + K_SCALE_OFF + (t * 8 + b) * 2) =
             d != 0.0f ? __builtin_bit_cast(uint16_t, d16) : (uint16_t)0;
+      if constexpr (V8) {  // values: Q8_0, the key rule
+        float vmax = fmaxf(fmaxf(fabsf(ye[0]), fabsf(ye[1])), fmaxf(fabsf(ye[2]), fabsf(ye[3])));
+        vmax = fmaxf(vmax, __shfl_xor(vmax, 1));
+        vmax = fmaxf(vmax, __shfl_xor(vmax, 2));
+        vmax = fmaxf(vmax, __shfl_xor(vmax, 4));
+        const _Float16 dq16 = q8_scale(vmax);
+        const float dq = (float)dq16;
+        const float inv = dq != 0.0f ? 1.0f / dq : 0.0f;
+        const int g = (u & 15) >> 2, j = 4 * (u >> 4) + (u & 3);
+        // dim 32b + 4s + i sits in half s/4, row 4(s%4) + i of block b's piece
+        uint8_t* dst = vrec + c * 8192 + b * 1024 + (16 * g + 4 * (s & 3)) * 16 + 8 * (s >> 2) + j;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[16 * i] = dq != 0.0f ? (uint8_t)q8_code(ye[i], inv) : (uint8_t)0;
+        if (s == 0)
+          *reinterpret_cast<uint16_t*>(vrec + K_SCALE_OFF + 2 * (((c * 8 + b) * 4 + g) * 8 + j)) =
+              dq != 0.0f ? __builtin_bit_cast(uint16_t, dq16) : (uint16_t)0;
+        continue;
+      }
       // values: Q4_0, the lowest-index element of largest magnitude sets the scale
       float am = fabsf(ye[0]), m = ye[0];
       int idx = 4 * s;
@@ -407,6 +463,7 @@ __device__ __forceinline__ void append_finish(const DecodeParams& p, AppendTile&
           for (int i = 0; i < 4; ++i) acc[gg][i] |= code[i] << bit;
     }
   }
+  if constexpr (V8) return;
   uint32_t* vw = reinterpret_cast<uint32_t*>(vrec);
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -420,8 +477,8 @@ __device__ __forceinline__ void append_finish(const DecodeParams& p, AppendTile&
 // WAVES: wavefronts per workgroup (4 or 8); either way two wavefronts share
 // a SIMD (two 4-wave workgroups or one 8-wave workgroup per CU), so every
 // lane may hold up to 256 VGPRs. With 8 waves, waves 4-7 stream the first
-// SLOW_SHARE/32 of the split's units and waves 0-3 the rest.
-template <int NT, int WAVES>
+// SLOW_SHARE/32 of the split's units and waves 0-3 the rest. V8: Q8_0 values.
+template <int NT, int WAVES, bool V8>
 __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
   constexpr int THREADS = 64 * WAVES;
   constexpr int NH = WAVES / 4;  // halves of the workgroup streaming a split
@@ -438,7 +495,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
   const int R = p.n_q_tok * p.gqa;
   const int n_heads = p.n_kv * p.gqa;
   constexpr int Q_BYTES = ((NT * 16 * Q_LDS_STRIDE * 2) + 1023) / 1024 * 1024;
-  uint8_t* slots = smem_raw + Q_BYTES + wave * SLOT_BYTES;
+  constexpr int VREC = V8 ? V8_REC : V_REC;
+  uint8_t* slots = smem_raw + Q_BYTES + wave * SLOT_BYTES<V8>;
 
   _Float16* q_lds = reinterpret_cast<_Float16*>(smem_raw);
   State<NT> st;
@@ -534,18 +592,18 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
         }
       }
       if (n_tiles > 64 && i0 > 0) refill(0);  // the loop starts from the first 64 units
-      if (app) append_issue(p, at, h, c, first_new, lane);
+      if (app) append_issue<V8>(p, at, h, c, first_new, lane);
     }
     const bool first_new_tile = app && valid && tok + 32 > first_new;
     if (!first_new_tile) {
       issue_keys(slot, p.k_pool + rec * K_REC, valid ? c : 0);
-      issue_values(slot, p.v_pool + rec * V_REC, valid ? c : 0);
+      issue_values<V8>(slot, p.v_pool + rec * VREC, valid ? c : 0);
     }
     if (first_new_tile) {
-      append_finish(p, at, h, c, first_new, lane);
+      append_finish<V8>(p, at, h, c, first_new, lane);
       wait_loads<0>();  // this wave's stores have completed
       issue_keys(slot, p.k_pool + rec * K_REC, c);
-      issue_values(slot, p.v_pool + rec * V_REC, c);
+      issue_values<V8>(slot, p.v_pool + rec * VREC, c);
     }
     app_pending = app && !first_new_tile;
   }
@@ -579,14 +637,14 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
     }
   }
   __syncthreads();
-  if (app_pending) append_finish(p, at, h, c, first_new, lane);
+  if (app_pending) append_finish<V8>(p, at, h, c, first_new, lane);
   for (int i = 0; i < n_tiles; ++i) {
     const bool more = i + 1 < n_tiles;
     if (more) locate(i + 1, tok_n, valid_n, rec_n);
     if (app_pending && i == 0) {
       wait_loads<0>();  // the appended tokens' stores (and all of tile 0) have completed
     } else {
-      wait_loads<V_LOADS>();  // keys of tile i have landed (its values may still fly)
+      wait_loads<V_LOADS<V8>>();  // keys of tile i have landed (its values may still fly)
     }
     auto refill_keys = [&] {
       if (more) {
@@ -598,13 +656,13 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
       }
     };
     if (valid) {
-      compute_tile<NT>(st, slot, tok, p.kv_len, min_limit, lane, r16, g, nib_mask, refill_keys);
+      compute_tile<NT, V8>(st, slot, tok, p.kv_len, min_limit, lane, r16, g, nib_mask, refill_keys);
     } else {
       refill_keys();
     }
     if (more) {
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): value reads of this slot are done
-      issue_values(slot, p.v_pool + rec_n * V_REC, valid_n ? c : 0);
+      issue_values<V8>(slot, p.v_pool + rec_n * VREC, valid_n ? c : 0);
     }
     tok = tok_n;
     rec = rec_n;
@@ -677,18 +735,18 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
   }
 }
 
-template <int NT>
+template <int NT, bool V8>
 hipError_t launch_nt(const DecodeParams& p, hipStream_t stream) {
   const size_t combine = sizeof(float) * DECODE_WAVES * 16 * 260;
   const size_t qbytes = ((NT * 16 * Q_LDS_STRIDE * 2) + 1023) / 1024 * 1024;
-  const size_t loop = qbytes + DECODE_WAVES * SLOT_BYTES;
+  const size_t loop = qbytes + DECODE_WAVES * SLOT_BYTES<V8>;
   const size_t shmem = combine > loop ? combine : loop;
   static std::atomic<uint64_t> lds_set{0};
   const hipError_t e = set_lds_limit(
-      lds_set, reinterpret_cast<const void*>(&decode_kernel<NT, DECODE_WAVES>), shmem);
+      lds_set, reinterpret_cast<const void*>(&decode_kernel<NT, DECODE_WAVES, V8>), shmem);
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)p.n_splits, (unsigned)p.n_kv);
-  hipLaunchKernelGGL((decode_kernel<NT, DECODE_WAVES>), grid, dim3(64 * DECODE_WAVES), shmem, stream, p);
+  hipLaunchKernelGGL((decode_kernel<NT, DECODE_WAVES, V8>), grid, dim3(64 * DECODE_WAVES), shmem, stream, p);
   return hipGetLastError();
 }
 
@@ -696,8 +754,8 @@ hipError_t launch_nt(const DecodeParams& p, hipStream_t stream) {
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const int R = p.n_q_tok * p.gqa;
-  if (R <= 16) return launch_nt<1>(p, stream);
-  return launch_nt<2>(p, stream);
+  if (p.v_q8) return R <= 16 ? launch_nt<1, true>(p, stream) : launch_nt<2, true>(p, stream);
+  return R <= 16 ? launch_nt<1, false>(p, stream) : launch_nt<2, false>(p, stream);
 }
 
 }  // namespace kvattn

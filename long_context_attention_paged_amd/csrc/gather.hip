@@ -11,20 +11,21 @@ namespace {
 
 constexpr int GATHER_THREADS = 256;
 constexpr int K_CHUNKS = K_REC / 16;  // 2176 16-byte chunks per key record
-constexpr int V_CHUNKS = V_REC / 16;  // 1152 per value record
-constexpr int G_PER_THREAD = (K_CHUNKS + V_CHUNKS + GATHER_THREADS - 1) / GATHER_THREADS;  // 13
 
-// grid (n_sel, n_kv). Workgroup (i, h) copies the key and value records of
+// grid (n_sel, n_kv), VREC the value record size (Q4_0 or Q8_0 values). Workgroup (i, h) copies the key and value records of
 // logical page blocks[h][i] (row stride n_blk) into record i * n_kv + h of the
 // destination pools and writes dst_blocks[h][i] (row stride n_sel) = i, or -1
 // (nothing copied) when the entry or its physical page is out of range. Each
-// thread requests all of its 13 chunks before storing any, so a record costs
-// about one round trip over the host link.
+// thread requests all of its chunks (13 with Q4_0 values, 17 with Q8_0) before
+// storing any, so a record costs about one round trip over the host link.
+template <int VREC>
 __global__ __launch_bounds__(GATHER_THREADS) void gather_kernel(
     const uint8_t* __restrict__ src_k, const uint8_t* __restrict__ src_v,
     const int32_t* __restrict__ page_table, int32_t n_logical, int32_t n_phys,
     const int32_t* __restrict__ blocks, int32_t n_blk, int32_t n_kv, uint8_t* __restrict__ dst_k,
     uint8_t* __restrict__ dst_v, int32_t* __restrict__ dst_blocks) {
+  constexpr int V_CHUNKS = VREC / 16;
+  constexpr int G_PER_THREAD = (K_CHUNKS + V_CHUNKS + GATHER_THREADS - 1) / GATHER_THREADS;
   const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int32_t lp = blocks[(int64_t)h * n_blk + i];
   int32_t ph = -1;
@@ -35,9 +36,9 @@ __global__ __launch_bounds__(GATHER_THREADS) void gather_kernel(
   if (tid == 0) dst_blocks[(int64_t)h * gridDim.x + i] = ph >= 0 ? i : -1;
   if (ph < 0) return;  // uniform across the workgroup
   const u32x4* ks = reinterpret_cast<const u32x4*>(src_k + ((int64_t)ph * n_kv + h) * K_REC);
-  const u32x4* vs = reinterpret_cast<const u32x4*>(src_v + ((int64_t)ph * n_kv + h) * V_REC);
+  const u32x4* vs = reinterpret_cast<const u32x4*>(src_v + ((int64_t)ph * n_kv + h) * VREC);
   u32x4* kd = reinterpret_cast<u32x4*>(dst_k + ((int64_t)i * n_kv + h) * K_REC);
-  u32x4* vd = reinterpret_cast<u32x4*>(dst_v + ((int64_t)i * n_kv + h) * V_REC);
+  u32x4* vd = reinterpret_cast<u32x4*>(dst_v + ((int64_t)i * n_kv + h) * VREC);
   u32x4 v[G_PER_THREAD];
 #pragma unroll
   for (int k = 0; k < G_PER_THREAD; ++k) {
@@ -58,9 +59,9 @@ __global__ __launch_bounds__(GATHER_THREADS) void gather_kernel(
 hipError_t launch_gather(const uint8_t* src_k, const uint8_t* src_v, const int32_t* page_table,
                          int32_t n_logical, int32_t n_phys, const int32_t* blocks, int32_t n_blk,
                          int32_t n_sel, int32_t n_kv, uint8_t* dst_k, uint8_t* dst_v,
-                         int32_t* dst_blocks, hipStream_t stream) {
+                         int32_t* dst_blocks, bool v_q8, hipStream_t stream) {
   dim3 grid((unsigned)n_sel, (unsigned)n_kv);
-  hipLaunchKernelGGL(gather_kernel, grid, dim3(GATHER_THREADS), 0, stream, src_k, src_v,
+  hipLaunchKernelGGL(v_q8 ? gather_kernel<V8_REC> : gather_kernel<V_REC>, grid, dim3(GATHER_THREADS), 0, stream, src_k, src_v,
                      page_table, n_logical, n_phys, blocks, n_blk, n_kv, dst_k, dst_v,
                      dst_blocks);
   return hipGetLastError();

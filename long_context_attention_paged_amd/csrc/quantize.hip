@@ -19,7 +19,9 @@ namespace {
 // One workgroup per (32-token group, KV head); thread (u, b) = (tid/8, tid%8)
 // quantises the 32-dim block b of token slot u, so all tokens of the group
 // are processed at once and each block's reductions stay in one thread.
-// Value codes go through LDS to be packed into the group's V words.
+// Value codes go through LDS to be packed into the group's V words (Q4_0) or
+// reordered into the group's 16-byte lane pieces (Q8_0, V8 true).
+template <bool V8>
 __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ k,
                                                        const float* __restrict__ v, int64_t pos0,
                                                        int32_t n_tok, int32_t n_kv,
@@ -38,12 +40,12 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
   const int32_t phys = page_table[lp];
   if (phys < 0 || phys >= n_phys) return;  // uniform across the workgroup
   uint8_t* krec = k_pool + ((int64_t)phys * n_kv + h) * K_REC;
-  uint8_t* vrec = v_pool + ((int64_t)phys * n_kv + h) * V_REC;
+  uint8_t* vrec = v_pool + ((int64_t)phys * n_kv + h) * (V8 ? V8_REC : V_REC);
   uint32_t* vwords = reinterpret_cast<uint32_t*>(vrec) + c * 1024;
   const int64_t end = pos0 + n_tok;
   const bool whole = gpos >= pos0 && gpos + 32 <= end;  // uniform
   uint32_t old[4] = {0u, 0u, 0u, 0u};
-  if (!whole) {
+  if (!V8 && !whole) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) old[q] = vwords[tid + 256 * q];
   }
@@ -87,29 +89,84 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
     *reinterpret_cast<uint16_t*>(krec + K_SCALE_OFF + (t * 8 + b) * 2) =
         d != 0.0f ? __builtin_bit_cast(uint16_t, d16) : (uint16_t)0;
 
-    // Q4_0: the lowest-index element of largest magnitude, signed, maps to -8.
-    float a = fabsf(y[0]), m = y[0];
+    if constexpr (V8) {  // Q8_0 values: the key rule
+      float vmax = 0.0f;
 #pragma unroll
-    for (int i = 1; i < 32; ++i)
-      if (fabsf(y[i]) > a) {
-        a = fabsf(y[i]);
-        m = y[i];
-      }
-    uint16_t bits4 = 0;
-    const _Float16 dv16 = q4_scale(m);
-    const float dv = (float)dv16;
-    if (a != 0.0f && dv != 0.0f) {
-      const float inv = 1.0f / dv;
+      for (int i = 0; i < 32; ++i) vmax = fmaxf(vmax, fabsf(y[i]));
+      const _Float16 dq16 = q8_scale(vmax);
+      const float dq = (float)dq16;
+      const float inv = dq != 0.0f ? 1.0f / dq : 0.0f;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) vcodes[u][32 * b + i] = (uint8_t)q4_code(y[i], inv);
-      bits4 = __builtin_bit_cast(uint16_t, dv16);
+      for (int i = 0; i < 32; ++i)
+        vcodes[u][32 * b + i] = dq != 0.0f ? (uint8_t)q8_code(y[i], inv) : (uint8_t)0;
+      vscales[u][b] = dq != 0.0f ? __builtin_bit_cast(uint16_t, dq16) : (uint16_t)0;
     } else {
+      // Q4_0: the lowest-index element of largest magnitude, signed, maps to -8.
+      float a = fabsf(y[0]), m = y[0];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) vcodes[u][32 * b + i] = 8;
+      for (int i = 1; i < 32; ++i)
+        if (fabsf(y[i]) > a) {
+          a = fabsf(y[i]);
+          m = y[i];
+        }
+      uint16_t bits4 = 0;
+      const _Float16 dv16 = q4_scale(m);
+      const float dv = (float)dv16;
+      if (a != 0.0f && dv != 0.0f) {
+        const float inv = 1.0f / dv;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) vcodes[u][32 * b + i] = (uint8_t)q4_code(y[i], inv);
+        bits4 = __builtin_bit_cast(uint16_t, dv16);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) vcodes[u][32 * b + i] = 8;
+      }
+      vscales[u][b] = bits4;
     }
-    vscales[u][b] = bits4;
   }
   __syncthreads();
+
+  if constexpr (V8) {
+    // 16-byte piece i of the group (512 of them): bytes (half, j) hold dim
+    // 32q + 16*half + r of slots 16*(j/4) + 4g + j%4; unwritten slots keep their bytes.
+    uint8_t* vbytes = vrec + c * 8192;
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      const int i = tid + 256 * qq;
+      const int r = i & 15, g = (i >> 4) & 3, q = i >> 6;
+      uint32_t w[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        uint32_t wv = 0;
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          const int half = x >> 1, j = 4 * (x & 1) + y;
+          const int uu = 16 * (j >> 2) + 4 * g + (j & 3);
+          wv |= (uint32_t)vcodes[uu][32 * q + 16 * half + r] << (8 * y);
+        }
+        w[x] = wv;
+      }
+      if (whole) {
+        reinterpret_cast<uint4*>(vbytes)[i] = uint4{w[0], w[1], w[2], w[3]};
+      } else {
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          const int j = x & 7;
+          const int64_t p = gpos + 16 * (j >> 2) + 4 * g + (j & 3);
+          if (p >= pos0 && p < end) vbytes[16 * i + x] = (uint8_t)(w[x >> 2] >> (8 * (x & 3)));
+        }
+      }
+    }
+    {
+      const int i = tid;
+      const int j = i & 7, g = (i >> 3) & 3, bb = i >> 5;
+      const int uu = 16 * (j >> 2) + 4 * g + (j & 3);
+      const int64_t p = gpos + uu;
+      if (p >= pos0 && p < end)
+        reinterpret_cast<uint16_t*>(vrec + K_SCALE_OFF)[c * 256 + i] = vscales[uu][bb];
+    }
+    return;
+  }
 
   // V words of this 32-slot group: word (q, g, d, e) holds dim 16*(4q+e)+d for
   // slots 16*(j/4) + 4g + j%4; slots outside the written range keep their bits.
@@ -184,10 +241,10 @@ __global__ __launch_bounds__(256) void summarize_kernel(const uint8_t* __restric
 
 hipError_t launch_quantize(const float* k, const float* v, int64_t pos0, int32_t n_tok,
                            int32_t n_kv, const int32_t* page_table, int32_t n_phys,
-                           uint8_t* k_pool, uint8_t* v_pool, hipStream_t stream) {
+                           uint8_t* k_pool, uint8_t* v_pool, bool v_q8, hipStream_t stream) {
   const int64_t g0 = pos0 / 32, g1 = (pos0 + n_tok - 1) / 32;
   dim3 grid((unsigned)(g1 - g0 + 1), (unsigned)n_kv);
-  hipLaunchKernelGGL(quantize_kernel, grid, dim3(256), 0, stream, k, v, pos0, n_tok, n_kv,
+  hipLaunchKernelGGL(v_q8 ? quantize_kernel<true> : quantize_kernel<false>, grid, dim3(256), 0, stream, k, v, pos0, n_tok, n_kv,
                      page_table, n_phys, k_pool, v_pool);
   return hipGetLastError();
 }

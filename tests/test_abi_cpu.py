@@ -276,3 +276,25 @@ def test_rotate_validation_before_device():
     if not torch.cuda.is_available():
         assert f(P(FAKE), 4, None) in (E_DEVICE, E_UNSUPPORTED)
         assert f(None, 0, None) in (E_DEVICE, E_UNSUPPORTED)
+
+
+def test_value_type_validation():
+    """v_type selects Q4_0 (0) or Q8_0 (1) value records; other values are
+    unsupported everywhere, and prefill supports Q4_0 values only."""
+    lib = kv.load_library()
+    bad = geom()
+    bad.v_type = 2
+    assert decode(bad)[0] == E_UNSUPPORTED
+    assert lib.kvattn_quantize_pages(ctypes.byref(bad), P(FAKE), P(FAKE), 0, 4, P(FAKE), 16,
+                                     P(FAKE), P(FAKE), None, None) == E_UNSUPPORTED
+    q8 = geom()
+    q8.v_type = kv.V_Q8_0
+    code, nb = decode(q8, ws=None)
+    assert code == OK and nb > 0                                 # workspace query accepted
+    nb = ctypes.c_size_t(0)
+    assert lib.kvattn_prefill_chunk(ctypes.byref(q8), P(FAKE), 100, P(FAKE), P(FAKE), P(FAKE), 16,
+                                    1000, 0.0625, P(FAKE), P(FAKE), 4, None, ctypes.byref(nb),
+                                    None) == E_UNSUPPORTED
+    assert kv.Geom(1, 1, 1).v_record_bytes == 18432
+    assert kv.Geom(1, 1, 1, v_type=kv.V_Q8_0).v_record_bytes == 34816
+    assert ctypes.sizeof(kv.Geom) == 24
