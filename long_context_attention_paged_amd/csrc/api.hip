@@ -287,7 +287,6 @@ kvattn_status check_prefill(const kvattn_geom* geom, const float* q, int32_t chu
                             float scale) {
   kvattn_status st = check_geom(geom);
   if (st) return st;
-  if (geom->v_type != KVATTN_V_Q4_0) return KVATTN_E_UNSUPPORTED;  // prefill reads Q4_0 values only
   if ((st = check_pools(geom, k_pool, v_pool))) return st;
   if (!q || !page_table || !aligned(q, 16)) return KVATTN_E_INVALID;
   if (chunk < 1 || pos0 < 0 || n_logical_pages < 1) return KVATTN_E_INVALID;
@@ -327,6 +326,7 @@ kvattn_status launch_prefill_partials(const kvattn_geom* geom, const float* q, i
   p.n_logical = n_logical_pages;
   p.n_phys = geom->n_phys_pages;
   p.qscale = scale * kLog2e;
+  p.v_q8 = geom->v_type == KVATTN_V_Q8_0;
   return launched(launch_prefill(p, s));
 }
 

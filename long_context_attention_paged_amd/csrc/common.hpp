@@ -55,6 +55,19 @@ __device__ __forceinline__ half8_t k_codes_to_f16(uint32_t w0, uint32_t w1, half
   return r;
 }
 
+// Eight int8 codes (two words, byte order) -> eight exact f16 values
+// (Q8_0 values: the scale is applied elsewhere).
+__device__ __forceinline__ half8_t v8_codes_to_f16(uint32_t w0, uint32_t w1) {
+  const half2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const uint32_t y0 = w0 ^ 0x80808080u, y1 = w1 ^ 0x80808080u;
+  const half2_t a = as_h2(__builtin_amdgcn_perm(0x64646464u, y0, 0x04010400u)) - off;
+  const half2_t b = as_h2(__builtin_amdgcn_perm(0x64646464u, y0, 0x04030402u)) - off;
+  const half2_t c = as_h2(__builtin_amdgcn_perm(0x64646464u, y1, 0x04010400u)) - off;
+  const half2_t e = as_h2(__builtin_amdgcn_perm(0x64646464u, y1, 0x04030402u)) - off;
+  half8_t r = {a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
+  return r;
+}
+
 // One V word (eight 4-bit codes, slot 2p at bit 4p, slot 2p+1 at bit 16+4p)
 // -> eight exact f16 values (code - 8) in slot order.
 __device__ __forceinline__ half8_t v_codes_to_f16(uint32_t w) {

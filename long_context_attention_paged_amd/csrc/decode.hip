@@ -124,17 +124,6 @@ __device__ __forceinline__ void issue_values(uint8_t* slot, const uint8_t* vrec,
     dma16(r, lane * 16, (V8 ? K_SCALE_OFF : V_SCALE_OFF) + c * 512, slot + SLOT_VS<V8>);
 }
 
-// Eight int8 codes (two words, byte order) -> eight exact f16 values.
-__device__ __forceinline__ half8_t v8_codes_to_f16(uint32_t w0, uint32_t w1) {
-  const half2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
-  const uint32_t y0 = w0 ^ 0x80808080u, y1 = w1 ^ 0x80808080u;
-  const half2_t a = as_h2(__builtin_amdgcn_perm(0x64646464u, y0, 0x04010400u)) - off;
-  const half2_t b = as_h2(__builtin_amdgcn_perm(0x64646464u, y0, 0x04030402u)) - off;
-  const half2_t c = as_h2(__builtin_amdgcn_perm(0x64646464u, y1, 0x04010400u)) - off;
-  const half2_t e = as_h2(__builtin_amdgcn_perm(0x64646464u, y1, 0x04030402u)) - off;
-  half8_t r = {a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
-  return r;
-}
 
 template <int NT>
 struct State {

@@ -90,6 +90,7 @@ struct PrefillParams {
   int32_t n_logical;
   int32_t n_phys;
   float qscale;
+  int32_t v_q8;              // value records hold Q8_0 codes (else Q4_0)
 };
 
 int32_t prefill_rows_per_tile();

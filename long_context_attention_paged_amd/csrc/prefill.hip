@@ -41,10 +41,13 @@ constexpr int STAGE_HALVES = K_LDS_HALVES + V_LDS_HALVES;  // one f16 sub-tile
 constexpr int N_STAGES = 3;
 constexpr float PF_RESCALE_MARGIN = 8.0f;
 // Raw (quantised) share of one wave per sub-tile: 4 key rows (1 KB), 128
-// value words (512 B), 4 x 16 B of key scales, 4 x 16 B of value scales.
-constexpr int RAW_K = 0, RAW_V = 1024, RAW_KS = 1536, RAW_VS = 1600;
-constexpr int RAW_WAVE = 1664;
-constexpr int RAW_STAGE = PF_WAVES * RAW_WAVE;
+// value words (512 B; with Q8_0 values, V8, 1 KB of value codes), 4 x 16 B
+// of key scales, 4 x 16 B of value scales.
+constexpr int RAW_K = 0, RAW_V = 1024;
+template <bool V8> constexpr int RAW_KS = V8 ? 2048 : 1536;
+template <bool V8> constexpr int RAW_VS = V8 ? 2112 : 1600;
+template <bool V8> constexpr int RAW_WAVE = V8 ? 2176 : 1664;
+template <bool V8> constexpr int RAW_STAGE = PF_WAVES * RAW_WAVE<V8>;
 constexpr int RAW_DEPTH = 2;                    // sub-tile i+2 refills sub-tile i's slot
 constexpr int RAW_LOADS = 3;                    // direct loads per wave per sub-tile
 
@@ -91,20 +94,27 @@ __device__ __forceinline__ void signal_count(int* c, int lane) {
 // dequantisation reads and writes LDS without bank conflicts:
 //  - key codes: lane i fetches row 4w + i%4, block (i/4)%8, half i/32 (16 B);
 //  - value words: q = w/2, lane groups g = 2(w%2), 2(w%2)+1: 128 consecutive
-//    words (lanes 0-31);
+//    words (lanes 0-31); Q8_0 value codes: the same dims and lane groups are
+//    blocks 2q, 2q+1, 512 consecutive bytes each (lanes 0-31, 32-63);
 //  - scales (lanes 0-7): key rows 4w..4w+3 (16 B each), then value blocks
 //    2q, 2q+1 for the two lane groups (16 B each).
+template <bool V8>
 __device__ __forceinline__ void issue_raw(uint8_t* raw, const uint8_t* krec, const uint8_t* vrec,
                                           int c, int w, int lane) {
   const int q = w >> 1, gh = w & 1;
   dma16(krec + (c * 32 + 4 * w + (lane & 3)) * D + 32 * ((lane >> 2) & 7) + 16 * (lane >> 5),
         raw + RAW_K);
-  if (lane < 32) dma16(vrec + (((c * 4 + q) * 4 + 2 * gh) * 64) * 4 + lane * 16, raw + RAW_V);
+  if constexpr (V8)
+    dma16(vrec + c * 8192 + (2 * q + (lane >> 5)) * 1024 + 2 * gh * 256 + (lane & 31) * 16,
+          raw + RAW_V);
+  else if (lane < 32)
+    dma16(vrec + (((c * 4 + q) * 4 + 2 * gh) * 64) * 4 + lane * 16, raw + RAW_V);
   if (lane < 8) {
+    const int vs_off = V8 ? K_SCALE_OFF : V_SCALE_OFF;
     const uint8_t* src =
         lane < 4 ? krec + K_SCALE_OFF + (c * 32 + 4 * w + lane) * 16
-                 : vrec + V_SCALE_OFF + ((c * 8 + 2 * q + ((lane - 4) >> 1)) * 4 + 2 * gh + (lane & 1)) * 16;
-    dma16(src, raw + RAW_KS);
+                 : vrec + vs_off + ((c * 8 + 2 * q + ((lane - 4) >> 1)) * 4 + 2 * gh + (lane & 1)) * 16;
+    dma16(src, raw + RAW_KS<V8>);
   }
 }
 
@@ -121,6 +131,26 @@ struct RawIn {
 };
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint8_t*)(p));
+}
+struct RawIn8 {
+  u32x4 k;      // 16 key codes
+  u32x4 v;      // 16 value codes: two dims x 8 slots
+  u32x4 vs;     // 8 value scales
+  uint32_t ks;  // key scale (low 16 bits)
+};
+__device__ __forceinline__ RawIn8 read_raw8(const uint8_t* k, const uint8_t* v, const uint8_t* vs,
+                                            const uint8_t* ks) {
+  RawIn8 r;
+  __asm__ __volatile__(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_u16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r.k), "=&v"(r.v), "=&v"(r.vs), "=&v"(r.ks)
+      : "v"(lds_addr(k)), "v"(lds_addr(v)), "v"(lds_addr(vs)), "v"(lds_addr(ks))
+      : "memory");
+  return r;
 }
 __device__ __forceinline__ RawIn read_raw(const uint8_t* k, const uint8_t* v, const uint8_t* vs,
                                           const uint8_t* ks) {
@@ -143,14 +173,28 @@ __device__ __forceinline__ RawIn read_raw(const uint8_t* k, const uint8_t* v, co
 // value scales are replaced by zeros. ln is the lane index.
 // Keys, lane (u, b, hh) = (l%4, (l/4)%8, l/32): 16 codes of row 4w + u.
 // Values, lane (d, ep, gl) = (l%16, (l/16)%2, l/32): words e = 2ep, 2ep+1 of
-// dim group q = w/2, lane group g = 2(w%2) + gl.
+// dim group q = w/2, lane group g = 2(w%2) + gl; with Q8_0 values the same
+// dims are the lane's 16-byte piece (row d) of block 2q + ep.
+template <bool V8>
 __device__ __forceinline__ void dequant_raw(const uint8_t* raw, _Float16* stage, int w, int ln,
                                             int n_live) {
   const int u = ln & 3, b = (ln >> 2) & 7, hh = ln >> 5;
   const int q = w >> 1, d = ln & 15, ep = (ln >> 4) & 1, gl = ln >> 5;
   const int g = 2 * (w & 1) + gl;
-  const RawIn in = read_raw(raw + RAW_K + ln * 16, raw + RAW_V + ((gl * 16 + d) * 4 + 2 * ep) * 4,
-                            raw + RAW_VS + (ep * 2 + gl) * 16, raw + RAW_KS + u * 16 + 2 * b);
+  RawIn in;
+  u32x4 v8 = {0u, 0u, 0u, 0u};
+  if constexpr (V8) {
+    const RawIn8 r8 = read_raw8(raw + RAW_K + ln * 16, raw + RAW_V + (ep * 32 + gl * 16 + d) * 16,
+                                raw + RAW_VS<V8> + (ep * 2 + gl) * 16,
+                                raw + RAW_KS<V8> + u * 16 + 2 * b);
+    in.k = r8.k;
+    in.vs = r8.vs;
+    in.ks = r8.ks;
+    v8 = r8.v;
+  } else {
+    in = read_raw(raw + RAW_K + ln * 16, raw + RAW_V + ((gl * 16 + d) * 4 + 2 * ep) * 4,
+                  raw + RAW_VS<V8> + (ep * 2 + gl) * 16, raw + RAW_KS<V8> + u * 16 + 2 * b);
+  }
   // n_live is wave-uniform and 32 on every sub-tile but a ragged last one
   const bool full = n_live >= 32;
   {
@@ -178,7 +222,11 @@ __device__ __forceinline__ void dequant_raw(const uint8_t* raw, _Float16* stage,
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int dim = 16 * (4 * q + 2 * ep + i) + d;
-      half8_t val = v_codes_to_f16(in.v[i]);
+      half8_t val;
+      if constexpr (V8)
+        val = v8_codes_to_f16(i ? v8.z : v8.x, i ? v8.w : v8.y);
+      else
+        val = v_codes_to_f16(in.v[i]);
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const half2_t pr = {val[2 * p], val[2 * p + 1]};
@@ -220,6 +268,7 @@ struct PageWindow {
   }
 };
 
+template <bool V8>
 __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
   _Float16* lds = reinterpret_cast<_Float16*>(lds_raw);                      // f16 stages
@@ -258,22 +307,22 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
   win.load(p, t, 0, h, lane);
   if (tid < 2 * N_STAGES) counters[tid] = 0;
 
-  uint8_t* const my_raw = raw_ring + wave * RAW_WAVE;
+  uint8_t* const my_raw = raw_ring + wave * RAW_WAVE<V8>;
   auto issue = [&](int sub) {
     const int32_t r = win.record(sub);
     const int64_t rec = r >= 0 ? r : 0;  // unmapped pages load record 0, then zero it
     int ln = lane;
     __asm__ __volatile__("" : "+v"(ln));  // recompute lane offsets here, do not hold them
-    issue_raw(my_raw + (sub % RAW_DEPTH) * RAW_STAGE, p.k_pool + rec * K_REC,
-              p.v_pool + rec * V_REC, r >= 0 ? (sub & 3) : 0, wave, ln);
+    issue_raw<V8>(my_raw + (sub % RAW_DEPTH) * RAW_STAGE<V8>, p.k_pool + rec * K_REC,
+                  p.v_pool + rec * (V8 ? V8_REC : V_REC), r >= 0 ? (sub & 3) : 0, wave, ln);
   };
   auto dequant = [&](int sub) {
     const int64_t left = kv_len - (t.pg0 * PAGE + (int64_t)sub * 32);
     const int n_live = win.record(sub) < 0 ? 0 : left >= 32 ? 32 : (int)left;
     int ln = lane;
     __asm__ __volatile__("" : "+v"(ln));  // recompute lane offsets here, do not hold them
-    dequant_raw(my_raw + (sub % RAW_DEPTH) * RAW_STAGE, lds + (sub % N_STAGES) * STAGE_HALVES,
-                wave, ln, n_live);
+    dequant_raw<V8>(my_raw + (sub % RAW_DEPTH) * RAW_STAGE<V8>,
+                    lds + (sub % N_STAGES) * STAGE_HALVES, wave, ln, n_live);
   };
   // start the raw stream before anything else
   if (n_sub > 0) issue(0);
@@ -474,17 +523,22 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
 
 int32_t prefill_rows_per_tile() { return PF_ROWS; }
 
-hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-  const size_t shmem = sizeof(_Float16) * N_STAGES * STAGE_HALVES + RAW_DEPTH * RAW_STAGE;
+template <bool V8>
+hipError_t launch_prefill_v(const PrefillParams& p, hipStream_t stream) {
+  const size_t shmem = sizeof(_Float16) * N_STAGES * STAGE_HALVES + RAW_DEPTH * RAW_STAGE<V8>;
   static std::atomic<uint64_t> lds_set{0};
   const hipError_t e =
-      set_lds_limit(lds_set, reinterpret_cast<const void*>(&prefill_kernel), shmem);
+      set_lds_limit(lds_set, reinterpret_cast<const void*>(&prefill_kernel<V8>), shmem);
   if (e != hipSuccess) return e;
   const int64_t rows_head = (int64_t)p.chunk * p.gqa;
   const unsigned n_qtiles = (unsigned)((rows_head + PF_ROWS - 1) / PF_ROWS);
   dim3 grid((unsigned)p.n_groups, n_qtiles, (unsigned)p.n_kv);
-  hipLaunchKernelGGL(prefill_kernel, grid, dim3(PF_THREADS), shmem, stream, p);
+  hipLaunchKernelGGL(prefill_kernel<V8>, grid, dim3(PF_THREADS), shmem, stream, p);
   return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
+  return p.v_q8 ? launch_prefill_v<true>(p, stream) : launch_prefill_v<false>(p, stream);
 }
 
 }  // namespace kvattn

@@ -280,7 +280,7 @@ def test_rotate_validation_before_device():
 
 def test_value_type_validation():
     """v_type selects Q4_0 (0) or Q8_0 (1) value records; other values are
-    unsupported everywhere, and prefill supports Q4_0 values only."""
+    unsupported everywhere."""
     lib = kv.load_library()
     bad = geom()
     bad.v_type = 2
@@ -294,7 +294,7 @@ def test_value_type_validation():
     nb = ctypes.c_size_t(0)
     assert lib.kvattn_prefill_chunk(ctypes.byref(q8), P(FAKE), 100, P(FAKE), P(FAKE), P(FAKE), 16,
                                     1000, 0.0625, P(FAKE), P(FAKE), 4, None, ctypes.byref(nb),
-                                    None) == E_UNSUPPORTED
+                                    None) == OK
     assert kv.Geom(1, 1, 1).v_record_bytes == 18432
     assert kv.Geom(1, 1, 1, v_type=kv.V_Q8_0).v_record_bytes == 34816
     assert ctypes.sizeof(kv.Geom) == 24

@@ -3,7 +3,8 @@ q8_0 / q8_0 cache pair of the Vulkan long-context page, section on the KV
 cache types): the pages kvattn_quantize_pages writes equal the oracle's bit
 for bit (bytes outside the written range untouched), decode and verify match
 the oracle's attention within the decode bar (2e-3 max-abs), gather copies the
-larger value records bit for bit, and prefill reports the pair unsupported."""
+larger value records bit for bit, and chunked prefill matches the oracle
+within the prefill bar (1e-2 max-abs)."""
 import numpy as np
 import pytest
 import torch
@@ -16,6 +17,7 @@ from kvtest_util import DEV, Pools, compare, fill, gpu, host
 pytestmark = pytest.mark.gpu
 
 DEC_TOL = 2e-3
+PRE_TOL = 1e-2
 V8 = kv.V_Q8_0
 
 
@@ -113,10 +115,20 @@ def test_gather_q8_values_bitexact():
             assert (got_v[i, h] == pools.ov[table[blocks[h, i]], h]).all()
 
 
-def test_prefill_q8_values_unsupported():
-    pools, table, _, _ = fill(1, 6, 256, v_type=V8)
-    q = torch.zeros((128, 6, 256), dtype=torch.float32, device=DEV)
-    with pytest.raises(kv.KvattnError) as e:
-        kv.kvattn_prefill_chunk(pools.geom, q, pools.gk, pools.gv, gpu(table, torch.int32), 128,
-                                1 / 16)
-    assert e.value.code == 2
+@pytest.mark.parametrize("chunk,pos0,gqa,n_kv,n_groups", [
+    (128, 0, 6, 1, 0),         # first chunk: causal inside one page
+    (200, 1000, 3, 2, 0),      # ragged chunk and history, several groups
+    (512, 64 * 128, 6, 1, 5),  # a 512-token chunk after 64 pages, chosen group count
+    (1, 5, 1, 1, 0),           # one query row, six keys
+])
+def test_prefill_q8_values_matches_oracle(chunk, pos0, gqa, n_kv, n_groups):
+    kv_len = pos0 + chunk
+    pools, table, _, _ = fill(n_kv, gqa, kv_len, seed=chunk + pos0, init_seed=8, v_type=V8)
+    q = np.random.default_rng(kv_len).standard_normal((chunk, n_kv * gqa, 256)).astype(np.float32)
+    out, lse = kv.kvattn_prefill_chunk(pools.geom, gpu(q), pools.gk, pools.gv,
+                                       gpu(table, torch.int32), pos0, 1 / 16, n_groups=n_groups)
+    ref_o, ref_l = oracle.prefill_chunk(q, gqa, pools.ok, pools.ov, table, len(table), pos0,
+                                        1 / 16)
+    eo, el, rr = compare(out, lse, ref_o, ref_l)
+    assert eo <= PRE_TOL, eo
+    assert el <= 5e-3 and rr <= 5e-3, (el, rr)
