@@ -27,6 +27,11 @@ V_RECORD_BYTES = V_CODES_BYTES + PAGE_TOKENS * N_BLOCKS * 2   # 18432
 # record of the key record's size, selected by the record size of the pool.
 V8_CODES_BYTES = PAGE_TOKENS * HEAD_DIM         # 32768
 V8_RECORD_BYTES = V8_CODES_BYTES + PAGE_TOKENS * N_BLOCKS * 2  # 34816
+# Q4_0 keys (the q4_0/q4_0 pair of [VULKAN] "坑 2": 18 KiB per token for K+V
+# at 16 layers x 4 KV heads x 256): a key record of the Q4_0 value record's
+# size, selected by the record size of the key pool.
+K4_CODES_BYTES = PAGE_TOKENS * HEAD_DIM // 2    # 16384
+K4_RECORD_BYTES = K4_CODES_BYTES + PAGE_TOKENS * N_BLOCKS * 2  # 18432
 
 
 def rn16(x):
@@ -236,6 +241,56 @@ def unpack_v8_record(rec):
     return codes, bits
 
 
+# Bit offset inside a 32-bit key word of dim 8w + k (k = 0..7): even k at
+# 4(k/2), odd k at 16 + 4(k/2), the nibble order of the value words.
+_K4_BIT = np.array([4 * (k // 2) + 16 * (k % 2) for k in range(8)], np.uint32)
+
+
+def pack_k4_record(codes, scale_bits):
+    """Q4_0 key record bytes from codes uint8 [..., 128, 256] (0..15) and
+    scales uint16 [..., 128, 8]; returns uint8 [..., 18432]. Slot t's codes
+    are the 32 little-endian words at byte t*128; word w holds dims 8w..8w+7."""
+    codes = np.asarray(codes, np.uint32)
+    lead = codes.shape[:-2]
+    c8 = codes.reshape(lead + (PAGE_TOKENS, HEAD_DIM // 8, 8))
+    words = np.zeros(lead + (PAGE_TOKENS, HEAD_DIM // 8), np.uint32)
+    for k in range(8):
+        words |= (c8[..., k] & np.uint32(0xF)) << _K4_BIT[k]
+    rec = np.zeros(lead + (K4_RECORD_BYTES,), np.uint8)
+    rec[..., :K4_CODES_BYTES] = np.ascontiguousarray(words.astype('<u4')).reshape(
+        lead + (-1,)).view(np.uint8)
+    sb = np.ascontiguousarray(np.asarray(scale_bits, np.uint16).astype('<u2'))
+    rec[..., K4_CODES_BYTES:] = sb.reshape(lead + (-1,)).view(np.uint8)
+    return rec
+
+
+def unpack_k4_record(rec):
+    """(codes uint8 [..., 128, 256], scale_bits uint16 [..., 128, 8]) of Q4_0 key records."""
+    rec = np.ascontiguousarray(np.asarray(rec, np.uint8))
+    lead = rec.shape[:-1]
+    words = np.ascontiguousarray(rec[..., :K4_CODES_BYTES]).view('<u4').astype(np.uint32)
+    words = words.reshape(lead + (PAGE_TOKENS, HEAD_DIM // 8))
+    codes = np.zeros(lead + (PAGE_TOKENS, HEAD_DIM // 8, 8), np.uint8)
+    for k in range(8):
+        codes[..., k] = (words >> _K4_BIT[k]) & 0xF
+    bits = np.ascontiguousarray(rec[..., K4_CODES_BYTES:]).view('<u2').astype(np.uint16)
+    return codes.reshape(lead + (PAGE_TOKENS, HEAD_DIM)), bits.reshape(lead + (PAGE_TOKENS, N_BLOCKS))
+
+
+def keys_are_q4(k_pool):
+    """True when a key pool (uint8 [..., record bytes]) holds Q4_0 records."""
+    n = np.asarray(k_pool).shape[-1]
+    assert n in (K_RECORD_BYTES, K4_RECORD_BYTES), n
+    return n == K4_RECORD_BYTES
+
+
+def unpack_keys(k_records):
+    """(codes, scale_bits, dequantiser) of key records of either type."""
+    if keys_are_q4(k_records):
+        return unpack_k4_record(k_records) + (q4_0_dequantize,)
+    return unpack_k_record(k_records) + (q8_0_dequantize,)
+
+
 def values_are_q8(v_pool):
     """True when a value pool (uint8 [..., record bytes]) holds Q8_0 records."""
     n = np.asarray(v_pool).shape[-1]
@@ -246,7 +301,8 @@ def values_are_q8(v_pool):
 def quantize_into_pool(k, v, pos0, page_table, k_pool, v_pool):
     """Write positions pos0 .. pos0+n_tok-1 into the pools (kvattn_quantize_pages
     semantics without summaries). k, v: float32 [n_tok, n_kv, 256].
-    k_pool: uint8 [n_phys, n_kv, 34816]; v_pool: uint8 [n_phys, n_kv, 18432]
+    k_pool: uint8 [n_phys, n_kv, 34816] (Q8_0 keys) or [n_phys, n_kv, 18432]
+    (Q4_0 keys, the value rule); v_pool: uint8 [n_phys, n_kv, 18432]
     (Q4_0 values) or [n_phys, n_kv, 34816] (Q8_0 values), both modified in
     place. Slots outside the written range keep their bytes.
     A page-table entry outside [0, n_phys) skips that page.
@@ -261,7 +317,8 @@ def quantize_into_pool(k, v, pos0, page_table, k_pool, v_pool):
     assert D == HEAD_DIM and v.shape == k.shape
     n_phys = k_pool.shape[0]
     v8 = values_are_q8(v_pool)
-    kc, ks = q8_0_quantize(k.reshape(n_tok, n_kv, N_BLOCKS, BLOCK))
+    k4 = keys_are_q4(k_pool)
+    kc, ks = (q4_0_quantize if k4 else q8_0_quantize)(k.reshape(n_tok, n_kv, N_BLOCKS, BLOCK))
     vq = q8_0_quantize if v8 else q4_0_quantize
     vc, vs = vq(v.reshape(n_tok, n_kv, N_BLOCKS, BLOCK))
     kc = kc.reshape(n_tok, n_kv, HEAD_DIM)
@@ -279,30 +336,31 @@ def quantize_into_pool(k, v, pos0, page_table, k_pool, v_pool):
     ok = (where < pages.size) & (pages[np.minimum(where, pages.size - 1)] == lps)
     tsel = np.nonzero(ok)[0]
     pidx, slot = where[tsel], pos[tsel] % PAGE_TOKENS
-    kcodes, kbits = unpack_k_record(k_pool[phys])                # [P, n_kv, 128, ...]
+    kcodes, kbits = (unpack_k4_record if k4 else unpack_k_record)(k_pool[phys])  # [P, n_kv, 128, ...]
     vcodes, vbits = (unpack_v8_record if v8 else unpack_v_record)(v_pool[phys])
     for h in range(n_kv):
         kcodes[pidx, h, slot] = kc[tsel, h]
         kbits[pidx, h, slot] = ks[tsel, h]
         vcodes[pidx, h, slot] = vc[tsel, h]
         vbits[pidx, h, slot] = vs[tsel, h]
-    k_pool[phys] = pack_k_record(kcodes, kbits)
+    k_pool[phys] = (pack_k4_record if k4 else pack_k_record)(kcodes, kbits)
     v_pool[phys] = (pack_v8_record if v8 else pack_v_record)(vcodes, vbits)
 
 
 def page_summaries(k_records):
     """Block summaries of full pages: RN32(binary64 sum over the 128 slots, in
     ascending slot order, of the dequantised keys, divided by 128).
-    k_records uint8 [..., 34816] -> float32 [..., 256].
+    k_records uint8 [..., 34816] (Q8_0 keys) or [..., 18432] (Q4_0 keys)
+    -> float32 [..., 256].
 
     The pages give no scoring function for KVMem ([KVMEM] "Recall 測試" only
     says retrieval picks the blocks relevant to the last user turn's query);
     the summary is the mean key of the block, the reading the workload
     description gives ("per-block summary = mean key").
     """
-    codes, bits = unpack_k_record(k_records)
+    codes, bits, dequantize = unpack_keys(k_records)
     lead = codes.shape[:-2]
-    khat = q8_0_dequantize(codes.reshape(lead + (PAGE_TOKENS, N_BLOCKS, BLOCK)), bits)
+    khat = dequantize(codes.reshape(lead + (PAGE_TOKENS, N_BLOCKS, BLOCK)), bits)
     khat = khat.reshape(lead + (PAGE_TOKENS, HEAD_DIM))
     acc = np.zeros(lead + (HEAD_DIM,), np.float64)
     for t in range(PAGE_TOKENS):                     # ascending t, binary64

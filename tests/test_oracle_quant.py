@@ -292,3 +292,58 @@ def test_q8_values_quantise_like_keys():
     kh, vh = oracle.dequant_page(kp[table], vp[table])
     assert (kh == vh).all()
     assert not (vh == 0).all()
+
+
+def test_q4_key_record_layout_positions():
+    """Q4_0 key records: nibbles at hand-computed positions of the layout in
+    include/kvattn.h (slot t's row of 32 words at byte t*128; dim 8w + k in
+    word w at bit 4(k/2) + 16(k%2)), 144 bytes per token and head (4.5 bits
+    per element, so q4_0 K + V is 288 bytes: 18 KiB per token at 16 layers
+    x 4 KV heads), scales in the Q8_0 key order, and a round trip."""
+    assert quant.K4_RECORD_BYTES == 18432 and quant.K4_RECORD_BYTES // 128 == 144
+    assert (144 + 144) * 16 * 4 == 18 * 1024
+    codes = np.zeros((128, 256), np.uint8)
+    bits = np.zeros((128, 8), np.uint16)
+    marks = {  # (slot, dim) -> (byte offset, shift inside the byte)
+        (0, 0): (0, 0), (0, 1): (2, 0), (0, 2): (0, 4), (0, 3): (2, 4), (0, 4): (1, 0),
+        (0, 7): (3, 4), (0, 8): (4, 0), (1, 0): (128, 0), (127, 255): (127 * 128 + 127, 4),
+    }
+    for n, (t, d) in enumerate(marks):
+        codes[t, d] = n + 1
+    rec = quant.pack_k4_record(codes, bits)
+    for n, ((t, d), (off, sh)) in enumerate(marks.items()):
+        assert (rec[off] >> sh) & 0xF == n + 1, (t, d, off, sh)
+    nib = np.stack([rec[:16384] & 0xF, rec[:16384] >> 4])
+    assert int(np.count_nonzero(nib)) == len(marks)      # nothing else written
+    g = np.random.default_rng(10)
+    c2 = g.integers(0, 16, (3, 128, 256)).astype(np.uint8)
+    b2 = g.integers(0, 1 << 16, (3, 128, 8)).astype(np.uint16)
+    c3, b3 = quant.unpack_k4_record(quant.pack_k4_record(c2, b2))
+    assert (c3 == c2).all() and (b3 == b2).all()
+    r8 = quant.pack_k_record(np.zeros((128, 256), np.int8), b2[0])
+    r4 = quant.pack_k4_record(np.zeros((128, 256), np.uint8), b2[0])
+    assert (r8[32768:] == r4[16384:]).all()
+
+
+def test_q4_keys_quantise_like_values():
+    """With a Q4_0 key pool the keys go through the Q4_0 value rule: the
+    pool's dequantised keys equal the dequantised values of the same numbers,
+    and a full page's summary is the binary64 mean of those keys."""
+    g = np.random.default_rng(11)
+    n_tok, n_kv = 300, 2
+    x = g.standard_normal((n_tok, n_kv, 256)).astype(np.float32)
+    x[5, 0, :32] = 0.0
+    x[6, 1, 32:64] = 0.5
+    x[6, 1, 40], x[6, 1, 50] = -2.0, 2.0                # tie: the lower index sets the sign
+    table = np.array([2, 0, 3], np.int32)
+    kp = np.zeros((4, n_kv, quant.K4_RECORD_BYTES), np.uint8)
+    vp = np.zeros((4, n_kv, quant.V_RECORD_BYTES), np.uint8)
+    quant.quantize_into_pool(x, x, 0, table, kp, vp)
+    kh, vh = oracle.dequant_page(kp[table], vp[table])
+    assert (kh == vh).all()
+    assert kh[0, 1, 6, 40] == -2.0 and kh[0, 1, 6, 50] == 2.0 * 7 / 8
+    s = quant.summaries_from_pool(kp, table, 2, n_kv)
+    for p in range(2):
+        for h in range(n_kv):
+            exact = np.float32(np.sum(kh[p, h], axis=0, dtype=np.float64) / 128.0)
+            assert np.abs(s[h, p] - exact).max() <= 1e-7 * (1 + np.abs(exact).max())
