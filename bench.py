@@ -81,7 +81,7 @@ def log(msg):
 class LayerPools:
     """One workload's 16 per-layer pools on the GPU plus per-layer queries."""
 
-    def __init__(self, w, dev, with_summary=False, chunk_tokens=32768, v_type=0):
+    def __init__(self, w, dev, with_summary=False, chunk_tokens=32768, v_type=0, k_type=0):
         import torch
         from long_context_attention_paged_amd import synth
         import long_context_attention_paged_amd as kv
@@ -89,7 +89,7 @@ class LayerPools:
         self.table_np = synth.page_table(w)
         self.table = torch.from_numpy(self.table_np).to(dev)
         self.n_phys = w.n_pages
-        self.geom = kv.Geom(w.n_kv, w.gqa, self.n_phys, v_type=v_type)
+        self.geom = kv.Geom(w.n_kv, w.gqa, self.n_phys, v_type=v_type, k_type=k_type)
         self.kp, self.vp, self.q, self.summ = [], [], [], []
         self.new_k, self.new_v = [], []
         n_new = w.chunk if w.chunk else w.n_q_tok
@@ -97,7 +97,8 @@ class LayerPools:
             t0 = time.time()
             q = synth.queries(w, layer)
             K, V = synth.kv_layer(w, layer, q, threads=16)
-            kp = torch.zeros(self.n_phys * w.n_kv * K_REC, dtype=torch.uint8, device=dev)
+            kp = torch.zeros(self.n_phys * w.n_kv * self.geom.k_record_bytes, dtype=torch.uint8,
+                             device=dev)
             vp = torch.zeros(self.n_phys * w.n_kv * self.geom.v_record_bytes, dtype=torch.uint8,
                              device=dev)
             summ = (torch.zeros((w.n_kv, w.n_pages, 256), dtype=torch.float32, device=dev)
@@ -173,12 +174,13 @@ def time_launches(call_fn, n_layers, reps):
     return start.elapsed_time(end) / (reps * n_layers)
 
 
-def bench_decode(w, dev, steps, warmup, sparse=False, v_type=0):
+def bench_decode(w, dev, steps, warmup, sparse=False, v_type=0, k_type=0):
     """Decode / verify workload: append the new tokens and attend (one launch), merge (x16).
-    v_type 1 caches the values as Q8_0 (272 bytes per token and KV head, as the keys)."""
+    v_type 1 caches the values as Q8_0 (272 bytes per token and KV head, as the keys);
+    k_type 1 the keys as Q4_0 (144 bytes, as Q4_0 values)."""
     import torch
     import long_context_attention_paged_amd as kv
-    pools = LayerPools(w, dev, with_summary=sparse, v_type=v_type)
+    pools = LayerPools(w, dev, with_summary=sparse, v_type=v_type, k_type=k_type)
     n_out = kv.kvattn_select_count(w.n_pages, w.n_recent, w.k_top) if sparse else 0
     outs = [torch.empty_like(q) for q in pools.q]
     lses = [torch.empty(q.shape[:2], dtype=torch.float32, device=dev) for q in pools.q]
@@ -231,7 +233,8 @@ def bench_decode(w, dev, steps, warmup, sparse=False, v_type=0):
     launch_ms = time_launches(decode_call, w.n_layers, max(steps, 3))
     kernel_ms = time_launches(kernel_call, w.n_layers, max(steps, 3))
     tokens = (w.k_top + w.n_recent) * 128 if sparse else w.kv_len
-    bytes_per_launch = tokens * w.n_kv * (272 + (272 if v_type == kv.V_Q8_0 else 144))
+    bytes_per_launch = tokens * w.n_kv * ((144 if k_type == kv.K_Q4_0 else 272) +
+                                          (272 if v_type == kv.V_Q8_0 else 144))
     res = {
         "ms_per_step": ms,
         "kv_bytes_per_step": bytes_per_launch * w.n_layers,
@@ -327,10 +330,10 @@ def prefill_flops_per_layer(w):
     return 4 * 256 * pairs * w.n_heads
 
 
-def bench_prefill(w, dev, steps, warmup, v_type=0):
+def bench_prefill(w, dev, steps, warmup, v_type=0, k_type=0):
     import torch
     import long_context_attention_paged_amd as kv
-    pools = LayerPools(w, dev, v_type=v_type)
+    pools = LayerPools(w, dev, v_type=v_type, k_type=k_type)
     outs = [torch.empty_like(q) for q in pools.q]
     lses = [torch.empty(q.shape[:2], dtype=torch.float32, device=dev) for q in pools.q]
     ws = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -719,17 +722,23 @@ def profile_kernels(dev, layers, reps):
     log(f"profile: prefill_kernel x {reps * layers}, {prefill_flops_per_layer(w)} flop each")
 
 
+# bench config -> (k_type, v_type, tag) of the other KV cache type pairs
+PAIRS = {"3q8": (0, 1, "q8_0-q8_0"), "4q8": (0, 1, "q8_0-q8_0"),
+         "3q4": (1, 0, "q4_0-q4_0"), "4q4": (1, 0, "q4_0-q4_0")}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--configs", default="3,4,2,5,3s,5h,3q8,4q8",
+    ap.add_argument("--configs", default="3,4,2,5,3s,5h,3q8,4q8,3q4,4q4",
                     help="workloads to run: 2 decode-131k, 3 verify-262k, 4 prefill, 5 kvmem, "
                          "4h prefill with the pool in pinned host memory, 3s verify with the "
                          "history streamed from host memory (2100 MiB device working set), "
                          "5h kvmem with its history in host memory (budget sweep), "
-                         "3q8 / 4q8 verify-262k / prefill with Q8_0 values")
+                         "3q8 / 4q8 verify-262k / prefill with the q8_0/q8_0 pair, "
+                         "3q4 / 4q4 with the q4_0/q4_0 pair")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="run only a short fixed kernel sequence for counter runs (no JSON line)")
@@ -774,23 +783,16 @@ def main():
             torch.cuda.empty_cache()
             log(f"{w.name} streamed: {json.dumps(res)}")
             continue
-        if c == "3q8":
-            w = synth.WORKLOADS[3]
-            log(f"workload {w.name} (Q8_0 values)")
-            res, pools = bench_decode(w, dev, args.steps, args.warmup, v_type=kv.V_Q8_0)
-            extra[w.name + "-q8-values"] = res
+        if c in PAIRS:  # the other cache type pairs: q8_0/q8_0, q4_0/q4_0
+            k_type, v_type, tag = PAIRS[c]
+            w = synth.WORKLOADS[int(c[0])]
+            log(f"workload {w.name} ({tag})")
+            fn = bench_decode if c[0] == "3" else bench_prefill
+            res, pools = fn(w, dev, args.steps, args.warmup, v_type=v_type, k_type=k_type)
+            extra[f"{w.name}-{tag}"] = res
             del pools
             torch.cuda.empty_cache()
-            log(f"{w.name} Q8_0 values: {json.dumps(res)}")
-            continue
-        if c == "4q8":
-            w = synth.WORKLOADS[4]
-            log(f"workload {w.name} (Q8_0 values)")
-            res, pools = bench_prefill(w, dev, args.steps, args.warmup, v_type=kv.V_Q8_0)
-            extra[w.name + "-q8-values"] = res
-            del pools
-            torch.cuda.empty_cache()
-            log(f"{w.name} Q8_0 values: {json.dumps(res)}")
+            log(f"{w.name} {tag}: {json.dumps(res)}")
             continue
         if c == "4h":
             w = synth.WORKLOADS[4]

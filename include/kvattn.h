@@ -80,6 +80,13 @@
  *                   16x16x32 tile reads for two 16-dim tiles of one block.
  *   [32768, 34816)  binary16 scale of (slot t(c,g,j), block b) at byte
  *                   32768 + 2*(((c*8 + b)*4 + g)*8 + j).
+ *  Q4_0 K record (k_type KVATTN_K_Q4_0), KVATTN_K4_RECORD_BYTES = 18432:
+ *   [0, 16384)      4-bit codes, slot t's row of 32 little-endian 32-bit
+ *                   words at byte t*128; word w holds dims 8w..8w+7, dim
+ *                   8w + k at bit 4*(k/2) + 16*(k%2) (the V word nibble
+ *                   order), so a lane turns a word into the f16 values of
+ *                   eight consecutive dims with one shift and mask per pair.
+ *   [16384, 18432)  binary16 scale of (slot t, block b) at 16384 + 2*(t*8 + b).
  *
  * Quantisation (per token, per KV head, per 32-dim block x[0..31]; RN32 and
  * RN16 are IEEE round-to-nearest-even to binary32 / binary16, rint rounds
@@ -89,6 +96,7 @@
  *   code_i = clamp(rint(RN32(x_i * inv)), -127, 127). Dequantised: d * code.
  *   34 bytes per 32 elements = 8.5 bits per element ([VULKAN] closing remark).
  *  Q8_0 values (v_type KVATTN_V_Q8_0) follow the key rule above.
+ *  Q4_0 keys (k_type KVATTN_K_Q4_0) follow the Q4_0 value rule below.
  *  Q4_0 (values): j* = lowest index with |x_j*| = amax; m = x_j* (signed);
  *   d = RN16(RN32(-m / 8)). If amax == 0 or d == 0, the stored scale is +0
  *   and every code is 8. Otherwise inv = RN32(1 / d) and
@@ -123,15 +131,19 @@ typedef int32_t kvattn_status;
 #define KVATTN_V8_RECORD_BYTES 34816 /* Q8_0 values (v_type KVATTN_V_Q8_0) */
 #define KVATTN_V_Q4_0 0 /* value cache type: Q4_0 (the default) */
 #define KVATTN_V_Q8_0 1 /* value cache type: Q8_0 (the q8_0/q8_0 pair) */
+#define KVATTN_K4_RECORD_BYTES 18432 /* Q4_0 keys (k_type KVATTN_K_Q4_0) */
+#define KVATTN_K_Q8_0 0 /* key cache type: Q8_0 (the default) */
+#define KVATTN_K_Q4_0 1 /* key cache type: Q4_0 (the q4_0/q4_0 pair) */
 #define KVATTN_MAX_QUERY_ROWS 32 /* n_q_tok * gqa per KV head in decode */
 #define KVATTN_MAX_APPEND_TOKENS 32 /* n_new of kvattn_append_decode */
 
 /* Geometry of one layer's pool. head_dim must be 256 and page_tokens 128
  * (the pages' shape: [VULKAN] "模型結構"; [KVMEM] --kvmem-block-tokens 128).
- * Query head hq uses KV head hq / gqa (grouped-query attention). Keys are
- * always Q8_0; v_type picks the value type: KVATTN_V_Q4_0 (the [STREAM]
- * -ctk q8_0 -ctv q4_0 pair) or KVATTN_V_Q8_0 (KVMem's q8_0/q8_0, [KVMEM]
- * 測試口徑 --kv-dtype q8_0), which sets the value record size. */
+ * Query head hq uses KV head hq / gqa (grouped-query attention). v_type picks
+ * the value type: KVATTN_V_Q4_0 (the [STREAM] -ctk q8_0 -ctv q4_0 pair) or
+ * KVATTN_V_Q8_0 (KVMem's q8_0/q8_0, [KVMEM] 測試口徑 --kv-dtype q8_0), and
+ * k_type the key type: KVATTN_K_Q8_0 or KVATTN_K_Q4_0 (the q4_0/q4_0 pair,
+ * [VULKAN] 坑 2); each sets its record size. */
 typedef struct kvattn_geom {
   int32_t n_kv_heads;   /* >= 1 */
   int32_t gqa;          /* query heads per KV head, >= 1 */
@@ -140,6 +152,7 @@ typedef struct kvattn_geom {
   int32_t n_phys_pages; /* physical pages in k_pool / v_pool, >= 1;
                           n_phys_pages * n_kv_heads <= INT32_MAX */
   int32_t v_type;       /* KVATTN_V_Q4_0 or KVATTN_V_Q8_0 */
+  int32_t k_type;       /* KVATTN_K_Q8_0 or KVATTN_K_Q4_0 */
 } kvattn_geom;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -162,7 +175,8 @@ int32_t kvattn_select_count(int32_t n_blocks, int32_t n_recent, int32_t k_top);
  *  page_table  int32 [n_logical_pages], values in [0, n_phys_pages).
  *              Requires pos0 >= 0, n_tok >= 1 and
  *              pos0 + n_tok <= n_logical_pages * 128.
- *  k_pool      n_phys_pages * n_kv_heads * 34816 bytes.
+ *  k_pool      n_phys_pages * n_kv_heads * the key record size (34816 bytes
+ *              for Q8_0 keys, 18432 for Q4_0).
  *  v_pool      n_phys_pages * n_kv_heads * the value record size (18432 bytes
  *              for Q4_0 values, 34816 for Q8_0).
  *  k_summary   fp32 [n_kv_heads][n_logical_pages][256] or NULL.

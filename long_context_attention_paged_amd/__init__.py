@@ -25,6 +25,8 @@ K_RECORD_BYTES = 34816
 V_RECORD_BYTES = 18432
 V8_RECORD_BYTES = 34816
 V_Q4_0, V_Q8_0 = 0, 1  # value cache types (kvattn_geom.v_type)
+K4_RECORD_BYTES = 18432
+K_Q8_0, K_Q4_0 = 0, 1  # key cache types (kvattn_geom.k_type)
 STATUS = {0: "OK", 1: "E_INVALID", 2: "E_UNSUPPORTED", 3: "E_WORKSPACE", 4: "E_DEVICE"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,11 +42,16 @@ class KvattnError(RuntimeError):
 class Geom(ctypes.Structure):
     _fields_ = [("n_kv_heads", ctypes.c_int32), ("gqa", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("page_tokens", ctypes.c_int32),
-                ("n_phys_pages", ctypes.c_int32), ("v_type", ctypes.c_int32)]
+                ("n_phys_pages", ctypes.c_int32), ("v_type", ctypes.c_int32),
+                ("k_type", ctypes.c_int32)]
 
     def __init__(self, n_kv_heads, gqa, n_phys_pages, head_dim=HEAD_DIM, page_tokens=PAGE_TOKENS,
-                 v_type=0):
-        super().__init__(n_kv_heads, gqa, head_dim, page_tokens, n_phys_pages, v_type)
+                 v_type=0, k_type=0):
+        super().__init__(n_kv_heads, gqa, head_dim, page_tokens, n_phys_pages, v_type, k_type)
+
+    @property
+    def k_record_bytes(self):
+        return K4_RECORD_BYTES if self.k_type == K_Q4_0 else K_RECORD_BYTES
 
     @property
     def v_record_bytes(self):
@@ -131,7 +138,7 @@ def _size(t, name, need):
 
 
 def _pools(geom, k_pool, v_pool):
-    _size(k_pool, "k_pool", geom.n_phys_pages * geom.n_kv_heads * K_RECORD_BYTES)
+    _size(k_pool, "k_pool", geom.n_phys_pages * geom.n_kv_heads * geom.k_record_bytes)
     _size(v_pool, "v_pool", geom.n_phys_pages * geom.n_kv_heads * geom.v_record_bytes)
 
 
@@ -455,7 +462,7 @@ def kvattn_gather_blocks(geom, src_k_pool, src_v_pool, page_table, blocks, n_sel
     n_sel = int(n_sel)
     _need(dst_k_pool, "dst_k_pool", torch.uint8)
     _need(dst_v_pool, "dst_v_pool", torch.uint8)
-    _size(dst_k_pool, "dst_k_pool", n_sel * geom.n_kv_heads * K_RECORD_BYTES)
+    _size(dst_k_pool, "dst_k_pool", n_sel * geom.n_kv_heads * geom.k_record_bytes)
     _size(dst_v_pool, "dst_v_pool", n_sel * geom.n_kv_heads * geom.v_record_bytes)
     if dst_blocks is None:
         dst_blocks = torch.empty((geom.n_kv_heads, max(n_sel, 1)), dtype=torch.int32,

@@ -11,6 +11,8 @@ constexpr int PAGE = 128;         // tokens per page
 constexpr int K_REC = 34816;      // bytes per (page, KV head) key record
 constexpr int V_REC = 18432;      // bytes per (page, KV head) value record, Q4_0 values
 constexpr int V8_REC = 34816;     // the same with Q8_0 values (laid out like a key record)
+constexpr int K4_REC = 18432;     // bytes per key record with Q4_0 keys
+constexpr int K4_SCALE_OFF = 16384;
 constexpr int K_SCALE_OFF = 32768;
 constexpr int V_SCALE_OFF = 16384;
 constexpr float LOG2E = 1.4426950408889634f;
@@ -90,6 +92,13 @@ __device__ __forceinline__ half8_t v_codes_to_f16_m(uint32_t w, uint32_t mask) {
   half2_t p3 = as_h2(((w >> 12) & mask) | 0x64006400u) - off;
   half8_t r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
   return r;
+}
+
+// One Q4_0 key word (dims 8w..8w+7, nibble order of the V words) -> eight
+// f16 values d * (code - 8); d2 holds the block scale in both halves.
+__device__ __forceinline__ half8_t k4_codes_to_f16(uint32_t w, uint32_t mask, half2_t d2) {
+  const half8_t d8 = __builtin_shufflevector(d2, d2, 0, 1, 0, 1, 0, 1, 0, 1);
+  return v_codes_to_f16_m(w, mask) * d8;
 }
 
 __device__ __forceinline__ u32x4 load16(const uint8_t* p) {

@@ -10,20 +10,21 @@ namespace kvattn {
 namespace {
 
 constexpr int GATHER_THREADS = 256;
-constexpr int K_CHUNKS = K_REC / 16;  // 2176 16-byte chunks per key record
 
-// grid (n_sel, n_kv), VREC the value record size (Q4_0 or Q8_0 values). Workgroup (i, h) copies the key and value records of
+// grid (n_sel, n_kv); KREC, VREC the key and value record sizes (Q8_0 or
+// Q4_0 keys, Q4_0 or Q8_0 values). Workgroup (i, h) copies the key and value records of
 // logical page blocks[h][i] (row stride n_blk) into record i * n_kv + h of the
 // destination pools and writes dst_blocks[h][i] (row stride n_sel) = i, or -1
 // (nothing copied) when the entry or its physical page is out of range. Each
-// thread requests all of its chunks (13 with Q4_0 values, 17 with Q8_0) before
+// thread requests all of its chunks (13 for the q8_0/q4_0 pair, at most 17) before
 // storing any, so a record costs about one round trip over the host link.
-template <int VREC>
+template <int KREC, int VREC>
 __global__ __launch_bounds__(GATHER_THREADS) void gather_kernel(
     const uint8_t* __restrict__ src_k, const uint8_t* __restrict__ src_v,
     const int32_t* __restrict__ page_table, int32_t n_logical, int32_t n_phys,
     const int32_t* __restrict__ blocks, int32_t n_blk, int32_t n_kv, uint8_t* __restrict__ dst_k,
     uint8_t* __restrict__ dst_v, int32_t* __restrict__ dst_blocks) {
+  constexpr int K_CHUNKS = KREC / 16;
   constexpr int V_CHUNKS = VREC / 16;
   constexpr int G_PER_THREAD = (K_CHUNKS + V_CHUNKS + GATHER_THREADS - 1) / GATHER_THREADS;
   const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
@@ -35,9 +36,9 @@ __global__ __launch_bounds__(GATHER_THREADS) void gather_kernel(
   }
   if (tid == 0) dst_blocks[(int64_t)h * gridDim.x + i] = ph >= 0 ? i : -1;
   if (ph < 0) return;  // uniform across the workgroup
-  const u32x4* ks = reinterpret_cast<const u32x4*>(src_k + ((int64_t)ph * n_kv + h) * K_REC);
+  const u32x4* ks = reinterpret_cast<const u32x4*>(src_k + ((int64_t)ph * n_kv + h) * KREC);
   const u32x4* vs = reinterpret_cast<const u32x4*>(src_v + ((int64_t)ph * n_kv + h) * VREC);
-  u32x4* kd = reinterpret_cast<u32x4*>(dst_k + ((int64_t)i * n_kv + h) * K_REC);
+  u32x4* kd = reinterpret_cast<u32x4*>(dst_k + ((int64_t)i * n_kv + h) * KREC);
   u32x4* vd = reinterpret_cast<u32x4*>(dst_v + ((int64_t)i * n_kv + h) * VREC);
   u32x4 v[G_PER_THREAD];
 #pragma unroll
@@ -59,9 +60,11 @@ __global__ __launch_bounds__(GATHER_THREADS) void gather_kernel(
 hipError_t launch_gather(const uint8_t* src_k, const uint8_t* src_v, const int32_t* page_table,
                          int32_t n_logical, int32_t n_phys, const int32_t* blocks, int32_t n_blk,
                          int32_t n_sel, int32_t n_kv, uint8_t* dst_k, uint8_t* dst_v,
-                         int32_t* dst_blocks, bool v_q8, hipStream_t stream) {
+                         int32_t* dst_blocks, bool v_q8, bool k_q4, hipStream_t stream) {
   dim3 grid((unsigned)n_sel, (unsigned)n_kv);
-  hipLaunchKernelGGL(v_q8 ? gather_kernel<V8_REC> : gather_kernel<V_REC>, grid, dim3(GATHER_THREADS), 0, stream, src_k, src_v,
+  auto kern = k_q4 ? (v_q8 ? gather_kernel<K4_REC, V8_REC> : gather_kernel<K4_REC, V_REC>)
+                   : (v_q8 ? gather_kernel<K_REC, V8_REC> : gather_kernel<K_REC, V_REC>);
+  hipLaunchKernelGGL(kern, grid, dim3(GATHER_THREADS), 0, stream, src_k, src_v,
                      page_table, n_logical, n_phys, blocks, n_blk, n_kv, dst_k, dst_v,
                      dst_blocks);
   return hipGetLastError();

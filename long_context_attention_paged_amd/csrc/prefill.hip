@@ -98,12 +98,19 @@ __device__ __forceinline__ void signal_count(int* c, int lane) {
 //    blocks 2q, 2q+1, 512 consecutive bytes each (lanes 0-31, 32-63);
 //  - scales (lanes 0-7): key rows 4w..4w+3 (16 B each), then value blocks
 //    2q, 2q+1 for the two lane groups (16 B each).
-template <bool V8>
+// With Q4_0 keys (K4) lanes 0-31 fetch row 4w + i%4, block (i/4)%8 (16 B:
+// the block's 32 nibbles).
+template <bool K4, bool V8>
 __device__ __forceinline__ void issue_raw(uint8_t* raw, const uint8_t* krec, const uint8_t* vrec,
                                           int c, int w, int lane) {
   const int q = w >> 1, gh = w & 1;
-  dma16(krec + (c * 32 + 4 * w + (lane & 3)) * D + 32 * ((lane >> 2) & 7) + 16 * (lane >> 5),
-        raw + RAW_K);
+  if constexpr (K4) {
+    if (lane < 32)
+      dma16(krec + (c * 32 + 4 * w + (lane & 3)) * (D / 2) + 16 * ((lane >> 2) & 7), raw + RAW_K);
+  } else {
+    dma16(krec + (c * 32 + 4 * w + (lane & 3)) * D + 32 * ((lane >> 2) & 7) + 16 * (lane >> 5),
+          raw + RAW_K);
+  }
   if constexpr (V8)
     dma16(vrec + c * 8192 + (2 * q + (lane >> 5)) * 1024 + 2 * gh * 256 + (lane & 31) * 16,
           raw + RAW_V);
@@ -112,7 +119,7 @@ __device__ __forceinline__ void issue_raw(uint8_t* raw, const uint8_t* krec, con
   if (lane < 8) {
     const int vs_off = V8 ? K_SCALE_OFF : V_SCALE_OFF;
     const uint8_t* src =
-        lane < 4 ? krec + K_SCALE_OFF + (c * 32 + 4 * w + lane) * 16
+        lane < 4 ? krec + (K4 ? K4_SCALE_OFF : K_SCALE_OFF) + (c * 32 + 4 * w + lane) * 16
                  : vrec + vs_off + ((c * 8 + 2 * q + ((lane - 4) >> 1)) * 4 + 2 * gh + (lane & 1)) * 16;
     dma16(src, raw + RAW_KS<V8>);
   }
@@ -175,7 +182,7 @@ __device__ __forceinline__ RawIn read_raw(const uint8_t* k, const uint8_t* v, co
 // Values, lane (d, ep, gl) = (l%16, (l/16)%2, l/32): words e = 2ep, 2ep+1 of
 // dim group q = w/2, lane group g = 2(w%2) + gl; with Q8_0 values the same
 // dims are the lane's 16-byte piece (row d) of block 2q + ep.
-template <bool V8>
+template <bool K4, bool V8>
 __device__ __forceinline__ void dequant_raw(const uint8_t* raw, _Float16* stage, int w, int ln,
                                             int n_live) {
   const int u = ln & 3, b = (ln >> 2) & 7, hh = ln >> 5;
@@ -183,8 +190,10 @@ __device__ __forceinline__ void dequant_raw(const uint8_t* raw, _Float16* stage,
   const int g = 2 * (w & 1) + gl;
   RawIn in;
   u32x4 v8 = {0u, 0u, 0u, 0u};
+  // Q4_0 keys: the lane's block chunk (row u, block b) is lane l%32's load
+  const int koff = K4 ? (ln & 31) * 16 : ln * 16;
   if constexpr (V8) {
-    const RawIn8 r8 = read_raw8(raw + RAW_K + ln * 16, raw + RAW_V + (ep * 32 + gl * 16 + d) * 16,
+    const RawIn8 r8 = read_raw8(raw + RAW_K + koff, raw + RAW_V + (ep * 32 + gl * 16 + d) * 16,
                                 raw + RAW_VS<V8> + (ep * 2 + gl) * 16,
                                 raw + RAW_KS<V8> + u * 16 + 2 * b);
     in.k = r8.k;
@@ -192,7 +201,7 @@ __device__ __forceinline__ void dequant_raw(const uint8_t* raw, _Float16* stage,
     in.ks = r8.ks;
     v8 = r8.v;
   } else {
-    in = read_raw(raw + RAW_K + ln * 16, raw + RAW_V + ((gl * 16 + d) * 4 + 2 * ep) * 4,
+    in = read_raw(raw + RAW_K + koff, raw + RAW_V + ((gl * 16 + d) * 4 + 2 * ep) * 4,
                   raw + RAW_VS<V8> + (ep * 2 + gl) * 16, raw + RAW_KS<V8> + u * 16 + 2 * b);
   }
   // n_live is wave-uniform and 32 on every sub-tile but a ragged last one
@@ -203,8 +212,13 @@ __device__ __forceinline__ void dequant_raw(const uint8_t* raw, _Float16* stage,
     if (!full && 4 * w + u >= n_live) dw = 0u;  // zero scale -> zeros
     const half2_t d2 = as_h2(dw);
     _Float16* krow = stage + (4 * w + u) * K_LDS_STRIDE + 32 * b + 16 * hh;
-    *reinterpret_cast<half8_t*>(krow + 0) = k_codes_to_f16(in.k.x, in.k.y, d2);
-    *reinterpret_cast<half8_t*>(krow + 8) = k_codes_to_f16(in.k.z, in.k.w, d2);
+    if constexpr (K4) {  // words 4b + 2hh, +1: dims 32b + 16hh + 0..7, 8..15
+      *reinterpret_cast<half8_t*>(krow + 0) = k4_codes_to_f16(hh ? in.k.z : in.k.x, 0x000F000Fu, d2);
+      *reinterpret_cast<half8_t*>(krow + 8) = k4_codes_to_f16(hh ? in.k.w : in.k.y, 0x000F000Fu, d2);
+    } else {
+      *reinterpret_cast<half8_t*>(krow + 0) = k_codes_to_f16(in.k.x, in.k.y, d2);
+      *reinterpret_cast<half8_t*>(krow + 8) = k_codes_to_f16(in.k.z, in.k.w, d2);
+    }
   }
   {
     // scales of block 2q + ep for lane group g (in.vs), masked past n_live
@@ -268,7 +282,7 @@ struct PageWindow {
   }
 };
 
-template <bool V8>
+template <bool K4, bool V8>
 __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
   _Float16* lds = reinterpret_cast<_Float16*>(lds_raw);                      // f16 stages
@@ -313,7 +327,7 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
     const int64_t rec = r >= 0 ? r : 0;  // unmapped pages load record 0, then zero it
     int ln = lane;
     __asm__ __volatile__("" : "+v"(ln));  // recompute lane offsets here, do not hold them
-    issue_raw<V8>(my_raw + (sub % RAW_DEPTH) * RAW_STAGE<V8>, p.k_pool + rec * K_REC,
+    issue_raw<K4, V8>(my_raw + (sub % RAW_DEPTH) * RAW_STAGE<V8>, p.k_pool + rec * (K4 ? K4_REC : K_REC),
                   p.v_pool + rec * (V8 ? V8_REC : V_REC), r >= 0 ? (sub & 3) : 0, wave, ln);
   };
   auto dequant = [&](int sub) {
@@ -321,7 +335,7 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
     const int n_live = win.record(sub) < 0 ? 0 : left >= 32 ? 32 : (int)left;
     int ln = lane;
     __asm__ __volatile__("" : "+v"(ln));  // recompute lane offsets here, do not hold them
-    dequant_raw<V8>(my_raw + (sub % RAW_DEPTH) * RAW_STAGE<V8>,
+    dequant_raw<K4, V8>(my_raw + (sub % RAW_DEPTH) * RAW_STAGE<V8>,
                     lds + (sub % N_STAGES) * STAGE_HALVES, wave, ln, n_live);
   };
   // start the raw stream before anything else
@@ -523,22 +537,23 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
 
 int32_t prefill_rows_per_tile() { return PF_ROWS; }
 
-template <bool V8>
+template <bool K4, bool V8>
 hipError_t launch_prefill_v(const PrefillParams& p, hipStream_t stream) {
   const size_t shmem = sizeof(_Float16) * N_STAGES * STAGE_HALVES + RAW_DEPTH * RAW_STAGE<V8>;
   static std::atomic<uint64_t> lds_set{0};
   const hipError_t e =
-      set_lds_limit(lds_set, reinterpret_cast<const void*>(&prefill_kernel<V8>), shmem);
+      set_lds_limit(lds_set, reinterpret_cast<const void*>(&prefill_kernel<K4, V8>), shmem);
   if (e != hipSuccess) return e;
   const int64_t rows_head = (int64_t)p.chunk * p.gqa;
   const unsigned n_qtiles = (unsigned)((rows_head + PF_ROWS - 1) / PF_ROWS);
   dim3 grid((unsigned)p.n_groups, n_qtiles, (unsigned)p.n_kv);
-  hipLaunchKernelGGL(prefill_kernel<V8>, grid, dim3(PF_THREADS), shmem, stream, p);
+  hipLaunchKernelGGL((prefill_kernel<K4, V8>), grid, dim3(PF_THREADS), shmem, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-  return p.v_q8 ? launch_prefill_v<true>(p, stream) : launch_prefill_v<false>(p, stream);
+  if (p.k_q4) return p.v_q8 ? launch_prefill_v<true, true>(p, stream) : launch_prefill_v<true, false>(p, stream);
+  return p.v_q8 ? launch_prefill_v<false, true>(p, stream) : launch_prefill_v<false, false>(p, stream);
 }
 
 }  // namespace kvattn

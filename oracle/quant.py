@@ -360,7 +360,8 @@ def page_summaries(k_records):
     """
     codes, bits, dequantize = unpack_keys(k_records)
     lead = codes.shape[:-2]
-    khat = dequantize(codes.reshape(lead + (PAGE_TOKENS, N_BLOCKS, BLOCK)), bits)
+    with np.errstate(invalid="ignore", over="ignore"):   # unwritten slots: any bytes
+        khat = dequantize(codes.reshape(lead + (PAGE_TOKENS, N_BLOCKS, BLOCK)), bits)
     khat = khat.reshape(lead + (PAGE_TOKENS, HEAD_DIM))
     acc = np.zeros(lead + (HEAD_DIM,), np.float64)
     for t in range(PAGE_TOKENS):                     # ascending t, binary64

@@ -26,9 +26,10 @@ class Pools:
     """A layer's pool on both sides: `ok`/`ov` are the oracle's uint8
     [n_phys, n_kv, rec] arrays, `gk`/`gv` the device copies the library writes."""
 
-    def __init__(self, n_phys, n_kv, gqa, init_seed=None, v_type=0):
+    def __init__(self, n_phys, n_kv, gqa, init_seed=None, v_type=0, k_type=0):
         self.n_phys, self.n_kv, self.gqa = n_phys, n_kv, gqa
-        shape_k = (n_phys, n_kv, quant.K_RECORD_BYTES)
+        k_rec = quant.K4_RECORD_BYTES if k_type == kv.K_Q4_0 else quant.K_RECORD_BYTES
+        shape_k = (n_phys, n_kv, k_rec)
         v_rec = quant.V8_RECORD_BYTES if v_type == kv.V_Q8_0 else quant.V_RECORD_BYTES
         shape_v = (n_phys, n_kv, v_rec)
         if init_seed is None:
@@ -40,7 +41,7 @@ class Pools:
             self.ov = g.integers(0, 256, shape_v, dtype=np.uint8)
         self.gk = gpu(self.ok.reshape(-1))
         self.gv = gpu(self.ov.reshape(-1))
-        self.geom = kv.Geom(n_kv, gqa, n_phys, v_type=v_type)
+        self.geom = kv.Geom(n_kv, gqa, n_phys, v_type=v_type, k_type=k_type)
 
     def write(self, K, V, pos0, table, summary=None):
         """Quantise on both sides. `summary` is a device tensor or None."""
@@ -54,7 +55,7 @@ class Pools:
 
 
 def fill(n_kv, gqa, kv_len, n_phys=None, seed=0, permute=True, scale_kv=1.0, init_seed=None,
-         v_type=0):
+         v_type=0, k_type=0):
     """Pools holding kv_len seeded N(0,1) tokens, written in one call."""
     n_pages = (kv_len + 127) // 128
     n_phys = n_phys or n_pages + 3
@@ -62,7 +63,7 @@ def fill(n_kv, gqa, kv_len, n_phys=None, seed=0, permute=True, scale_kv=1.0, ini
     table = (g.permutation(n_phys)[:n_pages] if permute else np.arange(n_pages)).astype(np.int32)
     K = (g.standard_normal((kv_len, n_kv, 256)) * scale_kv).astype(np.float32)
     V = (g.standard_normal((kv_len, n_kv, 256)) * scale_kv).astype(np.float32)
-    pools = Pools(n_phys, n_kv, gqa, init_seed, v_type)
+    pools = Pools(n_phys, n_kv, gqa, init_seed, v_type, k_type)
     pools.write(K, V, 0, table)
     return pools, table, K, V
 

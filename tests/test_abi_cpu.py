@@ -279,8 +279,8 @@ def test_rotate_validation_before_device():
 
 
 def test_value_type_validation():
-    """v_type selects Q4_0 (0) or Q8_0 (1) value records; other values are
-    unsupported everywhere."""
+    """v_type selects Q4_0 (0) or Q8_0 (1) value records and k_type Q8_0 (0)
+    or Q4_0 (1) key records; other values are unsupported everywhere."""
     lib = kv.load_library()
     bad = geom()
     bad.v_type = 2
@@ -297,4 +297,13 @@ def test_value_type_validation():
                                     None) == OK
     assert kv.Geom(1, 1, 1).v_record_bytes == 18432
     assert kv.Geom(1, 1, 1, v_type=kv.V_Q8_0).v_record_bytes == 34816
-    assert ctypes.sizeof(kv.Geom) == 24
+    assert ctypes.sizeof(kv.Geom) == 28
+    badk = geom()
+    badk.k_type = 2
+    assert decode(badk)[0] == E_UNSUPPORTED
+    q4 = geom()
+    q4.k_type = kv.K_Q4_0
+    code, nb = decode(q4, ws=None)
+    assert code == OK and nb > 0
+    assert kv.Geom(1, 1, 1, k_type=kv.K_Q4_0).k_record_bytes == 18432
+    assert kv.Geom(1, 1, 1).k_record_bytes == 34816

@@ -6,7 +6,8 @@ Per case, on pools pre-filled with random bytes and a permuted page table:
  - its out and lse equal kvattn_quantize_pages followed by kvattn_decode bit
    for bit, and the oracle's attention over the oracle's pool within the
    decode bar (2e-3 max-abs);
- - both value types: Q4_0 (read-modify-write of shared words) and Q8_0 (bytes);
+ - every key / value type pair: Q8_0 or Q4_0 keys (whole words per token),
+   Q4_0 values (read-modify-write of shared words) or Q8_0 values (bytes);
  - with a summary array, the summary of a page the append completes equals
    the two-call path's and the oracle's bit for bit.
 """
@@ -51,16 +52,17 @@ def plant_edges(Kn, Vn):
     Kn[0, 0, 128:160] *= 4.0                             # outlier block (the logits stay moderate)
 
 
-@pytest.mark.parametrize("v_type", [kv.V_Q4_0, kv.V_Q8_0])
+@pytest.mark.parametrize("k_type,v_type", [(kv.K_Q8_0, kv.V_Q4_0), (kv.K_Q8_0, kv.V_Q8_0),
+                                            (kv.K_Q4_0, kv.V_Q4_0), (kv.K_Q4_0, kv.V_Q8_0)])
 @pytest.mark.parametrize("n_kv,gqa,n_q_tok,n_new,kv_len,n_splits,sparse", CASES)
 def test_append_decode_matches_quantize_then_decode(n_kv, gqa, n_q_tok, n_new, kv_len, n_splits,
-                                                    sparse, v_type):
+                                                    sparse, k_type, v_type):
     g = np.random.default_rng(kv_len * 7 + n_new)
     n_pages = (kv_len + 127) // 128
     n_phys = n_pages + 3
     table = g.permutation(n_phys)[:n_pages].astype(np.int32)
     pos0 = kv_len - n_new
-    pools = Pools(n_phys, n_kv, gqa, init_seed=kv_len, v_type=v_type)
+    pools = Pools(n_phys, n_kv, gqa, init_seed=kv_len, v_type=v_type, k_type=k_type)
     if pos0 > 0:
         Kh = g.standard_normal((pos0, n_kv, 256)).astype(np.float32)
         Vh = g.standard_normal((pos0, n_kv, 256)).astype(np.float32)
