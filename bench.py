@@ -732,7 +732,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--configs", default="3,4,2,5,3s,5h,3q8,4q8,3q4,4q4",
+    ap.add_argument("--configs", default="3,4,2,5,3s,5h",
                     help="workloads to run: 2 decode-131k, 3 verify-262k, 4 prefill, 5 kvmem, "
                          "4h prefill with the pool in pinned host memory, 3s verify with the "
                          "history streamed from host memory (2100 MiB device working set), "
