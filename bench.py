@@ -46,14 +46,14 @@ WARM_SECONDS = 0.3             # untimed graph replays before each timed region
 # once either has changed.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
-    "decode": {"sources": {"decode.hip": "8a982992760cd5d2", "common.hpp": "ed6f88ee167a235a",
-                           "launch.hpp": "810d983b7c5bff94", "qround.hpp": "6d167bb0151cf907"},
+    "decode": {"sources": {"decode.hip": "636de517a737977d", "common.hpp": "cc85db156cb1b5ff",
+                           "launch.hpp": "48a924bd3d1493ab", "qround.hpp": "6d167bb0151cf907"},
                "flags": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-               "fetch_kib": 213552.0, "write_kib": 6168.0},
-    "prefill": {"sources": {"prefill.hip": "231dfa6bd3338761", "common.hpp": "ed6f88ee167a235a",
-                            "launch.hpp": "810d983b7c5bff94"},
+               "fetch_kib": 213557.0, "write_kib": 6168.0},
+    "prefill": {"sources": {"prefill.hip": "9335c014fa147b87", "common.hpp": "cc85db156cb1b5ff",
+                            "launch.hpp": "48a924bd3d1493ab"},
                 "flags": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
-                "fetch_kib": 369469.0, "write_kib": 199377.0},
+                "fetch_kib": 369487.0, "write_kib": 199289.0},
 }
 
 
