@@ -28,10 +28,11 @@ K_REC, V_REC = kv.K_RECORD_BYTES, kv.V_RECORD_BYTES
 PAGE = kv.PAGE_TOKENS
 
 
-def resident_pages_for_budget(budget_bytes, n_layers, n_pages, n_kv, v_record_bytes=V_REC):
+def resident_pages_for_budget(budget_bytes, n_layers, n_pages, n_kv, v_record_bytes=V_REC,
+                              k_record_bytes=K_REC):
     """Largest n_res such that n_layers * n_res resident pages plus two staging
     pools of n_pages - n_res pages fit in budget_bytes (at least one page)."""
-    page = n_kv * (K_REC + v_record_bytes)
+    page = n_kv * (k_record_bytes + v_record_bytes)
     n_res = (budget_bytes // page - 2 * n_pages) // (n_layers - 2) if n_layers > 2 else n_pages
     return int(max(1, min(n_pages, n_res)))
 
@@ -47,18 +48,18 @@ class StreamedLayer:
         dev = k_pool.device
         n_kv = geom.n_kv_heads
         table = torch.as_tensor(page_table, device=dev).long()
-        kview = k_pool.view(-1, n_kv * K_REC)
+        kview = k_pool.view(-1, n_kv * geom.k_record_bytes)
         vview = v_pool.view(-1, n_kv * geom.v_record_bytes)
         hist, res = table[:n_hist], table[n_hist:n_pages]
         self.n_hist, self.n_res = n_hist, n_pages - n_hist
         self.host_k = self.host_v = None
         if keep_history:
-            self.host_k = torch.empty(max(n_hist, 1) * n_kv * K_REC, dtype=torch.uint8,
-                                      pin_memory=True)
-            self.host_v = torch.empty(max(n_hist, 1) * n_kv * geom.v_record_bytes, dtype=torch.uint8,
-                                      pin_memory=True)
+            self.host_k = torch.empty(max(n_hist, 1) * n_kv * geom.k_record_bytes,
+                                      dtype=torch.uint8, pin_memory=True)
+            self.host_v = torch.empty(max(n_hist, 1) * n_kv * geom.v_record_bytes,
+                                      dtype=torch.uint8, pin_memory=True)
         if n_hist and keep_history:
-            self.host_k[:n_hist * n_kv * K_REC].copy_(kview[hist].reshape(-1))
+            self.host_k[:n_hist * n_kv * geom.k_record_bytes].copy_(kview[hist].reshape(-1))
             self.host_v[:n_hist * n_kv * geom.v_record_bytes].copy_(vview[hist].reshape(-1))
         self.res_k = kview[res].reshape(-1).contiguous()
         self.res_v = vview[res].reshape(-1).contiguous()
@@ -67,7 +68,8 @@ class StreamedLayer:
         self.res_table = torch.from_numpy(rt).to(dev)
         self.res_blocks = torch.from_numpy(
             np.tile(np.arange(n_hist, n_pages, dtype=np.int32), (n_kv, 1))).to(dev)
-        self.res_geom = kv.Geom(n_kv, geom.gqa, self.n_res, v_type=geom.v_type)
+        self.res_geom = kv.Geom(n_kv, geom.gqa, self.n_res, v_type=geom.v_type,
+                                k_type=geom.k_type)
         torch.cuda.synchronize()
 
 
@@ -81,11 +83,12 @@ class StreamedDecode:
         self.n_hist = layers[0].n_hist
         self.n_pages = n_pages
         n_kv = geom.n_kv_heads
-        self.hist_geom = kv.Geom(n_kv, geom.gqa, max(self.n_hist, 1), v_type=geom.v_type)
-        self.stage_k = [torch.empty(max(self.n_hist, 1) * n_kv * K_REC, dtype=torch.uint8,
-                                    device=dev) for _ in range(2)]
-        self.stage_v = [torch.empty(max(self.n_hist, 1) * n_kv * geom.v_record_bytes, dtype=torch.uint8,
-                                    device=dev) for _ in range(2)]
+        self.hist_geom = kv.Geom(n_kv, geom.gqa, max(self.n_hist, 1), v_type=geom.v_type,
+                                 k_type=geom.k_type)
+        self.stage_k = [torch.empty(max(self.n_hist, 1) * n_kv * geom.k_record_bytes,
+                                    dtype=torch.uint8, device=dev) for _ in range(2)]
+        self.stage_v = [torch.empty(max(self.n_hist, 1) * n_kv * geom.v_record_bytes,
+                                    dtype=torch.uint8, device=dev) for _ in range(2)]
         ht = np.full(n_pages, -1, np.int32)
         ht[:self.n_hist] = np.arange(self.n_hist, dtype=np.int32)
         self.hist_table = torch.from_numpy(ht).to(dev)
@@ -106,7 +109,8 @@ class StreamedDecode:
         return res + sum(t.numel() for t in self.stage_k + self.stage_v)
 
     def host_to_device_bytes_per_step(self):
-        return sum(self.n_hist * L.res_geom.n_kv_heads * (K_REC + L.res_geom.v_record_bytes) for L in self.layers)
+        return sum(self.n_hist * L.res_geom.n_kv_heads *
+                   (L.res_geom.k_record_bytes + L.res_geom.v_record_bytes) for L in self.layers)
 
     def step(self, q, k_new, v_new, kv_len, scale, outs, lses):
         """Enqueue one step over every layer: append the new tokens to the
@@ -190,8 +194,8 @@ class KVMemHostDecode:
         self.blocks = torch.empty((n_kv, self.n_out), dtype=torch.int32, device=dev)
         self.sel_ws = torch.empty(8 * n_kv * max(n_pages, 1) + 4096, dtype=torch.uint8, device=dev)
         n_st = max(self.k_sel, 1)
-        self.stage_geom = kv.Geom(n_kv, geom.gqa, n_st, v_type=geom.v_type)
-        self.stage_k = torch.empty(n_st * n_kv * K_REC, dtype=torch.uint8, device=dev)
+        self.stage_geom = kv.Geom(n_kv, geom.gqa, n_st, v_type=geom.v_type, k_type=geom.k_type)
+        self.stage_k = torch.empty(n_st * n_kv * geom.k_record_bytes, dtype=torch.uint8, device=dev)
         self.stage_v = torch.empty(n_st * n_kv * geom.v_record_bytes, dtype=torch.uint8, device=dev)
         self.stage_blocks = torch.empty((n_kv, n_st), dtype=torch.int32, device=dev)
         st = np.full(n_pages, -1, np.int32)
@@ -207,7 +211,8 @@ class KVMemHostDecode:
                      for _ in layers]
 
     def host_to_device_bytes_per_step(self):
-        return len(self.layers) * self.k_sel * self.geom.n_kv_heads * (K_REC + self.geom.v_record_bytes)
+        return (len(self.layers) * self.k_sel * self.geom.n_kv_heads *
+                (self.geom.k_record_bytes + self.geom.v_record_bytes))
 
     def device_bytes(self):
         res = sum(L.recent.res_k.numel() + L.recent.res_v.numel() + L.summary.numel() * 4

@@ -11,7 +11,8 @@ itself (nothing the GPU produced is fed to it):
   - KVMem summaries and selected blocks of two KV heads, bit for bit, the
     sparse decode of one head, and needle recall;
   - the verify step's fused append + decode: whole pools and outputs against
-    quantise + decode bit for bit, one head against the oracle.
+    quantise + decode bit for bit, one head against the oracle;
+  - verify with the q8_0/q8_0 and q4_0/q4_0 caches: sampled pages, one head.
 """
 import numpy as np
 import pytest
@@ -32,16 +33,15 @@ CHUNK = 32768  # tokens per quantisation call when filling a pool (as the benchm
 class FullLayer:
     """Layer 0 of workload w on the GPU, plus the host inputs it came from."""
 
-    def __init__(self, w, summaries=False):
+    def __init__(self, w, summaries=False, k_type=0, v_type=0):
         self.w = w
         self.q = synth.queries(w, 0)
         self.K, self.V = synth.kv_layer(w, 0, self.q, threads=16)
         self.table = synth.page_table(w)
-        self.geom = kv.Geom(w.n_kv, w.gqa, w.n_pages)
-        self.kp = torch.zeros(w.n_pages * w.n_kv * quant.K_RECORD_BYTES, dtype=torch.uint8,
-                              device=DEV)
-        self.vp = torch.zeros(w.n_pages * w.n_kv * quant.V_RECORD_BYTES, dtype=torch.uint8,
-                              device=DEV)
+        self.geom = kv.Geom(w.n_kv, w.gqa, w.n_pages, v_type=v_type, k_type=k_type)
+        self.k_rec, self.v_rec = self.geom.k_record_bytes, self.geom.v_record_bytes
+        self.kp = torch.zeros(w.n_pages * w.n_kv * self.k_rec, dtype=torch.uint8, device=DEV)
+        self.vp = torch.zeros(w.n_pages * w.n_kv * self.v_rec, dtype=torch.uint8, device=DEV)
         self.td = gpu(self.table, torch.int32)
         self.summ = (torch.zeros((w.n_kv, w.n_pages, 256), dtype=torch.float32, device=DEV)
                      if summaries else None)
@@ -54,8 +54,8 @@ class FullLayer:
     def oracle_pool(self, h):
         """The oracle's own pool for KV head h (n_kv = 1)."""
         w = self.w
-        ok = np.zeros((w.n_pages, 1, quant.K_RECORD_BYTES), np.uint8)
-        ov = np.zeros((w.n_pages, 1, quant.V_RECORD_BYTES), np.uint8)
+        ok = np.zeros((w.n_pages, 1, self.k_rec), np.uint8)
+        ov = np.zeros((w.n_pages, 1, self.v_rec), np.uint8)
         quant.quantize_into_pool(self.K[:, h:h + 1], self.V[:, h:h + 1], 0, self.table, ok, ov)
         return ok, ov
 
@@ -67,8 +67,8 @@ class FullLayer:
         for lp in pages:
             one = np.full(w.n_pages, -1, np.int32)
             one[lp] = 0
-            ok = np.zeros((1, w.n_kv, quant.K_RECORD_BYTES), np.uint8)
-            ov = np.zeros((1, w.n_kv, quant.V_RECORD_BYTES), np.uint8)
+            ok = np.zeros((1, w.n_kv, self.k_rec), np.uint8)
+            ov = np.zeros((1, w.n_kv, self.v_rec), np.uint8)
             sl = slice(lp * 128, min(w.kv_len, (lp + 1) * 128))
             quant.quantize_into_pool(self.K[sl], self.V[sl], lp * 128, one, ok, ov)
             ph = self.table[lp]
@@ -99,6 +99,24 @@ def test_decode_full_size_one_head(cfg, head):
     L.check_pages(sample_pages(w, np.random.default_rng(cfg)))
     out, lse = kv.kvattn_decode(L.geom, gpu(L.q), L.kp, L.vp, L.td, w.kv_len, 1 / 16)
     torch.cuda.synchronize()
+    ok, ov = L.oracle_pool(head)
+    rows = slice(head * w.gqa, (head + 1) * w.gqa)
+    ref_o, ref_l = oracle.decode(L.q[:, rows], w.gqa, ok, ov, L.table, w.n_pages, w.kv_len,
+                                 1 / 16)
+    eo, el, rr = compare(out[:, rows], lse[:, rows], ref_o, ref_l)
+    assert eo <= DEC_TOL and el <= 1e-3 and rr <= 2e-3, (eo, el, rr)
+
+
+@pytest.mark.parametrize("k_type,v_type", [(kv.K_Q8_0, kv.V_Q8_0), (kv.K_Q4_0, kv.V_Q4_0)])
+def test_verify_full_size_other_pairs(k_type, v_type):
+    """verify-262k with the q8_0/q8_0 and q4_0/q4_0 caches: sampled pages bit
+    for bit, one KV head's outputs against the oracle."""
+    w = synth.WORKLOADS[3]
+    L = FullLayer(w, k_type=k_type, v_type=v_type)
+    L.check_pages(sample_pages(w, np.random.default_rng(7 + k_type)))
+    out, lse = kv.kvattn_decode(L.geom, gpu(L.q), L.kp, L.vp, L.td, w.kv_len, 1 / 16)
+    torch.cuda.synchronize()
+    head = 1 + k_type
     ok, ov = L.oracle_pool(head)
     rows = slice(head * w.gqa, (head + 1) * w.gqa)
     ref_o, ref_l = oracle.decode(L.q[:, rows], w.gqa, ok, ov, L.table, w.n_pages, w.kv_len,

@@ -19,21 +19,24 @@ pytestmark = pytest.mark.gpu
 DEC_TOL = 2e-3
 
 
+@pytest.mark.parametrize("k_type,v_type", [(0, 0), (1, 1)])  # q8_0/q4_0 and q4_0/q8_0 caches
 @pytest.mark.parametrize("n_kv,gqa,n_q_tok,kv_len,n_hist,n_layers", [
-    (2, 6, 4, 40 * 128 - 50, 28, 3),   # verify: history + resident, three layers (both staging slots)
+    (2, 6, 4, 40 * 128 - 50, 28, 3),   # verify: history + resident, three layers (both slots)
     (1, 6, 1, 9 * 128 + 1, 8, 2),      # decode: the new token opens the resident last page
     (2, 6, 4, 12 * 128, 0, 2),         # no history: everything resident
 ])
-def test_streamed_decode_matches_oracle(n_kv, gqa, n_q_tok, kv_len, n_hist, n_layers):
+def test_streamed_decode_matches_oracle(n_kv, gqa, n_q_tok, kv_len, n_hist, n_layers, k_type,
+                                        v_type):
     g = np.random.default_rng(kv_len + n_hist)
     n_pages = (kv_len + 127) // 128
     n_phys = n_pages + 2
     pos0 = kv_len - n_q_tok
-    geom = kv.Geom(n_kv, gqa, n_phys)
+    geom = kv.Geom(n_kv, gqa, n_phys, v_type=v_type, k_type=k_type)
     layers, pools, tables, qs, kns, vns = [], [], [], [], [], []
     for _ in range(n_layers):
         table = g.permutation(n_phys)[:n_pages].astype(np.int32)
-        p = Pools(n_phys, n_kv, gqa, init_seed=int(g.integers(1 << 30)))
+        p = Pools(n_phys, n_kv, gqa, init_seed=int(g.integers(1 << 30)), v_type=v_type,
+                  k_type=k_type)
         p.write(g.standard_normal((pos0, n_kv, 256)).astype(np.float32),
                 g.standard_normal((pos0, n_kv, 256)).astype(np.float32), 0, table)
         layers.append(streaming.StreamedLayer(geom, p.gk, p.gv, gpu(table, torch.int32), n_pages,
@@ -63,7 +66,8 @@ def test_streamed_decode_matches_oracle(n_kv, gqa, n_q_tok, kv_len, n_hist, n_la
         ref_o, ref_l = oracle.decode(qs[c], gqa, p.ok, p.ov, table, n_pages, kv_len, 1 / 16)
         eo, el, rr = compare(outs[c], lses[c], ref_o, ref_l)
         assert eo <= DEC_TOL and el <= 1e-3 and rr <= 2e-3, (c, eo, el, rr)
-    assert sd.host_to_device_bytes_per_step() == n_layers * n_hist * n_kv * 53248
+    assert sd.host_to_device_bytes_per_step() == n_layers * n_hist * n_kv * (
+        geom.k_record_bytes + geom.v_record_bytes)
 
 
 
