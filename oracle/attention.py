@@ -15,24 +15,24 @@ lse = -inf.
 import numpy as np
 
 from .quant import (HEAD_DIM, PAGE_TOKENS, BLOCK, N_BLOCKS, unpack_k_record,
-                    unpack_v_record, unpack_v8_record, values_are_q8, unpack_keys,
+                    unpack_v_record, unpack_v8_record, values_are_q8, dequantize_keys,
                     q8_0_dequantize,
                     q4_0_dequantize)
 
 
 def dequant_page(k_records, v_records):
     """Dequantised keys and values (binary64, exact) of page records.
-    k_records uint8 [..., 34816] (Q8_0 keys) or [..., 18432] (Q4_0 keys),
+    k_records uint8 [..., 34816] (Q8_0 keys), [..., 18432] (Q4_0 keys) or
+    [..., 24576] (Q5_1 keys),
     v_records uint8 [..., 18432] (Q4_0) or
     [..., 34816] (Q8_0) -> (Khat [..., 128, 256], Vhat [..., 128, 256])."""
-    kc, kb, kdq = unpack_keys(k_records)
     v8 = values_are_q8(v_records)
     vc, vb = (unpack_v8_record if v8 else unpack_v_record)(v_records)
-    lead = kc.shape[:-2]
+    lead = vc.shape[:-2]
     shp = lead + (PAGE_TOKENS, N_BLOCKS, BLOCK)
     # unwritten slots may hold any bytes (inf/nan scales); callers drop them
     with np.errstate(invalid="ignore", over="ignore"):
-        khat = kdq(kc.reshape(shp), kb).reshape(lead + (PAGE_TOKENS, HEAD_DIM))
+        khat = dequantize_keys(k_records)
         vdq = q8_0_dequantize if v8 else q4_0_dequantize
         vhat = vdq(vc.reshape(shp), vb).reshape(lead + (PAGE_TOKENS, HEAD_DIM))
     return khat, vhat

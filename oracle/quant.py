@@ -32,6 +32,13 @@ V8_RECORD_BYTES = V8_CODES_BYTES + PAGE_TOKENS * N_BLOCKS * 2  # 34816
 # size, selected by the record size of the key pool.
 K4_CODES_BYTES = PAGE_TOKENS * HEAD_DIM // 2    # 16384
 K4_RECORD_BYTES = K4_CODES_BYTES + PAGE_TOKENS * N_BLOCKS * 2  # 18432
+# Q5_1 keys (the q5_1/q4_0 pair, [VULKAN] 坑 3's allowed type list; q5_1 is 6
+# bits per element, [VULKAN] 坑 2): low nibbles as in the Q4_0 key record, then
+# one byte of fifth bits per 8 dims, then the scales d, then the minimums m.
+K5_HI_OFF = K4_CODES_BYTES                              # 16384
+K5_D_OFF = K5_HI_OFF + PAGE_TOKENS * HEAD_DIM // 8      # 20480
+K5_M_OFF = K5_D_OFF + PAGE_TOKENS * N_BLOCKS * 2        # 22528
+K5_RECORD_BYTES = K5_M_OFF + PAGE_TOKENS * N_BLOCKS * 2  # 24576
 
 
 def rn16(x):
@@ -106,6 +113,41 @@ def q4_0_quantize(x):
     codes = np.where(zero[..., None], 8, codes).astype(np.uint8)
     bits = np.where(zero, np.uint16(0), f16_bits(d16)).astype(np.uint16)
     return codes, bits
+
+
+def q5_1_quantize(x):
+    """Q5_1 of 32-element blocks along the last axis (keys of the q5_1 pair).
+
+    x: float32 [..., 32]. Returns (codes uint8 in [0,31] [..., 32], d_bits,
+    m_bits). mn = min x, mx = max x; d = RN16(RN32((mx - mn) / 31)),
+    m = RN16(mn). d == 0 -> scale +0 and every code 0; else inv = RN32(1/d),
+    code = clamp(rint(RN32(RN32(x - m) * inv)), 0, 31). Dequantised:
+    d * code + m.
+    """
+    x = np.asarray(x, np.float32)
+    assert x.shape[-1] == BLOCK
+    mn = np.min(x, axis=-1)
+    mx = np.max(x, axis=-1)
+    with np.errstate(over="ignore"):
+        d16 = rn16((mx - mn) / np.float32(31.0))
+    m16 = rn16(mn)
+    zero = d16 == 0
+    d_safe = np.where(zero, np.float32(1.0), d16)
+    inv = np.float32(1.0) / d_safe
+    diff = x - m16[..., None]                        # RN32
+    prod = diff * inv[..., None]                     # RN32
+    codes = np.clip(np.rint(prod), 0, 31)
+    codes = np.where(zero[..., None], 0, codes).astype(np.uint8)
+    d_bits = np.where(zero, np.uint16(0), f16_bits(d16)).astype(np.uint16)
+    return codes, d_bits, f16_bits(m16)
+
+
+def q5_1_dequantize(codes, d_bits, m_bits):
+    """Dequantised Q5_1 block values d*code + m in binary64 (the product is
+    exact, the sum rounds once)."""
+    d = f16_from_bits(d_bits).astype(np.float64)
+    m = f16_from_bits(m_bits).astype(np.float64)
+    return np.asarray(codes, np.float64) * d[..., None] + m[..., None]
 
 
 def q4_0_dequantize(codes, scale_bits):
@@ -277,18 +319,72 @@ def unpack_k4_record(rec):
     return codes.reshape(lead + (PAGE_TOKENS, HEAD_DIM)), bits.reshape(lead + (PAGE_TOKENS, N_BLOCKS))
 
 
+def pack_k5_record(codes, d_bits, m_bits):
+    """Q5_1 key record bytes from codes uint8 [..., 128, 256] (0..31) and
+    d, m bits uint16 [..., 128, 8]; returns uint8 [..., 24576]. The low
+    nibbles form a Q4_0 key record's code area; byte 16384 + t*32 + w holds
+    the fifth bits of dims 8w..8w+7: dim 8w + 2p at bit p, 8w + 2p + 1 at
+    bit 4 + p."""
+    codes = np.asarray(codes, np.uint8)
+    lead = codes.shape[:-2]
+    rec = np.zeros(lead + (K5_RECORD_BYTES,), np.uint8)
+    zeros = np.zeros(lead + (PAGE_TOKENS, N_BLOCKS), np.uint16)
+    rec[..., :K4_CODES_BYTES] = pack_k4_record(codes & 0xF, zeros)[..., :K4_CODES_BYTES]
+    hi = ((codes >> 4) & 1).reshape(lead + (PAGE_TOKENS, HEAD_DIM // 8, 8)).astype(np.uint8)
+    byte = np.zeros(lead + (PAGE_TOKENS, HEAD_DIM // 8), np.uint8)
+    for k in range(8):
+        byte |= hi[..., k] << np.uint8((k // 2) + 4 * (k % 2))
+    rec[..., K5_HI_OFF:K5_D_OFF] = byte.reshape(lead + (-1,))
+    for off, bits in ((K5_D_OFF, d_bits), (K5_M_OFF, m_bits)):
+        b = np.ascontiguousarray(np.asarray(bits, np.uint16).astype('<u2'))
+        rec[..., off:off + PAGE_TOKENS * N_BLOCKS * 2] = b.reshape(lead + (-1,)).view(np.uint8)
+    return rec
+
+
+def unpack_k5_record(rec):
+    """(codes uint8 [..., 128, 256], d_bits, m_bits uint16 [..., 128, 8]) of Q5_1 key records."""
+    rec = np.ascontiguousarray(np.asarray(rec, np.uint8))
+    lead = rec.shape[:-1]
+    k4 = np.zeros(lead + (K4_RECORD_BYTES,), np.uint8)
+    k4[..., :K4_CODES_BYTES] = rec[..., :K4_CODES_BYTES]
+    low, _ = unpack_k4_record(k4)
+    byte = rec[..., K5_HI_OFF:K5_D_OFF].reshape(lead + (PAGE_TOKENS, HEAD_DIM // 8))
+    hi = np.zeros(lead + (PAGE_TOKENS, HEAD_DIM // 8, 8), np.uint8)
+    for k in range(8):
+        hi[..., k] = (byte >> np.uint8((k // 2) + 4 * (k % 2))) & 1
+    codes = low | (hi.reshape(lead + (PAGE_TOKENS, HEAD_DIM)) << 4)
+    shp = lead + (PAGE_TOKENS, N_BLOCKS)
+    d_bits = np.ascontiguousarray(rec[..., K5_D_OFF:K5_M_OFF]).view('<u2').astype(np.uint16)
+    m_bits = np.ascontiguousarray(rec[..., K5_M_OFF:]).view('<u2').astype(np.uint16)
+    return codes, d_bits.reshape(shp), m_bits.reshape(shp)
+
+
+def key_type(k_pool):
+    """'q8_0', 'q4_0' or 'q5_1' from a key pool's record size."""
+    n = np.asarray(k_pool).shape[-1]
+    kinds = {K_RECORD_BYTES: "q8_0", K4_RECORD_BYTES: "q4_0", K5_RECORD_BYTES: "q5_1"}
+    assert n in kinds, n
+    return kinds[n]
+
+
 def keys_are_q4(k_pool):
     """True when a key pool (uint8 [..., record bytes]) holds Q4_0 records."""
-    n = np.asarray(k_pool).shape[-1]
-    assert n in (K_RECORD_BYTES, K4_RECORD_BYTES), n
-    return n == K4_RECORD_BYTES
+    return key_type(k_pool) == "q4_0"
 
 
-def unpack_keys(k_records):
-    """(codes, scale_bits, dequantiser) of key records of either type."""
-    if keys_are_q4(k_records):
-        return unpack_k4_record(k_records) + (q4_0_dequantize,)
-    return unpack_k_record(k_records) + (q8_0_dequantize,)
+def dequantize_keys(k_records):
+    """Dequantised keys (binary64) [..., 128, 256] of key records of any type."""
+    kind = key_type(k_records)
+    if kind == "q5_1":
+        codes, db, mb = unpack_k5_record(k_records)
+        lead = codes.shape[:-2]
+        c = codes.reshape(lead + (PAGE_TOKENS, N_BLOCKS, BLOCK))
+        return q5_1_dequantize(c, db, mb).reshape(lead + (PAGE_TOKENS, HEAD_DIM))
+    codes, bits = (unpack_k4_record if kind == "q4_0" else unpack_k_record)(k_records)
+    lead = codes.shape[:-2]
+    dq = q4_0_dequantize if kind == "q4_0" else q8_0_dequantize
+    c = codes.reshape(lead + (PAGE_TOKENS, N_BLOCKS, BLOCK))
+    return dq(c, bits).reshape(lead + (PAGE_TOKENS, HEAD_DIM))
 
 
 def values_are_q8(v_pool):
@@ -317,8 +413,12 @@ def quantize_into_pool(k, v, pos0, page_table, k_pool, v_pool):
     assert D == HEAD_DIM and v.shape == k.shape
     n_phys = k_pool.shape[0]
     v8 = values_are_q8(v_pool)
-    k4 = keys_are_q4(k_pool)
-    kc, ks = (q4_0_quantize if k4 else q8_0_quantize)(k.reshape(n_tok, n_kv, N_BLOCKS, BLOCK))
+    kind = key_type(k_pool)
+    kb = k.reshape(n_tok, n_kv, N_BLOCKS, BLOCK)
+    if kind == "q5_1":
+        kc, ks, km = q5_1_quantize(kb)
+    else:
+        kc, ks = (q4_0_quantize if kind == "q4_0" else q8_0_quantize)(kb)
     vq = q8_0_quantize if v8 else q4_0_quantize
     vc, vs = vq(v.reshape(n_tok, n_kv, N_BLOCKS, BLOCK))
     kc = kc.reshape(n_tok, n_kv, HEAD_DIM)
@@ -336,14 +436,22 @@ def quantize_into_pool(k, v, pos0, page_table, k_pool, v_pool):
     ok = (where < pages.size) & (pages[np.minimum(where, pages.size - 1)] == lps)
     tsel = np.nonzero(ok)[0]
     pidx, slot = where[tsel], pos[tsel] % PAGE_TOKENS
-    kcodes, kbits = (unpack_k4_record if k4 else unpack_k_record)(k_pool[phys])  # [P, n_kv, 128, ...]
+    if kind == "q5_1":
+        kcodes, kbits, kmins = unpack_k5_record(k_pool[phys])      # [P, n_kv, 128, ...]
+    else:
+        kcodes, kbits = (unpack_k4_record if kind == "q4_0" else unpack_k_record)(k_pool[phys])
     vcodes, vbits = (unpack_v8_record if v8 else unpack_v_record)(v_pool[phys])
     for h in range(n_kv):
         kcodes[pidx, h, slot] = kc[tsel, h]
         kbits[pidx, h, slot] = ks[tsel, h]
+        if kind == "q5_1":
+            kmins[pidx, h, slot] = km[tsel, h]
         vcodes[pidx, h, slot] = vc[tsel, h]
         vbits[pidx, h, slot] = vs[tsel, h]
-    k_pool[phys] = (pack_k4_record if k4 else pack_k_record)(kcodes, kbits)
+    if kind == "q5_1":
+        k_pool[phys] = pack_k5_record(kcodes, kbits, kmins)
+    else:
+        k_pool[phys] = (pack_k4_record if kind == "q4_0" else pack_k_record)(kcodes, kbits)
     v_pool[phys] = (pack_v8_record if v8 else pack_v_record)(vcodes, vbits)
 
 
@@ -358,11 +466,9 @@ def page_summaries(k_records):
     the summary is the mean key of the block, the reading the workload
     description gives ("per-block summary = mean key").
     """
-    codes, bits, dequantize = unpack_keys(k_records)
-    lead = codes.shape[:-2]
+    lead = np.asarray(k_records).shape[:-1]
     with np.errstate(invalid="ignore", over="ignore"):   # unwritten slots: any bytes
-        khat = dequantize(codes.reshape(lead + (PAGE_TOKENS, N_BLOCKS, BLOCK)), bits)
-    khat = khat.reshape(lead + (PAGE_TOKENS, HEAD_DIM))
+        khat = dequantize_keys(k_records)
     acc = np.zeros(lead + (HEAD_DIM,), np.float64)
     for t in range(PAGE_TOKENS):                     # ascending t, binary64
         acc = acc + khat[..., t, :]

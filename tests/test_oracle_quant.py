@@ -347,3 +347,89 @@ def test_q4_keys_quantise_like_values():
         for h in range(n_kv):
             exact = np.float32(np.sum(kh[p, h], axis=0, dtype=np.float64) / 128.0)
             assert np.abs(s[h, p] - exact).max() <= 1e-7 * (1 + np.abs(exact).max())
+
+
+def test_q5_1_rule_closed_forms():
+    """Q5_1: a block on an exact grid m + d*k keeps its codes and values; a
+    constant block has scale 0 and dequantises to RN16 of the constant; any
+    block dequantises within d/2 plus the binary16 rounding of m."""
+    d, m = 0.125, -1.5                                    # both exact in binary16
+    k = np.arange(32)
+    x = (m + d * k).astype(np.float32)[::-1].copy()       # order does not matter
+    codes, db, mb = quant.q5_1_quantize(x)
+    assert (codes == k[::-1]).all()
+    assert quant.f16_from_bits(db) == np.float32(d) and quant.f16_from_bits(mb) == np.float32(m)
+    assert (quant.q5_1_dequantize(codes, db, mb) == x).all()
+    c = np.full(32, 0.3, np.float32)
+    codes, db, mb = quant.q5_1_quantize(c)
+    assert db == 0 and (codes == 0).all()
+    assert (quant.q5_1_dequantize(codes, db, mb) == np.float32(np.float16(0.3))).all()
+    g = np.random.default_rng(12)
+    x = (g.standard_normal((500, 32)) * np.exp(g.standard_normal((500, 1)))).astype(np.float32)
+    codes, db, mb = quant.q5_1_quantize(x)
+    dq = quant.q5_1_dequantize(codes, db, mb)
+    dd = quant.f16_from_bits(db).astype(np.float64)
+    mm = quant.f16_from_bits(mb).astype(np.float64)
+    bound = dd / 2 * (1 + 1e-3) + np.abs(mm - x.min(axis=1)) + 1e-12
+    assert (np.abs(dq - x).max(axis=1) <= bound + dd * 1e-3).all()
+    assert codes.max() == 31 and codes.min() == 0
+
+
+def test_q5_1_key_record_layout_positions():
+    """Q5_1 key records: low nibbles where a Q4_0 key record puts them, the
+    fifth bits at hand-computed bit positions (byte 16384 + t*32 + w, dim
+    8w + 2p at bit p, 8w + 2p + 1 at bit 4 + p), d at 20480 + 2(t*8 + b), m at
+    22528 + 2(t*8 + b); 192 bytes per token and head (6 bits per element);
+    a round trip."""
+    assert quant.K5_RECORD_BYTES == 24576 and quant.K5_RECORD_BYTES // 128 == 192
+    codes = np.zeros((128, 256), np.uint8)
+    z = np.zeros((128, 8), np.uint16)
+    marks = {(0, 0): (16384, 0), (0, 1): (16384, 4), (0, 2): (16384, 1), (0, 7): (16384, 7),
+             (0, 8): (16385, 0), (3, 255): (16384 + 3 * 32 + 31, 7)}
+    for (t, dm) in marks:
+        codes[t, dm] = 16                                # only the fifth bit set
+    rec = quant.pack_k5_record(codes, z, z)
+    assert not rec[:16384].any()
+    for (t, dm), (off, bit) in marks.items():
+        assert (rec[off] >> bit) & 1 == 1, (t, dm)
+    assert int(np.unpackbits(rec[16384:20480]).sum()) == len(marks)
+    db = np.zeros((128, 8), np.uint16)
+    mb = np.zeros((128, 8), np.uint16)
+    db[5, 3], mb[5, 3] = 0x1234, 0xABCD
+    rec = quant.pack_k5_record(np.zeros((128, 256), np.uint8), db, mb)
+    o = 2 * (5 * 8 + 3)
+    assert rec[20480 + o] == 0x34 and rec[20481 + o] == 0x12
+    assert rec[22528 + o] == 0xCD and rec[22529 + o] == 0xAB
+    c4 = np.random.default_rng(13).integers(0, 16, (128, 256)).astype(np.uint8)
+    r4 = quant.pack_k4_record(c4, z)
+    r5 = quant.pack_k5_record(c4, z, z)
+    assert (r4[:16384] == r5[:16384]).all()
+    g = np.random.default_rng(14)
+    c2 = g.integers(0, 32, (2, 128, 256)).astype(np.uint8)
+    d2 = g.integers(0, 1 << 16, (2, 128, 8)).astype(np.uint16)
+    m2 = g.integers(0, 1 << 16, (2, 128, 8)).astype(np.uint16)
+    c3, d3, m3 = quant.unpack_k5_record(quant.pack_k5_record(c2, d2, m2))
+    assert (c3 == c2).all() and (d3 == d2).all() and (m3 == m2).all()
+
+
+def test_q5_1_keys_in_pool_and_summary():
+    """A Q5_1 key pool holds the rule's codes; the summary of a full page is
+    the binary64 mean of d*code + m."""
+    g = np.random.default_rng(15)
+    n_tok, n_kv = 260, 2
+    x = g.standard_normal((n_tok, n_kv, 256)).astype(np.float32)
+    x[3, 1, 64:96] = 2.0
+    table = np.array([1, 2, 0], np.int32)
+    kp = np.zeros((3, n_kv, quant.K5_RECORD_BYTES), np.uint8)
+    vp = np.zeros((3, n_kv, quant.V_RECORD_BYTES), np.uint8)
+    quant.quantize_into_pool(x, x, 0, table, kp, vp)
+    codes, db, mb = quant.q5_1_quantize(x.reshape(n_tok, n_kv, 8, 32))
+    kh, _ = oracle.dequant_page(kp[table], vp[table])
+    ref = quant.q5_1_dequantize(codes, db, mb).reshape(n_tok, n_kv, 256)
+    assert (kh[0].transpose(1, 0, 2) == ref[:128]).all()
+    assert (kh[2, :, :4].transpose(1, 0, 2) == ref[256:260]).all()
+    assert (kh[0, 1, 3, 64:96] == np.float64(np.float16(2.0))).all()
+    s = quant.summaries_from_pool(kp, table, 2, n_kv)
+    for p in range(2):
+        exact = (np.sum(ref[128 * p:128 * (p + 1)], axis=0) / 128.0).astype(np.float32)
+        assert (s[:, p] == exact).all()
