@@ -177,7 +177,7 @@ def time_launches(call_fn, n_layers, reps):
 def bench_decode(w, dev, steps, warmup, sparse=False, v_type=0, k_type=0):
     """Decode / verify workload: append the new tokens and attend (one launch), merge (x16).
     v_type 1 caches the values as Q8_0 (272 bytes per token and KV head, as the keys);
-    k_type 1 the keys as Q4_0 (144 bytes, as Q4_0 values)."""
+    k_type 1 the keys as Q4_0 (144 bytes, as Q4_0 values), k_type 2 as Q5_1 (192 bytes)."""
     import torch
     import long_context_attention_paged_amd as kv
     pools = LayerPools(w, dev, with_summary=sparse, v_type=v_type, k_type=k_type)
@@ -233,8 +233,8 @@ def bench_decode(w, dev, steps, warmup, sparse=False, v_type=0, k_type=0):
     launch_ms = time_launches(decode_call, w.n_layers, max(steps, 3))
     kernel_ms = time_launches(kernel_call, w.n_layers, max(steps, 3))
     tokens = (w.k_top + w.n_recent) * 128 if sparse else w.kv_len
-    bytes_per_launch = tokens * w.n_kv * ((144 if k_type == kv.K_Q4_0 else 272) +
-                                          (272 if v_type == kv.V_Q8_0 else 144))
+    k_bytes = {kv.K_Q4_0: 144, kv.K_Q5_1: 192}.get(k_type, 272)  # per token and KV head
+    bytes_per_launch = tokens * w.n_kv * (k_bytes + (272 if v_type == kv.V_Q8_0 else 144))
     res = {
         "ms_per_step": ms,
         "kv_bytes_per_step": bytes_per_launch * w.n_layers,
@@ -724,7 +724,8 @@ def profile_kernels(dev, layers, reps):
 
 # bench config -> (k_type, v_type, tag) of the other KV cache type pairs
 PAIRS = {"3q8": (0, 1, "q8_0-q8_0"), "4q8": (0, 1, "q8_0-q8_0"),
-         "3q4": (1, 0, "q4_0-q4_0"), "4q4": (1, 0, "q4_0-q4_0")}
+         "3q4": (1, 0, "q4_0-q4_0"), "4q4": (1, 0, "q4_0-q4_0"),
+         "3q5": (2, 0, "q5_1-q4_0"), "4q5": (2, 0, "q5_1-q4_0")}
 
 
 def main():
@@ -738,7 +739,7 @@ def main():
                          "history streamed from host memory (2100 MiB device working set), "
                          "5h kvmem with its history in host memory (budget sweep), "
                          "3q8 / 4q8 verify-262k / prefill with the q8_0/q8_0 pair, "
-                         "3q4 / 4q4 with the q4_0/q4_0 pair")
+                         "3q4 / 4q4 with the q4_0/q4_0 pair, 3q5 / 4q5 with q5_1/q4_0")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="run only a short fixed kernel sequence for counter runs (no JSON line)")

@@ -87,6 +87,13 @@
  *                   order), so a lane turns a word into the f16 values of
  *                   eight consecutive dims with one shift and mask per pair.
  *   [16384, 18432)  binary16 scale of (slot t, block b) at 16384 + 2*(t*8 + b).
+ *  Q5_1 K record (k_type KVATTN_K_Q5_1), KVATTN_K5_RECORD_BYTES = 24576:
+ *   [0, 16384)      the low 4 bits of each 5-bit code, as in a Q4_0 K record.
+ *   [16384, 20480)  fifth bits: byte 16384 + t*32 + w holds those of dims
+ *                   8w..8w+7 of slot t, dim 8w + 2p at bit p and dim
+ *                   8w + 2p + 1 at bit 4 + p (p = 0..3).
+ *   [20480, 22528)  binary16 scale d of (slot t, block b) at 20480 + 2*(t*8 + b).
+ *   [22528, 24576)  binary16 minimum m of (slot t, block b) at 22528 + 2*(t*8 + b).
  *
  * Quantisation (per token, per KV head, per 32-dim block x[0..31]; RN32 and
  * RN16 are IEEE round-to-nearest-even to binary32 / binary16, rint rounds
@@ -97,6 +104,11 @@
  *   34 bytes per 32 elements = 8.5 bits per element ([VULKAN] closing remark).
  *  Q8_0 values (v_type KVATTN_V_Q8_0) follow the key rule above.
  *  Q4_0 keys (k_type KVATTN_K_Q4_0) follow the Q4_0 value rule below.
+ *  Q5_1 (keys, k_type KVATTN_K_Q5_1): mn = min x_i, mx = max x_i;
+ *   d = RN16(RN32((mx - mn) / 31)), m = RN16(mn). If d == 0 every code is 0
+ *   and the stored scale is +0. Otherwise inv = RN32(1 / d) and
+ *   code_i = clamp(rint(RN32(RN32(x_i - m) * inv)), 0, 31). Dequantised:
+ *   d * code + m. 24 bytes per 32 elements (6 bits per element).
  *  Q4_0 (values): j* = lowest index with |x_j*| = amax; m = x_j* (signed);
  *   d = RN16(RN32(-m / 8)). If amax == 0 or d == 0, the stored scale is +0
  *   and every code is 8. Otherwise inv = RN32(1 / d) and
@@ -134,6 +146,8 @@ typedef int32_t kvattn_status;
 #define KVATTN_K4_RECORD_BYTES 18432 /* Q4_0 keys (k_type KVATTN_K_Q4_0) */
 #define KVATTN_K_Q8_0 0 /* key cache type: Q8_0 (the default) */
 #define KVATTN_K_Q4_0 1 /* key cache type: Q4_0 (the q4_0/q4_0 pair) */
+#define KVATTN_K5_RECORD_BYTES 24576 /* Q5_1 keys (k_type KVATTN_K_Q5_1) */
+#define KVATTN_K_Q5_1 2 /* key cache type: Q5_1 (the q5_1/q4_0 pair) */
 #define KVATTN_MAX_QUERY_ROWS 32 /* n_q_tok * gqa per KV head in decode */
 #define KVATTN_MAX_APPEND_TOKENS 32 /* n_new of kvattn_append_decode */
 
@@ -142,8 +156,9 @@ typedef int32_t kvattn_status;
  * Query head hq uses KV head hq / gqa (grouped-query attention). v_type picks
  * the value type: KVATTN_V_Q4_0 (the [STREAM] -ctk q8_0 -ctv q4_0 pair) or
  * KVATTN_V_Q8_0 (KVMem's q8_0/q8_0, [KVMEM] 測試口徑 --kv-dtype q8_0), and
- * k_type the key type: KVATTN_K_Q8_0 or KVATTN_K_Q4_0 (the q4_0/q4_0 pair,
- * [VULKAN] 坑 2); each sets its record size. */
+ * k_type the key type: KVATTN_K_Q8_0, KVATTN_K_Q4_0 (the q4_0/q4_0 pair,
+ * [VULKAN] 坑 2) or KVATTN_K_Q5_1 (the q5_1/q4_0 pair of [VULKAN] 坑 3's
+ * allowed list); each sets its record size. */
 typedef struct kvattn_geom {
   int32_t n_kv_heads;   /* >= 1 */
   int32_t gqa;          /* query heads per KV head, >= 1 */
@@ -152,7 +167,7 @@ typedef struct kvattn_geom {
   int32_t n_phys_pages; /* physical pages in k_pool / v_pool, >= 1;
                           n_phys_pages * n_kv_heads <= INT32_MAX */
   int32_t v_type;       /* KVATTN_V_Q4_0 or KVATTN_V_Q8_0 */
-  int32_t k_type;       /* KVATTN_K_Q8_0 or KVATTN_K_Q4_0 */
+  int32_t k_type;       /* KVATTN_K_Q8_0, KVATTN_K_Q4_0 or KVATTN_K_Q5_1 */
 } kvattn_geom;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -176,7 +191,7 @@ int32_t kvattn_select_count(int32_t n_blocks, int32_t n_recent, int32_t k_top);
  *              Requires pos0 >= 0, n_tok >= 1 and
  *              pos0 + n_tok <= n_logical_pages * 128.
  *  k_pool      n_phys_pages * n_kv_heads * the key record size (34816 bytes
- *              for Q8_0 keys, 18432 for Q4_0).
+ *              for Q8_0 keys, 18432 for Q4_0, 24576 for Q5_1).
  *  v_pool      n_phys_pages * n_kv_heads * the value record size (18432 bytes
  *              for Q4_0 values, 34816 for Q8_0).
  *  k_summary   fp32 [n_kv_heads][n_logical_pages][256] or NULL.

@@ -26,7 +26,8 @@ V_RECORD_BYTES = 18432
 V8_RECORD_BYTES = 34816
 V_Q4_0, V_Q8_0 = 0, 1  # value cache types (kvattn_geom.v_type)
 K4_RECORD_BYTES = 18432
-K_Q8_0, K_Q4_0 = 0, 1  # key cache types (kvattn_geom.k_type)
+K5_RECORD_BYTES = 24576
+K_Q8_0, K_Q4_0, K_Q5_1 = 0, 1, 2  # key cache types (kvattn_geom.k_type)
 STATUS = {0: "OK", 1: "E_INVALID", 2: "E_UNSUPPORTED", 3: "E_WORKSPACE", 4: "E_DEVICE"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -51,7 +52,7 @@ class Geom(ctypes.Structure):
 
     @property
     def k_record_bytes(self):
-        return K4_RECORD_BYTES if self.k_type == K_Q4_0 else K_RECORD_BYTES
+        return {K_Q4_0: K4_RECORD_BYTES, K_Q5_1: K5_RECORD_BYTES}.get(self.k_type, K_RECORD_BYTES)
 
     @property
     def v_record_bytes(self):

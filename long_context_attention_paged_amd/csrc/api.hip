@@ -83,13 +83,16 @@ kvattn_status check_geom(const kvattn_geom* g) {
   if ((int64_t)g->n_kv_heads * g->gqa > (1 << 20)) return KVATTN_E_INVALID;
   if ((int64_t)g->n_phys_pages * g->n_kv_heads > INT32_MAX) return KVATTN_E_INVALID;  // record index
   if (g->v_type != KVATTN_V_Q4_0 && g->v_type != KVATTN_V_Q8_0) return KVATTN_E_UNSUPPORTED;
-  if (g->k_type != KVATTN_K_Q8_0 && g->k_type != KVATTN_K_Q4_0) return KVATTN_E_UNSUPPORTED;
+  if (g->k_type != KVATTN_K_Q8_0 && g->k_type != KVATTN_K_Q4_0 && g->k_type != KVATTN_K_Q5_1)
+    return KVATTN_E_UNSUPPORTED;
   return KVATTN_OK;
 }
 
 // Bytes of one (page, KV head) key record for the geometry's key type.
 size_t k_record_bytes(const kvattn_geom* g) {
-  return g->k_type == KVATTN_K_Q4_0 ? KVATTN_K4_RECORD_BYTES : KVATTN_K_RECORD_BYTES;
+  return g->k_type == KVATTN_K_Q4_0   ? KVATTN_K4_RECORD_BYTES
+         : g->k_type == KVATTN_K_Q5_1 ? KVATTN_K5_RECORD_BYTES
+                                      : KVATTN_K_RECORD_BYTES;
 }
 
 // Bytes of one (page, KV head) value record for the geometry's value type.
@@ -163,7 +166,7 @@ kvattn_status kvattn_quantize_pages(const kvattn_geom* geom, const float* k, con
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = launched(launch_quantize(k, v, pos0, n_tok, geom->n_kv_heads, page_table,
                                 geom->n_phys_pages, k_pool, v_pool,
-                                geom->v_type == KVATTN_V_Q8_0, geom->k_type == KVATTN_K_Q4_0, s));
+                                geom->v_type == KVATTN_V_Q8_0, geom->k_type, s));
   if (st || !k_summary) return st;
   const int64_t first = pos0 / KVATTN_PAGE_TOKENS;
   const int64_t last_full = (pos0 + n_tok) / KVATTN_PAGE_TOKENS - 1;
@@ -171,7 +174,7 @@ kvattn_status kvattn_quantize_pages(const kvattn_geom* geom, const float* k, con
   return launched(launch_summarize(k_pool, page_table, geom->n_kv_heads, geom->n_phys_pages,
                                    n_logical_pages, (int32_t)first,
                                    (int32_t)(last_full - first + 1), k_summary,
-                                   geom->k_type == KVATTN_K_Q4_0, s));
+                                   geom->k_type, s));
 }
 
 kvattn_status kvattn_select_blocks(const kvattn_geom* geom, const float* q,
@@ -285,7 +288,7 @@ kvattn_status launch_decode_partials(const kvattn_geom* geom, const float* q, in
   p.v_pool_w = app ? app->v_pool : nullptr;
   p.n_new = app ? app->n_new : 0;
   p.v_q8 = geom->v_type == KVATTN_V_Q8_0;
-  p.k_q4 = geom->k_type == KVATTN_K_Q4_0;
+  p.k_type = geom->k_type;
   return launched(launch_decode(p, s));
 }
 
@@ -335,7 +338,7 @@ kvattn_status launch_prefill_partials(const kvattn_geom* geom, const float* q, i
   p.n_phys = geom->n_phys_pages;
   p.qscale = scale * kLog2e;
   p.v_q8 = geom->v_type == KVATTN_V_Q8_0;
-  p.k_q4 = geom->k_type == KVATTN_K_Q4_0;
+  p.k_type = geom->k_type;
   return launched(launch_prefill(p, s));
 }
 
@@ -431,7 +434,7 @@ kvattn_status kvattn_append_decode(const kvattn_geom* geom, const float* k_new, 
   return launched(launch_summarize(k_pool, page_table, geom->n_kv_heads, geom->n_phys_pages,
                                    n_logical_pages, (int32_t)first,
                                    (int32_t)(last_full - first + 1), k_summary,
-                                   geom->k_type == KVATTN_K_Q4_0,
+                                   geom->k_type,
                                    static_cast<hipStream_t>(stream)));
 }
 
@@ -554,7 +557,7 @@ kvattn_status kvattn_gather_blocks(const kvattn_geom* geom, const uint8_t* src_k
   return launched(launch_gather(static_cast<const uint8_t*>(sk), static_cast<const uint8_t*>(sv),
                                 page_table, n_logical_pages, geom->n_phys_pages, blocks, n_blk,
                                 n_sel, geom->n_kv_heads, dst_k_pool, dst_v_pool, dst_blocks,
-                                geom->v_type == KVATTN_V_Q8_0, geom->k_type == KVATTN_K_Q4_0,
+                                geom->v_type == KVATTN_V_Q8_0, geom->k_type,
                                 static_cast<hipStream_t>(stream)));
 }
 

@@ -13,8 +13,15 @@ constexpr int V_REC = 18432;      // bytes per (page, KV head) value record, Q4_
 constexpr int V8_REC = 34816;     // the same with Q8_0 values (laid out like a key record)
 constexpr int K4_REC = 18432;     // bytes per key record with Q4_0 keys
 constexpr int K4_SCALE_OFF = 16384;
+constexpr int K5_REC = 24576;     // bytes per key record with Q5_1 keys
+constexpr int K5_HI_OFF = 16384;  // fifth bits: byte t*32 + w for dims 8w..8w+7
+constexpr int K5_D_OFF = 20480;   // scales d
+constexpr int K5_M_OFF = 22528;   // minimums m
 constexpr int K_SCALE_OFF = 32768;
 constexpr int V_SCALE_OFF = 16384;
+// Key record size and scale offset by key type (0 Q8_0, 1 Q4_0, 2 Q5_1).
+template <int KT> constexpr int KREC_OF = KT == 0 ? K_REC : KT == 1 ? K4_REC : K5_REC;
+template <int KT> constexpr int KSCALE_OF = KT == 0 ? K_SCALE_OFF : KT == 1 ? K4_SCALE_OFF : K5_D_OFF;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -99,6 +106,23 @@ __device__ __forceinline__ half8_t v_codes_to_f16_m(uint32_t w, uint32_t mask) {
 __device__ __forceinline__ half8_t k4_codes_to_f16(uint32_t w, uint32_t mask, half2_t d2) {
   const half8_t d8 = __builtin_shufflevector(d2, d2, 0, 1, 0, 1, 0, 1, 0, 1);
   return v_codes_to_f16_m(w, mask) * d8;
+}
+
+// One Q5_1 key word (low nibbles as a Q4_0 key word) and its byte e of fifth
+// bits (dim 8w + 2p at bit p, 8w + 2p + 1 at bit 4 + p) -> eight f16 values
+// d * code + m (one rounding); d2, m2 hold the block's d and m in both halves.
+__device__ __forceinline__ half8_t k5_codes_to_f16(uint32_t w, uint32_t e, half2_t d2, half2_t m2) {
+  const uint32_t hs = ((e & 0xFu) << 4) | ((e & 0xF0u) << 16);
+  const half2_t off = {(_Float16)1024.0f, (_Float16)1024.0f};
+  half8_t r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t c = ((w >> (4 * p)) & 0x000F000Fu) | ((hs >> p) & 0x00100010u);
+    const half2_t v = __builtin_elementwise_fma(as_h2(c | 0x64006400u) - off, d2, m2);
+    r[2 * p] = v[0];
+    r[2 * p + 1] = v[1];
+  }
+  return r;
 }
 
 __device__ __forceinline__ u32x4 load16(const uint8_t* p) {

@@ -48,14 +48,17 @@ constexpr int SLOW_SHARE = 12;          // 32nds of a split's units for waves 4-
 //   [8832, 12928)  value words (4 x 1 KB, lane-ordered: each lane reads its own);
 //   [12928, 13440) value scales.
 // With Q8_0 values the value codes take 8 x 1 KB (lane-ordered the same way),
-// the scales follow at 17024 and a slot is 17536 bytes. With Q4_0 keys (K4)
+// the scales follow at 17024 and a slot is 17536 bytes. With Q4_0 keys (KT)
 // the key codes take 4 loads of 8 token rows (128 B each) placed at
 // k4base(i), 4288 bytes in all, and everything after moves down.
 constexpr int SLOT_K = 0;
-template <bool K4> constexpr int SLOT_KS = K4 ? 4288 : 8320;
-template <bool K4> constexpr int SLOT_V = SLOT_KS<K4> + 512;
-template <bool K4, bool V8> constexpr int SLOT_VS = SLOT_V<K4> + (V8 ? 8192 : 4096);
-template <bool K4, bool V8> constexpr int SLOT_BYTES = SLOT_VS<K4, V8> + 512;
+// With Q5_1 keys (KT 2) the 32 rows' bytes of fifth bits (1 KB) follow the
+// nibbles at 4288, the scales d sit at 5312 and the minimums m after them.
+constexpr int SLOT_KH = 4288;
+template <int KT> constexpr int SLOT_KS = KT == 0 ? 8320 : KT == 1 ? 4288 : 5312;
+template <int KT> constexpr int SLOT_V = SLOT_KS<KT> + (KT == 2 ? 1024 : 512);
+template <int KT, bool V8> constexpr int SLOT_VS = SLOT_V<KT> + (V8 ? 8192 : 4096);
+template <int KT, bool V8> constexpr int SLOT_BYTES = SLOT_VS<KT, V8> + 512;
 constexpr int Q_LDS_STRIDE = 264;       // halves per query row in LDS (256 + pad)
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -95,7 +98,7 @@ __device__ __forceinline__ void wait_loads() {
 //            9 loads with Q8_0 values (8 x 1 KB codes + scales).
 // Lane (r16, g) brings exactly the 16-byte code chunks it will feed to the
 // matrix cores, so those LDS reads are lane-local and conflict-free.
-template <bool K4> constexpr int K_LOADS = K4 ? 5 : 9;
+template <int KT> constexpr int K_LOADS = KT == 0 ? 9 : KT == 1 ? 5 : 7;
 template <bool V8> constexpr int V_LOADS = V8 ? 9 : 5;
 
 // LDS base of key load i (4 token rows): 1 KB apart plus a 16-byte shift per
@@ -111,16 +114,19 @@ __device__ __forceinline__ int kpos(int a, int s) { return 16 * a + ((s + 4 * a)
 __device__ __forceinline__ int k4base(int i) { return i * 1088; }
 __device__ __forceinline__ int k4pos(int a, int s) { return a * 128 + 16 * (s ^ (a >> 1)); }
 
-template <bool K4>
+template <int KT>
 __device__ __forceinline__ void issue_keys(uint8_t* slot, const uint8_t* krec, int c) {
-  if constexpr (K4) {
-    const __amdgpu_buffer_rsrc_t r = record(krec, K4_REC);
+  if constexpr (KT != 0) {
+    const __amdgpu_buffer_rsrc_t r = record(krec, KREC_OF<KT>);
     const int lane = opaque_lane();
     const int a = lane >> 3, s = (lane & 7) ^ (a >> 1);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       dma16(r, a * 128 + 16 * s, (c * 32 + 8 * i) * 128, slot + SLOT_K + k4base(i));
-    if (lane < 32) dma16(r, lane * 16, K4_SCALE_OFF + c * 512, slot + SLOT_KS<true>);
+    if constexpr (KT == 2) dma16(r, lane * 16, K5_HI_OFF + c * 1024, slot + SLOT_KH);
+    if (lane < 32) dma16(r, lane * 16, KSCALE_OF<KT> + c * 512, slot + SLOT_KS<KT>);
+    if constexpr (KT == 2)
+      if (lane < 32) dma16(r, lane * 16, K5_M_OFF + c * 512, slot + SLOT_KS<KT> + 512);
     return;
   }
   const __amdgpu_buffer_rsrc_t r = record(krec, K_REC);
@@ -129,19 +135,19 @@ __device__ __forceinline__ void issue_keys(uint8_t* slot, const uint8_t* krec, i
   const int a = lane >> 4, s = ((lane & 15) - 4 * a) & 15;
 #pragma unroll
   for (int i = 0; i < 8; ++i) dma16(r, a * D + 16 * s, (c * 32 + 4 * i) * D, slot + SLOT_K + kbase(i));
-  if (lane < 32) dma16(r, lane * 16, K_SCALE_OFF + c * 512, slot + SLOT_KS<false>);
+  if (lane < 32) dma16(r, lane * 16, K_SCALE_OFF + c * 512, slot + SLOT_KS<0>);
 }
 
-template <bool K4, bool V8>
+template <int KT, bool V8>
 __device__ __forceinline__ void issue_values(uint8_t* slot, const uint8_t* vrec, int c) {
   constexpr int NQ = V8 ? 8 : 4;
   const __amdgpu_buffer_rsrc_t r = record(vrec, V8 ? V8_REC : V_REC);
   // value codes are stored lane-ordered: load q of group c is 1 KB at (NQ*c + q) KB
   const int lane = opaque_lane();
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) dma16(r, lane * 16, (c * NQ + q) * 1024, slot + SLOT_V<K4> + q * 1024);
+  for (int q = 0; q < NQ; ++q) dma16(r, lane * 16, (c * NQ + q) * 1024, slot + SLOT_V<KT> + q * 1024);
   if (lane < 32)
-    dma16(r, lane * 16, (V8 ? K_SCALE_OFF : V_SCALE_OFF) + c * 512, slot + SLOT_VS<K4, V8>);
+    dma16(r, lane * 16, (V8 ? K_SCALE_OFF : V_SCALE_OFF) + c * 512, slot + SLOT_VS<KT, V8>);
 }
 
 
@@ -154,19 +160,25 @@ struct State {
   floatx4 o[NT][16];      // O^T accumulators: dims 16mt + 4g + i, row nt*16 + r16
 };
 
-template <int NT, bool K4, bool V8, typename MidFn>
+template <int NT, int KT, bool V8, typename MidFn>
 __device__ __forceinline__ void compute_tile(State<NT>& st, const uint8_t* slot, int64_t tok0,
                                              int64_t kv_len, int64_t min_limit, int lane, int r16,
                                              int g, uint32_t nib_mask, MidFn&& after_keys) {
   // ---- S^T = Khat . Q'^T --------------------------------------------------
   // Both 16-token halves (m) share each q' operand read.
   floatx4 s[2][NT];
-  half2_t dlo[2], dhi[2];
+  half2_t dlo[2], dhi[2], mlo[2], mhi[2];
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
-    const uint32_t sw = *reinterpret_cast<const uint32_t*>(slot + SLOT_KS<K4> + (16 * m + r16) * 16 + 4 * g);
+    const uint32_t sw = *reinterpret_cast<const uint32_t*>(slot + SLOT_KS<KT> + (16 * m + r16) * 16 + 4 * g);
     dlo[m] = as_h2((sw & 0xFFFFu) | (sw << 16));
     dhi[m] = as_h2((sw >> 16) | (sw & 0xFFFF0000u));
+    if constexpr (KT == 2) {  // block minimums, laid out as the scales
+      const uint32_t mw =
+          *reinterpret_cast<const uint32_t*>(slot + SLOT_KS<KT> + 512 + (16 * m + r16) * 16 + 4 * g);
+      mlo[m] = as_h2((mw & 0xFFFFu) | (mw << 16));
+      mhi[m] = as_h2((mw >> 16) | (mw & 0xFFFF0000u));
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) s[m][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
@@ -175,7 +187,7 @@ __device__ __forceinline__ void compute_tile(State<NT>& st, const uint8_t* slot,
   int ln = lane;
   __asm__ volatile("" : "+v"(ln));
   const int kr16 = ln & 15, kg = ln >> 4;
-  if constexpr (K4) {
+  if constexpr (KT != 0) {
     // dims 64g + 8ks .. +7 are word 8g + ks of the row: chunk 2g + ks/4, word ks%4
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -187,7 +199,12 @@ __device__ __forceinline__ void compute_tile(State<NT>& st, const uint8_t* slot,
         for (int m = 0; m < 2; ++m) {
           const uint32_t w = *reinterpret_cast<const uint32_t*>(
               slot + SLOT_K + k4base(2 * m + (kr16 >> 3)) + k4pos(kr16 & 7, 2 * kg + hh) + 4 * q4);
-          a[m] = k4_codes_to_f16(w, nib_mask, hh ? dhi[m] : dlo[m]);
+          if constexpr (KT == 2) {
+            const uint32_t e = slot[SLOT_KH + (16 * m + kr16) * 32 + 8 * kg + ks];
+            a[m] = k5_codes_to_f16(w, e, hh ? dhi[m] : dlo[m], hh ? mhi[m] : mlo[m]);
+          } else {
+            a[m] = k4_codes_to_f16(w, nib_mask, hh ? dhi[m] : dlo[m]);
+          }
         }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -285,21 +302,21 @@ __device__ __forceinline__ void compute_tile(State<NT>& st, const uint8_t* slot,
   // block b (two dim tiles), read one block ahead.
   u32x4 vw[4];
   if constexpr (V8) {
-    vw[0] = *reinterpret_cast<const u32x4*>(slot + SLOT_V<K4> + lane * 16);
+    vw[0] = *reinterpret_cast<const u32x4*>(slot + SLOT_V<KT> + lane * 16);
   } else {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      vw[q] = *reinterpret_cast<const u32x4*>(slot + SLOT_V<K4> + q * 1024 + lane * 16);
+      vw[q] = *reinterpret_cast<const u32x4*>(slot + SLOT_V<KT> + q * 1024 + lane * 16);
   }
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
     u32x4 v8cur;
     if constexpr (V8) {
       v8cur = vw[0];
-      if (b < 7) vw[0] = *reinterpret_cast<const u32x4*>(slot + SLOT_V<K4> + (b + 1) * 1024 + lane * 16);
+      if (b < 7) vw[0] = *reinterpret_cast<const u32x4*>(slot + SLOT_V<KT> + (b + 1) * 1024 + lane * 16);
     }
     const u32x4 sc =
-        *reinterpret_cast<const u32x4*>(slot + SLOT_VS<K4, V8> + (b * 4 + g) * 16) & vmask;
+        *reinterpret_cast<const u32x4*>(slot + SLOT_VS<KT, V8> + (b * 4 + g) * 16) & vmask;
     const uint32_t scw[4] = {sc.x, sc.y, sc.z, sc.w};
     half8_t bb[NT];
 #pragma unroll
@@ -379,7 +396,7 @@ __device__ __forceinline__ void append_load(const DecodeParams& p, const AppendT
 }
 
 // Requests the first slots' inputs and the old words of partly new V words.
-template <bool K4, bool V8>
+template <int KT, bool V8>
 __device__ __forceinline__ void append_issue(const DecodeParams& p, AppendTile& a, int h, int c,
                                              int64_t first_new, int lane) {
   a.ub = (int)(first_new > a.tok ? first_new - a.tok : 0);
@@ -406,11 +423,11 @@ __device__ __forceinline__ void append_issue(const DecodeParams& p, AppendTile& 
 }
 
 // Quantises every new slot of the tile and writes codes, scales and words.
-template <bool K4, bool V8>
+template <int KT, bool V8>
 __device__ __forceinline__ void append_finish(const DecodeParams& p, AppendTile& a, int h, int c,
                                               int64_t first_new, int lane) {
   const int b = lane >> 3, s = lane & 7;
-  uint8_t* krec = p.k_pool_w + a.rec * (K4 ? K4_REC : K_REC);
+  uint8_t* krec = p.k_pool_w + a.rec * (KREC_OF<KT>);
   uint8_t* vrec = p.v_pool_w + a.rec * (V8 ? V8_REC : V_REC);
   uint32_t acc[4][4] = {};
   for (int u0 = a.ub; u0 < a.ue; u0 += 4) {
@@ -422,7 +439,40 @@ __device__ __forceinline__ void append_finish(const DecodeParams& p, AppendTile&
       const int t = c * 32 + u;
       const float xe[4] = {a.x[k].x, a.x[k].y, a.x[k].z, a.x[k].w};
       const float ye[4] = {a.y[k].x, a.y[k].y, a.y[k].z, a.y[k].w};
-      if constexpr (K4) {  // keys: Q4_0, the value rule
+      if constexpr (KT == 2) {  // keys: Q5_1 from the block's extremes
+        float mn = fminf(fminf(xe[0], xe[1]), fminf(xe[2], xe[3]));
+        float mx = fmaxf(fmaxf(xe[0], xe[1]), fmaxf(xe[2], xe[3]));
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) {
+          mn = fminf(mn, __shfl_xor(mn, o));
+          mx = fmaxf(mx, __shfl_xor(mx, o));
+        }
+        const _Float16 d16 = q5_scale(mx, mn), m16 = (_Float16)mn;
+        const float dk = (float)d16, mk = (float)m16;
+        const bool live = dk != 0.0f;
+        const float inv = live ? 1.0f / dk : 0.0f;
+        uint32_t part = 0u, hpart = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t code = live ? q5_code(xe[j], mk, inv) : 0u;
+          const int k = 4 * (s & 1) + j;
+          part |= (code & 0xFu) << v_slot_bit(k);
+          hpart |= (code >> 4) << k5_hi_bit(k);
+        }
+        const uint32_t word = part | __shfl_xor(part, 1);
+        const uint32_t hbyte = hpart | __shfl_xor(hpart, 1);
+        const int wi = 4 * b + (s >> 1);
+        if ((s & 1) == 0) {
+          *reinterpret_cast<uint32_t*>(krec + t * (D / 2) + 4 * wi) = word;
+          krec[K5_HI_OFF + t * 32 + wi] = (uint8_t)hbyte;
+        }
+        if (s == 0) {
+          *reinterpret_cast<uint16_t*>(krec + K5_D_OFF + (t * 8 + b) * 2) =
+              live ? __builtin_bit_cast(uint16_t, d16) : (uint16_t)0;
+          *reinterpret_cast<uint16_t*>(krec + K5_M_OFF + (t * 8 + b) * 2) =
+              __builtin_bit_cast(uint16_t, m16);
+        }
+      } else if constexpr (KT == 1) {  // keys: Q4_0, the value rule
         float ak = fabsf(xe[0]), mk = xe[0];
         int ik = 4 * s;
 #pragma unroll
@@ -550,7 +600,7 @@ __device__ __forceinline__ void append_finish(const DecodeParams& p, AppendTile&
 // a SIMD (two 4-wave workgroups or one 8-wave workgroup per CU), so every
 // lane may hold up to 256 VGPRs. With 8 waves, waves 4-7 stream the first
 // SLOW_SHARE/32 of the split's units and waves 0-3 the rest. V8: Q8_0 values.
-template <int NT, int WAVES, bool K4, bool V8>
+template <int NT, int WAVES, int KT, bool V8>
 __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
   constexpr int THREADS = 64 * WAVES;
   constexpr int NH = WAVES / 4;  // halves of the workgroup streaming a split
@@ -568,8 +618,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
   const int n_heads = p.n_kv * p.gqa;
   constexpr int Q_BYTES = ((NT * 16 * Q_LDS_STRIDE * 2) + 1023) / 1024 * 1024;
   constexpr int VREC = V8 ? V8_REC : V_REC;
-  constexpr int KREC = K4 ? K4_REC : K_REC;
-  uint8_t* slots = smem_raw + Q_BYTES + wave * SLOT_BYTES<K4, V8>;
+  constexpr int KREC = KREC_OF<KT>;
+  uint8_t* slots = smem_raw + Q_BYTES + wave * SLOT_BYTES<KT, V8>;
 
   _Float16* q_lds = reinterpret_cast<_Float16*>(smem_raw);
   State<NT> st;
@@ -665,18 +715,18 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
         }
       }
       if (n_tiles > 64 && i0 > 0) refill(0);  // the loop starts from the first 64 units
-      if (app) append_issue<K4, V8>(p, at, h, c, first_new, lane);
+      if (app) append_issue<KT, V8>(p, at, h, c, first_new, lane);
     }
     const bool first_new_tile = app && valid && tok + 32 > first_new;
     if (!first_new_tile) {
-      issue_keys<K4>(slot, p.k_pool + rec * KREC, valid ? c : 0);
-      issue_values<K4, V8>(slot, p.v_pool + rec * VREC, valid ? c : 0);
+      issue_keys<KT>(slot, p.k_pool + rec * KREC, valid ? c : 0);
+      issue_values<KT, V8>(slot, p.v_pool + rec * VREC, valid ? c : 0);
     }
     if (first_new_tile) {
-      append_finish<K4, V8>(p, at, h, c, first_new, lane);
+      append_finish<KT, V8>(p, at, h, c, first_new, lane);
       wait_loads<0>();  // this wave's stores have completed
-      issue_keys<K4>(slot, p.k_pool + rec * KREC, c);
-      issue_values<K4, V8>(slot, p.v_pool + rec * VREC, c);
+      issue_keys<KT>(slot, p.k_pool + rec * KREC, c);
+      issue_values<KT, V8>(slot, p.v_pool + rec * VREC, c);
     }
     app_pending = app && !first_new_tile;
   }
@@ -710,7 +760,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
     }
   }
   __syncthreads();
-  if (app_pending) append_finish<K4, V8>(p, at, h, c, first_new, lane);
+  if (app_pending) append_finish<KT, V8>(p, at, h, c, first_new, lane);
   for (int i = 0; i < n_tiles; ++i) {
     const bool more = i + 1 < n_tiles;
     if (more) locate(i + 1, tok_n, valid_n, rec_n);
@@ -722,20 +772,20 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
     auto refill_keys = [&] {
       if (more) {
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): key reads of this slot are done
-        issue_keys<K4>(slot, p.k_pool + rec_n * KREC, valid_n ? c : 0);
-        wait_loads<K_LOADS<K4>>();  // values of tile i have landed
+        issue_keys<KT>(slot, p.k_pool + rec_n * KREC, valid_n ? c : 0);
+        wait_loads<K_LOADS<KT>>();  // values of tile i have landed
       } else {
         wait_loads<0>();
       }
     };
     if (valid) {
-      compute_tile<NT, K4, V8>(st, slot, tok, p.kv_len, min_limit, lane, r16, g, nib_mask, refill_keys);
+      compute_tile<NT, KT, V8>(st, slot, tok, p.kv_len, min_limit, lane, r16, g, nib_mask, refill_keys);
     } else {
       refill_keys();
     }
     if (more) {
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): value reads of this slot are done
-      issue_values<K4, V8>(slot, p.v_pool + rec_n * VREC, valid_n ? c : 0);
+      issue_values<KT, V8>(slot, p.v_pool + rec_n * VREC, valid_n ? c : 0);
     }
     tok = tok_n;
     rec = rec_n;
@@ -808,18 +858,18 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
   }
 }
 
-template <int NT, bool K4, bool V8>
+template <int NT, int KT, bool V8>
 hipError_t launch_nt(const DecodeParams& p, hipStream_t stream) {
   const size_t combine = sizeof(float) * DECODE_WAVES * 16 * 260;
   const size_t qbytes = ((NT * 16 * Q_LDS_STRIDE * 2) + 1023) / 1024 * 1024;
-  const size_t loop = qbytes + DECODE_WAVES * SLOT_BYTES<K4, V8>;
+  const size_t loop = qbytes + DECODE_WAVES * SLOT_BYTES<KT, V8>;
   const size_t shmem = combine > loop ? combine : loop;
   static std::atomic<uint64_t> lds_set{0};
   const hipError_t e = set_lds_limit(
-      lds_set, reinterpret_cast<const void*>(&decode_kernel<NT, DECODE_WAVES, K4, V8>), shmem);
+      lds_set, reinterpret_cast<const void*>(&decode_kernel<NT, DECODE_WAVES, KT, V8>), shmem);
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)p.n_splits, (unsigned)p.n_kv);
-  hipLaunchKernelGGL((decode_kernel<NT, DECODE_WAVES, K4, V8>), grid, dim3(64 * DECODE_WAVES), shmem, stream, p);
+  hipLaunchKernelGGL((decode_kernel<NT, DECODE_WAVES, KT, V8>), grid, dim3(64 * DECODE_WAVES), shmem, stream, p);
   return hipGetLastError();
 }
 
@@ -827,12 +877,16 @@ hipError_t launch_nt(const DecodeParams& p, hipStream_t stream) {
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const int R = p.n_q_tok * p.gqa;
-  if (p.k_q4) {
-    if (p.v_q8) return R <= 16 ? launch_nt<1, true, true>(p, stream) : launch_nt<2, true, true>(p, stream);
-    return R <= 16 ? launch_nt<1, true, false>(p, stream) : launch_nt<2, true, false>(p, stream);
+  if (p.k_type == 2) {
+    if (p.v_q8) return R <= 16 ? launch_nt<1, 2, true>(p, stream) : launch_nt<2, 2, true>(p, stream);
+    return R <= 16 ? launch_nt<1, 2, false>(p, stream) : launch_nt<2, 2, false>(p, stream);
   }
-  if (p.v_q8) return R <= 16 ? launch_nt<1, false, true>(p, stream) : launch_nt<2, false, true>(p, stream);
-  return R <= 16 ? launch_nt<1, false, false>(p, stream) : launch_nt<2, false, false>(p, stream);
+  if (p.k_type == 1) {
+    if (p.v_q8) return R <= 16 ? launch_nt<1, 1, true>(p, stream) : launch_nt<2, 1, true>(p, stream);
+    return R <= 16 ? launch_nt<1, 1, false>(p, stream) : launch_nt<2, 1, false>(p, stream);
+  }
+  if (p.v_q8) return R <= 16 ? launch_nt<1, 0, true>(p, stream) : launch_nt<2, 0, true>(p, stream);
+  return R <= 16 ? launch_nt<1, 0, false>(p, stream) : launch_nt<2, 0, false>(p, stream);
 }
 
 }  // namespace kvattn

@@ -11,8 +11,8 @@ namespace {
 
 constexpr int GATHER_THREADS = 256;
 
-// grid (n_sel, n_kv); KREC, VREC the key and value record sizes (Q8_0 or
-// Q4_0 keys, Q4_0 or Q8_0 values). Workgroup (i, h) copies the key and value records of
+// grid (n_sel, n_kv); KREC, VREC the key and value record sizes (Q8_0,
+// Q4_0 or Q5_1 keys, Q4_0 or Q8_0 values). Workgroup (i, h) copies the key and value records of
 // logical page blocks[h][i] (row stride n_blk) into record i * n_kv + h of the
 // destination pools and writes dst_blocks[h][i] (row stride n_sel) = i, or -1
 // (nothing copied) when the entry or its physical page is out of range. Each
@@ -60,10 +60,11 @@ __global__ __launch_bounds__(GATHER_THREADS) void gather_kernel(
 hipError_t launch_gather(const uint8_t* src_k, const uint8_t* src_v, const int32_t* page_table,
                          int32_t n_logical, int32_t n_phys, const int32_t* blocks, int32_t n_blk,
                          int32_t n_sel, int32_t n_kv, uint8_t* dst_k, uint8_t* dst_v,
-                         int32_t* dst_blocks, bool v_q8, bool k_q4, hipStream_t stream) {
+                         int32_t* dst_blocks, bool v_q8, int k_type, hipStream_t stream) {
   dim3 grid((unsigned)n_sel, (unsigned)n_kv);
-  auto kern = k_q4 ? (v_q8 ? gather_kernel<K4_REC, V8_REC> : gather_kernel<K4_REC, V_REC>)
-                   : (v_q8 ? gather_kernel<K_REC, V8_REC> : gather_kernel<K_REC, V_REC>);
+  auto kern = k_type == 2   ? (v_q8 ? gather_kernel<K5_REC, V8_REC> : gather_kernel<K5_REC, V_REC>)
+              : k_type == 1 ? (v_q8 ? gather_kernel<K4_REC, V8_REC> : gather_kernel<K4_REC, V_REC>)
+                            : (v_q8 ? gather_kernel<K_REC, V8_REC> : gather_kernel<K_REC, V_REC>);
   hipLaunchKernelGGL(kern, grid, dim3(GATHER_THREADS), 0, stream, src_k, src_v,
                      page_table, n_logical, n_phys, blocks, n_blk, n_kv, dst_k, dst_v,
                      dst_blocks);

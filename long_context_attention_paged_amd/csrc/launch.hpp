@@ -26,12 +26,12 @@ inline hipError_t set_lds_limit(std::atomic<uint64_t>& done, const void* kernel,
 
 hipError_t launch_quantize(const float* k, const float* v, int64_t pos0, int32_t n_tok,
                            int32_t n_kv, const int32_t* page_table, int32_t n_phys,
-                           uint8_t* k_pool, uint8_t* v_pool, bool v_q8, bool k_q4,
+                           uint8_t* k_pool, uint8_t* v_pool, bool v_q8, int k_type,
                            hipStream_t stream);
 
 hipError_t launch_summarize(const uint8_t* k_pool, const int32_t* page_table, int32_t n_kv,
                             int32_t n_phys, int32_t n_logical, int32_t first_page,
-                            int32_t n_pages, float* k_summary, bool k_q4, hipStream_t stream);
+                            int32_t n_pages, float* k_summary, int k_type, hipStream_t stream);
 
 hipError_t launch_score(const float* q, const float* k_summary, int32_t n_kv, int32_t gqa,
                         int32_t n_logical, int32_t n_cand, double* scores,
@@ -67,7 +67,7 @@ struct DecodeParams {
   uint8_t* v_pool_w;
   int32_t n_new;
   int32_t v_q8;              // value records hold Q8_0 codes (else Q4_0)
-  int32_t k_q4;              // key records hold Q4_0 codes (else Q8_0)
+  int32_t k_type;            // key records: 0 Q8_0, 1 Q4_0, 2 Q5_1
 };
 
 // Wavefronts per decode workgroup. The kernel is sized for one workgroup of
@@ -93,7 +93,7 @@ struct PrefillParams {
   int32_t n_phys;
   float qscale;
   int32_t v_q8;              // value records hold Q8_0 codes (else Q4_0)
-  int32_t k_q4;              // key records hold Q4_0 codes (else Q8_0)
+  int32_t k_type;            // key records: 0 Q8_0, 1 Q4_0, 2 Q5_1
 };
 
 int32_t prefill_rows_per_tile();
@@ -102,7 +102,7 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_gather(const uint8_t* src_k, const uint8_t* src_v, const int32_t* page_table,
                          int32_t n_logical, int32_t n_phys, const int32_t* blocks, int32_t n_blk,
                          int32_t n_sel, int32_t n_kv, uint8_t* dst_k, uint8_t* dst_v,
-                         int32_t* dst_blocks, bool v_q8, bool k_q4, hipStream_t stream);
+                         int32_t* dst_blocks, bool v_q8, int k_type, hipStream_t stream);
 
 hipError_t launch_rotate(float* x, int64_t n_rows, hipStream_t stream);
 

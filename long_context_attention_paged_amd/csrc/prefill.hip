@@ -46,8 +46,10 @@ constexpr float PF_RESCALE_MARGIN = 8.0f;
 constexpr int RAW_K = 0, RAW_V = 1024;
 template <bool V8> constexpr int RAW_KS = V8 ? 2048 : 1536;
 template <bool V8> constexpr int RAW_VS = V8 ? 2112 : 1600;
-template <bool V8> constexpr int RAW_WAVE = V8 ? 2176 : 1664;
-template <bool V8> constexpr int RAW_STAGE = PF_WAVES * RAW_WAVE<V8>;
+// Q5_1 keys add the 4 rows' bytes of fifth bits (128 B, after the 512 B of
+// nibbles) and 4 x 16 B of block minimums after the scales.
+template <int KT, bool V8> constexpr int RAW_WAVE = (V8 ? 2176 : 1664) + (KT == 2 ? 64 : 0);
+template <int KT, bool V8> constexpr int RAW_STAGE = PF_WAVES * RAW_WAVE<KT, V8>;
 constexpr int RAW_DEPTH = 2;                    // sub-tile i+2 refills sub-tile i's slot
 constexpr int RAW_LOADS = 3;                    // direct loads per wave per sub-tile
 
@@ -98,13 +100,18 @@ __device__ __forceinline__ void signal_count(int* c, int lane) {
 //    blocks 2q, 2q+1, 512 consecutive bytes each (lanes 0-31, 32-63);
 //  - scales (lanes 0-7): key rows 4w..4w+3 (16 B each), then value blocks
 //    2q, 2q+1 for the two lane groups (16 B each).
-// With Q4_0 keys (K4) lanes 0-31 fetch row 4w + i%4, block (i/4)%8 (16 B:
+// With Q4_0 keys (KT) lanes 0-31 fetch row 4w + i%4, block (i/4)%8 (16 B:
 // the block's 32 nibbles).
-template <bool K4, bool V8>
+template <int KT, bool V8>
 __device__ __forceinline__ void issue_raw(uint8_t* raw, const uint8_t* krec, const uint8_t* vrec,
                                           int c, int w, int lane) {
   const int q = w >> 1, gh = w & 1;
-  if constexpr (K4) {
+  if constexpr (KT == 2) {  // lanes 32-39: the fifth bits of rows 4w..4w+3 (32 B each)
+    const uint8_t* src =
+        lane < 32 ? krec + (c * 32 + 4 * w + (lane & 3)) * (D / 2) + 16 * ((lane >> 2) & 7)
+                  : krec + K5_HI_OFF + (c * 32 + 4 * w + ((lane - 32) >> 1)) * 32 + 16 * (lane & 1);
+    if (lane < 40) dma16(src, raw + RAW_K);
+  } else if constexpr (KT == 1) {
     if (lane < 32)
       dma16(krec + (c * 32 + 4 * w + (lane & 3)) * (D / 2) + 16 * ((lane >> 2) & 7), raw + RAW_K);
   } else {
@@ -116,11 +123,12 @@ __device__ __forceinline__ void issue_raw(uint8_t* raw, const uint8_t* krec, con
           raw + RAW_V);
   else if (lane < 32)
     dma16(vrec + (((c * 4 + q) * 4 + 2 * gh) * 64) * 4 + lane * 16, raw + RAW_V);
-  if (lane < 8) {
+  if (lane < (KT == 2 ? 12 : 8)) {  // lanes 8-11: Q5_1 block minimums of rows 4w..4w+3
     const int vs_off = V8 ? K_SCALE_OFF : V_SCALE_OFF;
     const uint8_t* src =
-        lane < 4 ? krec + (K4 ? K4_SCALE_OFF : K_SCALE_OFF) + (c * 32 + 4 * w + lane) * 16
-                 : vrec + vs_off + ((c * 8 + 2 * q + ((lane - 4) >> 1)) * 4 + 2 * gh + (lane & 1)) * 16;
+        lane < 4   ? krec + KSCALE_OF<KT> + (c * 32 + 4 * w + lane) * 16
+        : lane < 8 ? vrec + vs_off + ((c * 8 + 2 * q + ((lane - 4) >> 1)) * 4 + 2 * gh + (lane & 1)) * 16
+                   : krec + K5_M_OFF + (c * 32 + 4 * w + lane - 8) * 16;
     dma16(src, raw + RAW_KS<V8>);
   }
 }
@@ -182,7 +190,7 @@ __device__ __forceinline__ RawIn read_raw(const uint8_t* k, const uint8_t* v, co
 // Values, lane (d, ep, gl) = (l%16, (l/16)%2, l/32): words e = 2ep, 2ep+1 of
 // dim group q = w/2, lane group g = 2(w%2) + gl; with Q8_0 values the same
 // dims are the lane's 16-byte piece (row d) of block 2q + ep.
-template <bool K4, bool V8>
+template <int KT, bool V8>
 __device__ __forceinline__ void dequant_raw(const uint8_t* raw, _Float16* stage, int w, int ln,
                                             int n_live) {
   const int u = ln & 3, b = (ln >> 2) & 7, hh = ln >> 5;
@@ -191,7 +199,7 @@ __device__ __forceinline__ void dequant_raw(const uint8_t* raw, _Float16* stage,
   RawIn in;
   u32x4 v8 = {0u, 0u, 0u, 0u};
   // Q4_0 keys: the lane's block chunk (row u, block b) is lane l%32's load
-  const int koff = K4 ? (ln & 31) * 16 : ln * 16;
+  const int koff = KT != 0 ? (ln & 31) * 16 : ln * 16;
   if constexpr (V8) {
     const RawIn8 r8 = read_raw8(raw + RAW_K + koff, raw + RAW_V + (ep * 32 + gl * 16 + d) * 16,
                                 raw + RAW_VS<V8> + (ep * 2 + gl) * 16,
@@ -212,7 +220,22 @@ __device__ __forceinline__ void dequant_raw(const uint8_t* raw, _Float16* stage,
     if (!full && 4 * w + u >= n_live) dw = 0u;  // zero scale -> zeros
     const half2_t d2 = as_h2(dw);
     _Float16* krow = stage + (4 * w + u) * K_LDS_STRIDE + 32 * b + 16 * hh;
-    if constexpr (K4) {  // words 4b + 2hh, +1: dims 32b + 16hh + 0..7, 8..15
+    if constexpr (KT == 2) {  // as Q4_0, with the fifth bits and the block minimum
+      uint32_t kh, km;
+      __asm__ __volatile__(
+          "ds_read_u16 %0, %2\n\t"
+          "ds_read_u16 %1, %3\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(kh), "=&v"(km)
+          : "v"(lds_addr(raw + RAW_K + 512 + u * 32 + 4 * b + 2 * hh)),
+            "v"(lds_addr(raw + RAW_KS<V8> + 128 + u * 16 + 2 * b))
+          : "memory");
+      uint32_t mw = km & 0xFFFFu;
+      if (!full && 4 * w + u >= n_live) mw = 0u;
+      const half2_t m2 = as_h2(mw | (mw << 16));
+      *reinterpret_cast<half8_t*>(krow + 0) = k5_codes_to_f16(hh ? in.k.z : in.k.x, kh & 0xFFu, d2, m2);
+      *reinterpret_cast<half8_t*>(krow + 8) = k5_codes_to_f16(hh ? in.k.w : in.k.y, (kh >> 8) & 0xFFu, d2, m2);
+    } else if constexpr (KT == 1) {  // words 4b + 2hh, +1: dims 32b + 16hh + 0..7, 8..15
       *reinterpret_cast<half8_t*>(krow + 0) = k4_codes_to_f16(hh ? in.k.z : in.k.x, 0x000F000Fu, d2);
       *reinterpret_cast<half8_t*>(krow + 8) = k4_codes_to_f16(hh ? in.k.w : in.k.y, 0x000F000Fu, d2);
     } else {
@@ -282,7 +305,7 @@ struct PageWindow {
   }
 };
 
-template <bool K4, bool V8>
+template <int KT, bool V8>
 __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
   _Float16* lds = reinterpret_cast<_Float16*>(lds_raw);                      // f16 stages
@@ -321,13 +344,13 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
   win.load(p, t, 0, h, lane);
   if (tid < 2 * N_STAGES) counters[tid] = 0;
 
-  uint8_t* const my_raw = raw_ring + wave * RAW_WAVE<V8>;
+  uint8_t* const my_raw = raw_ring + wave * RAW_WAVE<KT, V8>;
   auto issue = [&](int sub) {
     const int32_t r = win.record(sub);
     const int64_t rec = r >= 0 ? r : 0;  // unmapped pages load record 0, then zero it
     int ln = lane;
     __asm__ __volatile__("" : "+v"(ln));  // recompute lane offsets here, do not hold them
-    issue_raw<K4, V8>(my_raw + (sub % RAW_DEPTH) * RAW_STAGE<V8>, p.k_pool + rec * (K4 ? K4_REC : K_REC),
+    issue_raw<KT, V8>(my_raw + (sub % RAW_DEPTH) * RAW_STAGE<KT, V8>, p.k_pool + rec * KREC_OF<KT>,
                   p.v_pool + rec * (V8 ? V8_REC : V_REC), r >= 0 ? (sub & 3) : 0, wave, ln);
   };
   auto dequant = [&](int sub) {
@@ -335,7 +358,7 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
     const int n_live = win.record(sub) < 0 ? 0 : left >= 32 ? 32 : (int)left;
     int ln = lane;
     __asm__ __volatile__("" : "+v"(ln));  // recompute lane offsets here, do not hold them
-    dequant_raw<K4, V8>(my_raw + (sub % RAW_DEPTH) * RAW_STAGE<V8>,
+    dequant_raw<KT, V8>(my_raw + (sub % RAW_DEPTH) * RAW_STAGE<KT, V8>,
                     lds + (sub % N_STAGES) * STAGE_HALVES, wave, ln, n_live);
   };
   // start the raw stream before anything else
@@ -537,23 +560,24 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
 
 int32_t prefill_rows_per_tile() { return PF_ROWS; }
 
-template <bool K4, bool V8>
+template <int KT, bool V8>
 hipError_t launch_prefill_v(const PrefillParams& p, hipStream_t stream) {
-  const size_t shmem = sizeof(_Float16) * N_STAGES * STAGE_HALVES + RAW_DEPTH * RAW_STAGE<V8>;
+  const size_t shmem = sizeof(_Float16) * N_STAGES * STAGE_HALVES + RAW_DEPTH * RAW_STAGE<KT, V8>;
   static std::atomic<uint64_t> lds_set{0};
   const hipError_t e =
-      set_lds_limit(lds_set, reinterpret_cast<const void*>(&prefill_kernel<K4, V8>), shmem);
+      set_lds_limit(lds_set, reinterpret_cast<const void*>(&prefill_kernel<KT, V8>), shmem);
   if (e != hipSuccess) return e;
   const int64_t rows_head = (int64_t)p.chunk * p.gqa;
   const unsigned n_qtiles = (unsigned)((rows_head + PF_ROWS - 1) / PF_ROWS);
   dim3 grid((unsigned)p.n_groups, n_qtiles, (unsigned)p.n_kv);
-  hipLaunchKernelGGL((prefill_kernel<K4, V8>), grid, dim3(PF_THREADS), shmem, stream, p);
+  hipLaunchKernelGGL((prefill_kernel<KT, V8>), grid, dim3(PF_THREADS), shmem, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-  if (p.k_q4) return p.v_q8 ? launch_prefill_v<true, true>(p, stream) : launch_prefill_v<true, false>(p, stream);
-  return p.v_q8 ? launch_prefill_v<false, true>(p, stream) : launch_prefill_v<false, false>(p, stream);
+  if (p.k_type == 2) return p.v_q8 ? launch_prefill_v<2, true>(p, stream) : launch_prefill_v<2, false>(p, stream);
+  if (p.k_type == 1) return p.v_q8 ? launch_prefill_v<1, true>(p, stream) : launch_prefill_v<1, false>(p, stream);
+  return p.v_q8 ? launch_prefill_v<0, true>(p, stream) : launch_prefill_v<0, false>(p, stream);
 }
 
 }  // namespace kvattn

@@ -34,6 +34,23 @@ __device__ __forceinline__ uint32_t q4_code(float y, float inv) {
   return (uint32_t)((int)r + 8);
 }
 
+// Q5_1 block scale from the block's extremes: RN16(RN32((mx - mn) / 31)).
+__device__ __forceinline__ _Float16 q5_scale(float mx, float mn) {
+#pragma clang fp contract(off)
+  return (_Float16)((mx - mn) / 31.0f);
+}
+
+// Q5_1 code (0..31) of x under the stored minimum m and inv = RN32(1 / d):
+// clamp(rint(RN32(RN32(x - m) * inv)), 0, 31).
+__device__ __forceinline__ uint32_t q5_code(float x, float m, float inv) {
+#pragma clang fp contract(off)
+  const float r = fminf(fmaxf(rintf((x - m) * inv), 0.0f), 31.0f);
+  return (uint32_t)(int)r;
+}
+
+// Bit of dim 8w + k (k = 0..7) in the byte of fifth bits of word w.
+__device__ __forceinline__ int k5_hi_bit(int k) { return (k >> 1) + 4 * (k & 1); }
+
 // Bit offset of slot j (0..7) inside a V word: slot pairs share a byte.
 __device__ __forceinline__ int v_slot_bit(int j) { return 4 * (j >> 1) + 16 * (j & 1); }
 

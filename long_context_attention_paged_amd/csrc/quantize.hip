@@ -21,7 +21,7 @@ namespace {
 // are processed at once and each block's reductions stay in one thread.
 // Value codes go through LDS to be packed into the group's V words (Q4_0) or
 // reordered into the group's 16-byte lane pieces (Q8_0, V8 true).
-template <bool V8, bool K4>
+template <bool V8, int KT>
 __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ k,
                                                        const float* __restrict__ v, int64_t pos0,
                                                        int32_t n_tok, int32_t n_kv,
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
   const int c = (int)((gpos % PAGE) / 32);
   const int32_t phys = page_table[lp];
   if (phys < 0 || phys >= n_phys) return;  // uniform across the workgroup
-  uint8_t* krec = k_pool + ((int64_t)phys * n_kv + h) * (K4 ? K4_REC : K_REC);
+  uint8_t* krec = k_pool + ((int64_t)phys * n_kv + h) * (KREC_OF<KT>);
   uint8_t* vrec = v_pool + ((int64_t)phys * n_kv + h) * (V8 ? V8_REC : V_REC);
   uint32_t* vwords = reinterpret_cast<uint32_t*>(vrec) + c * 1024;
   const int64_t end = pos0 + n_tok;
@@ -63,7 +63,35 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
       x[4 * i] = a.x; x[4 * i + 1] = a.y; x[4 * i + 2] = a.z; x[4 * i + 3] = a.w;
       y[4 * i] = e.x; y[4 * i + 1] = e.y; y[4 * i + 2] = e.z; y[4 * i + 3] = e.w;
     }
-    if constexpr (K4) {  // Q4_0 keys: the value rule; word i of the block holds dims 8i..8i+7
+    if constexpr (KT == 2) {  // Q5_1 keys: word i of the block holds the low bits of dims 8i..8i+7
+      float mn = x[0], mx = x[0];
+#pragma unroll
+      for (int i = 1; i < 32; ++i) {
+        mn = fminf(mn, x[i]);
+        mx = fmaxf(mx, x[i]);
+      }
+      const _Float16 dk16 = q5_scale(mx, mn), mk16 = (_Float16)mn;
+      const float dk = (float)dk16, mk = (float)mk16;
+      const bool live = dk != 0.0f;
+      const float inv = live ? 1.0f / dk : 0.0f;
+      uint32_t kw[4], hb = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t wv = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t code = live ? q5_code(x[8 * i + j], mk, inv) : 0u;
+          wv |= (code & 0xFu) << v_slot_bit(j);
+          hb |= (code >> 4) << (8 * i + k5_hi_bit(j));
+        }
+        kw[i] = wv;
+      }
+      *reinterpret_cast<uint4*>(krec + t * (D / 2) + 16 * b) = uint4{kw[0], kw[1], kw[2], kw[3]};
+      *reinterpret_cast<uint32_t*>(krec + K5_HI_OFF + t * 32 + 4 * b) = hb;
+      *reinterpret_cast<uint16_t*>(krec + K5_D_OFF + (t * 8 + b) * 2) =
+          live ? __builtin_bit_cast(uint16_t, dk16) : (uint16_t)0;
+      *reinterpret_cast<uint16_t*>(krec + K5_M_OFF + (t * 8 + b) * 2) = __builtin_bit_cast(uint16_t, mk16);
+    } else if constexpr (KT == 1) {  // Q4_0 keys: the value rule; word i of the block holds dims 8i..8i+7
       float a = fabsf(x[0]), m = x[0];
 #pragma unroll
       for (int i = 1; i < 32; ++i)
@@ -225,8 +253,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
 // summary[h][p][n] = RN32(binary64 sum over slots t = 0..127 ascending of
 // d(t, n/32) * code(t, n), divided by 128). One workgroup per (page, head):
 // the record's codes and scales are staged in LDS with 16-byte loads, then
-// thread n sums its column in order. K4: Q4_0 key records.
-template <bool K4>
+// thread n sums its column in order. KT: Q4_0 key records.
+template <int KT>
 __global__ __launch_bounds__(256) void summarize_kernel(const uint8_t* __restrict__ k_pool,
                                                         const int32_t* __restrict__ page_table,
                                                         int32_t n_kv, int32_t n_phys,
@@ -238,8 +266,8 @@ __global__ __launch_bounds__(256) void summarize_kernel(const uint8_t* __restric
   const int32_t lp = first_page + blockIdx.x;
   const int32_t phys = page_table[lp];
   if (phys < 0 || phys >= n_phys) return;  // uniform across the workgroup
-  constexpr int REC = K4 ? K4_REC : K_REC;
-  constexpr int PIECES = (REC / 16 + 255) / 256;  // 9 (Q8_0 keys) or 5 (Q4_0)
+  constexpr int REC = KREC_OF<KT>;
+  constexpr int PIECES = (REC / 16 + 255) / 256;  // 9 (Q8_0 keys), 5 (Q4_0) or 6 (Q5_1)
   const uint8_t* krec = k_pool + ((int64_t)phys * n_kv + h) * REC;
   {  // the record's 16-byte pieces, PIECES per thread, issued together
     uint4 v[PIECES];
@@ -255,12 +283,19 @@ __global__ __launch_bounds__(256) void summarize_kernel(const uint8_t* __restric
     }
   }
   __syncthreads();
-  const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec + (K4 ? K4_SCALE_OFF : K_SCALE_OFF));
+  const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec + KSCALE_OF<KT>);
   double acc = 0.0;
   for (int t = 0; t < PAGE; ++t) {
     const float d = f16_value(sc[t * 8 + n / 32]);
     float code;
-    if constexpr (K4) {  // dim n = 8w + k: word w of row t, nibble at v_slot_bit(k)
+    if constexpr (KT == 2) {  // d * code + m in binary64, as the oracle's Q5_1 dequantisation
+      const uint32_t w = reinterpret_cast<const uint32_t*>(rec)[t * 32 + n / 8];
+      const uint32_t c5 = ((w >> v_slot_bit(n & 7)) & 0xFu) |
+                          (((uint32_t)rec[K5_HI_OFF + t * 32 + n / 8] >> k5_hi_bit(n & 7)) & 1u) << 4;
+      const double mk = (double)f16_value(reinterpret_cast<const uint16_t*>(rec + K5_M_OFF)[t * 8 + n / 32]);
+      acc = acc + ((double)d * (double)c5 + mk);
+      continue;
+    } else if constexpr (KT == 1) {  // dim n = 8w + k: word w of row t, nibble at v_slot_bit(k)
       const uint32_t w = reinterpret_cast<const uint32_t*>(rec)[t * 32 + n / 8];
       code = (float)((int)((w >> v_slot_bit(n & 7)) & 0xFu) - 8);
     } else {
@@ -276,12 +311,13 @@ __global__ __launch_bounds__(256) void summarize_kernel(const uint8_t* __restric
 
 hipError_t launch_quantize(const float* k, const float* v, int64_t pos0, int32_t n_tok,
                            int32_t n_kv, const int32_t* page_table, int32_t n_phys,
-                           uint8_t* k_pool, uint8_t* v_pool, bool v_q8, bool k_q4,
+                           uint8_t* k_pool, uint8_t* v_pool, bool v_q8, int k_type,
                            hipStream_t stream) {
   const int64_t g0 = pos0 / 32, g1 = (pos0 + n_tok - 1) / 32;
   dim3 grid((unsigned)(g1 - g0 + 1), (unsigned)n_kv);
-  auto kern = k_q4 ? (v_q8 ? quantize_kernel<true, true> : quantize_kernel<false, true>)
-                   : (v_q8 ? quantize_kernel<true, false> : quantize_kernel<false, false>);
+  auto kern = k_type == 2   ? (v_q8 ? quantize_kernel<true, 2> : quantize_kernel<false, 2>)
+              : k_type == 1 ? (v_q8 ? quantize_kernel<true, 1> : quantize_kernel<false, 1>)
+                            : (v_q8 ? quantize_kernel<true, 0> : quantize_kernel<false, 0>);
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, k, v, pos0, n_tok, n_kv,
                      page_table, n_phys, k_pool, v_pool);
   return hipGetLastError();
@@ -289,9 +325,10 @@ hipError_t launch_quantize(const float* k, const float* v, int64_t pos0, int32_t
 
 hipError_t launch_summarize(const uint8_t* k_pool, const int32_t* page_table, int32_t n_kv,
                             int32_t n_phys, int32_t n_logical, int32_t first_page,
-                            int32_t n_pages, float* k_summary, bool k_q4, hipStream_t stream) {
+                            int32_t n_pages, float* k_summary, int k_type, hipStream_t stream) {
   dim3 grid((unsigned)n_pages, (unsigned)n_kv);
-  hipLaunchKernelGGL(k_q4 ? summarize_kernel<true> : summarize_kernel<false>, grid, dim3(256), 0, stream, k_pool, page_table, n_kv,
+  auto kern = k_type == 2 ? summarize_kernel<2> : k_type == 1 ? summarize_kernel<1> : summarize_kernel<0>;
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, k_pool, page_table, n_kv,
                      n_phys, n_logical, first_page, k_summary);
   return hipGetLastError();
 }

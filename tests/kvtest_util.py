@@ -28,7 +28,8 @@ class Pools:
 
     def __init__(self, n_phys, n_kv, gqa, init_seed=None, v_type=0, k_type=0):
         self.n_phys, self.n_kv, self.gqa = n_phys, n_kv, gqa
-        k_rec = quant.K4_RECORD_BYTES if k_type == kv.K_Q4_0 else quant.K_RECORD_BYTES
+        k_rec = {kv.K_Q4_0: quant.K4_RECORD_BYTES,
+                 kv.K_Q5_1: quant.K5_RECORD_BYTES}.get(k_type, quant.K_RECORD_BYTES)
         shape_k = (n_phys, n_kv, k_rec)
         v_rec = quant.V8_RECORD_BYTES if v_type == kv.V_Q8_0 else quant.V_RECORD_BYTES
         shape_v = (n_phys, n_kv, v_rec)

@@ -299,11 +299,15 @@ def test_value_type_validation():
     assert kv.Geom(1, 1, 1, v_type=kv.V_Q8_0).v_record_bytes == 34816
     assert ctypes.sizeof(kv.Geom) == 28
     badk = geom()
-    badk.k_type = 2
-    assert decode(badk)[0] == E_UNSUPPORTED
     q4 = geom()
     q4.k_type = kv.K_Q4_0
     code, nb = decode(q4, ws=None)
     assert code == OK and nb > 0
     assert kv.Geom(1, 1, 1, k_type=kv.K_Q4_0).k_record_bytes == 18432
     assert kv.Geom(1, 1, 1).k_record_bytes == 34816
+    assert kv.Geom(1, 1, 1, k_type=kv.K_Q5_1).k_record_bytes == 24576
+    q5 = geom()
+    q5.k_type = kv.K_Q5_1
+    assert decode(q5, ws=None)[0] == OK
+    badk.k_type = 3
+    assert decode(badk)[0] == E_UNSUPPORTED

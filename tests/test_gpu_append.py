@@ -6,7 +6,7 @@ Per case, on pools pre-filled with random bytes and a permuted page table:
  - its out and lse equal kvattn_quantize_pages followed by kvattn_decode bit
    for bit, and the oracle's attention over the oracle's pool within the
    decode bar (2e-3 max-abs);
- - every key / value type pair: Q8_0 or Q4_0 keys (whole words per token),
+ - every key / value type pair: Q8_0, Q4_0 or Q5_1 keys (whole words per token),
    Q4_0 values (read-modify-write of shared words) or Q8_0 values (bytes);
  - with a summary array, the summary of a page the append completes equals
    the two-call path's and the oracle's bit for bit.
@@ -53,7 +53,8 @@ def plant_edges(Kn, Vn):
 
 
 @pytest.mark.parametrize("k_type,v_type", [(kv.K_Q8_0, kv.V_Q4_0), (kv.K_Q8_0, kv.V_Q8_0),
-                                            (kv.K_Q4_0, kv.V_Q4_0), (kv.K_Q4_0, kv.V_Q8_0)])
+                                            (kv.K_Q4_0, kv.V_Q4_0), (kv.K_Q4_0, kv.V_Q8_0),
+                                            (kv.K_Q5_1, kv.V_Q4_0)])
 @pytest.mark.parametrize("n_kv,gqa,n_q_tok,n_new,kv_len,n_splits,sparse", CASES)
 def test_append_decode_matches_quantize_then_decode(n_kv, gqa, n_q_tok, n_new, kv_len, n_splits,
                                                     sparse, k_type, v_type):

@@ -107,16 +107,17 @@ def test_decode_full_size_one_head(cfg, head):
     assert eo <= DEC_TOL and el <= 1e-3 and rr <= 2e-3, (eo, el, rr)
 
 
-@pytest.mark.parametrize("k_type,v_type", [(kv.K_Q8_0, kv.V_Q8_0), (kv.K_Q4_0, kv.V_Q4_0)])
+@pytest.mark.parametrize("k_type,v_type", [(kv.K_Q8_0, kv.V_Q8_0), (kv.K_Q4_0, kv.V_Q4_0),
+                                            (kv.K_Q5_1, kv.V_Q4_0)])
 def test_verify_full_size_other_pairs(k_type, v_type):
-    """verify-262k with the q8_0/q8_0 and q4_0/q4_0 caches: sampled pages bit
+    """verify-262k with the q8_0/q8_0, q4_0/q4_0 and q5_1/q4_0 caches: sampled pages bit
     for bit, one KV head's outputs against the oracle."""
     w = synth.WORKLOADS[3]
     L = FullLayer(w, k_type=k_type, v_type=v_type)
     L.check_pages(sample_pages(w, np.random.default_rng(7 + k_type)))
     out, lse = kv.kvattn_decode(L.geom, gpu(L.q), L.kp, L.vp, L.td, w.kv_len, 1 / 16)
     torch.cuda.synchronize()
-    head = 1 + k_type
+    head = (1 + k_type) % w.n_kv
     ok, ov = L.oracle_pool(head)
     rows = slice(head * w.gqa, (head + 1) * w.gqa)
     ref_o, ref_l = oracle.decode(L.q[:, rows], w.gqa, ok, ov, L.table, w.n_pages, w.kv_len,
