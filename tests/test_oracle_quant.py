@@ -51,6 +51,82 @@ def test_rn16_ieee_facts(x, expect):
     assert float(quant.rn16(np.float32(x))) == expect
 
 
+def _f16_finite_nonneg():
+    """Every non-negative finite binary16 value, ascending (bit patterns
+    0x0000 .. 0x7BFF decoded exactly), as binary64."""
+    return np.arange(0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def test_rn16_every_midpoint_and_neighbours():
+    """Exhaustive round-to-nearest-even to binary16: for every pair of
+    adjacent finite binary16 values a < b (both signs), the binary32 midpoint
+    (exact: it needs 12 significant bits) rounds to the one whose bit pattern
+    is even, and the binary32 numbers just below and just above it round to a
+    and to b. The top midpoint 65520 overflows to infinity (its even
+    neighbour 65536 is out of range) and the number below it gives 65504."""
+    v = _f16_finite_nonneg()
+    a, b = v[:-1], v[1:]
+    mid = ((a + b) / 2).astype(np.float32)
+    assert (mid.astype(np.float64) == (a + b) / 2).all()          # midpoints exact
+    even_is_a = (np.arange(len(a)) % 2) == 0                      # bit pattern of a even
+    want = np.where(even_is_a, a, b)
+    below = np.nextafter(mid, np.float32(-np.inf))
+    above = np.nextafter(mid, np.float32(np.inf))
+    for sign in (1.0, -1.0):
+        s32 = np.float32(sign)
+        assert (quant.rn16(s32 * mid).astype(np.float64) == sign * want).all()
+        assert (quant.rn16(s32 * below).astype(np.float64) == sign * a).all()
+        assert (quant.rn16(s32 * above).astype(np.float64) == sign * b).all()
+    top = np.float32(65520.0)
+    assert quant.rn16(top) == np.inf and quant.rn16(-top) == -np.inf
+    assert quant.rn16(np.nextafter(top, np.float32(0))) == 65504.0
+    # every binary16 value is a fixed point
+    assert (quant.rn16(v.astype(np.float32)).astype(np.float64) == v).all()
+
+
+def test_code_rounding_ties_go_to_even():
+    """Code rounding is rint, half to even (include/kvattn.h): hand-built
+    blocks whose products x * inv land exactly on k + 1/2. Rounding half away
+    from zero would give the codes in the comments instead."""
+    # Q8_0 with amax 127 -> d = 1, inv = 1
+    x = np.zeros(32, np.float32)
+    x[0] = 127.0
+    x[1:9] = [2.5, 3.5, -2.5, -3.5, 0.5, -0.5, 1.5, 126.5]
+    c, b = quant.q8_0_quantize(x)
+    assert quant.f16_from_bits(b) == 1.0
+    assert list(c[1:9]) == [2, 4, -2, -4, 0, 0, 2, 126]   # away: 3, 4, -3, -4, 1, -1, 2, 127
+    # Q4_0 with the extreme -8 at index 0 -> d = 1, inv = 1; code = rint(x) + 8
+    x = np.zeros(32, np.float32)
+    x[0] = -8.0
+    x[1:8] = [2.5, 3.5, -2.5, -3.5, 0.5, -0.5, 6.5]
+    c, b = quant.q4_0_quantize(x)
+    assert quant.f16_from_bits(b) == 1.0 and c[0] == 0
+    assert list(c[1:8]) == [10, 12, 6, 4, 8, 8, 14]       # away: 11, 12, 5, 4, 9, 7, 15
+    # Q5_1 with min 0 and max 31 -> d = 1, m = 0, inv = 1; code = rint(x)
+    x = np.zeros(32, np.float32)
+    x[31] = 31.0
+    x[1:7] = [2.5, 3.5, 10.5, 11.5, 0.5, 30.5]
+    c, db, mb = quant.q5_1_quantize(x)
+    assert quant.f16_from_bits(db) == 1.0 and quant.f16_from_bits(mb) == 0.0
+    assert list(c[1:7]) == [2, 4, 10, 12, 0, 30]          # away: 3, 4, 11, 12, 1, 31
+
+
+def test_q5_1_codes_use_the_stored_minimum():
+    """Q5_1 codes are taken from x - m with m the STORED binary16 minimum
+    (include/kvattn.h): block minimum 0.1f, which binary16 stores as
+    0.0999755859375 (bits 0x2E66), maximum 1.06875f, so d = RN16(0.96875 / 31)
+    = 2^-5 and inv = 32. For x = 0.42810997f, (x - m) * 32 = 10.5003 gives
+    code 11; the unrounded minimum would give 10.4995 and code 10."""
+    mn, mx, x5 = np.float32(0.1), np.float32(1.06875), np.float32(0.42810997)
+    blk = np.linspace(mn, mx, 32).astype(np.float32)
+    blk[0], blk[31], blk[5] = mn, mx, x5
+    c, db, mb = quant.q5_1_quantize(blk)
+    assert mb == 0x2E66 and quant.f16_from_bits(mb) == np.float32(0.0999755859375)
+    assert quant.f16_from_bits(db) == np.float32(2.0 ** -5)
+    assert c[5] == 11
+    assert c[0] == 0 and c[31] == 31
+
+
 def test_q8_0_closed_forms():
     # zero block: codes 0, scale +0 (bits 0x0000)
     c, b = quant.q8_0_quantize(np.zeros(32, np.float32))
