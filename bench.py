@@ -191,14 +191,14 @@ def bench_decode(w, dev, steps, warmup, sparse=False, v_type=0, k_type=0):
     def decode_call(layer):
         nonlocal ws
         if ws is None:
-            ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+            ws = kv.workspace(64 << 20, dev)
         kv.kvattn_decode(pools.geom, pools.q[layer], pools.kp[layer], pools.vp[layer],
                          pools.table, w.kv_len, 1.0 / 16.0,
                          blocks=blocks[layer] if sparse else None, out=outs[layer],
                          lse=lses[layer], workspace=ws)
 
-    sel_ws = torch.empty(8 << 20, dtype=torch.uint8, device=dev) if sparse else None
-    step_ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+    sel_ws = kv.workspace(8 << 20, dev) if sparse else None
+    step_ws = kv.workspace(64 << 20, dev)
 
     def step():
         # per layer: [select the blocks (kvmem)], then one launch that appends
@@ -336,7 +336,7 @@ def bench_prefill(w, dev, steps, warmup, v_type=0, k_type=0):
     pools = LayerPools(w, dev, v_type=v_type, k_type=k_type)
     outs = [torch.empty_like(q) for q in pools.q]
     lses = [torch.empty(q.shape[:2], dtype=torch.float32, device=dev) for q in pools.q]
-    ws = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    ws = kv.workspace(512 << 20, dev)
 
     def prefill_call(layer):
         kv.kvattn_prefill_chunk(pools.geom, pools.q[layer], pools.kp[layer], pools.vp[layer],
@@ -401,7 +401,7 @@ def bench_prefill_host_pool(w, dev, steps, warmup):
     pages = list(range(pools.n_phys))
     outs = [torch.empty_like(q) for q in pools.q]
     lses = [torch.empty(q.shape[:2], dtype=torch.float32, device=dev) for q in pools.q]
-    ws = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    ws = kv.workspace(512 << 20, dev)
     copy = torch.cuda.Stream()
     compute = torch.cuda.current_stream()
 
@@ -412,6 +412,8 @@ def bench_prefill_host_pool(w, dev, steps, warmup):
             if layer < w.n_layers:  # copy layer `layer` once its staging slot is free
                 if layer >= 2:
                     copy.wait_event(done[layer - 2])
+                else:  # the slot's last reader is the previous step's layer 14 / 15
+                    copy.wait_stream(compute)
                 kv.kvattn_prefetch_pages(pools.geom, hk[layer], hv[layer], stage_k[layer % 2],
                                          stage_v[layer % 2], pages, stream=copy)
                 copied[layer].record(copy)
@@ -507,7 +509,7 @@ def bench_kvmem_host(w, dev, steps, warmup, budgets=(32768, 65536, 98304)):
     import long_context_attention_paged_amd as kv
     from long_context_attention_paged_amd import streaming
     pools = LayerPools(w, dev, with_summary=True)
-    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+    ws = kv.workspace(64 << 20, dev)
     lse_full = []
     for layer in range(w.n_layers):  # full attention (with this step's append) for the coverage
         o = torch.empty_like(pools.q[layer])

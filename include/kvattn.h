@@ -47,6 +47,15 @@
  *  - Workspace protocol: when `workspace` is NULL the function stores the
  *    required byte count in *workspace_bytes, returns KVATTN_OK and enqueues
  *    nothing. Otherwise *workspace_bytes is the size of `workspace`.
+ *  - The first KVATTN_WORKSPACE_SYNC_BYTES bytes of every workspace are
+ *    counters through which a launch's workgroups coordinate. They must be
+ *    zero when a workspace is first used (allocate it zeroed), and every
+ *    call leaves them zero, so one workspace serves every entry point and
+ *    any number of calls; the partials and scores follow them. Bytes 0..3
+ *    are an error word: bit 0 is set by a prefill launch in which a
+ *    wavefront's bounded wait on the others of its workgroup gave up (never
+ *    expected; that call's output is unspecified). Concurrent calls must not
+ *    share a workspace.
  *  - Calls that overlap on one stream are ordered by the stream; concurrent
  *    calls on different streams must not share outputs or workspace.
  *
@@ -149,6 +158,7 @@ typedef int32_t kvattn_status;
 #define KVATTN_K5_RECORD_BYTES 24576 /* Q5_1 keys (k_type KVATTN_K_Q5_1) */
 #define KVATTN_K_Q5_1 2 /* key cache type: Q5_1 (the q5_1/q4_0 pair) */
 #define KVATTN_MAX_QUERY_ROWS 32 /* n_q_tok * gqa per KV head in decode */
+#define KVATTN_WORKSPACE_SYNC_BYTES 2048 /* counters at the start of a workspace */
 #define KVATTN_MAX_APPEND_TOKENS 32 /* n_new of kvattn_append_decode */
 
 /* Geometry of one layer's pool. head_dim must be 256 and page_tokens 128
@@ -252,8 +262,12 @@ kvattn_status kvattn_select_blocks(const kvattn_geom *geom, const float *q,
  *  n_splits work splits per KV head, 0 = chosen by the library.
  *  workspace holds the split partials; query its size with workspace==NULL
  *           (the size depends on every argument above, including n_splits).
+ *           The result is kvattn_decode_partials + kvattn_merge_lse of the
+ *           same splits, bit for bit.
  * Arithmetic: f16 matrix-core products with fp32 accumulation; the result is
- * within 2e-3 (max-abs) of exact attention over the dequantised pages. */
+ * within 2e-3 (max-abs) of exact attention over the dequantised pages for
+ * keys and values with |x| <= 65504 (the binary16 range the dequantised keys
+ * and the scaled probabilities are formed in). */
 kvattn_status kvattn_decode(const kvattn_geom *geom, const float *q,
                             int32_t n_q_tok, const uint8_t *k_pool,
                             const uint8_t *v_pool, const int32_t *page_table,
@@ -283,7 +297,10 @@ kvattn_status kvattn_decode(const kvattn_geom *geom, const float *q,
  *  Sparse form: every logical page that holds a new token must appear in
  *                blocks[h] of every KV head h (kvattn_select_blocks' recent
  *                window does); the tokens of a page that is not listed are
- *                not written.
+ *                not written. If a list repeats such a page, each listing
+ *                writes the same bytes and a repeat may read them while they
+ *                are written (before or after the new tokens land: its share
+ *                of the result is then unspecified); list it once.
  * Other arguments, the workspace protocol and errors as kvattn_decode
  * (KVATTN_E_INVALID also for bad k_new, v_new or n_new). */
 kvattn_status kvattn_append_decode(const kvattn_geom *geom, const float *k_new,
@@ -328,6 +345,7 @@ kvattn_status kvattn_decode_partials(const kvattn_geom *geom, const float *q,
  * the current device; 0 if geom is invalid or n_units < 1. */
 int32_t kvattn_decode_splits(const kvattn_geom *geom, int32_t n_units);
 
+
 /* a6 — chunked prefill attention ([RDNA4] "Online Log-Sum-Exp prefill":
  * chunked prefill across pages with online LSE accumulation; [STREAM] step ④
  * -ub 512). Query token t (0 <= t < chunk) sits at position pos0 + t and sees
@@ -339,6 +357,10 @@ int32_t kvattn_decode_splits(const kvattn_geom *geom, int32_t n_units);
  *  out      fp32 [chunk][n_kv_heads*gqa][256]; lse fp32 [chunk][..].
  *  n_groups page groups per (KV head, query tile) merged by LSE; 0 = chosen
  *           by the library.
+ *  workspace holds the group partials after the counter area; query its
+ *           size with workspace == NULL. Bit 0 of its error word is set if a
+ *           wavefront's bounded wait on the others of its workgroup gave up
+ *           (never expected; the output is then unspecified).
  * Arithmetic: K/V tiles dequantised to f16 in LDS, f16 matrix-core products,
  * fp32 accumulation; within 1e-2 (max-abs) of exact attention. q and the
  * pool's scales must be finite: the kernel is compiled assuming no NaN

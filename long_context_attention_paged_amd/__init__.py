@@ -15,7 +15,7 @@ __all__ = [
     "kvattn_quantize_pages", "kvattn_select_blocks", "kvattn_decode",
     "kvattn_decode_partials", "kvattn_decode_splits", "kvattn_prefill_chunk",
     "kvattn_prefill_partials", "kvattn_prefill_groups", "kvattn_merge_lse",
-    "kvattn_prefetch_pages", "kvattn_select_count",
+    "kvattn_prefetch_pages", "kvattn_select_count", "workspace", "workspace_error",
     "K_RECORD_BYTES", "V_RECORD_BYTES", "HEAD_DIM", "PAGE_TOKENS",
 ]
 
@@ -148,15 +148,32 @@ def _check(func, code):
         raise KvattnError(func, code)
 
 
-def _workspace(query, workspace, device):
-    """Size the workspace with a NULL query, allocate it if not given."""
+WORKSPACE_SYNC_BYTES = 2048  # counters at the start of every workspace (include/kvattn.h)
+
+
+def workspace(nbytes, device):
+    """A workspace of nbytes (at least the counter area), zeroed as the
+    library requires before its first use."""
+    torch = _torch()
+    return torch.zeros(max(int(nbytes), WORKSPACE_SYNC_BYTES), dtype=torch.uint8, device=device)
+
+
+def workspace_error(ws):
+    """The workspace's error word (bytes 0..3): bit 0 is set by a prefill
+    launch whose bounded waits gave up (never expected). Synchronises with
+    the device."""
+    return int(ws[:4].view(_torch().int32).item())
+
+
+def _workspace(query, ws, device):
+    """Size the workspace with a NULL query, allocate it (zeroed) if not given."""
     torch = _torch()
     size = ctypes.c_size_t(0)
     _check("workspace query", query(None, ctypes.byref(size)))
-    if workspace is None:
-        workspace = torch.empty(max(int(size.value), 256), dtype=torch.uint8, device=device)
-    _need(workspace, "workspace", torch.uint8)
-    return workspace, ctypes.c_size_t(workspace.numel())
+    if ws is None:
+        ws = workspace(int(size.value), device)
+    _need(ws, "workspace", torch.uint8)
+    return ws, ctypes.c_size_t(ws.numel())
 
 
 def kvattn_select_count(n_blocks, n_recent, k_top):

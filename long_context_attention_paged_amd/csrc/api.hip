@@ -108,6 +108,12 @@ kvattn_status check_pools(const kvattn_geom* g, const uint8_t* k_pool, const uin
 
 size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Every workspace starts with kSyncBytes of counters: zero before the first
+// call that uses the workspace, and left zero by every call. Word 0 is the
+// error word (bit 0: a prefill launch's bounded waits gave up).
+constexpr size_t kSyncBytes = 2048;
+
+
 kvattn_status launched(hipError_t e) {
   if (e != hipSuccess) return KVATTN_E_DEVICE;
   if (hipGetLastError() != hipSuccess) return KVATTN_E_DEVICE;
@@ -192,13 +198,14 @@ kvattn_status kvattn_select_blocks(const kvattn_geom* geom, const float* q,
   const int32_t n_cand = n_blocks - r;
   const int32_t k_sel = k_top < n_cand ? k_top : n_cand;
   const int32_t n_out = k_sel + r;
-  const size_t need = round_up(sizeof(double) * (size_t)geom->n_kv_heads * (size_t)n_cand);
+  const size_t need =
+      kSyncBytes + round_up(sizeof(double) * (size_t)geom->n_kv_heads * (size_t)n_cand);
   bool query_only = false;
   if ((st = workspace_check(workspace, workspace_bytes, need, &query_only))) return st;
   if (query_only) return KVATTN_OK;
   if ((st = current_device(nullptr))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  double* scores = static_cast<double*>(workspace);
+  double* scores = reinterpret_cast<double*>(static_cast<uint8_t*>(workspace) + kSyncBytes);
   if (k_sel > 0 && k_sel < n_cand) {
     if ((st = launched(launch_score(q, k_summary, geom->n_kv_heads, geom->gqa, n_logical_pages,
                                     n_cand, scores, s))))
@@ -321,7 +328,7 @@ kvattn_status launch_prefill_partials(const kvattn_geom* geom, const float* q, i
                                       const uint8_t* k_pool, const uint8_t* v_pool,
                                       const int32_t* page_table, int32_t n_logical_pages,
                                       int64_t pos0, float scale, int32_t groups, float* o_part,
-                                      float* lse_part, hipStream_t s) {
+                                      float* lse_part, hipStream_t s, uint32_t* flag = nullptr) {
   PrefillParams p;
   p.q = q;
   p.k_pool = k_pool;
@@ -339,6 +346,7 @@ kvattn_status launch_prefill_partials(const kvattn_geom* geom, const float* q, i
   p.qscale = scale * kLog2e;
   p.v_q8 = geom->v_type == KVATTN_V_Q8_0;
   p.k_type = geom->k_type;
+  p.flag = flag;
   return launched(launch_prefill(p, s));
 }
 
@@ -382,14 +390,15 @@ kvattn_status decode_impl(const kvattn_geom* geom, const float* q, int32_t n_q_t
   if (splits > n_units) splits = n_units;
   const int64_t rows = (int64_t)n_q_tok * geom->n_kv_heads * geom->gqa;
   const size_t o_bytes = round_up(sizeof(float) * (size_t)splits * rows * KVATTN_HEAD_DIM);
-  const size_t need = o_bytes + round_up(sizeof(float) * (size_t)splits * rows);
+  const size_t need = kSyncBytes + o_bytes + round_up(sizeof(float) * (size_t)splits * rows);
   bool query_only = false;
   if ((st = workspace_check(workspace, workspace_bytes, need, &query_only))) return st;
   if (query_only) return KVATTN_OK;
   if ((st = current_device(nullptr))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* o_part = static_cast<float*>(workspace);
-  float* lse_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + o_bytes);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* o_part = reinterpret_cast<float*>(ws + kSyncBytes);
+  float* lse_part = reinterpret_cast<float*>(ws + kSyncBytes + o_bytes);
   if ((st = launch_decode_partials(geom, q, n_q_tok, k_pool, v_pool, page_table, n_logical_pages,
                                    blocks, n_blk, kv_len, scale, n_units, splits, o_part, lse_part,
                                    s, app)))
@@ -483,16 +492,18 @@ kvattn_status kvattn_prefill_chunk(const kvattn_geom* geom, const float* q, int3
   }
   if (groups > n_pages) groups = n_pages;
   const size_t o_bytes = round_up(sizeof(float) * (size_t)groups * rows * KVATTN_HEAD_DIM);
-  const size_t need = o_bytes + round_up(sizeof(float) * (size_t)groups * rows);
+  const size_t need = kSyncBytes + o_bytes + round_up(sizeof(float) * (size_t)groups * rows);
   bool query_only = false;
   if ((st = workspace_check(workspace, workspace_bytes, need, &query_only))) return st;
   if (query_only) return KVATTN_OK;
   if ((st = current_device(nullptr))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* o_part = static_cast<float*>(workspace);
-  float* lse_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + o_bytes);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* o_part = reinterpret_cast<float*>(ws + kSyncBytes);
+  float* lse_part = reinterpret_cast<float*>(ws + kSyncBytes + o_bytes);
   if ((st = launch_prefill_partials(geom, q, chunk, k_pool, v_pool, page_table, n_logical_pages,
-                                    pos0, scale, groups, o_part, lse_part, s)))
+                                    pos0, scale, groups, o_part, lse_part, s,
+                                    reinterpret_cast<uint32_t*>(ws))))
     return st;
   return launched(launch_merge(groups, rows, KVATTN_HEAD_DIM, o_part, lse_part, out, lse, s));
 }

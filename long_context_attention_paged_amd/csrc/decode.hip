@@ -37,7 +37,12 @@
 namespace kvattn {
 namespace {
 
-constexpr float RESCALE_MARGIN = 8.0f;  // log2 units
+// The lazy reference max lets P' reach 2^RESCALE_MARGIN before a rescale.
+// The value scale is folded into P' in f16, so |P' * d_V| <= 2^3 * 8188 =
+// 65504 for every value block whose scale a finite |v| <= 65504 gives
+// (Q4_0: |d_V| <= 65504 / 8): the products stay finite in f16.
+constexpr float RESCALE_MARGIN = 3.0f;  // log2 units
+
 constexpr int SLOW_SHARE = 12;          // 32nds of a split's units for waves 4-7
 // One 32-token tile of one KV head in LDS:
 //   [0, 8320)      key codes: 8 loads of 4 whole token rows (1 KB contiguous in
@@ -697,9 +702,15 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
   // (n_new <= 32, and a wave keeps one 32-token group c of every page). Its
   // inputs and old words are requested before the first tile's loads; the
   // codes are computed and stored after the q' staging, while the first
-  // tile's loads fly, and the first wait of the loop covers those stores
-  // (vmcnt counts them), so every later tile load sees them. When the first
-  // tile is the appended one, it is loaded only after the stores complete.
+  // tile's loads fly. The loop's first iteration then waits with vmcnt(0)
+  // (app_pending, i == 0), which covers those stores, so every later tile
+  // load of this wave sees them. When the first tile is the appended one, it
+  // is loaded only after the stores complete. Within a launch only this wave
+  // reads the appended tile, except when a sparse list repeats its page: then
+  // another wave or workgroup may read the tile while it is being written,
+  // which is harmless only because every writer of those bytes stores the
+  // same values (each wave whose list holds the page quantises the same
+  // tokens); the header states this.
   const int64_t first_new = p.kv_len - p.n_new;
   bool app = false, app_pending = false;
   AppendTile at;

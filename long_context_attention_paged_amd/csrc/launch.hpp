@@ -70,6 +70,7 @@ struct DecodeParams {
   int32_t k_type;            // key records: 0 Q8_0, 1 Q4_0, 2 Q5_1
 };
 
+
 // Wavefronts per decode workgroup. The kernel is sized for one workgroup of
 // 8 (or two of 4) per CU; the default split count fills every CU once.
 constexpr int DECODE_WAVES = 8;
@@ -94,6 +95,7 @@ struct PrefillParams {
   float qscale;
   int32_t v_q8;              // value records hold Q8_0 codes (else Q4_0)
   int32_t k_type;            // key records: 0 Q8_0, 1 Q4_0, 2 Q5_1
+  uint32_t* flag;            // workspace error word (bit 0: a wave's wait gave up) or nullptr
 };
 
 int32_t prefill_rows_per_tile();

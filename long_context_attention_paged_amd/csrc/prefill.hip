@@ -71,15 +71,21 @@ __device__ __forceinline__ void wait_loads() {
 // waiter (see the loop in prefill_kernel), so it ends. The poll has no sleep
 // (each round trip to LDS paces it, and a sleeping wave wakes late); it is
 // capped all the same (2^20 polls, tens of milliseconds), so a broken
-// invariant cannot hang the GPU.
-__device__ __forceinline__ void wait_count(const int* c, int target) {
+// invariant cannot hang the GPU. Returns false if the cap was reached: the
+// kernel then raises the workspace's error flag at its end.
+__device__ __forceinline__ bool wait_count(const int* c, int target) {
+  bool reached = false;
   for (int spin = 0; spin < (1 << 20); ++spin) {
     // an LDS read (a generic one would also wait for the raw tile loads)
     const volatile __attribute__((address_space(3))) int* lc =
         (const volatile __attribute__((address_space(3))) int*)(c);
-    if (__builtin_amdgcn_readfirstlane(*lc) >= target) break;
+    if (__builtin_amdgcn_readfirstlane(*lc) >= target) {
+      reached = true;
+      break;
+    }
   }
   __asm__ __volatile__("" ::: "memory");
+  return reached;
 }
 
 // Publish this wave's LDS accesses before it: all of them have completed when
@@ -410,6 +416,7 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
   }
   __syncthreads();  // counters cleared
 
+  bool gave_up = false;  // a wait on another wave reached its cap (never expected)
   // Step i: multiply sub-tile i once all eighths of it are in, then
   // dequantise this wave's eighth of sub-tile i+1. The slowest wave never
   // waits on a faster one: what it needs (sub-tile i-2 read, sub-tile i
@@ -426,7 +433,8 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
   auto produce = [&](int nx) {
     if (nx < n_sub) {
       if (nx + 1 < n_sub) wait_loads<RAW_LOADS>(); else wait_loads<0>();  // raw sub-tile nx in
-      if (nx >= N_STAGES) wait_count(consumed + nx % N_STAGES, PF_WAVES * (nx / N_STAGES));
+      if (nx >= N_STAGES)
+        gave_up |= !wait_count(consumed + nx % N_STAGES, PF_WAVES * (nx / N_STAGES));
       // Every wave waits for all eighths of a stage, so a dequantising wave
       // holds up the workgroup: it outranks its SIMD partner's products
       // until its eighth is published.
@@ -447,7 +455,7 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
       win.load(p, t, sub >> 2, h, lane);
     }
     const int st = sub % N_STAGES;
-    wait_count(produced + st, PF_WAVES * (sub / N_STAGES + 1));
+    gave_up |= !wait_count(produced + st, PF_WAVES * (sub / N_STAGES + 1));
     const int64_t cur_tok0 = t.pg0 * PAGE + (int64_t)sub * 32;
     const bool compute = win.record(sub) >= 0 && wave_active && cur_tok0 <= wave_max_limit;
     if (compute) {
@@ -554,6 +562,8 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
             l > 0.f ? (mrow[nt] + __log2f(l)) * LN2 : neg_inf();
     }
   }
+  if (gave_up && p.flag && lane == 0)  // wave-uniform
+    __hip_atomic_fetch_or(p.flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace

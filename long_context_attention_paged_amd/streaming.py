@@ -100,7 +100,7 @@ class StreamedDecode:
         self.parts = torch.empty((1 + self.splits, rows, kv.HEAD_DIM), dtype=torch.float32,
                                  device=dev)
         self.lparts = torch.empty((1 + self.splits, rows), dtype=torch.float32, device=dev)
-        self.ws = torch.empty(workspace_bytes, dtype=torch.uint8, device=dev)
+        self.ws = kv.workspace(workspace_bytes, dev)
         self.copy = torch.cuda.Stream(device=dev)
 
     def device_bytes(self):
@@ -192,7 +192,7 @@ class KVMemHostDecode:
         self.k_sel = min(k_top, n_pages - r)
         self.n_out = kv.kvattn_select_count(n_pages, n_recent, k_top)
         self.blocks = torch.empty((n_kv, self.n_out), dtype=torch.int32, device=dev)
-        self.sel_ws = torch.empty(8 * n_kv * max(n_pages, 1) + 4096, dtype=torch.uint8, device=dev)
+        self.sel_ws = kv.workspace(8 * n_kv * max(n_pages, 1) + 4096, dev)
         n_st = max(self.k_sel, 1)
         self.stage_geom = kv.Geom(n_kv, geom.gqa, n_st, v_type=geom.v_type, k_type=geom.k_type)
         self.stage_k = torch.empty(n_st * n_kv * geom.k_record_bytes, dtype=torch.uint8, device=dev)
@@ -206,7 +206,7 @@ class KVMemHostDecode:
         self.parts = torch.empty((1 + self.splits, rows, kv.HEAD_DIM), dtype=torch.float32,
                                  device=dev)
         self.lparts = torch.empty((1 + self.splits, rows), dtype=torch.float32, device=dev)
-        self.ws = torch.empty(workspace_bytes, dtype=torch.uint8, device=dev)
+        self.ws = kv.workspace(workspace_bytes, dev)
         self.kept = [torch.empty((n_kv, self.n_out), dtype=torch.int32, device=dev)
                      for _ in layers]
 

@@ -78,3 +78,24 @@ def compare(out_gpu, lse_gpu, out_ref, lse_ref):
     el = np.abs(l_[fin] - lse_ref[fin]).max() if fin.any() else 0.0
     rr = np.sqrt(((o - out_ref) ** 2).sum() / max((out_ref ** 2).sum(), 1e-300))
     return eo, el, rr
+
+
+def prefill_checked(geom, q, k_pool, v_pool, page_table, pos0, scale, n_groups=0):
+    """kvattn_prefill_chunk on a fresh zeroed workspace; asserts afterwards that
+    no wavefront's bounded wait gave up (the workspace's error word is 0)."""
+    import ctypes
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    nb = ctypes.c_size_t(0)
+    code = kv.load_library().kvattn_prefill_chunk(
+        ctypes.byref(geom), ctypes.c_void_p(q.data_ptr()), q.shape[0],
+        ctypes.c_void_p(k_pool.data_ptr()), ctypes.c_void_p(v_pool.data_ptr()),
+        ctypes.c_void_p(page_table.data_ptr()), page_table.numel(), int(pos0), float(scale),
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse.data_ptr()), int(n_groups), None,
+        ctypes.byref(nb), None)
+    assert code == 0, code
+    ws = kv.workspace(nb.value, q.device)
+    out, lse = kv.kvattn_prefill_chunk(geom, q, k_pool, v_pool, page_table, pos0, scale,
+                                       out=out, lse=lse, n_groups=n_groups, workspace=ws)
+    assert kv.workspace_error(ws) == 0, "a prefill wavefront's wait gave up"
+    return out, lse

@@ -85,8 +85,9 @@ def test_decode_validation_before_device():
 def test_decode_workspace_protocol():
     code, need = decode(geom(), ws=None, nbytes=0, n_splits=8)
     assert code == OK
-    # 8 splits x 24 rows x 256 floats, plus 8 x 24 lse (768 bytes, a multiple of 256)
-    assert need == 8 * 24 * 256 * 4 + 768
+    # the 2048-byte counter area, 8 splits x 24 rows x 256 floats, plus 8 x 24 lse
+    # (768 bytes, a multiple of 256)
+    assert need == kv.WORKSPACE_SYNC_BYTES + 8 * 24 * 256 * 4 + 768
     code, _ = decode(geom(), n_splits=8, nbytes=need - 1)
     assert code == E_WORKSPACE
     code, need1 = decode(geom(), ws=None, nbytes=0, n_splits=0)
@@ -134,10 +135,10 @@ def test_prefill_and_select_validation():
              P(FAKE), P(FAKE), 0, None, ctypes.byref(nb), None) == E_INVALID  # past the table
     assert f(ctypes.byref(g), P(FAKE), 100, P(FAKE), P(FAKE), P(FAKE), 16, 1000, 0.0625,
              P(FAKE), P(FAKE), 4, None, ctypes.byref(nb), None) == OK
-    assert nb.value == 4 * 2400 * 256 * 4 + 4 * 2400 * 4       # 4 groups x 2400 rows
+    assert nb.value == 2048 + 4 * 2400 * 256 * 4 + 4 * 2400 * 4  # counters + 4 groups x 2400 rows
     assert f(ctypes.byref(g), P(FAKE), 100, P(FAKE), P(FAKE), P(FAKE), 16, 0, 0.0625,
              P(FAKE), P(FAKE), 4, None, ctypes.byref(nb), None) == OK
-    assert nb.value == 2400 * 256 * 4 + 9728                   # groups capped at 1 page
+    assert nb.value == 2048 + 2400 * 256 * 4 + 9728            # groups capped at 1 page
     s = lib.kvattn_select_blocks
     assert s(ctypes.byref(g), P(FAKE), P(FAKE), 16, 17, 2, 4, P(FAKE), None, ctypes.byref(nb),
              None) == E_INVALID                                               # NB > pages
@@ -145,7 +146,7 @@ def test_prefill_and_select_validation():
              None) == E_INVALID
     assert s(ctypes.byref(g), P(FAKE), P(FAKE), 16, 16, 2, 4, P(FAKE), None, ctypes.byref(nb),
              None) == OK
-    assert nb.value == 8 * 4 * 14 + (256 - (8 * 4 * 14) % 256)
+    assert nb.value == 2048 + 8 * 4 * 14 + (256 - (8 * 4 * 14) % 256)
     assert s(ctypes.byref(g), P(FAKE), P(FAKE), 16, 16, 2, 4, P(FAKE), P(FAKE),
              ctypes.byref(ctypes.c_size_t(8)), None) == E_WORKSPACE
 

@@ -35,7 +35,9 @@ CASES = [
     (1, 8, 3, 7, 1000, 0, False),              # an odd count
     (1, 6, 4, 4, 40, 1, False),                # the appended tile is a wave's first tile
     (2, 6, 4, 4, 9 * 128 + 3, 10, False),      # one page per split
-    (2, 6, 4, 4, 64 * 128 * 3 + 5, 0, False),  # several pages per wave, partial last page
+    # one split over 193 pages: the appended tile is unit 120 of waves 0-3,
+    # found after the search reloads the 64-unit page window
+    (2, 6, 4, 4, 64 * 128 * 3 + 5, 1, False),
     (2, 6, 1, 3, 4 * 128, 0, True),            # sparse; completes a page (summary)
     (1, 6, 2, 2, 6 * 128 + 1, 0, True),        # sparse; the new tokens straddle two listed pages
 ]

@@ -22,7 +22,7 @@ import oracle
 from oracle import quant
 import long_context_attention_paged_amd as kv
 from long_context_attention_paged_amd import synth
-from kvtest_util import DEV, compare, gpu, host
+from kvtest_util import DEV, compare, gpu, host, prefill_checked
 
 pytestmark = pytest.mark.gpu
 
@@ -133,7 +133,7 @@ def test_prefill_full_size_sampled_tokens():
     head = 3
     L = FullLayer(w)
     L.check_pages(sample_pages(w, np.random.default_rng(4)) + [w.n_pages - 2])
-    out, lse = kv.kvattn_prefill_chunk(L.geom, gpu(L.q), L.kp, L.vp, L.td, w.pos0, 1 / 16)
+    out, lse = prefill_checked(L.geom, gpu(L.q), L.kp, L.vp, L.td, w.pos0, 1 / 16)
     torch.cuda.synchronize()
     toks = [0, 1, 127, 128, 300, 510, 511]
     ok, ov = L.oracle_pool(head)

@@ -13,7 +13,7 @@ import torch
 import oracle
 from oracle import quant
 import long_context_attention_paged_amd as kv
-from kvtest_util import DEV, Pools, compare, fill, gpu, host
+from kvtest_util import DEV, Pools, compare, fill, gpu, host, prefill_checked
 
 pytestmark = pytest.mark.gpu
 
@@ -126,7 +126,7 @@ def test_prefill_nibble_keys_matches_oracle(chunk, pos0, gqa, n_kv, n_groups, v_
     pools, table, _, _ = fill(n_kv, gqa, kv_len, seed=chunk + pos0, init_seed=8, v_type=v_type,
                               k_type=k_type)
     q = np.random.default_rng(kv_len).standard_normal((chunk, n_kv * gqa, 256)).astype(np.float32)
-    out, lse = kv.kvattn_prefill_chunk(pools.geom, gpu(q), pools.gk, pools.gv,
+    out, lse = prefill_checked(pools.geom, gpu(q), pools.gk, pools.gv,
                                        gpu(table, torch.int32), pos0, 1 / 16, n_groups=n_groups)
     ref_o, ref_l = oracle.prefill_chunk(q, gqa, pools.ok, pools.ov, table, len(table), pos0,
                                         1 / 16)

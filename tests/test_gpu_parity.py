@@ -14,7 +14,7 @@ import torch
 import oracle
 from oracle import quant
 import long_context_attention_paged_amd as kv
-from kvtest_util import DEV, Pools, compare, fill, gpu, host
+from kvtest_util import DEV, Pools, compare, fill, gpu, host, prefill_checked
 
 pytestmark = pytest.mark.gpu
 
@@ -129,7 +129,10 @@ DECODE_CASES = [
     (1, 1, 3, 130, 64),
     (1, 6, 1, 1100, 2),       # 9 pages over 2 splits: 4 and 5 (odd) per split
     (2, 16, 1, 2500, 0),      # 32 rows
-    (4, 6, 2, 64 * 128 * 3 + 5, 0),  # several pages per wave, partial last page
+    # one split over 193 pages: waves 4-7 take 72 units, waves 0-3 121, so
+    # both halves reload their 64-unit page window; partial last page
+    (4, 6, 2, 64 * 128 * 3 + 5, 1),
+    (1, 6, 1, 300 * 128 - 40, 1),   # 300 pages, one split: windows reloaded twice
 ]
 
 
@@ -283,7 +286,7 @@ def test_prefill_parity(chunk, pos0, gqa, n_kv, n_groups):
     kv_len = pos0 + chunk
     pools, table, _, _ = fill(n_kv, gqa, kv_len, seed=chunk + pos0, init_seed=8)
     q = np.random.default_rng(kv_len).standard_normal((chunk, n_kv * gqa, 256)).astype(np.float32)
-    out, lse = kv.kvattn_prefill_chunk(pools.geom, gpu(q), pools.gk, pools.gv,
+    out, lse = prefill_checked(pools.geom, gpu(q), pools.gk, pools.gv,
                                        gpu(table, torch.int32), pos0, 1 / 16, n_groups=n_groups)
     ref_o, ref_l = oracle.prefill_chunk(q, gqa, pools.ok, pools.ov, table, len(table), pos0,
                                         1 / 16)
@@ -296,7 +299,7 @@ def test_prefill_indicator_causal_exact():
     kv_len, pos0, gqa = 1500, 1100, 3
     pools, table = indicator_pools(kv_len, 14, 13, gqa=gqa)
     q = np.random.default_rng(2).standard_normal((kv_len - pos0, gqa, 256)).astype(np.float32)
-    out, _ = kv.kvattn_prefill_chunk(pools.geom, gpu(q), pools.gk, pools.gv,
+    out, _ = prefill_checked(pools.geom, gpu(q), pools.gk, pools.gv,
                                      gpu(table, torch.int32), pos0, 1 / 16)
     o = host(out)
     for t in (0, 1, 27, 127, 128, 399):
@@ -366,7 +369,7 @@ def test_prefill_partials_merge_to_prefill():
     pools, table, _, _ = fill(n_kv, gqa, kv_len, seed=36, init_seed=11)
     q = np.random.default_rng(37).standard_normal((chunk, n_kv * gqa, 256)).astype(np.float32)
     qd, td = gpu(q), gpu(table, torch.int32)
-    out, lse = kv.kvattn_prefill_chunk(pools.geom, qd, pools.gk, pools.gv, td, pos0, 1 / 16,
+    out, lse = prefill_checked(pools.geom, qd, pools.gk, pools.gv, td, pos0, 1 / 16,
                                        n_groups=G)
     op, lp = kv.kvattn_prefill_partials(pools.geom, qd, pools.gk, pools.gv, td, pos0, 1 / 16, G)
     o2, l2 = kv.kvattn_merge_lse(op, lp)
@@ -428,3 +431,48 @@ def test_decode_over_prefetched_staging_pool():
     o2, l2 = kv.kvattn_decode(pools.geom, qd, pools.gk, pools.gv, td, kv_len, 1 / 16, n_splits=8)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.gpu
+def test_decode_window_reloads_one_split():
+    """One split over hundreds of units, so each wave half reloads its 64-unit
+    page window several times (units past 64, 128, ...): dense over 300
+    pages through kvattn_decode and kvattn_decode_partials, a sparse list of
+    260 blocks, and kvattn_append_decode over that list with the new tokens
+    on its last block (found by the append's search past two reloads)."""
+    n_kv, gqa, kv_len = 1, 6, 300 * 128 - 40
+    pools, table, _, _ = fill(n_kv, gqa, kv_len, seed=91, init_seed=11)
+    n_pages = len(table)
+    g = np.random.default_rng(92)
+    q = g.standard_normal((4, gqa, 256)).astype(np.float32)
+    td = gpu(table, torch.int32)
+    out, lse = kv.kvattn_decode(pools.geom, gpu(q), pools.gk, pools.gv, td, kv_len, 1 / 16,
+                                n_splits=1)
+    ref_o, ref_l = oracle.decode(q, gqa, pools.ok, pools.ov, table, n_pages, kv_len, 1 / 16)
+    eo, el, rr = compare(out, lse, ref_o.reshape(4, -1, 256), ref_l)
+    assert eo <= DEC_TOL and el <= 1e-3 and rr <= 2e-3, (eo, el, rr)
+    op, lp = kv.kvattn_decode_partials(pools.geom, gpu(q), pools.gk, pools.gv, td, kv_len, 1 / 16, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(op.reshape(out.shape), out) and torch.equal(lp.reshape(lse.shape), lse)
+    blocks = np.r_[np.sort(g.choice(n_pages - 1, 259, replace=False)), n_pages - 1]
+    blocks = blocks[None, :].astype(np.int32)
+    out, lse = kv.kvattn_decode(pools.geom, gpu(q), pools.gk, pools.gv, td, kv_len, 1 / 16,
+                                blocks=gpu(blocks, torch.int32), n_splits=1)
+    ref_o, ref_l = oracle.decode(q, gqa, pools.ok, pools.ov, table, n_pages, kv_len, 1 / 16,
+                                 blocks=blocks)
+    eo, el, rr = compare(out, lse, ref_o.reshape(4, -1, 256), ref_l)
+    assert eo <= DEC_TOL and el <= 1e-3 and rr <= 2e-3, (eo, el, rr)
+    # append four tokens at the end of the cache, attend over the same list
+    n_new = 4
+    Kn = g.standard_normal((n_new, n_kv, 256)).astype(np.float32)
+    Vn = g.standard_normal((n_new, n_kv, 256)).astype(np.float32)
+    out, lse = kv.kvattn_append_decode(pools.geom, gpu(Kn), gpu(Vn), gpu(q), pools.gk, pools.gv,
+                                       td, kv_len + n_new, 1 / 16,
+                                       blocks=gpu(blocks, torch.int32), n_splits=1)
+    quant.quantize_into_pool(Kn, Vn, kv_len, table, pools.ok, pools.ov)
+    gk, gv = pools.gpu_bytes()
+    assert (gk == pools.ok).all() and (gv == pools.ov).all()
+    ref_o, ref_l = oracle.decode(q, gqa, pools.ok, pools.ov, table, n_pages, kv_len + n_new,
+                                 1 / 16, blocks=blocks)
+    eo, el, rr = compare(out, lse, ref_o.reshape(4, -1, 256), ref_l)
+    assert eo <= DEC_TOL and el <= 1e-3 and rr <= 2e-3, (eo, el, rr)
