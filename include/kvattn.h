@@ -288,8 +288,11 @@ kvattn_status kvattn_decode(const kvattn_geom *geom, const float *q,
  * summaries, out and lse are identical bit for bit. The decode kernel itself
  * quantises the tokens: the wavefront that streams the tile holding them
  * writes them before it reads that tile, so no separate quantisation launch
- * is made (the summary of a page the append completes, when k_summary is not
- * NULL, is one more launch after the merge).
+ * is made. When k_summary is not NULL, the summary of the page the append
+ * completes (the new positions complete at most one page) is written by the
+ * same launch: the workgroup that streams that page sums it once its new
+ * tokens are written, so in the sparse form the page must be listed (as the
+ * rule below already requires).
  *  k_new, v_new  fp32 [n_new][n_kv_heads][256], finite; the keys and values
  *                of positions kv_len - n_new .. kv_len - 1.
  *  n_new         1 <= n_new <= min(KVATTN_MAX_APPEND_TOKENS, kv_len).

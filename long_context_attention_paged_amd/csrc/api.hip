@@ -262,6 +262,7 @@ struct AppendArgs {
   uint8_t* k_pool;
   uint8_t* v_pool;
   int32_t n_new;
+  float* k_summary;  // when not NULL: the summary of a page the append completes
 };
 
 kvattn_status launch_decode_partials(const kvattn_geom* geom, const float* q, int32_t n_q_tok,
@@ -296,6 +297,12 @@ kvattn_status launch_decode_partials(const kvattn_geom* geom, const float* q, in
   p.n_new = app ? app->n_new : 0;
   p.v_q8 = geom->v_type == KVATTN_V_Q8_0;
   p.k_type = geom->k_type;
+  // the appended positions kv_len - n_new .. kv_len - 1 (n_new <= 32 < 128)
+  // complete at most one page: the one ending at a multiple of 128 among them
+  p.sum_page = -1;
+  p.k_summary = app ? app->k_summary : nullptr;
+  if (app && app->k_summary && kv_len / KVATTN_PAGE_TOKENS > (kv_len - app->n_new) / KVATTN_PAGE_TOKENS)
+    p.sum_page = (int32_t)(kv_len / KVATTN_PAGE_TOKENS - 1);
   return launched(launch_decode(p, s));
 }
 
@@ -430,21 +437,11 @@ kvattn_status kvattn_append_decode(const kvattn_geom* geom, const float* k_new, 
   if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16)) return KVATTN_E_INVALID;
   if (n_new < 1 || n_new > KVATTN_MAX_APPEND_TOKENS || n_new > kv_len) return KVATTN_E_INVALID;
   if (k_summary && !aligned(k_summary, 16)) return KVATTN_E_INVALID;
-  const AppendArgs app{k_new, v_new, k_pool, v_pool, n_new};
-  const kvattn_status st =
-      decode_impl(geom, q, n_q_tok, k_pool, v_pool, page_table, n_logical_pages, blocks, n_blk,
-                  kv_len, scale, out, lse, n_splits, workspace, workspace_bytes, stream, &app);
-  if (st || !workspace || !k_summary) return st;
-  // the summaries of the pages this append completes, from the updated pool
-  const int64_t pos0 = kv_len - n_new;
-  const int64_t first = pos0 / KVATTN_PAGE_TOKENS;
-  const int64_t last_full = kv_len / KVATTN_PAGE_TOKENS - 1;
-  if (last_full < first) return KVATTN_OK;
-  return launched(launch_summarize(k_pool, page_table, geom->n_kv_heads, geom->n_phys_pages,
-                                   n_logical_pages, (int32_t)first,
-                                   (int32_t)(last_full - first + 1), k_summary,
-                                   geom->k_type,
-                                   static_cast<hipStream_t>(stream)));
+  // the summary of a page the append completes is written by the decode
+  // launch itself, from the updated pool
+  const AppendArgs app{k_new, v_new, k_pool, v_pool, n_new, k_summary};
+  return decode_impl(geom, q, n_q_tok, k_pool, v_pool, page_table, n_logical_pages, blocks, n_blk,
+                     kv_len, scale, out, lse, n_splits, workspace, workspace_bytes, stream, &app);
 }
 
 kvattn_status kvattn_decode_partials(const kvattn_geom* geom, const float* q, int32_t n_q_tok,

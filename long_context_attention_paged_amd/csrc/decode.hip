@@ -606,6 +606,109 @@ __device__ __forceinline__ void append_finish(const DecodeParams& p, AppendTile&
   }
 }
 
+// ---- summary of the page an append completes ---------------------------------
+// summary[n] = RN32((binary64 sum over slots t = 0..127, ascending, of the
+// dequantised key K[t][n]) / 128), as quantize.hip's summarize_kernel. Every
+// dequantised key is a multiple of 2^-24 (a binary16 scale times an integer
+// code, plus a binary16 minimum for Q5_1). While the terms' magnitudes add up
+// to less than 2^29, every partial sum, in any order, is a multiple of 2^-24
+// below 2^29 and so exact in binary64: the ascending sum equals a sum in any
+// order, here fused multiply-adds of code and scale. Q4_0 keys (|K| <= 8 x
+// 65504) and Q5_1 keys (|d c| + |m| <= 32 x 65504) always stay below that
+// bound over 128 slots; for Q8_0 keys the bound 127 x (sum of the 128 scales'
+// magnitudes) is checked per 32-dim block, and where it is reached (scales
+// near the binary16 limit) the ascending sum is run as written. The workgroup
+// whose units hold the page computes it once its own appended bytes are in
+// place: thread (tg = tid / 64, lane) sums dims 4 lane .. +3 over slots tg,
+// tg + 8, ..., tg + 120.
+
+// The ascending binary64 sum for dim n of a Q8_0 key record.
+__device__ __noinline__ float summary_sequential_q8(const uint8_t* krec, int n) {
+  double acc = 0.0;
+  for (int t = 0; t < PAGE; ++t) {
+    const float d = f16_value(reinterpret_cast<const uint16_t*>(krec + KSCALE_OF<0>)[t * 8 + n / 32]);
+    const float kh = d * (float)(int8_t)krec[t * D + n];  // exact in binary32
+    acc = acc + (double)kh;
+  }
+  return (float)(acc / 128.0);
+}
+
+// The page's key codes and scales this thread sums, in registers.
+struct SummaryLoads {
+  uint32_t w[16], sc[16], hi[16], mm[16];
+};
+
+template <int KT>
+__device__ __forceinline__ void summary_issue(const uint8_t* krec, SummaryLoads& L) {
+  const int lane = threadIdx.x & 63, tg = threadIdx.x >> 6;
+  const int n4 = 4 * lane;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {  // every load in flight at once
+    const int t = tg + 8 * j;
+    const int sidx = t * 8 + n4 / 32;
+    L.sc[j] = reinterpret_cast<const uint16_t*>(krec + KSCALE_OF<KT>)[sidx];
+    if constexpr (KT == 0) {
+      L.w[j] = *reinterpret_cast<const uint32_t*>(krec + t * D + n4);
+    } else {
+      L.w[j] = reinterpret_cast<const uint32_t*>(krec)[t * 32 + n4 / 8];
+    }
+    if constexpr (KT == 2) {
+      L.hi[j] = krec[K5_HI_OFF + t * 32 + n4 / 8];
+      L.mm[j] = reinterpret_cast<const uint16_t*>(krec + K5_M_OFF)[sidx];
+    }
+  }
+}
+
+template <int KT, int THREADS>
+__device__ __forceinline__ void summary_finish(const uint8_t* krec, const SummaryLoads& L,
+                                               float* out, uint8_t* lds) {
+  static_assert(THREADS == 512, "eight slot groups of 64 lanes");
+  const int tid = threadIdx.x, lane = tid & 63, tg = tid >> 6;
+  const int n4 = 4 * lane;
+  double S[4] = {0.0, 0.0, 0.0, 0.0};
+  double B = 0.0;  // sum of |d| over this thread's slots (Q8_0 keys)
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const double d = (double)f16_value(L.sc[j]);
+    if constexpr (KT == 0) B += __builtin_fabs(d);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (KT == 0) {
+        S[e] = __builtin_fma((double)(int)(int8_t)(L.w[j] >> (8 * e)), d, S[e]);
+      } else {
+        const int k = (n4 & 7) + e;  // dim 8w + k of the word
+        const int code = (int)((L.w[j] >> v_slot_bit(k)) & 0xFu);
+        if constexpr (KT == 1) {
+          S[e] = __builtin_fma((double)(code - 8), d, S[e]);
+        } else {
+          const int c5 = code | (int)(((L.hi[j] >> k5_hi_bit(k)) & 1u) << 4);
+          S[e] = __builtin_fma((double)c5, d, S[e]) + (double)f16_value(L.mm[j]);
+        }
+      }
+    }
+  }
+  double* Ssh = reinterpret_cast<double*>(lds);
+  double* Bsh = Ssh + 8 * D;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) Ssh[tg * D + n4 + e] = S[e];
+  if constexpr (KT == 0) Bsh[tg * 64 + lane] = B;
+  __syncthreads();
+  if (tid < D) {
+    double s = 0.0, b = 0.0;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      s += Ssh[g * D + tid];
+      if constexpr (KT == 0) b += Bsh[g * 64 + tid / 4];
+    }
+    const float exact = (float)(s * 0x1p-7);
+    if constexpr (KT == 0) {
+      out[tid] = 127.0 * b < 0x1p29 ? exact : summary_sequential_q8(krec, tid);
+    } else {
+      out[tid] = exact;
+    }
+  }
+}
+
 // WAVES: wavefronts per workgroup (4 or 8); either way two wavefronts share
 // a SIMD (two 4-wave workgroups or one 8-wave workgroup per CU), so every
 // lane may hold up to 256 VGPRs. With 8 waves, waves 4-7 stream the first
@@ -683,6 +786,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
   };
   // Tile i's record; invalid tiles (skipped pages, tokens past kv_len) still
   // load from record 0 so every wait count below is a constant.
+  int sum_ph = -1;  // physical page of the page to summarise, once this wave streams it
   auto locate = [&](int i, int64_t& tok, bool& valid, int64_t& rec) {
     if (i % 64 == 0) refill(i);
     const int lp = __builtin_amdgcn_readlane(lp_vec, i % 64);
@@ -690,6 +794,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
     valid = ph >= 0;
     tok = (int64_t)lp * PAGE + c * 32;
     rec = valid ? (int64_t)ph * p.n_kv + h : 0;
+    if (valid && lp == p.sum_page) sum_ph = ph;
   };
 
   // One LDS slot per wave with separately refilled key and value halves:
@@ -749,6 +854,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
   // The first tile is in flight: stage q' rows (f16) into LDS, shared by all
   // waves (padding rows are zero). Row r of this KV head is query token
   // r / gqa, query head h*gqa + r % gqa; its global row goes to s_rowg.
+  __shared__ int s_sum_ph;  // 1 + physical page to summarise (0: none here)
+  if (threadIdx.x == 0) s_sum_ph = 0;
   if (threadIdx.x < NT * 16) {
     const int r = threadIdx.x;
     const int tq = r / p.gqa, gi = r - tq * p.gqa;
@@ -811,7 +918,22 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
   // ---- combine the wavefronts, write this split's partial --------------------
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) st.l[nt] = wave_sum_xor_16_32(st.l[nt]);
+  // The page the append completes is summarised by the workgroup whose units
+  // hold it: a unit is a whole page, whose four 32-token groups are streamed
+  // by four waves of one workgroup (group c by a wave with wave % 4 == c),
+  // including the wave that wrote the page's new tokens. The waves of a workgroup share one vector L1; the explicit wait
+  // (vmcnt, expcnt and lgkmcnt all zero) has that wave's stores complete
+  // before the barrier, so the summary's reads, issued after it and in
+  // flight while the partial is combined, see them.
+  if (p.sum_page >= 0) {
+    if (sum_ph >= 0) s_sum_ph = sum_ph + 1;
+    __builtin_amdgcn_s_waitcnt(0);
+  }
   __syncthreads();  // every wave is done with the LDS ring and q_lds
+  const int sum_ph1 = p.sum_page >= 0 ? s_sum_ph : 0;  // uniform
+  const uint8_t* sum_rec = p.k_pool + ((int64_t)(sum_ph1 - 1) * p.n_kv + h) * KREC;
+  SummaryLoads sl;
+  if (sum_ph1 != 0) summary_issue<KT>(sum_rec, sl);
   if (g == 0) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -872,11 +994,16 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
       if (s_m[w][r] != neg_inf()) L += s_l[w][r] * __builtin_amdgcn_exp2f(s_m[w][r] - M);
     p.lse_part[(int64_t)split * rows_total + rowg] = (L > 0.f) ? (M + __log2f(L)) * LN2 : neg_inf();
   }
+  if (sum_ph1 != 0)  // the combine buffer is free after the partial's last barrier
+    summary_finish<KT, THREADS>(sum_rec, sl, p.k_summary + ((int64_t)h * p.n_logical + p.sum_page) * D,
+                                smem_raw);
 }
 
 template <int NT, int KT, bool V8>
 hipError_t launch_nt(const DecodeParams& p, hipStream_t stream) {
   const size_t combine = sizeof(float) * DECODE_WAVES * 16 * 260;
+  static_assert(sizeof(float) * DECODE_WAVES * 16 * 260 >= (8 * D + 8 * 64) * sizeof(double),
+                "the page summary's partial sums fit the combine area");
   const size_t qbytes = ((NT * 16 * Q_LDS_STRIDE * 2) + 1023) / 1024 * 1024;
   const size_t loop = qbytes + DECODE_WAVES * SLOT_BYTES<KT, V8>;
   const size_t shmem = combine > loop ? combine : loop;

@@ -68,8 +68,11 @@ struct DecodeParams {
   int32_t n_new;
   int32_t v_q8;              // value records hold Q8_0 codes (else Q4_0)
   int32_t k_type;            // key records: 0 Q8_0, 1 Q4_0, 2 Q5_1
+  // Summary of the logical page the append completes (-1: none): written to
+  // k_summary [n_kv][n_logical][256] by the workgroup whose units hold it.
+  int32_t sum_page;
+  float* k_summary;
 };
-
 
 // Wavefronts per decode workgroup. The kernel is sized for one workgroup of
 // 8 (or two of 4) per CU; the default split count fills every CU once.

@@ -40,6 +40,12 @@ CASES = [
     (2, 6, 4, 4, 64 * 128 * 3 + 5, 1, False),
     (2, 6, 1, 3, 4 * 128, 0, True),            # sparse; completes a page (summary)
     (1, 6, 2, 2, 6 * 128 + 1, 0, True),        # sparse; the new tokens straddle two listed pages
+    (2, 6, 4, 4, 3 * 128, 0, False),           # dense; completes the last page (summary)
+    (1, 6, 1, 3, 5 * 128 + 1, 1, False),       # dense, one split; completes the next-to-last page
+    (2, 6, 4, 4, 40 * 128, 7, False),          # dense, seven splits; completes the last page
+    # dense, two splits of two pages: the completed page 2 is the first unit
+    # of split 1, streamed by waves 4-7; the new tokens straddle into page 3
+    (1, 6, 1, 3, 3 * 128 + 1, 2, False),
 ]
 
 
@@ -88,8 +94,8 @@ def test_append_decode_matches_quantize_then_decode(n_kv, gqa, n_q_tok, n_new, k
 
     # the two-call path on a copy of the device pools
     gk2, gv2 = pools.gk.clone(), pools.gv.clone()
-    summ = torch.zeros((n_kv, n_pages, 256), dtype=torch.float32, device=DEV) if sparse else None
-    summ2 = summ.clone() if sparse else None
+    summ = torch.zeros((n_kv, n_pages, 256), dtype=torch.float32, device=DEV)
+    summ2 = summ.clone()
     kv.kvattn_quantize_pages(pools.geom, gpu(Kn), gpu(Vn), pos0, table_d, gk2, gv2, summ2)
     o2, l2 = kv.kvattn_decode(pools.geom, gpu(q), gk2, gv2, table_d, kv_len, 1 / 16,
                               blocks=blocks_d, n_splits=n_splits)
@@ -111,17 +117,18 @@ def test_append_decode_matches_quantize_then_decode(n_kv, gqa, n_q_tok, n_new, k
     eo, el, rr = compare(out, lse, ref_o.reshape(n_q_tok, -1, 256), ref_l)
     assert eo <= DEC_TOL and el <= 1e-3 and rr <= 2e-3, (eo, el, rr)
 
-    if sparse:
-        assert torch.equal(summ, summ2)
-        full = kv_len // 128
-        done = [p for p in range(pos0 // 128, full)]
-        ref_s = quant.summaries_from_pool(pools.ok, table, full, n_kv)
-        got = host(summ)
-        for p in range(n_pages):
-            if p in done:
-                assert (got[:, p].view(np.uint32) == ref_s[:, p].view(np.uint32)).all()
-            else:
-                assert (got[:, p] == 0).all()
+    # the summary of a page the append completes (written by the decode
+    # launch) equals the separate summary launch's and the oracle's
+    assert torch.equal(summ, summ2)
+    full = kv_len // 128
+    done = [p for p in range(pos0 // 128, full)]
+    ref_s = quant.summaries_from_pool(pools.ok, table, full, n_kv)
+    got = host(summ)
+    for p in range(n_pages):
+        if p in done:
+            assert (got[:, p].view(np.uint32) == ref_s[:, p].view(np.uint32)).all()
+        else:
+            assert (got[:, p] == 0).all()
 
 
 def test_append_decode_repeated_steps():
@@ -151,3 +158,42 @@ def test_append_decode_repeated_steps():
             assert eo <= DEC_TOL and el <= 1e-3 and rr <= 2e-3, (step, eo, el, rr)
     gk, gv = pools.gpu_bytes()
     assert (gk == pools.ok).all() and (gv == pools.ov).all()
+
+
+def test_append_summary_of_large_q8_keys():
+    """Q8_0 keys of magnitude 5e6 .. 8e6 (scales near the binary16 limit): the
+    magnitudes of a page add up past 2^53 units of 2^-24, so the summary takes
+    the ascending binary64 sum as written; it still equals the separate
+    summary launch and the oracle bit for bit (attention over such keys is
+    outside the decode's range and is not checked). Q4_0 and Q5_1 keys cannot
+    reach that bound."""
+    n_kv, gqa, kv_len, n_new = 1, 6, 2 * 128, 2
+    g = np.random.default_rng(90)
+    n_pages = kv_len // 128
+    table = np.array([2, 0], np.int32)
+    pools = Pools(3, n_kv, gqa, init_seed=91, k_type=kv.K_Q8_0)
+    pos0 = kv_len - n_new
+
+    def big(n):
+        mag = g.uniform(5.0e6, 8.0e6, (n, n_kv, 256))
+        return (mag * g.choice([-1.0, 1.0], mag.shape)).astype(np.float32)
+
+    pools.write(big(pos0), g.standard_normal((pos0, n_kv, 256)).astype(np.float32), 0, table)
+    Kn = big(n_new)
+    Vn = g.standard_normal((n_new, n_kv, 256)).astype(np.float32)
+    q = g.standard_normal((1, n_kv * gqa, 256)).astype(np.float32)
+    table_d = gpu(table, torch.int32)
+    gk2, gv2 = pools.gk.clone(), pools.gv.clone()
+    summ = torch.zeros((n_kv, n_pages, 256), dtype=torch.float32, device=DEV)
+    summ2 = summ.clone()
+    kv.kvattn_quantize_pages(pools.geom, gpu(Kn), gpu(Vn), pos0, table_d, gk2, gv2, summ2)
+    kv.kvattn_append_decode(pools.geom, gpu(Kn), gpu(Vn), gpu(q), pools.gk, pools.gv, table_d,
+                            kv_len, 1 / 16, k_summary=summ)
+    torch.cuda.synchronize()
+    quant.quantize_into_pool(Kn, Vn, pos0, table, pools.ok, pools.ov)
+    ref_s = quant.summaries_from_pool(pools.ok, table, n_pages, n_kv)
+    kh = quant.dequantize_keys(pools.ok[table[1]])
+    assert np.isfinite(kh).all()
+    assert np.abs(kh).sum(axis=-2).max() * 2.0 ** 24 >= 2.0 ** 53  # the fallback is taken
+    assert torch.equal(summ[:, 1], summ2[:, 1])
+    assert (host(summ)[:, 1].view(np.uint32) == ref_s[:, 1].view(np.uint32)).all()

@@ -102,6 +102,24 @@ def test_select_bitexact(n_blocks, n_recent, k_top):
     run_select(summ, q, gqa, n_blocks, n_recent, k_top)
 
 
+def test_select_wide_range_and_many_candidates():
+    """Scores of both signs spanning many binade (the radix select starts at
+    the highest bit where candidates differ), and more candidates than the
+    ranking keeps in LDS (keys re-read from the scores)."""
+    g = np.random.default_rng(13)
+    n_kv, gqa = 2, 6
+    for nb, k in ((600, 50), (9000, 300), (12000, 7000)):
+        summ = (g.standard_normal((n_kv, nb, 256)) * 0.05).astype(np.float32)
+        summ *= np.exp2(g.integers(-40, 40, (n_kv, nb, 1))).astype(np.float32)
+        q = g.standard_normal((n_kv * gqa, 256)).astype(np.float32)
+        run_select(summ, q, gqa, nb, 16, k)
+    # all candidates of one sign and magnitude but the last bits: a deep select
+    summ = np.tile((g.standard_normal((n_kv, 1, 256)) * 0.05).astype(np.float32), (1, 700, 1))
+    summ[:, :, 0] += np.float32(1e-6) * g.integers(0, 4, (n_kv, 700)).astype(np.float32)
+    q = g.standard_normal((n_kv * gqa, 256)).astype(np.float32)
+    run_select(summ, q, gqa, 700, 10, 123)
+
+
 def test_select_ties_and_signed_zero():
     """Equal scores (duplicated summaries, zero summaries that score +0 and -0)
     go to the lowest block index."""
