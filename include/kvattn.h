@@ -160,6 +160,7 @@ typedef int32_t kvattn_status;
 #define KVATTN_MAX_QUERY_ROWS 32 /* n_q_tok * gqa per KV head in decode */
 #define KVATTN_WORKSPACE_SYNC_BYTES 2048 /* counters at the start of a workspace */
 #define KVATTN_MAX_APPEND_TOKENS 32 /* n_new of kvattn_append_decode */
+#define KVATTN_NOALLOC_SCRATCH_BYTES 16777216 /* kvattn_append_decode_noalloc */
 
 /* Geometry of one layer's pool. head_dim must be 256 and page_tokens 128
  * (the pages' shape: [VULKAN] "模型結構"; [KVMEM] --kvmem-block-tokens 128).
@@ -317,6 +318,32 @@ kvattn_status kvattn_append_decode(const kvattn_geom *geom, const float *k_new,
                                    float *k_summary, float *out, float *lse,
                                    int32_t n_splits, void *workspace,
                                    size_t *workspace_bytes, void *stream);
+
+/* kvattn_append_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. Same arguments, result and errors as kvattn_append_decode
+ * without the workspace: the split-K partials go to a static array of
+ * KVATTN_NOALLOC_SCRATCH_BYTES in the library, one per GPU (reserved when the
+ * library's code is loaded on that GPU, kept until the process ends), looked
+ * up on the first call on each device. The call allocates nothing, and its
+ * out, lse, pool bytes and summaries equal kvattn_append_decode's bit for
+ * bit. The partials take splits * n_q_tok * n_kv_heads * gqa * 1028 bytes
+ * (each of the two arrays rounded up to 256): 6.3 MB for 4 KV heads x 24
+ * rows per KV head at the default 64 splits. A call that needs more returns
+ * KVATTN_E_WORKSPACE and enqueues nothing. Every call on one GPU uses that
+ * GPU's one array: calls on one stream are ordered, but calls that overlap
+ * on one GPU (other streams, other threads) race and their results are
+ * unspecified. */
+kvattn_status kvattn_append_decode_noalloc(const kvattn_geom *geom, const float *k_new,
+                                           const float *v_new, int32_t n_new,
+                                           const float *q, int32_t n_q_tok,
+                                           uint8_t *k_pool, uint8_t *v_pool,
+                                           const int32_t *page_table,
+                                           int32_t n_logical_pages,
+                                           const int32_t *blocks, int32_t n_blk,
+                                           int64_t kv_len, float scale,
+                                           float *k_summary, float *out, float *lse,
+                                           int32_t n_splits, void *stream);
 
 /* a3 alone — the split-K partials of kvattn_decode, without the merge, for
  * callers that combine them with partials computed elsewhere (other pages,

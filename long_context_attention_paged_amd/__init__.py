@@ -84,6 +84,8 @@ def load_library():
         "kvattn_decode_partials": ([G, P, I32, P, P, P, I32, P, I32, I64, F32, I32, P, P, P], I32),
         "kvattn_append_decode": ([G, P, P, I32, P, I32, P, P, P, I32, P, I32, I64, F32, P, P, P,
                                   I32, P, SZP, P], I32),
+        "kvattn_append_decode_noalloc": ([G, P, P, I32, P, I32, P, P, P, I32, P, I32, I64, F32, P,
+                                          P, P, I32, P], I32),
         "kvattn_decode_splits": ([G, I32], I32),
         "kvattn_prefill_chunk": ([G, P, I32, P, P, P, I32, I64, F32, P, P, I32, P, SZP, P], I32),
         "kvattn_prefill_partials": ([G, P, I32, P, P, P, I32, I64, F32, I32, P, P, P], I32),
@@ -149,6 +151,7 @@ def _check(func, code):
 
 
 WORKSPACE_SYNC_BYTES = 2048  # counters at the start of every workspace (include/kvattn.h)
+NOALLOC_SCRATCH_BYTES = 16 << 20  # the static partials of kvattn_append_decode_noalloc
 
 
 def workspace(nbytes, device):
@@ -311,6 +314,38 @@ def kvattn_append_decode(geom, k_new, v_new, q, k_pool, v_pool, page_table, kv_l
 
     workspace, nbytes = _workspace(call, workspace, q.device)
     _check("kvattn_append_decode", call(_ptr(workspace), ctypes.byref(nbytes)))
+    return out, lse
+
+
+def kvattn_append_decode_noalloc(geom, k_new, v_new, q, k_pool, v_pool, page_table, kv_len,
+                                 scale, out, lse, blocks=None, k_summary=None, n_splits=0,
+                                 stream=None):
+    """kvattn_append_decode with its partials in the library's static
+    per-GPU scratch: no workspace, and no allocation here either, so out and
+    lse are required. Raises KvattnError (KVATTN_E_WORKSPACE) when the
+    partials exceed NOALLOC_SCRATCH_BYTES."""
+    torch = _torch()
+    lib = load_library()
+    n_blk = _decode_args(geom, q, k_pool, v_pool, page_table, blocks)
+    n_new = k_new.shape[0]
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _need(t, name, torch.float32)
+        _size(t, name, n_new * geom.n_kv_heads * HEAD_DIM)
+    if k_summary is not None:
+        _need(k_summary, "k_summary", torch.float32)
+        _size(k_summary, "k_summary", geom.n_kv_heads * page_table.numel() * HEAD_DIM)
+    n_q_tok = q.shape[0]
+    _need(out, "out", torch.float32)
+    _need(lse, "lse", torch.float32)
+    _size(out, "out", q.numel())
+    _size(lse, "lse", n_q_tok * geom.n_kv_heads * geom.gqa)
+    _check("kvattn_append_decode_noalloc",
+           lib.kvattn_append_decode_noalloc(ctypes.byref(geom), _ptr(k_new), _ptr(v_new), n_new,
+                                            _ptr(q), n_q_tok, _ptr(k_pool), _ptr(v_pool),
+                                            _ptr(page_table), page_table.numel(), _ptr(blocks),
+                                            n_blk, int(kv_len), float(scale), _ptr(k_summary),
+                                            _ptr(out), _ptr(lse), int(n_splits),
+                                            _stream(stream)))
     return out, lse
 
 

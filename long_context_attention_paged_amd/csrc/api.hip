@@ -4,11 +4,21 @@
 // enqueued, and no path falls back to the CPU.
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/kvattn.h"
 #include "launch.hpp"
 
 using namespace kvattn;
+
+// Scratch of kvattn_append_decode_noalloc: the split-K partials of the entry
+// point that allocates nothing live in this file-scope array, one copy per
+// GPU at its own address, held until the process ends. In host code `scratch`
+// names a host-side stand-in, never the device memory: it is used only
+// through the per-device address that hipGetSymbolAddress returns. Calls on
+// one GPU share the array; calls that overlap on one GPU (other streams,
+// other threads) race.
+static __device__ __align__(256) uint8_t scratch[KVATTN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -372,6 +382,60 @@ int32_t kvattn_decode_splits(const kvattn_geom* geom, int32_t n_units) {
 
 namespace {
 
+// Split count, rows and partial sizes of one decode call.
+struct DecodePlan {
+  int32_t n_units = 0, splits = 0;
+  int64_t rows = 0;
+  size_t o_bytes = 0, lse_bytes = 0;
+};
+
+// Validates a decode call and sizes its partials. `need_device`: the split
+// count must come from the current device's CU count (a launch); otherwise
+// (a workspace query) a machine without a device sizes for 256 CUs, and the
+// launch recomputes with the real count, so query and launch must run on the
+// same device.
+kvattn_status decode_plan(const kvattn_geom* geom, const float* q, int32_t n_q_tok,
+                          const uint8_t* k_pool, const uint8_t* v_pool,
+                          const int32_t* page_table, int32_t n_logical_pages,
+                          const int32_t* blocks, int32_t n_blk, int64_t kv_len, float scale,
+                          float* out, float* lse, int32_t n_splits, bool need_device,
+                          DecodePlan* plan) {
+  kvattn_status st = check_decode(geom, q, n_q_tok, k_pool, v_pool, page_table, n_logical_pages,
+                                  blocks, n_blk, kv_len, scale, &plan->n_units);
+  if (st) return st;
+  if (!out || !lse || !aligned(out, 16) || n_splits < 0) return KVATTN_E_INVALID;
+  int32_t splits = n_splits;
+  if (splits == 0) {
+    int n_cu = 256;
+    if (need_device && (st = current_device(&n_cu))) return st;
+    if (!need_device && current_device(&n_cu) != KVATTN_OK) n_cu = 256;
+    splits = auto_decode_splits(geom->n_kv_heads, plan->n_units, n_cu);
+  }
+  if (splits > plan->n_units) splits = plan->n_units;
+  plan->splits = splits;
+  plan->rows = (int64_t)n_q_tok * geom->n_kv_heads * geom->gqa;
+  plan->o_bytes = round_up(sizeof(float) * (size_t)splits * plan->rows * KVATTN_HEAD_DIM);
+  plan->lse_bytes = round_up(sizeof(float) * (size_t)splits * plan->rows);
+  return KVATTN_OK;
+}
+
+// The decode kernel into o_part / lse_part, then the merge.
+kvattn_status decode_launch(const kvattn_geom* geom, const float* q, int32_t n_q_tok,
+                            const uint8_t* k_pool, const uint8_t* v_pool,
+                            const int32_t* page_table, int32_t n_logical_pages,
+                            const int32_t* blocks, int32_t n_blk, int64_t kv_len, float scale,
+                            float* out, float* lse, const DecodePlan& plan, float* o_part,
+                            float* lse_part, void* stream, const AppendArgs* app) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const kvattn_status st =
+      launch_decode_partials(geom, q, n_q_tok, k_pool, v_pool, page_table, n_logical_pages,
+                             blocks, n_blk, kv_len, scale, plan.n_units, plan.splits, o_part,
+                             lse_part, s, app);
+  if (st) return st;
+  return launched(launch_merge(plan.splits, plan.rows, KVATTN_HEAD_DIM, o_part, lse_part, out,
+                               lse, s));
+}
+
 // kvattn_decode, with the fused append when `app` is given.
 kvattn_status decode_impl(const kvattn_geom* geom, const float* q, int32_t n_q_tok,
                           const uint8_t* k_pool, const uint8_t* v_pool,
@@ -379,38 +443,55 @@ kvattn_status decode_impl(const kvattn_geom* geom, const float* q, int32_t n_q_t
                           const int32_t* blocks, int32_t n_blk, int64_t kv_len, float scale,
                           float* out, float* lse, int32_t n_splits, void* workspace,
                           size_t* workspace_bytes, void* stream, const AppendArgs* app) {
-  int32_t n_units = 0;
-  kvattn_status st = check_decode(geom, q, n_q_tok, k_pool, v_pool, page_table, n_logical_pages,
-                                  blocks, n_blk, kv_len, scale, &n_units);
+  DecodePlan plan;
+  kvattn_status st = decode_plan(geom, q, n_q_tok, k_pool, v_pool, page_table, n_logical_pages,
+                                 blocks, n_blk, kv_len, scale, out, lse, n_splits,
+                                 workspace != nullptr, &plan);
   if (st) return st;
-  if (!out || !lse || !aligned(out, 16) || n_splits < 0) return KVATTN_E_INVALID;
-  int32_t splits = n_splits;
-  if (splits == 0) {
-    // With a workspace query on a machine without a device, size for the
-    // default CU count; the launch below recomputes with the real count, so
-    // query and launch must run on the same device.
-    int n_cu = 256;
-    if (workspace && (st = current_device(&n_cu))) return st;
-    if (!workspace && current_device(&n_cu) != KVATTN_OK) n_cu = 256;
-    splits = auto_decode_splits(geom->n_kv_heads, n_units, n_cu);
-  }
-  if (splits > n_units) splits = n_units;
-  const int64_t rows = (int64_t)n_q_tok * geom->n_kv_heads * geom->gqa;
-  const size_t o_bytes = round_up(sizeof(float) * (size_t)splits * rows * KVATTN_HEAD_DIM);
-  const size_t need = kSyncBytes + o_bytes + round_up(sizeof(float) * (size_t)splits * rows);
+  const size_t need = kSyncBytes + plan.o_bytes + plan.lse_bytes;
   bool query_only = false;
   if ((st = workspace_check(workspace, workspace_bytes, need, &query_only))) return st;
   if (query_only) return KVATTN_OK;
   if ((st = current_device(nullptr))) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  float* o_part = reinterpret_cast<float*>(ws + kSyncBytes);
-  float* lse_part = reinterpret_cast<float*>(ws + kSyncBytes + o_bytes);
-  if ((st = launch_decode_partials(geom, q, n_q_tok, k_pool, v_pool, page_table, n_logical_pages,
-                                   blocks, n_blk, kv_len, scale, n_units, splits, o_part, lse_part,
-                                   s, app)))
-    return st;
-  return launched(launch_merge(splits, rows, KVATTN_HEAD_DIM, o_part, lse_part, out, lse, s));
+  return decode_launch(geom, q, n_q_tok, k_pool, v_pool, page_table, n_logical_pages, blocks,
+                       n_blk, kv_len, scale, out, lse, plan,
+                       reinterpret_cast<float*>(ws + kSyncBytes),
+                       reinterpret_cast<float*>(ws + kSyncBytes + plan.o_bytes), stream, app);
+}
+
+// The current device's copy of `scratch` (above), found once per device.
+struct ScratchAddress {
+  std::atomic<uint8_t*> ptr{nullptr};
+  std::mutex init;
+};
+ScratchAddress g_scratch[kMaxDevices];
+
+// The current device's copy of `scratch`, looked up once per device (with
+// that device current) on its first use.
+kvattn_status scratch_address(uint8_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return KVATTN_E_DEVICE;
+  }
+  ScratchAddress& a = g_scratch[dev];
+  uint8_t* p = a.ptr.load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(a.init);
+    p = a.ptr.load(std::memory_order_relaxed);
+    if (!p) {
+      void* addr = nullptr;
+      if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) {
+        (void)hipGetLastError();
+        return KVATTN_E_DEVICE;
+      }
+      p = static_cast<uint8_t*>(addr);
+      a.ptr.store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return KVATTN_OK;
 }
 
 }  // namespace
@@ -442,6 +523,32 @@ kvattn_status kvattn_append_decode(const kvattn_geom* geom, const float* k_new, 
   const AppendArgs app{k_new, v_new, k_pool, v_pool, n_new, k_summary};
   return decode_impl(geom, q, n_q_tok, k_pool, v_pool, page_table, n_logical_pages, blocks, n_blk,
                      kv_len, scale, out, lse, n_splits, workspace, workspace_bytes, stream, &app);
+}
+
+kvattn_status kvattn_append_decode_noalloc(const kvattn_geom* geom, const float* k_new,
+                                           const float* v_new, int32_t n_new, const float* q,
+                                           int32_t n_q_tok, uint8_t* k_pool, uint8_t* v_pool,
+                                           const int32_t* page_table, int32_t n_logical_pages,
+                                           const int32_t* blocks, int32_t n_blk, int64_t kv_len,
+                                           float scale, float* k_summary, float* out, float* lse,
+                                           int32_t n_splits, void* stream) {
+  if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16)) return KVATTN_E_INVALID;
+  if (n_new < 1 || n_new > KVATTN_MAX_APPEND_TOKENS || n_new > kv_len) return KVATTN_E_INVALID;
+  if (k_summary && !aligned(k_summary, 16)) return KVATTN_E_INVALID;
+  DecodePlan plan;
+  kvattn_status st = decode_plan(geom, q, n_q_tok, k_pool, v_pool, page_table, n_logical_pages,
+                                 blocks, n_blk, kv_len, scale, out, lse, n_splits, true, &plan);
+  if (st) return st;
+  // every partial is written by the decode kernel before the merge reads it,
+  // so nothing in the scratch needs clearing between calls
+  if (plan.o_bytes + plan.lse_bytes > KVATTN_NOALLOC_SCRATCH_BYTES) return KVATTN_E_WORKSPACE;
+  if ((st = current_device(nullptr))) return st;
+  uint8_t* base = nullptr;
+  if ((st = scratch_address(&base))) return st;
+  const AppendArgs app{k_new, v_new, k_pool, v_pool, n_new, k_summary};
+  return decode_launch(geom, q, n_q_tok, k_pool, v_pool, page_table, n_logical_pages, blocks,
+                       n_blk, kv_len, scale, out, lse, plan, reinterpret_cast<float*>(base),
+                       reinterpret_cast<float*>(base + plan.o_bytes), stream, &app);
 }
 
 kvattn_status kvattn_decode_partials(const kvattn_geom* geom, const float* q, int32_t n_q_tok,

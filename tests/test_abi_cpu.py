@@ -124,6 +124,35 @@ def test_append_decode_validation_and_workspace():
     assert append_decode(g, n_splits=8, nbytes=need - 1)[0] == E_WORKSPACE
 
 
+def append_decode_noalloc(g, **kw):
+    a = dict(k_new=FAKE, v_new=FAKE, n_new=4, q=FAKE, n_q_tok=4, k_pool=FAKE, v_pool=FAKE,
+             table=FAKE, n_logical=16, blocks=None, n_blk=0, kv_len=1000, scale=0.0625,
+             summ=None, out=FAKE, lse=FAKE, n_splits=8)
+    a.update(kw)
+    return kv.load_library().kvattn_append_decode_noalloc(
+        ctypes.byref(g), P(a["k_new"]), P(a["v_new"]), a["n_new"], P(a["q"]), a["n_q_tok"],
+        P(a["k_pool"]), P(a["v_pool"]), P(a["table"]), a["n_logical"], P(a["blocks"]), a["n_blk"],
+        a["kv_len"], a["scale"], P(a["summ"]), P(a["out"]), P(a["lse"]), a["n_splits"], None)
+
+
+def test_append_decode_noalloc_validation():
+    g = geom()
+    assert append_decode_noalloc(g, k_new=0) == E_INVALID
+    assert append_decode_noalloc(g, v_new=FAKE + 4) == E_INVALID
+    assert append_decode_noalloc(g, n_new=0) == E_INVALID
+    assert append_decode_noalloc(g, n_new=33) == E_INVALID
+    assert append_decode_noalloc(g, summ=FAKE + 4) == E_INVALID
+    assert append_decode_noalloc(g, out=0) == E_INVALID
+    assert append_decode_noalloc(g, n_splits=-1) == E_INVALID
+    assert append_decode_noalloc(g, n_q_tok=6) == E_UNSUPPORTED   # decode's own checks apply
+    # partials beyond the static scratch: 64 splits x 8 KV heads x 32 rows
+    # x 1028 bytes > KVATTN_NOALLOC_SCRATCH_BYTES; rejected before any device call
+    g8 = geom(n_kv=8, gqa=8, n_phys=64)
+    big = dict(n_q_tok=4, n_logical=64, kv_len=64 * 128, n_splits=64)
+    assert append_decode_noalloc(g8, **big) == E_WORKSPACE
+    assert 64 * 8 * 32 * 1028 > kv.NOALLOC_SCRATCH_BYTES >= 32 * 8 * 32 * 1028 + 512
+
+
 def test_prefill_and_select_validation():
     lib = kv.load_library()
     g = geom()
