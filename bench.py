@@ -250,6 +250,7 @@ def bench_decode(w, dev, steps, warmup, sparse=False, v_type=0, k_type=0):
     }
     if sparse:
         res["recall"] = needle_recall(w, pools, blocks)
+        pools.blocks0 = blocks[0]  # layer 0's selection, for the CPU baseline
     return res, pools
 
 
@@ -380,12 +381,14 @@ def bench_prefill(w, dev, steps, warmup, v_type=0, k_type=0):
 
 
 def bench_prefill_host_pool(w, dev, steps, warmup):
-    """Prefill with the page pool resident in pinned host memory (a7): while
-    layer L computes from one device staging pool, a copy stream fills the
-    other with layer L+1's pages; events order the two streams. The rate is
-    bound by the host link, not by the GPU."""
+    """Prefill with every layer's pool in pinned host memory (a7,
+    streaming.HostPoolPrefill): while layer L computes from one device staging
+    pool, a copy stream fills the other with layer L+1's pages, and each
+    layer's chunk pages go back to the host pool. Bound by the host link, not
+    by the GPU."""
     import torch
     import long_context_attention_paged_amd as kv
+    from long_context_attention_paged_amd import streaming
     pools = LayerPools(w, dev)
     hk, hv = [], []
     for layer in range(w.n_layers):  # move every layer's pool to pinned host memory
@@ -396,36 +399,12 @@ def bench_prefill_host_pool(w, dev, steps, warmup):
     torch.cuda.synchronize()
     pools.kp = pools.vp = None
     torch.cuda.empty_cache()
-    stage_k = [torch.empty(hk[0].numel(), dtype=torch.uint8, device=dev) for _ in range(2)]
-    stage_v = [torch.empty(hv[0].numel(), dtype=torch.uint8, device=dev) for _ in range(2)]
-    pages = list(range(pools.n_phys))
+    hp = streaming.HostPoolPrefill(pools.geom, hk, hv, pools.table, dev)
     outs = [torch.empty_like(q) for q in pools.q]
     lses = [torch.empty(q.shape[:2], dtype=torch.float32, device=dev) for q in pools.q]
-    ws = kv.workspace(512 << 20, dev)
-    copy = torch.cuda.Stream()
-    compute = torch.cuda.current_stream()
 
     def step():
-        copied = [torch.cuda.Event() for _ in range(w.n_layers)]
-        done = [torch.cuda.Event() for _ in range(w.n_layers)]
-        for layer in range(w.n_layers + 1):
-            if layer < w.n_layers:  # copy layer `layer` once its staging slot is free
-                if layer >= 2:
-                    copy.wait_event(done[layer - 2])
-                else:  # the slot's last reader is the previous step's layer 14 / 15
-                    copy.wait_stream(compute)
-                kv.kvattn_prefetch_pages(pools.geom, hk[layer], hv[layer], stage_k[layer % 2],
-                                         stage_v[layer % 2], pages, stream=copy)
-                copied[layer].record(copy)
-            c = layer - 1           # compute the previous layer meanwhile
-            if c >= 0:
-                compute.wait_event(copied[c])
-                kv.kvattn_quantize_pages(pools.geom, pools.new_k[c], pools.new_v[c], w.pos0,
-                                         pools.table, stage_k[c % 2], stage_v[c % 2])
-                kv.kvattn_prefill_chunk(pools.geom, pools.q[c], stage_k[c % 2], stage_v[c % 2],
-                                        pools.table, w.pos0, 1.0 / 16.0, out=outs[c],
-                                        lse=lses[c], workspace=ws)
-                done[c].record(compute)
+        hp.step(pools.q, pools.new_k, pools.new_v, w.pos0, 1.0 / 16.0, outs, lses)
 
     for _ in range(warmup):
         step()
@@ -436,14 +415,21 @@ def bench_prefill_host_pool(w, dev, steps, warmup):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) / steps * 1e3
     fl = prefill_flops_per_layer(w)
-    pool_bytes = (hk[0].numel() + hv[0].numel()) * w.n_layers
+    geom = pools.geom
+    page = geom.n_kv_heads * (geom.k_record_bytes + geom.v_record_bytes)
+    h2d = len(hp.pages_read(w.pos0, w.chunk)) * page * w.n_layers
+    d2h = len(hp.pages_written(w.pos0, w.chunk)) * page * w.n_layers
     return {
         "ms_per_step": ms,
         "tokens_per_s": w.chunk / (ms * 1e-3),
         "tflops": fl * w.n_layers / (ms * 1e-3) / 1e12,
-        "host_to_device_bytes_per_step": pool_bytes,
-        "host_to_device_gbs": pool_bytes / (ms * 1e-3) / 1e9,
-        "note": "pool in pinned host memory, layer-ahead page prefetch on a copy stream",
+        "host_to_device_bytes_per_step": h2d,
+        "host_to_device_gbs": h2d / (ms * 1e-3) / 1e9,
+        "device_to_host_bytes_per_step": d2h,
+        "device_pool_bytes": hp.device_bytes(),
+        "workspace_error": kv.workspace_error(hp.ws),
+        "note": "pools in pinned host memory, layer-ahead page prefetch on a copy stream, "
+                "chunk pages written back",
     }, pools
 
 
@@ -566,23 +552,26 @@ def bench_kvmem_host(w, dev, steps, warmup, budgets=(32768, 65536, 98304)):
     return res, pools
 
 
-def cpu_baseline_decode(w, pools):
-    """The oracle, as it stands, on one (layer, KV head) of the workload."""
-    import numpy as np
+def cpu_baseline_decode(w, pools, blocks=None):
+    """The oracle, as it stands, on layer 0 of the workload (every KV head;
+    with `blocks`, layer 0's selected block lists: the sparse decode)."""
     import oracle
-    from long_context_attention_paged_amd import synth
     kp = pools.kp[0].cpu().numpy().reshape(pools.n_phys, w.n_kv, K_REC)
     vp = pools.vp[0].cpu().numpy().reshape(pools.n_phys, w.n_kv, V_REC)
     q = pools.q[0].cpu().numpy()
+    blk = None if blocks is None else blocks.cpu().numpy()
     t0 = time.perf_counter()
     oracle.decode(q, w.gqa, kp, vp, pools.table_np, w.n_pages, w.kv_len, 1.0 / 16.0,
-                  kv_heads=[0])
+                  blocks=blk)
     dt = time.perf_counter() - t0
-    nbytes = w.kv_len * (272 + 144)
+    tokens = w.kv_len if blk is None else blk.shape[1] * 128
+    nbytes = tokens * w.n_kv * (272 + 144)
+    what = (f"{tokens} tokens" if blk is None else
+            f"the {blk.shape[1]} selected blocks ({tokens} tokens)")
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": blas_threads(),
             "kind": "oracle", "seconds": dt,
-            "sample": f"{w.name}: layer 0, KV head 0 ({w.kv_len} tokens x {w.gqa * w.n_q_tok} "
-                      f"query rows), binary64, numpy + OpenBLAS"}
+            "sample": f"{w.name}: layer 0 of {w.n_layers}, all {w.n_kv} KV heads ({what} x "
+                      f"{w.gqa * w.n_q_tok} query rows per KV head), binary64, numpy + OpenBLAS"}
 
 
 def cpu_baseline_prefill(w, pools, n_tok=24):
@@ -670,13 +659,24 @@ def blas_threads():
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it, with its family / model /
+    stepping, clock and the logical CPUs this process may run on."""
+    info = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = line.split(":", 1)
+                info.setdefault(k.strip(), v.strip())
     except OSError:
-        pass
-    return platform.processor()
+        return platform.processor()
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return (f"{info.get('model name', platform.processor())} (family {info.get('cpu family', '?')}"
+            f" model {info.get('model', '?')} stepping {info.get('stepping', '?')}, "
+            f"{info.get('cpu MHz', '?')} MHz, {info.get('cpu cores', '?')} cores per socket, "
+            f"{usable} logical CPUs usable)")
 
 
 def profile_kernels(dev, layers, reps):
@@ -735,8 +735,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--configs", default="3,4,2,5,3s,5h",
-                    help="workloads to run: 2 decode-131k, 3 verify-262k, 4 prefill, 5 kvmem, "
+    ap.add_argument("--configs", default="3,4,2,5,1,3s,5h,4h,3q4,3q5",
+                    help="workloads to run: 1 tiny-decode-4k (latency), 2 decode-131k, "
+                         "3 verify-262k, 4 prefill, 5 kvmem, "
                          "4h prefill with the pool in pinned host memory, 3s verify with the "
                          "history streamed from host memory (2100 MiB device working set), "
                          "5h kvmem with its history in host memory (budget sweep), "
@@ -811,8 +812,14 @@ def main():
         log(f"workload {w.name}")
         if c in (1, 2, 3):
             res, pools = bench_decode(w, dev, args.steps, args.warmup)
+            if c == 1:  # a latency case: one small layer per step
+                res["us_per_step"] = res["ms_per_step"] * 1e3
+                res["kernel_us"] = res["kernel_ms"] * 1e3
+                res["call_us"] = res["launch_ms"] * 1e3
             if c == 2:
                 res["key_rotation"] = rotation_quality(w, pools, dev)
+                if not args.no_cpu_baseline:
+                    res["cpu_baseline"] = cpu_baseline_decode(w, pools)
             if c == 3:
                 decode_res = res
                 if not args.no_cpu_baseline:
@@ -826,6 +833,8 @@ def main():
             extra[w.name] = res
         elif c == 5:
             res, pools = bench_decode(w, dev, args.steps, args.warmup, sparse=True)
+            if not args.no_cpu_baseline:
+                res["cpu_baseline"] = cpu_baseline_decode(w, pools, blocks=pools.blocks0)
             extra[w.name] = res
         del pools
         torch.cuda.empty_cache()

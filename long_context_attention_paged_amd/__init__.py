@@ -431,6 +431,21 @@ def kvattn_prefill_chunk(geom, q, k_pool, v_pool, page_table, pos0, scale, out=N
     return out, lse
 
 
+def prefill_workspace_bytes(geom, q, k_pool, v_pool, page_table, pos0, n_groups=0):
+    """Workspace bytes kvattn_prefill_chunk needs for these arguments (its
+    NULL-workspace query; nothing is enqueued)."""
+    lib = load_library()
+    n_heads = geom.n_kv_heads * geom.gqa
+    size = ctypes.c_size_t(0)
+    # out and lse are only checked for presence by the query
+    _check("kvattn_prefill_chunk", lib.kvattn_prefill_chunk(
+        ctypes.byref(geom), _ptr(q), q.shape[0], _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
+        page_table.numel(), int(pos0), 1.0, _ptr(q), _ptr(q), int(n_groups), None,
+        ctypes.byref(size), None))
+    assert q.shape[1] == n_heads
+    return int(size.value)
+
+
 def kvattn_prefill_groups(geom, chunk, pos0):
     """Page-group count kvattn_prefill_chunk picks by itself."""
     return load_library().kvattn_prefill_groups(ctypes.byref(geom), int(chunk), int(pos0))
@@ -533,18 +548,18 @@ def kvattn_gather_blocks(geom, src_k_pool, src_v_pool, page_table, blocks, n_sel
 def kvattn_prefetch_pages(geom, src_k_pool, src_v_pool, dst_k_pool, dst_v_pool, pages,
                           stream=None):
     """Page prefetch (a7): copy the records of physical `pages` (a host
-    sequence of ints) from the src pools (typically pinned host tensors) to the
-    dst pools (device tensors), asynchronously on `stream`."""
+    sequence of ints) from the src pools to the dst pools, asynchronously on
+    `stream`. Each pool is a device tensor or a pinned host tensor: typically
+    host to device, and device to host to write pages back."""
     import numpy as np
     torch = _torch()
     lib = load_library()
-    for name, t in (("src_k_pool", src_k_pool), ("src_v_pool", src_v_pool)):
+    for name, t in (("src_k_pool", src_k_pool), ("src_v_pool", src_v_pool),
+                    ("dst_k_pool", dst_k_pool), ("dst_v_pool", dst_v_pool)):
         if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or not t.is_contiguous():
             raise TypeError(f"{name} must be a contiguous uint8 torch tensor")
         if not t.is_cuda and not t.is_pinned():
             raise ValueError(f"{name} must be on the GPU or in pinned host memory")
-    _need(dst_k_pool, "dst_k_pool", torch.uint8)
-    _need(dst_v_pool, "dst_v_pool", torch.uint8)
     _pools(geom, dst_k_pool, dst_v_pool)
     _pools(geom, src_k_pool, src_v_pool)
     idx = np.ascontiguousarray(np.asarray(pages, dtype=np.int32))

@@ -19,6 +19,12 @@ every copy is the library's hipMemcpyAsync:
    the two, which is exact (the LSE merge is associative over any page split).
 
 Device working set: n_layers * n_res pages resident plus 2 * n_hist staged.
+
+HostPoolPrefill does the same for chunked prefill ([RDNA4] "Online Log-Sum-Exp
+prefill & pipelined prefetch"): every layer's whole pool stays in pinned host
+memory as the cache of record, the pages a chunk reads are copied into one of
+two device staging pools a layer ahead, the chunk is quantised and attended
+there, and the chunk's pages go back to the host pool.
 """
 import numpy as np
 
@@ -242,3 +248,97 @@ class KVMemHostDecode:
                                       lse_part=self.lparts[1:])
             kv.kvattn_merge_lse(self.parts, self.lparts, out=outs[c].view(-1, kv.HEAD_DIM),
                                 lse=lses[c].view(-1))
+
+
+class HostPoolPrefill:
+    """Chunked prefill with every layer's pool in pinned host memory (a7:
+    [RDNA4] "Online Log-Sum-Exp prefill & pipelined prefetch"; [STREAM] step
+    ④ prefill with -ub 512 over a host-resident cache). host_k[L], host_v[L]
+    are pinned uint8 pools of geom's size (the physical layout of a device
+    pool) and page_table the logical-to-physical map shared by the layers.
+
+    Per step and layer, on two streams ordered by events:
+     - copy stream: the physical pages of logical pages 0 .. ceil((pos0 +
+       chunk) / 128) - 1 go from the host pool to the same slots of one of two
+       device staging pools (kvattn_prefetch_pages; layer L+1 copies while
+       layer L computes);
+     - compute stream: kvattn_quantize_pages writes the chunk's tokens into
+       the staged pages, kvattn_prefill_chunk attends;
+     - copy stream again: the pages holding the chunk go back to the host pool
+       (device to host), so the next chunk reads them there.
+    A staging slot is refilled only after its layer's compute and write-back
+    are done. Device working set: two staging pools (2 x one layer's pool)."""
+
+    def __init__(self, geom, host_k, host_v, page_table, dev, workspace_bytes=0):
+        import torch
+        self.geom, self.host_k, self.host_v = geom, host_k, host_v
+        self.table = torch.as_tensor(page_table, dtype=torch.int32).to(dev)
+        self.table_host = np.asarray(torch.as_tensor(page_table).cpu(), np.int32)
+        for t in list(host_k) + list(host_v):
+            if not t.is_pinned():
+                raise ValueError("HostPoolPrefill needs pinned host pools")
+        self.stage_k = [torch.empty(host_k[0].numel(), dtype=torch.uint8, device=dev)
+                        for _ in range(2)]
+        self.stage_v = [torch.empty(host_v[0].numel(), dtype=torch.uint8, device=dev)
+                        for _ in range(2)]
+        self.ws = kv.workspace(workspace_bytes, dev)  # grown on demand (zeroed)
+        self.dev = dev
+        self.copy = torch.cuda.Stream(device=dev)
+
+    def device_bytes(self):
+        return sum(t.numel() for t in self.stage_k + self.stage_v)
+
+    def _workspace_for(self, q, pos0):
+        need = kv.prefill_workspace_bytes(self.geom, q, self.stage_k[0], self.stage_v[0],
+                                          self.table, pos0)
+        if self.ws.numel() < need:
+            import torch
+            torch.cuda.current_stream().synchronize()  # the old one may still be in use
+            self.ws = kv.workspace(need, self.dev)
+
+    def pages_read(self, pos0, chunk):
+        """Physical pages a chunk at pos0 reads, ascending (so runs coalesce)."""
+        n = (pos0 + chunk + PAGE - 1) // PAGE
+        return sorted(set(int(x) for x in self.table_host[:n]))
+
+    def pages_written(self, pos0, chunk):
+        """Physical pages that hold the chunk's tokens."""
+        return sorted(set(int(x) for x in
+                          self.table_host[pos0 // PAGE:(pos0 + chunk - 1) // PAGE + 1]))
+
+    def step(self, q, k_new, v_new, pos0, scale, outs, lses):
+        """Enqueue one chunk over every layer: q[L] [chunk, n_heads, 256] and
+        k_new[L], v_new[L] [chunk, n_kv, 256] (positions pos0 ..), results
+        into outs[L], lses[L]."""
+        import torch
+        compute = torch.cuda.current_stream()
+        n = len(q)
+        chunk = q[0].shape[0]
+        read = self.pages_read(pos0, chunk)
+        written = self.pages_written(pos0, chunk)
+        self._workspace_for(q[0], pos0)
+        copied = [torch.cuda.Event() for _ in range(n)]
+        done = [torch.cuda.Event() for _ in range(n)]
+        for layer in range(n + 1):
+            if layer < n:  # stage layer `layer` once its slot is free
+                if layer < 2:
+                    self.copy.wait_stream(compute)  # the previous step's last layers
+                else:  # its write-back was enqueued before on this stream
+                    self.copy.wait_event(done[layer - 2])
+                kv.kvattn_prefetch_pages(self.geom, self.host_k[layer], self.host_v[layer],
+                                         self.stage_k[layer % 2], self.stage_v[layer % 2],
+                                         read, stream=self.copy)
+                copied[layer].record(self.copy)
+            c = layer - 1  # compute the previous layer meanwhile
+            if c < 0:
+                continue
+            sk, sv = self.stage_k[c % 2], self.stage_v[c % 2]
+            compute.wait_event(copied[c])
+            kv.kvattn_quantize_pages(self.geom, k_new[c], v_new[c], pos0, self.table, sk, sv)
+            kv.kvattn_prefill_chunk(self.geom, q[c], sk, sv, self.table, pos0, scale,
+                                    out=outs[c], lse=lses[c], workspace=self.ws)
+            done[c].record(compute)
+            self.copy.wait_event(done[c])
+            kv.kvattn_prefetch_pages(self.geom, sk, sv, self.host_k[c], self.host_v[c], written,
+                                     stream=self.copy)
+        compute.wait_stream(self.copy)  # the write-backs end the step

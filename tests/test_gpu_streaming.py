@@ -153,3 +153,61 @@ def test_kvmem_host_tier_matches_oracle():
     full = quant.summaries_from_pool(pools.ok, table, n_pages, n_kv)
     got = host(summ)
     assert (got[:, n_pages - 1].view(np.uint32) == full[:, n_pages - 1].view(np.uint32)).all()
+
+
+@pytest.mark.parametrize("k_type,v_type", [(0, 0), (2, 1)])  # q8_0/q4_0 and q5_1/q8_0 caches
+def test_host_pool_prefill_matches_oracle(k_type, v_type):
+    """streaming.HostPoolPrefill (a7): three layers whose pools live only in
+    pinned host memory, two consecutive chunks. Each chunk's out and lse match
+    the oracle's prefill over the oracle's pool (prefill bar 1e-2 max-abs),
+    and the host pools afterwards equal the oracle's quantisation bit for bit.
+    The second chunk reads the first chunk's tokens from the host pools, where
+    only the write-back put them; every workspace error word stays 0."""
+    n_kv, gqa, n_layers = 2, 6, 3
+    pos0, chunk0, chunk1 = 36 * 128 + 50, 200, 150
+    n_pages = (pos0 + chunk0 + chunk1 + 127) // 128
+    n_phys = n_pages + 2
+    g = np.random.default_rng(70 + k_type)
+    geom = kv.Geom(n_kv, gqa, n_phys, v_type=v_type, k_type=k_type)
+    table = g.permutation(n_phys)[:n_pages].astype(np.int32)
+    pools, host_k, host_v = [], [], []
+    for _ in range(n_layers):
+        p = Pools(n_phys, n_kv, gqa, init_seed=int(g.integers(1 << 30)), v_type=v_type,
+                  k_type=k_type)
+        p.write(g.standard_normal((pos0, n_kv, 256)).astype(np.float32),
+                g.standard_normal((pos0, n_kv, 256)).astype(np.float32), 0, table)
+        torch.cuda.synchronize()
+        hk = torch.empty(p.gk.numel(), dtype=torch.uint8, pin_memory=True)
+        hv = torch.empty(p.gv.numel(), dtype=torch.uint8, pin_memory=True)
+        hk.copy_(p.gk)
+        hv.copy_(p.gv)
+        p.gk = p.gv = None  # the device pools are gone: the host pools are the cache
+        pools.append(p)
+        host_k.append(hk)
+        host_v.append(hv)
+    hp = streaming.HostPoolPrefill(geom, host_k, host_v, table, DEV)
+    start = pos0
+    for chunk in (chunk0, chunk1):
+        qs = [g.standard_normal((chunk, n_kv * gqa, 256)).astype(np.float32)
+              for _ in range(n_layers)]
+        kns = [g.standard_normal((chunk, n_kv, 256)).astype(np.float32) for _ in range(n_layers)]
+        vns = [g.standard_normal((chunk, n_kv, 256)).astype(np.float32) for _ in range(n_layers)]
+        outs = [torch.empty((chunk, n_kv * gqa, 256), dtype=torch.float32, device=DEV)
+                for _ in range(n_layers)]
+        lses = [torch.empty((chunk, n_kv * gqa), dtype=torch.float32, device=DEV)
+                for _ in range(n_layers)]
+        print(f"host-pool prefill: chunk {chunk} at {start}", flush=True)
+        hp.step([gpu(x) for x in qs], [gpu(x) for x in kns], [gpu(x) for x in vns], start,
+                1 / 16, outs, lses)
+        torch.cuda.synchronize()
+        assert kv.workspace_error(hp.ws) == 0
+        for c in range(n_layers):
+            p = pools[c]
+            quant.quantize_into_pool(kns[c], vns[c], start, table, p.ok, p.ov)
+            assert (host(host_k[c]).reshape(p.ok.shape) == p.ok).all()
+            assert (host(host_v[c]).reshape(p.ov.shape) == p.ov).all()
+            ref_o, ref_l = oracle.prefill_chunk(qs[c], gqa, p.ok, p.ov, table, n_pages, start,
+                                                1 / 16)
+            eo, el, rr = compare(outs[c], lses[c], ref_o, ref_l)
+            assert eo <= 1e-2 and el <= 1e-2, (chunk, c, eo, el, rr)
+        start += chunk
