@@ -325,6 +325,67 @@ def needle_recall(w, pools, blocks):
     return {"needles": len(needles), "min_found": min(hits), "mean_found": sum(hits) / len(hits)}
 
 
+def recall_curve(dev, n_layers=2, contexts=(131072, 262144, 393216, 523264),
+                 budgets=(32768, 65536, 98304), per_block=3):
+    """Needle recall of the selection against context length and budget, with
+    faint needles (synth.faint_needle_keys: `per_block` needle tokens in each
+    of 20 needle blocks, all within the first 112K tokens so every context
+    holds them). The keys of the longest context are quantised once per layer
+    (with their block summaries); a shorter context selects over the prefix of
+    its blocks (its own recent window of 128 blocks, k_top = budget / 128).
+    Recall = needle blocks kept, over every (layer, KV head)."""
+    import numpy as np
+    import torch
+    import long_context_attention_paged_amd as kv
+    from long_context_attention_paged_amd import synth
+    w = synth.WORKLOADS[5]
+    n_pages = w.n_pages
+    span = min(contexts) // 128 - w.n_recent
+    geom = kv.Geom(w.n_kv, w.gqa, n_pages)
+    table = torch.arange(n_pages, dtype=torch.int32, device=dev)
+    kp = torch.zeros(n_pages * w.n_kv * geom.k_record_bytes, dtype=torch.uint8, device=dev)
+    vp = torch.zeros(n_pages * w.n_kv * geom.v_record_bytes, dtype=torch.uint8, device=dev)
+    summ = torch.zeros((w.n_kv, n_pages, 256), dtype=torch.float32, device=dev)
+    ws = kv.workspace(8 * w.n_kv * n_pages + 4096, dev)
+    points = [(c, 32768) for c in contexts] + [(contexts[-1], b) for b in budgets if b != 32768]
+    found = {p: [] for p in points}
+    for layer in range(n_layers):
+        q = synth.queries(w, layer)
+        K = np.empty((w.kv_len, w.n_kv, 256), np.float32)
+        needles = None
+        for h in range(w.n_kv):
+            K[:, h], needles = synth.faint_needle_keys(w, layer, h, q, span, per_block)
+        step = 65536
+        zeros = torch.zeros((step, w.n_kv, 256), dtype=torch.float32, device=dev)
+        for a in range(0, w.kv_len, step):
+            b = min(w.kv_len, a + step)
+            kv.kvattn_quantize_pages(geom, torch.from_numpy(K[a:b]).to(dev), zeros[:b - a], a,
+                                     table, kp, vp, summ)
+        del K
+        qd = torch.from_numpy(q[-1]).to(dev)
+        nset = set(int(x) for x in needles)
+        for ctx, budget in points:
+            nb = ctx // 128
+            out = torch.empty((w.n_kv, kv.kvattn_select_count(nb, w.n_recent, budget // 128)),
+                              dtype=torch.int32, device=dev)
+            kv.kvattn_select_blocks(geom, qd, summ, n_pages, nb, w.n_recent, budget // 128,
+                                    out_blocks=out, workspace=ws)
+            sel = out.cpu().numpy()
+            for h in range(w.n_kv):
+                found[(ctx, budget)].append(len(nset & set(sel[h].tolist())))
+    return {
+        "needle_model": f"{per_block} needle tokens (cosine 1/2 to the query group's sum) in each "
+                        f"of {w.n_needles} blocks among the first {span} blocks, N(0,1) keys "
+                        f"otherwise; {n_layers} layers x {w.n_kv} KV heads",
+        "points": [{"context": ctx, "budget": budget, "k_top": budget // 128,
+                    "candidates": ctx // 128 - w.n_recent,
+                    "mean_found": float(np.mean(found[(ctx, budget)])),
+                    "min_found": int(np.min(found[(ctx, budget)])),
+                    "max_found": int(np.max(found[(ctx, budget)])), "of": w.n_needles}
+                   for ctx, budget in points],
+    }
+
+
 def prefill_flops_per_layer(w):
     """4 * D flops per unmasked (query head, key) pair, one layer."""
     pairs = w.chunk * w.pos0 + w.chunk * (w.chunk + 1) // 2
@@ -836,6 +897,11 @@ def main():
             if not args.no_cpu_baseline:
                 res["cpu_baseline"] = cpu_baseline_decode(w, pools, blocks=pools.blocks0)
             extra[w.name] = res
+            del pools
+            torch.cuda.empty_cache()
+            pools = None
+            res["recall_curve"] = recall_curve(dev)
+            log(f"{w.name} recall curve: {json.dumps(res['recall_curve'])}")
         del pools
         torch.cuda.empty_cache()
         log(f"{w.name}: {json.dumps(res)}")

@@ -118,6 +118,22 @@ kvattn_status check_pools(const kvattn_geom* g, const uint8_t* k_pool, const uin
 
 size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
 
+// a * b * c rounded up to 256, or 0 when the product does not fit in half of
+// size_t (the caller rejects such a call as invalid).
+size_t checked_bytes(uint64_t a, uint64_t b, uint64_t c) {
+  uint64_t ab = 0, abc = 0;
+  if (__builtin_mul_overflow(a, b, &ab) || __builtin_mul_overflow(ab, c, &abc) ||
+      abc > (uint64_t)(SIZE_MAX >> 1))
+    return 0;
+  return round_up((size_t)abc);
+}
+
+// Whether positions [pos0, pos0 + n) fit in n_logical_pages pages, with no
+// overflow for any pos0 >= 0 and n >= 1.
+bool fits_pages(int64_t pos0, int64_t n, int32_t n_logical_pages) {
+  return pos0 <= (int64_t)n_logical_pages * KVATTN_PAGE_TOKENS - n;
+}
+
 // Every workspace starts with kSyncBytes of counters: zero before the first
 // call that uses the workspace, and left zero by every call. Word 0 is the
 // error word (bit 0: a prefill launch's bounded waits gave up).
@@ -177,7 +193,7 @@ kvattn_status kvattn_quantize_pages(const kvattn_geom* geom, const float* k, con
   if (!k || !v || !page_table || !aligned(k, 16) || !aligned(v, 16)) return KVATTN_E_INVALID;
   if (k_summary && !aligned(k_summary, 16)) return KVATTN_E_INVALID;
   if (pos0 < 0 || n_tok < 1 || n_logical_pages < 1) return KVATTN_E_INVALID;
-  if (pos0 + n_tok > (int64_t)n_logical_pages * KVATTN_PAGE_TOKENS) return KVATTN_E_INVALID;
+  if (!fits_pages(pos0, n_tok, n_logical_pages)) return KVATTN_E_INVALID;
   if ((st = current_device(nullptr))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = launched(launch_quantize(k, v, pos0, n_tok, geom->n_kv_heads, page_table,
@@ -325,14 +341,17 @@ kvattn_status check_prefill(const kvattn_geom* geom, const float* q, int32_t chu
   if ((st = check_pools(geom, k_pool, v_pool))) return st;
   if (!q || !page_table || !aligned(q, 16)) return KVATTN_E_INVALID;
   if (chunk < 1 || pos0 < 0 || n_logical_pages < 1) return KVATTN_E_INVALID;
-  if (pos0 + chunk > (int64_t)n_logical_pages * KVATTN_PAGE_TOKENS) return KVATTN_E_INVALID;
+  if (!fits_pages(pos0, chunk, n_logical_pages)) return KVATTN_E_INVALID;
   return check_scale(scale);
 }
 
 // Page groups chosen by the library: about three rounds of the grid, at most
 // one group per page.
 int32_t auto_prefill_groups(const kvattn_geom* geom, int32_t chunk, int64_t pos0, int n_cu) {
-  const int64_t n_pages = (pos0 + chunk + KVATTN_PAGE_TOKENS - 1) / KVATTN_PAGE_TOKENS;
+  // ceil((pos0 + chunk) / 128) without forming pos0 + chunk
+  const int64_t n_pages = pos0 / KVATTN_PAGE_TOKENS +
+                          (pos0 % KVATTN_PAGE_TOKENS + chunk + KVATTN_PAGE_TOKENS - 1) /
+                              KVATTN_PAGE_TOKENS;
   const int64_t rows_per_head = (int64_t)chunk * geom->gqa;
   const int64_t tiles =
       geom->n_kv_heads * ((rows_per_head + prefill_rows_per_tile() - 1) / prefill_rows_per_tile());
@@ -414,8 +433,9 @@ kvattn_status decode_plan(const kvattn_geom* geom, const float* q, int32_t n_q_t
   if (splits > plan->n_units) splits = plan->n_units;
   plan->splits = splits;
   plan->rows = (int64_t)n_q_tok * geom->n_kv_heads * geom->gqa;
-  plan->o_bytes = round_up(sizeof(float) * (size_t)splits * plan->rows * KVATTN_HEAD_DIM);
-  plan->lse_bytes = round_up(sizeof(float) * (size_t)splits * plan->rows);
+  plan->o_bytes = checked_bytes(splits, plan->rows, sizeof(float) * KVATTN_HEAD_DIM);
+  plan->lse_bytes = checked_bytes(splits, plan->rows, sizeof(float));
+  if (!plan->o_bytes || !plan->lse_bytes) return KVATTN_E_INVALID;  // beyond any memory
   return KVATTN_OK;
 }
 
@@ -595,8 +615,10 @@ kvattn_status kvattn_prefill_chunk(const kvattn_geom* geom, const float* q, int3
     groups = auto_prefill_groups(geom, chunk, pos0, n_cu);
   }
   if (groups > n_pages) groups = n_pages;
-  const size_t o_bytes = round_up(sizeof(float) * (size_t)groups * rows * KVATTN_HEAD_DIM);
-  const size_t need = kSyncBytes + o_bytes + round_up(sizeof(float) * (size_t)groups * rows);
+  const size_t o_bytes = checked_bytes(groups, rows, sizeof(float) * KVATTN_HEAD_DIM);
+  const size_t lse_bytes = checked_bytes(groups, rows, sizeof(float));
+  if (!o_bytes || !lse_bytes) return KVATTN_E_INVALID;  // beyond any memory
+  const size_t need = kSyncBytes + o_bytes + lse_bytes;
   bool query_only = false;
   if ((st = workspace_check(workspace, workspace_bytes, need, &query_only))) return st;
   if (query_only) return KVATTN_OK;

@@ -24,7 +24,7 @@ import numpy as np
 HEAD_DIM = 256
 PAGE_TOKENS = 128
 
-ROLE_K, ROLE_V, ROLE_Q, ROLE_OUTLIER, ROLE_PAGES, ROLE_NEEDLE = range(6)
+ROLE_K, ROLE_V, ROLE_Q, ROLE_OUTLIER, ROLE_PAGES, ROLE_NEEDLE, ROLE_FAINT = range(7)
 
 
 @dataclass(frozen=True)
@@ -134,6 +134,27 @@ def kv_head(w, layer, head, q=None):
             sl = slice(b * PAGE_TOKENS, (b + 1) * PAGE_TOKENS)
             K[sl] = _needle_keys(K[sl], grp)
     return K, V
+
+
+def faint_needle_keys(w, layer, head, q, span_blocks, per_block=3):
+    """Keys float32 [kv_len, 256] of one (layer, KV head) for the recall curve:
+    N(0,1) keys in which each of w.n_needles blocks, drawn among the first
+    span_blocks, holds `per_block` needle tokens (seeded slots) turned toward
+    the group's summed query at cosine 1/2, the rest of the block plain.
+    A block summary averages its 128 keys, so one faint fact in a block of
+    noise moves it only a little above the noise: whether it ranks among the
+    kept blocks depends on how many candidates compete, i.e. on the context
+    length and the budget. The needles are mutually similar (all point at the
+    same query direction), as in [KVMEM] "Recall 測試", where a miss returns
+    another, similar needle."""
+    K = normal(rng(w, layer, head, ROLE_K), (w.kv_len, HEAD_DIM))
+    g = rng(w, layer, head, ROLE_FAINT)
+    blocks = np.sort(rng(w, 0, 0, ROLE_FAINT).choice(span_blocks, w.n_needles, replace=False))
+    grp = q[-1, head * w.gqa:(head + 1) * w.gqa]
+    for b in blocks:
+        slots = b * PAGE_TOKENS + g.choice(PAGE_TOKENS, per_block, replace=False)
+        K[slots] = _needle_keys(K[slots], grp)
+    return K, blocks
 
 
 def kv_layer(w, layer, q=None, threads=8):
