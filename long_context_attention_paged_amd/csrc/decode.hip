@@ -921,52 +921,58 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
   // The page the append completes is summarised by the workgroup whose units
   // hold it: a unit is a whole page, whose four 32-token groups are streamed
   // by four waves of one workgroup (group c by a wave with wave % 4 == c),
-  // including the wave that wrote the page's new tokens. The waves of a workgroup share one vector L1; the explicit wait
-  // (vmcnt, expcnt and lgkmcnt all zero) has that wave's stores complete
+  // including the wave that wrote the page's new tokens. The waves of a
+  // workgroup share one vector L1; the explicit wait (vmcnt, expcnt and
+  // lgkmcnt all zero) has that wave's stores complete
   // before the barrier, so the summary's reads, issued after it and in
   // flight while the partial is combined, see them.
   if (p.sum_page >= 0) {
     if (sum_ph >= 0) s_sum_ph = sum_ph + 1;
     __builtin_amdgcn_s_waitcnt(0);
   }
-  __syncthreads();  // every wave is done with the LDS ring and q_lds
-  const int sum_ph1 = p.sum_page >= 0 ? s_sum_ph : 0;  // uniform
-  const uint8_t* sum_rec = p.k_pool + ((int64_t)(sum_ph1 - 1) * p.n_kv + h) * KREC;
-  SummaryLoads sl;
-  if (sum_ph1 != 0) summary_issue<KT>(sum_rec, sl);
-  if (g == 0) {
+  if (g == 0) {  // each wave's row maxima and sums, for the weights below
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       s_m[wave][nt * 16 + r16] = st.m[nt];
       s_l[wave][nt * 16 + r16] = st.l[nt];
     }
   }
-  __syncthreads();
+  __syncthreads();  // every wave is done with the LDS ring and q_lds
+  const int sum_ph1 = p.sum_page >= 0 ? s_sum_ph : 0;  // uniform
+  const uint8_t* sum_rec = p.k_pool + ((int64_t)(sum_ph1 - 1) * p.n_kv + h) * KREC;
+  SummaryLoads sl;
+  if (sum_ph1 != 0) summary_issue<KT>(sum_rec, sl);
   constexpr int RS = 260;  // padded row stride of the combine buffer
   const int64_t rows_total = (int64_t)p.n_q_tok * n_heads;
+  __shared__ float s_f[WAVES][32];  // wave w's weight for row r: exp2(m_w - M) / L
+  if (threadIdx.x < WAVES * NT * 16) {
+    const int w = threadIdx.x / (NT * 16), row = threadIdx.x % (NT * 16);
+    float M = neg_inf();
+#pragma unroll
+    for (int v = 0; v < WAVES; ++v) M = fmaxf(M, s_m[v][row]);
+    float L = 0.f;
+#pragma unroll
+    for (int v = 0; v < WAVES; ++v)
+      if (s_m[v][row] != neg_inf()) L += s_l[v][row] * __builtin_amdgcn_exp2f(s_m[v][row] - M);
+    s_f[w][row] =
+        (L > 0.f && s_m[w][row] != neg_inf()) ? __builtin_amdgcn_exp2f(s_m[w][row] - M) / L : 0.f;
+  }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    {
-      const int row = nt * 16 + r16;
-      float M = neg_inf();
-#pragma unroll
-      for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][row]);
-      float L = 0.f;
-#pragma unroll
-      for (int w = 0; w < WAVES; ++w)
-        if (s_m[w][row] != neg_inf()) L += s_l[w][row] * __builtin_amdgcn_exp2f(s_m[w][row] - M);
-      const float f =
-          (L > 0.f && st.m[nt] != neg_inf()) ? __builtin_amdgcn_exp2f(st.m[nt] - M) / L : 0.f;
+    // every wave dumps its unnormalised rows (padding rows are never read);
+    // the threads that add them up apply the weights
+    if (s_rowg[nt * 16 + r16] >= 0) {
       float* buf = smem + (size_t)wave * 16 * RS;
 #pragma unroll
       for (int mt = 0; mt < 16; ++mt)
-        *reinterpret_cast<floatx4*>(buf + r16 * RS + 16 * mt + 4 * g) = st.o[nt][mt] * f;
+        *reinterpret_cast<floatx4*>(buf + r16 * RS + 16 * mt + 4 * g) = st.o[nt][mt];
     }
     __syncthreads();
-    // 16 rows x 64 float4 columns, the waves' values added pairwise in a
-    // fixed order
+    // 16 rows x 64 float4 columns: the waves' weighted rows, added pairwise
+    // in a fixed order (products rounded before the sums)
 #pragma unroll
     for (int k = 0; k < 16 * 64 / THREADS; ++k) {
+#pragma clang fp contract(off)
       const int idx = threadIdx.x + THREADS * k;
       const int rr = idx >> 6, c4 = idx & 63;
       const int rowg = s_rowg[nt * 16 + rr];
@@ -974,7 +980,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
         floatx4 v[WAVES];
 #pragma unroll
         for (int w = 0; w < WAVES; ++w)
-          v[w] = *reinterpret_cast<const floatx4*>(smem + (w * 16 + rr) * RS + 4 * c4);
+          v[w] = *reinterpret_cast<const floatx4*>(smem + (w * 16 + rr) * RS + 4 * c4) *
+                 s_f[w][nt * 16 + rr];
 #pragma unroll
         for (int step = 1; step < WAVES; step *= 2)
 #pragma unroll
