@@ -46,14 +46,14 @@ WARM_SECONDS = 0.3             # untimed graph replays before each timed region
 # once either has changed.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
-    "decode": {"sources": {"decode.hip": "f08f4763aeda0ce9", "common.hpp": "abcffce6ae06d4dc",
-                           "launch.hpp": "222b45861ae4df22", "qround.hpp": "bfca159575b5ee34"},
+    "decode": {"sources": {"decode.hip": "6a88e369e9d98000", "common.hpp": "abcffce6ae06d4dc",
+                           "launch.hpp": "b600f3ce4d4bbf1d", "qround.hpp": "bfca159575b5ee34"},
                "flags": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-               "fetch_kib": 213556.0, "write_kib": 6168.0},
-    "prefill": {"sources": {"prefill.hip": "d33de3a2111fdf55", "common.hpp": "abcffce6ae06d4dc",
-                            "launch.hpp": "222b45861ae4df22"},
+               "fetch_kib": 213561.0, "write_kib": 6168.0},
+    "prefill": {"sources": {"prefill.hip": "2fd0eccd0525f114", "common.hpp": "abcffce6ae06d4dc",
+                            "launch.hpp": "b600f3ce4d4bbf1d"},
                 "flags": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
-                "fetch_kib": 369440.0, "write_kib": 199425.0},
+                "fetch_kib": 369400.0, "write_kib": 199298.0},
 }
 
 
