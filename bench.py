@@ -494,6 +494,60 @@ def bench_prefill_host_pool(w, dev, steps, warmup):
     }, pools
 
 
+def bench_prefill_budgeted(w, dev, steps, warmup, budget=450 << 20):
+    """Prefill with every layer's pool in pinned host memory and a bounded
+    device working set (streaming.BudgetedHostPrefill; the Adaptive KV
+    Streaming guide's --kv-resident-mib 450): each layer's pages pass through
+    two staging slots of budget / 2 in page ranges, one range ahead of the
+    compute, and the ranges' partials are merged by LSE. Bound by the host
+    link."""
+    import torch
+    import long_context_attention_paged_amd as kv
+    from long_context_attention_paged_amd import streaming
+    pools = LayerPools(w, dev)
+    hk, hv = [], []
+    tl = pools.table.long()
+    for layer in range(w.n_layers):  # each layer's pages to a host tier in logical order
+        kview = pools.kp[layer].view(pools.n_phys, -1)
+        vview = pools.vp[layer].view(pools.n_phys, -1)
+        hk.append(torch.empty(w.n_pages * kview.shape[1], dtype=torch.uint8, pin_memory=True))
+        hv.append(torch.empty(w.n_pages * vview.shape[1], dtype=torch.uint8, pin_memory=True))
+        hk[layer].copy_(kview[tl].reshape(-1))
+        hv[layer].copy_(vview[tl].reshape(-1))
+        torch.cuda.synchronize()
+    pools.kp = pools.vp = None
+    torch.cuda.empty_cache()
+    bp = streaming.BudgetedHostPrefill(pools.geom, hk, hv, w.n_pages, dev, budget)
+    outs = [torch.empty_like(q) for q in pools.q]
+    lses = [torch.empty(q.shape[:2], dtype=torch.float32, device=dev) for q in pools.q]
+
+    def step():
+        bp.step(pools.q, pools.new_k, pools.new_v, w.pos0, 1.0 / 16.0, outs, lses)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    fl = prefill_flops_per_layer(w)
+    h2d = bp.host_to_device_bytes_per_step(w.n_layers, w.pos0, w.chunk)
+    return {
+        "ms_per_step": ms,
+        "tokens_per_s": w.chunk / (ms * 1e-3),
+        "tflops": fl * w.n_layers / (ms * 1e-3) / 1e12,
+        "device_budget_bytes": budget,
+        "device_pool_bytes": bp.device_bytes(),
+        "ranges_per_layer": len(bp.ranges(w.pos0, w.chunk)),
+        "host_to_device_bytes_per_step": h2d,
+        "host_to_device_gbs": h2d / (ms * 1e-3) / 1e9,
+        "note": "pages in a pinned host tier (logical order), page ranges copied into two "
+                "budget/2 staging slots one range ahead, range partials merged by LSE",
+    }, pools
+
+
 def bench_verify_streamed(w, dev, steps, warmup, budget=2100 << 20):
     """Verify with adaptive host-resident KV streaming: a device working set of
     `budget` bytes (the pages' decode figure, 2100 MiB) holds each layer's
@@ -796,10 +850,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--configs", default="3,4,2,5,1,3s,5h,4h,3q4,3q5",
+    ap.add_argument("--configs", default="3,4,2,5,1,3s,5h,4b,3q4,3q5",
                     help="workloads to run: 1 tiny-decode-4k (latency), 2 decode-131k, "
                          "3 verify-262k, 4 prefill, 5 kvmem, "
-                         "4h prefill with the pool in pinned host memory, 3s verify with the "
+                         "4h prefill with the pool in pinned host memory (whole layers "
+                         "staged), 4b the same under a 450 MiB device budget (page ranges), "
+                         "3s verify with the "
                          "history streamed from host memory (2100 MiB device working set), "
                          "5h kvmem with its history in host memory (budget sweep), "
                          "3q8 / 4q8 verify-262k / prefill with the q8_0/q8_0 pair, "
@@ -858,6 +914,15 @@ def main():
             del pools
             torch.cuda.empty_cache()
             log(f"{w.name} {tag}: {json.dumps(res)}")
+            continue
+        if c == "4b":
+            w = synth.WORKLOADS[4]
+            log(f"workload {w.name} (host pool, 450 MiB device budget)")
+            res, pools = bench_prefill_budgeted(w, dev, max(2, min(args.steps, 5)), 1)
+            extra[w.name + "-host-budget-450mib"] = res
+            del pools
+            torch.cuda.empty_cache()
+            log(f"{w.name} host pool, budget: {json.dumps(res)}")
             continue
         if c == "4h":
             w = synth.WORKLOADS[4]

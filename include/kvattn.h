@@ -421,6 +421,29 @@ kvattn_status kvattn_prefill_partials(const kvattn_geom *geom, const float *q,
                                       float *o_part, float *lse_part,
                                       void *stream);
 
+/* a6 over a page range — the partials of kvattn_prefill_partials restricted
+ * to the keys of logical pages [page_begin, page_end): the groups split that
+ * range (group gi covers [b + (e-b)*gi/n_groups, b + (e-b)*(gi+1)/n_groups),
+ * b = page_begin, e = page_end), and no key outside it is read, so the pool
+ * and page table need to hold only those pages (entries outside the range are
+ * never looked up). Partials of ranges that tile [0, ceil((pos0+chunk)/128))
+ * merged by kvattn_merge_lse give the chunk's prefill ([RDNA4] "Online
+ * Log-Sum-Exp prefill & pipelined prefetch": partial results over streamed
+ * page ranges combine by LSE; the Adaptive KV Streaming guide's bounded
+ * prefill working set, step ④ --kv-resident-mib 450). A group whose keys are
+ * all masked for a row writes o = 0 and lse = -inf for it.
+ *  0 <= page_begin < page_end <= ceil((pos0+chunk)/128); n_groups >= 1;
+ *  other arguments and errors as kvattn_prefill_partials. */
+kvattn_status kvattn_prefill_range_partials(const kvattn_geom *geom, const float *q,
+                                            int32_t chunk, const uint8_t *k_pool,
+                                            const uint8_t *v_pool,
+                                            const int32_t *page_table,
+                                            int32_t n_logical_pages, int64_t pos0,
+                                            float scale, int32_t page_begin,
+                                            int32_t page_end, int32_t n_groups,
+                                            float *o_part, float *lse_part,
+                                            void *stream);
+
 /* The group count kvattn_prefill_chunk chooses (n_groups = 0) on the current
  * device; 0 if geom is invalid, chunk < 1 or pos0 < 0. */
 int32_t kvattn_prefill_groups(const kvattn_geom *geom, int32_t chunk,

@@ -89,6 +89,8 @@ def load_library():
         "kvattn_decode_splits": ([G, I32], I32),
         "kvattn_prefill_chunk": ([G, P, I32, P, P, P, I32, I64, F32, P, P, I32, P, SZP, P], I32),
         "kvattn_prefill_partials": ([G, P, I32, P, P, P, I32, I64, F32, I32, P, P, P], I32),
+        "kvattn_prefill_range_partials": ([G, P, I32, P, P, P, I32, I64, F32, I32, I32, I32, P,
+                                           P, P], I32),
         "kvattn_prefill_groups": ([G, I32, I64], I32),
         "kvattn_merge_lse": ([I32, I64, I32, P, P, P, P, P], I32),
         "kvattn_prefetch_pages": ([G, P, P, P, P, P, I32, P], I32),
@@ -472,6 +474,32 @@ def kvattn_prefill_partials(geom, q, k_pool, v_pool, page_table, pos0, scale, n_
                                        _ptr(v_pool), _ptr(page_table), page_table.numel(),
                                        int(pos0), float(scale), int(n_groups), _ptr(o_part),
                                        _ptr(lse_part), _stream(stream)))
+    return o_part, lse_part
+
+
+def kvattn_prefill_range_partials(geom, q, k_pool, v_pool, page_table, pos0, scale, page_begin,
+                                  page_end, n_groups, o_part=None, lse_part=None, stream=None):
+    """Prefill partials over the keys of logical pages [page_begin, page_end)
+    only (a6 over a page range): -> (o_part [n_groups, chunk*n_heads, 256],
+    lse_part); the pool and table need to hold only that range's pages."""
+    torch = _torch()
+    lib = load_library()
+    _decode_args(geom, q, k_pool, v_pool, page_table, None)
+    rows = q.shape[0] * q.shape[1]
+    if o_part is None:
+        o_part = torch.empty((n_groups, rows, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((n_groups, rows), dtype=torch.float32, device=q.device)
+    _need(o_part, "o_part", torch.float32)
+    _need(lse_part, "lse_part", torch.float32)
+    _size(o_part, "o_part", n_groups * rows * HEAD_DIM)
+    _size(lse_part, "lse_part", n_groups * rows)
+    _check("kvattn_prefill_range_partials",
+           lib.kvattn_prefill_range_partials(ctypes.byref(geom), _ptr(q), q.shape[0], _ptr(k_pool),
+                                             _ptr(v_pool), _ptr(page_table), page_table.numel(),
+                                             int(pos0), float(scale), int(page_begin),
+                                             int(page_end), int(n_groups), _ptr(o_part),
+                                             _ptr(lse_part), _stream(stream)))
     return o_part, lse_part
 
 

@@ -364,8 +364,12 @@ kvattn_status launch_prefill_partials(const kvattn_geom* geom, const float* q, i
                                       const uint8_t* k_pool, const uint8_t* v_pool,
                                       const int32_t* page_table, int32_t n_logical_pages,
                                       int64_t pos0, float scale, int32_t groups, float* o_part,
-                                      float* lse_part, hipStream_t s, uint32_t* flag = nullptr) {
+                                      float* lse_part, hipStream_t s, uint32_t* flag = nullptr,
+                                      int32_t pg_begin = 0, int32_t pg_end = -1) {
   PrefillParams p;
+  p.pg_begin = pg_begin;
+  p.pg_end = pg_end >= 0 ? pg_end
+                         : (int32_t)((pos0 + chunk + KVATTN_PAGE_TOKENS - 1) / KVATTN_PAGE_TOKENS);
   p.q = q;
   p.k_pool = k_pool;
   p.v_pool = v_pool;
@@ -647,6 +651,25 @@ kvattn_status kvattn_prefill_partials(const kvattn_geom* geom, const float* q, i
   return launch_prefill_partials(geom, q, chunk, k_pool, v_pool, page_table, n_logical_pages, pos0,
                                  scale, n_groups, o_part, lse_part,
                                  static_cast<hipStream_t>(stream));
+}
+
+kvattn_status kvattn_prefill_range_partials(const kvattn_geom* geom, const float* q,
+                                            int32_t chunk, const uint8_t* k_pool,
+                                            const uint8_t* v_pool, const int32_t* page_table,
+                                            int32_t n_logical_pages, int64_t pos0, float scale,
+                                            int32_t page_begin, int32_t page_end,
+                                            int32_t n_groups, float* o_part, float* lse_part,
+                                            void* stream) {
+  kvattn_status st =
+      check_prefill(geom, q, chunk, k_pool, v_pool, page_table, n_logical_pages, pos0, scale);
+  if (st) return st;
+  if (!o_part || !lse_part || !aligned(o_part, 16) || n_groups < 1) return KVATTN_E_INVALID;
+  const int64_t n_pages = (pos0 + chunk + KVATTN_PAGE_TOKENS - 1) / KVATTN_PAGE_TOKENS;
+  if (page_begin < 0 || page_end <= page_begin || page_end > n_pages) return KVATTN_E_INVALID;
+  if ((st = current_device(nullptr))) return st;
+  return launch_prefill_partials(geom, q, chunk, k_pool, v_pool, page_table, n_logical_pages, pos0,
+                                 scale, n_groups, o_part, lse_part,
+                                 static_cast<hipStream_t>(stream), nullptr, page_begin, page_end);
 }
 
 kvattn_status kvattn_merge_lse(int32_t n_parts, int64_t rows, int32_t head_dim,

@@ -99,6 +99,7 @@ struct PrefillParams {
   int32_t v_q8;              // value records hold Q8_0 codes (else Q4_0)
   int32_t k_type;            // key records: 0 Q8_0, 1 Q4_0, 2 Q5_1
   uint32_t* flag;            // workspace error word (bit 0: a wave's wait gave up) or nullptr
+  int32_t pg_begin, pg_end;  // logical pages the groups split (keys outside are not read)
 };
 
 int32_t prefill_rows_per_tile();

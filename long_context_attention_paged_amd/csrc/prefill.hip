@@ -329,7 +329,6 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
   const int n_heads = p.n_kv * p.gqa;
   const int64_t rows_head = (int64_t)p.chunk * p.gqa;
   const int64_t kv_len = p.pos0 + p.chunk;
-  const int64_t n_pages = (kv_len + PAGE - 1) / PAGE;
 
   // ---- this group's sub-tiles (32 tokens each) ------------------------------
   const int64_t tile_last_row = ((int64_t)qtile + 1) * PF_ROWS - 1 < rows_head
@@ -337,8 +336,9 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
                                     : rows_head - 1;
   const int64_t wg_max_pos = p.pos0 + tile_last_row / p.gqa;  // last key any row here sees
   SubTiles t;
-  t.pg0 = n_pages * group / p.n_groups;
-  t.pg1 = n_pages * (group + 1) / p.n_groups;
+  const int64_t span = p.pg_end - p.pg_begin;  // the groups split [pg_begin, pg_end)
+  t.pg0 = p.pg_begin + span * group / p.n_groups;
+  t.pg1 = p.pg_begin + span * (group + 1) / p.n_groups;
   if (t.pg1 > wg_max_pos / PAGE + 1) t.pg1 = wg_max_pos / PAGE + 1;
   t.n_sub = t.pg1 > t.pg0 ? (int)((t.pg1 - t.pg0) * 4) : 0;
   if (t.n_sub > 0) {  // drop trailing 32-token groups no row sees

@@ -342,3 +342,167 @@ class HostPoolPrefill:
             kv.kvattn_prefetch_pages(self.geom, sk, sv, self.host_k[c], self.host_v[c], written,
                                      stream=self.copy)
         compute.wait_stream(self.copy)  # the write-backs end the step
+
+
+class BudgetedHostPrefill:
+    """Chunked prefill from a host tier under a device page budget (the
+    Adaptive KV Streaming guide's bounded prefill working set, [STREAM] step
+    ④ --kv-resident-mib 450; [RDNA4] "Online Log-Sum-Exp prefill & pipelined
+    prefetch"). host_k[L], host_v[L] are pinned pools holding layer L's pages
+    in logical page order (page p at record p * n_kv, as StreamedLayer keeps
+    its history), so any run of pages is one contiguous copy per pool.
+
+    Two device staging slots of `slot_pages` pages each (budget_bytes / 2 of
+    page records) hold page ranges, not whole layers. A chunk at pos0 reads
+    logical pages [0, n_read), n_read = ceil((pos0 + chunk) / 128), cut into
+    ranges of at most slot_pages pages, the last one ending at n_read (so it
+    holds every page the chunk writes). Per (layer, range), in order:
+     - copy stream: the range is copied from the host tier into a staging
+       slot (kvattn_prefetch_pages: one hipMemcpyAsync per pool), one item
+       ahead of the compute;
+     - compute: for the last range kvattn_quantize_pages writes the chunk's
+       tokens into the staged pages, then kvattn_prefill_range_partials
+       attends over that range alone into its share of the partials;
+     - after a layer's last range, kvattn_merge_lse combines the ranges'
+       partials (the LSE merge is associative over any page split), and the
+       staged pages holding the chunk go back to the host tier.
+    A slot is refilled only after the compute (and write-back) that read it.
+    Device working set: 2 x slot_pages pages, plus the partials."""
+
+    def __init__(self, geom, host_k, host_v, n_logical_pages, dev, budget_bytes):
+        import torch
+        self.geom, self.host_k, self.host_v, self.dev = geom, host_k, host_v, dev
+        self.n_logical = int(n_logical_pages)
+        n_kv = geom.n_kv_heads
+        self.k_page = n_kv * geom.k_record_bytes
+        self.v_page = n_kv * geom.v_record_bytes
+        for t in list(host_k) + list(host_v):
+            if not t.is_pinned():
+                raise ValueError("BudgetedHostPrefill needs pinned host pools")
+        for t in host_k:
+            if t.numel() < self.n_logical * self.k_page:
+                raise ValueError("a host key pool is smaller than n_logical_pages pages")
+        for t in host_v:
+            if t.numel() < self.n_logical * self.v_page:
+                raise ValueError("a host value pool is smaller than n_logical_pages pages")
+        self.page_bytes = self.k_page + self.v_page
+        self.slot_pages = int(budget_bytes // (2 * self.page_bytes))
+        if self.slot_pages < 1:
+            raise ValueError("budget too small for two one-page staging slots")
+        S = self.slot_pages
+        self.stage_geom = kv.Geom(n_kv, geom.gqa, S, v_type=geom.v_type, k_type=geom.k_type)
+        self.stage_k = [torch.empty(S * self.k_page, dtype=torch.uint8, device=dev)
+                        for _ in range(2)]
+        self.stage_v = [torch.empty(S * self.v_page, dtype=torch.uint8, device=dev)
+                        for _ in range(2)]
+        self.copy = torch.cuda.Stream(device=dev)
+        self._plan_key = None
+
+    def device_bytes(self):
+        """Staging bytes held on the device (the page budget actually used)."""
+        return sum(t.numel() for t in self.stage_k + self.stage_v)
+
+    def ranges(self, pos0, chunk):
+        """Logical page ranges [a, b) a chunk at pos0 reads, in order."""
+        n_read = (pos0 + chunk + PAGE - 1) // PAGE
+        S = self.slot_pages
+        if n_read - pos0 // PAGE > S:
+            raise ValueError(f"the chunk's {n_read - pos0 // PAGE} pages exceed a slot of {S}")
+        if n_read > self.n_logical:
+            raise ValueError("the chunk runs past the host tier's pages")
+        last = max(0, n_read - S)
+        out = [(a, min(a + S, last)) for a in range(0, last, S)]
+        return out + [(last, n_read)]
+
+    def _plan(self, q0, pos0):
+        import torch
+        chunk = q0.shape[0]
+        if self._plan_key == (pos0, chunk):
+            return
+        rng = self.ranges(pos0, chunk)
+        n_read = rng[-1][1]
+        g_full = kv.kvattn_prefill_groups(self.stage_geom, chunk, pos0)
+        self.plan = []
+        first = 0
+        for a, b in rng:
+            g = max(1, -(-g_full * (b - a) // n_read))  # groups in proportion to the range
+            tab = np.full(self.n_logical, -1, np.int32)
+            tab[a:b] = np.arange(b - a, dtype=np.int32)
+            self.plan.append({"a": a, "b": b, "groups": g, "first": first,
+                              "table": torch.from_numpy(tab).to(self.dev),
+                              "slots": list(range(b - a)),
+                              "geom": kv.Geom(self.geom.n_kv_heads, self.geom.gqa, b - a,
+                                              v_type=self.geom.v_type, k_type=self.geom.k_type)})
+            first += g
+        rows = chunk * self.geom.n_kv_heads * self.geom.gqa
+        self.o_parts = torch.empty((first, rows, kv.HEAD_DIM), dtype=torch.float32,
+                                   device=self.dev)
+        self.lse_parts = torch.empty((first, rows), dtype=torch.float32, device=self.dev)
+        a_last = rng[-1][0]
+        self.wb_first = pos0 // PAGE                    # the chunk's pages, logical
+        self.wb_count = (pos0 + chunk - 1) // PAGE + 1 - self.wb_first
+        self.wb_slot = self.wb_first - a_last           # their first slot in the last range
+        self._plan_key = (pos0, chunk)
+
+    def host_to_device_bytes_per_step(self, n_layers, pos0, chunk):
+        return n_layers * sum(b - a for a, b in self.ranges(pos0, chunk)) * self.page_bytes
+
+    def step(self, q, k_new, v_new, pos0, scale, outs, lses):
+        """Enqueue one chunk over every layer: q[L] [chunk, n_heads, 256],
+        k_new[L], v_new[L] [chunk, n_kv, 256] (positions pos0 ..), results
+        into outs[L], lses[L]."""
+        import torch
+        compute = torch.cuda.current_stream()
+        self._plan(q[0], pos0)
+        items = [(L, r) for L in range(len(q)) for r in range(len(self.plan))]
+        copied = [torch.cuda.Event() for _ in items]
+        done = [torch.cuda.Event() for _ in items]
+
+        def stage(i):
+            L, r = items[i]
+            pr = self.plan[r]
+            a, b = pr["a"], pr["b"]
+            if i < 2:
+                self.copy.wait_stream(compute)  # the previous step's last items
+            else:
+                self.copy.wait_event(done[i - 2])  # slot i % 2 has been read
+            kv.kvattn_prefetch_pages(
+                pr["geom"], self.host_k[L][a * self.k_page:b * self.k_page],
+                self.host_v[L][a * self.v_page:b * self.v_page],
+                self.stage_k[i % 2], self.stage_v[i % 2], pr["slots"], stream=self.copy)
+            copied[i].record(self.copy)
+
+        if items:
+            stage(0)
+        for i, (L, r) in enumerate(items):
+            if i + 1 < len(items):
+                stage(i + 1)
+            pr = self.plan[r]
+            sk, sv = self.stage_k[i % 2], self.stage_v[i % 2]
+            compute.wait_event(copied[i])
+            last = r == len(self.plan) - 1
+            if last:
+                kv.kvattn_quantize_pages(self.stage_geom, k_new[L], v_new[L], pos0, pr["table"],
+                                         sk, sv)
+            g0, g = pr["first"], pr["groups"]
+            kv.kvattn_prefill_range_partials(self.stage_geom, q[L], sk, sv, pr["table"], pos0,
+                                             scale, pr["a"], pr["b"], g,
+                                             o_part=self.o_parts[g0:g0 + g],
+                                             lse_part=self.lse_parts[g0:g0 + g])
+            done[i].record(compute)
+            if last:
+                kv.kvattn_merge_lse(self.o_parts, self.lse_parts,
+                                    out=outs[L].view(-1, kv.HEAD_DIM), lse=lses[L].view(-1))
+                # the chunk's pages back to the host tier (one contiguous run
+                # per pool), before the slot is refilled
+                self.copy.wait_event(done[i])
+                s0, p0, n = self.wb_slot, self.wb_first, self.wb_count
+                wb_geom = kv.Geom(self.geom.n_kv_heads, self.geom.gqa, n,
+                                  v_type=self.geom.v_type, k_type=self.geom.k_type)
+                kv.kvattn_prefetch_pages(
+                    wb_geom, sk[s0 * self.k_page:(s0 + n) * self.k_page],
+                    sv[s0 * self.v_page:(s0 + n) * self.v_page],
+                    self.host_k[L][p0 * self.k_page:(p0 + n) * self.k_page],
+                    self.host_v[L][p0 * self.v_page:(p0 + n) * self.v_page],
+                    list(range(n)), stream=self.copy)
+        compute.wait_stream(self.copy)  # the write-backs end the step

@@ -142,6 +142,13 @@ int main() {
                               INT32_MAX, nullptr, &nb, nullptr), INV);
   EXPECT(kvattn_prefill_partials(&g, PF, 1, P8, P8, PI, 8, INT64_MAX, 0.0625f, 1, PF, PF,
                                  nullptr), INV);
+  EXPECT(kvattn_prefill_range_partials(&g, PF, 512, P8, P8, PI, INT32_MAX,
+                                       (int64_t)INT32_MAX * 128 - 512, 0.0625f, 0, INT32_MAX, 1,
+                                       PF, PF, nullptr), DEV);
+  EXPECT(kvattn_prefill_range_partials(&g, PF, 1, P8, P8, PI, 8, INT64_MAX, 0.0625f, 0, 1, 1,
+                                       PF, PF, nullptr), INV);
+  EXPECT(kvattn_prefill_range_partials(&g, PF, 100, P8, P8, PI, 16, 1000, 0.0625f, INT32_MIN, 2,
+                                       1, PF, PF, nullptr), INV);
   EXPECT(kvattn_prefill_groups(&g, INT32_MAX, INT64_MAX) >= 0, 1);
   EXPECT(kvattn_prefill_groups(&g, 512, (int64_t)1 << 40) >= 1, 1);
   EXPECT(kvattn_prefill_groups(&g, 0, 0), 0);

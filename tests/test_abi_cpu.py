@@ -153,6 +153,23 @@ def test_append_decode_noalloc_validation():
     assert 64 * 8 * 32 * 1028 > kv.NOALLOC_SCRATCH_BYTES >= 32 * 8 * 32 * 1028 + 512
 
 
+def test_prefill_range_validation():
+    lib = kv.load_library()
+    g = geom()
+
+    def call(pos0=1000, chunk=100, begin=0, end=9, groups=2, n_logical=16):
+        return lib.kvattn_prefill_range_partials(ctypes.byref(g), P(FAKE), chunk, P(FAKE),
+                                                 P(FAKE), P(FAKE), n_logical, pos0, 0.0625,
+                                                 begin, end, groups, P(FAKE), P(FAKE), None)
+    # 1100 tokens -> 9 pages; the range must lie in [0, 9) and be non-empty
+    assert call(end=10) == E_INVALID
+    assert call(begin=-1) == E_INVALID
+    assert call(begin=5, end=5) == E_INVALID
+    assert call(groups=0) == E_INVALID
+    assert call(pos0=2**62) == E_INVALID
+    assert call() == E_DEVICE            # valid arguments reach the device check
+
+
 def test_prefill_and_select_validation():
     lib = kv.load_library()
     g = geom()

@@ -211,3 +211,111 @@ def test_host_pool_prefill_matches_oracle(k_type, v_type):
             eo, el, rr = compare(outs[c], lses[c], ref_o, ref_l)
             assert eo <= 1e-2 and el <= 1e-2, (chunk, c, eo, el, rr)
         start += chunk
+
+
+@pytest.mark.parametrize("k_type,v_type", [(0, 0), (1, 1)])  # q8_0/q4_0 and q4_0/q8_0 caches
+def test_budgeted_host_prefill_matches_oracle(k_type, v_type):
+    """streaming.BudgetedHostPrefill: each layer's pages only in a pinned host
+    tier (logical page order), a device budget of two 15-page staging slots,
+    so each layer's pages go through three ranges (one copy per pool each,
+    kvattn_prefill_range_partials per range, kvattn_merge_lse); two
+    consecutive chunks over three layers. Out and lse match the oracle's
+    prefill (1e-2 max-abs), the host tier afterwards equals the oracle's
+    quantisation bit for bit, and the second chunk reads the first chunk's
+    tokens from the host tier."""
+    n_kv, gqa, n_layers = 2, 6, 3
+    pos0, chunk0, chunk1 = 36 * 128 + 50, 200, 150
+    n_pages = (pos0 + chunk0 + chunk1 + 127) // 128
+    n_phys = n_pages + 2
+    g = np.random.default_rng(80 + k_type)
+    geom = kv.Geom(n_kv, gqa, n_phys, v_type=v_type, k_type=k_type)
+    table = g.permutation(n_phys)[:n_pages].astype(np.int32)
+    pools, host_k, host_v = [], [], []
+    for _ in range(n_layers):
+        p = Pools(n_phys, n_kv, gqa, init_seed=int(g.integers(1 << 30)), v_type=v_type,
+                  k_type=k_type)
+        p.write(g.standard_normal((pos0, n_kv, 256)).astype(np.float32),
+                g.standard_normal((pos0, n_kv, 256)).astype(np.float32), 0, table)
+        torch.cuda.synchronize()
+        # the host tier in logical page order: page p's records at p * n_kv
+        tl = torch.from_numpy(table.astype(np.int64)).to(DEV)
+        hk = torch.empty(n_pages * n_kv * geom.k_record_bytes, dtype=torch.uint8,
+                         pin_memory=True)
+        hv = torch.empty(n_pages * n_kv * geom.v_record_bytes, dtype=torch.uint8,
+                         pin_memory=True)
+        hk.copy_(p.gk.view(n_phys, -1)[tl].reshape(-1))
+        hv.copy_(p.gv.view(n_phys, -1)[tl].reshape(-1))
+        p.gk = p.gv = None
+        pools.append(p)
+        host_k.append(hk)
+        host_v.append(hv)
+    page_bytes = n_kv * (geom.k_record_bytes + geom.v_record_bytes)
+    bp = streaming.BudgetedHostPrefill(geom, host_k, host_v, n_pages, DEV,
+                                       budget_bytes=2 * 15 * page_bytes)
+    assert bp.slot_pages == 15 and bp.device_bytes() == 2 * 15 * page_bytes
+    start = pos0
+    for chunk in (chunk0, chunk1):
+        rng = bp.ranges(start, chunk)
+        assert len(rng) == 3 and rng[0][0] == 0 and rng[-1][1] == (start + chunk + 127) // 128
+        assert all(a < b <= a + 15 for a, b in rng)
+        assert all(rng[i][1] == rng[i + 1][0] for i in range(len(rng) - 1))
+        qs = [g.standard_normal((chunk, n_kv * gqa, 256)).astype(np.float32)
+              for _ in range(n_layers)]
+        kns = [g.standard_normal((chunk, n_kv, 256)).astype(np.float32) for _ in range(n_layers)]
+        vns = [g.standard_normal((chunk, n_kv, 256)).astype(np.float32) for _ in range(n_layers)]
+        outs = [torch.empty((chunk, n_kv * gqa, 256), dtype=torch.float32, device=DEV)
+                for _ in range(n_layers)]
+        lses = [torch.empty((chunk, n_kv * gqa), dtype=torch.float32, device=DEV)
+                for _ in range(n_layers)]
+        print(f"budgeted prefill: chunk {chunk} at {start}, ranges {rng}", flush=True)
+        bp.step([gpu(x) for x in qs], [gpu(x) for x in kns], [gpu(x) for x in vns], start,
+                1 / 16, outs, lses)
+        torch.cuda.synchronize()
+        for c in range(n_layers):
+            p = pools[c]
+            quant.quantize_into_pool(kns[c], vns[c], start, table, p.ok, p.ov)
+            # the host tier holds the oracle's pool in logical page order
+            assert (host(host_k[c]).reshape(n_pages, n_kv, -1) == p.ok[table]).all()
+            assert (host(host_v[c]).reshape(n_pages, n_kv, -1) == p.ov[table]).all()
+            ref_o, ref_l = oracle.prefill_chunk(qs[c], gqa, p.ok, p.ov, table, n_pages, start,
+                                                1 / 16)
+            eo, el, rr = compare(outs[c], lses[c], ref_o, ref_l)
+            assert eo <= 1e-2 and el <= 1e-2, (chunk, c, eo, el, rr)
+        start += chunk
+
+
+def test_prefill_range_partials_tile_the_chunk():
+    """kvattn_prefill_range_partials over ranges that tile the chunk's pages
+    (one of them holding a single page, one the causal tail), merged with
+    kvattn_merge_lse, against the oracle and against kvattn_prefill_chunk;
+    the last range, whose keys all lie past the causal limit of the chunk's
+    early rows, gives those rows lse = -inf."""
+    n_kv, gqa = 2, 6
+    pos0, chunk = 9 * 128 + 17, 160
+    n_pages = (pos0 + chunk + 127) // 128
+    g = np.random.default_rng(33)
+    table = g.permutation(n_pages + 1)[:n_pages].astype(np.int32)
+    pools = Pools(n_pages + 1, n_kv, gqa, init_seed=34)
+    pools.write(g.standard_normal((pos0 + chunk, n_kv, 256)).astype(np.float32),
+                g.standard_normal((pos0 + chunk, n_kv, 256)).astype(np.float32), 0, table)
+    q = g.standard_normal((chunk, n_kv * gqa, 256)).astype(np.float32)
+    qd, td = gpu(q), gpu(table, torch.int32)
+    parts, lparts = [], []
+    for a, b, gr in [(0, 4, 3), (4, 5, 2), (5, 10, 2), (10, n_pages, 1)]:
+        o, l_ = kv.kvattn_prefill_range_partials(pools.geom, qd, pools.gk, pools.gv, td, pos0,
+                                                 1 / 16, a, b, gr)
+        parts.append(o)
+        lparts.append(l_)
+    o_all, l_all = torch.cat(parts), torch.cat(lparts)
+    out, lse = kv.kvattn_merge_lse(o_all, l_all)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.prefill_chunk(q, gqa, pools.ok, pools.ov, table, n_pages, pos0, 1 / 16)
+    eo, el, rr = compare(out.view(chunk, -1, 256), lse.view(chunk, -1), ref_o, ref_l)
+    assert eo <= 1e-2 and el <= 1e-2, (eo, el, rr)
+    o2, l2 = kv.kvattn_prefill_chunk(pools.geom, qd, pools.gk, pools.gv, td, pos0, 1 / 16)
+    assert (out.view_as(o2) - o2).abs().max().item() <= 2e-3
+    # the last range [10, n_pages) holds only keys at positions >= 1280 > pos0:
+    # query token t sees them only if pos0 + t >= 1280
+    l_last = host(lparts[-1]).reshape(chunk, -1)
+    first_seen = 10 * 128 - pos0
+    assert np.isneginf(l_last[:first_seen]).all() and np.isfinite(l_last[first_seen:]).all()
