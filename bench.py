@@ -47,13 +47,13 @@ WARM_SECONDS = 0.3             # untimed graph replays before each timed region
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
     "decode": {"sources": {"decode.hip": "6a88e369e9d98000", "common.hpp": "abcffce6ae06d4dc",
-                           "launch.hpp": "b600f3ce4d4bbf1d", "qround.hpp": "bfca159575b5ee34"},
+                           "launch.hpp": "525dbebac0e478f8", "qround.hpp": "bfca159575b5ee34"},
                "flags": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
                "fetch_kib": 213561.0, "write_kib": 6168.0},
-    "prefill": {"sources": {"prefill.hip": "2fd0eccd0525f114", "common.hpp": "abcffce6ae06d4dc",
-                            "launch.hpp": "b600f3ce4d4bbf1d"},
+    "prefill": {"sources": {"prefill.hip": "d8a770e575036885", "common.hpp": "abcffce6ae06d4dc",
+                            "launch.hpp": "525dbebac0e478f8"},
                 "flags": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
-                "fetch_kib": 369400.0, "write_kib": 199298.0},
+                "fetch_kib": 369364.0, "write_kib": 199420.0},
 }
 
 
