@@ -344,6 +344,23 @@ class HostPoolPrefill:
         compute.wait_stream(self.copy)  # the write-backs end the step
 
 
+def prefill_ranges(pos0, chunk, slot_pages, n_logical_pages):
+    """The page ranges [a, b) through which a chunk at pos0 reads its keys
+    with staging slots of slot_pages pages: they tile [0, n_read), n_read =
+    ceil((pos0 + chunk) / 128), in order, none longer than a slot, and the
+    last one ends at n_read and starts at most at pos0's page, so it holds
+    every page the chunk writes."""
+    n_read = (pos0 + chunk + PAGE - 1) // PAGE
+    S = slot_pages
+    if n_read - pos0 // PAGE > S:
+        raise ValueError(f"the chunk's {n_read - pos0 // PAGE} pages exceed a slot of {S}")
+    if n_read > n_logical_pages:
+        raise ValueError("the chunk runs past the host tier's pages")
+    last = max(0, n_read - S)
+    out = [(a, min(a + S, last)) for a in range(0, last, S)]
+    return out + [(last, n_read)]
+
+
 class BudgetedHostPrefill:
     """Chunked prefill from a host tier under a device page budget (the
     Adaptive KV Streaming guide's bounded prefill working set, [STREAM] step
@@ -404,15 +421,7 @@ class BudgetedHostPrefill:
 
     def ranges(self, pos0, chunk):
         """Logical page ranges [a, b) a chunk at pos0 reads, in order."""
-        n_read = (pos0 + chunk + PAGE - 1) // PAGE
-        S = self.slot_pages
-        if n_read - pos0 // PAGE > S:
-            raise ValueError(f"the chunk's {n_read - pos0 // PAGE} pages exceed a slot of {S}")
-        if n_read > self.n_logical:
-            raise ValueError("the chunk runs past the host tier's pages")
-        last = max(0, n_read - S)
-        out = [(a, min(a + S, last)) for a in range(0, last, S)]
-        return out + [(last, n_read)]
+        return prefill_ranges(pos0, chunk, self.slot_pages, self.n_logical)
 
     def _plan(self, q0, pos0):
         import torch
