@@ -101,3 +101,33 @@ def test_noalloc_rejects_partials_beyond_the_scratch():
                                     kv_len, 1 / 16, out, lse, n_splits=32)
     torch.cuda.synchronize()
     assert torch.equal(out, o_ref) and torch.equal(lse, l_ref)
+
+
+def test_noalloc_replays_under_graph_capture():
+    """The entry point's own use case: captured in a HIP graph (no allocation
+    during capture) and replayed three times with eager work between the
+    replays; every replay's out and lse equal the eager call's bit for bit
+    (the append writes the same bytes each time)."""
+    pools, table, k_new, v_new, q, blocks, n_pages = make_case(2, 6, 2, 2, 20 * 128 + 9, seed=16)
+    kv_len = 20 * 128 + 9
+    out0 = torch.empty_like(q)
+    lse0 = torch.empty(q.shape[:2], dtype=torch.float32, device=DEV)
+    kv.kvattn_append_decode_noalloc(pools.geom, k_new, v_new, q, pools.gk, pools.gv, table,
+                                    kv_len, 1 / 16, out0, lse0)
+    torch.cuda.synchronize()
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        kv.kvattn_append_decode_noalloc(pools.geom, k_new, v_new, q, pools.gk, pools.gv, table,
+                                        kv_len, 1 / 16, out, lse, stream=s)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, out0) and torch.equal(lse, lse0), rep
+        _ = (q * 2).sum().item()  # eager work between the replays
