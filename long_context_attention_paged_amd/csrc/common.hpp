@@ -77,52 +77,64 @@ __device__ __forceinline__ half8_t v8_codes_to_f16(uint32_t w0, uint32_t w1) {
   return r;
 }
 
-// One V word (eight 4-bit codes, slot 2p at bit 4p, slot 2p+1 at bit 16+4p)
-// -> eight exact f16 values (code - 8) in slot order.
-__device__ __forceinline__ half8_t v_codes_to_f16(uint32_t w) {
-  const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
-  half2_t p0 = as_h2((w & 0x000F000Fu) | 0x64006400u) - off;
-  half2_t p1 = as_h2(((w >> 4) & 0x000F000Fu) | 0x64006400u) - off;
-  half2_t p2 = as_h2(((w >> 8) & 0x000F000Fu) | 0x64006400u) - off;
-  half2_t p3 = as_h2(((w >> 12) & 0x000F000Fu) | 0x64006400u) - off;
+// Nibble unpacking. A word holds eight 4-bit codes; pair p (the f16 pair
+// 2p, 2p+1) is the nibbles at bits 4p and 16 + 4p. A pair at bits 0-3/16-19
+// is put under the exponent of 2^10, where the mantissa step is 1: the f16 is
+// 1024 + code. A pair at bits 4-7/20-23 is put, without a shift, under the
+// exponent of 2^6, where the step is 1/16, so the code four bits up reads as
+// 64 + code. One shift by 8 brings the other two pairs to those places, so a
+// word takes five bitwise ops (the masks in VGPRs, the exponents in SGPRs).
+constexpr uint32_t NIB_LO = 0x000F000Fu, NIB_HI = 0x00F000F0u;
+constexpr uint32_t EXP_1024 = 0x64006400u, EXP_64 = 0x54005400u;
+
+// One V word -> eight exact f16 values (code - 8) in pair order.
+__device__ __forceinline__ half8_t v_codes_to_f16_m(uint32_t w, uint32_t mlo, uint32_t mhi) {
+  const half2_t off_lo = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const half2_t off_hi = {(_Float16)72.0f, (_Float16)72.0f};
+  const uint32_t t = w >> 8;
+  const half2_t p0 = as_h2((w & mlo) | EXP_1024) - off_lo;
+  const half2_t p1 = as_h2((w & mhi) | EXP_64) - off_hi;
+  const half2_t p2 = as_h2((t & mlo) | EXP_1024) - off_lo;
+  const half2_t p3 = as_h2((t & mhi) | EXP_64) - off_hi;
   half8_t r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
   return r;
 }
-
-// As v_codes_to_f16, with the nibble mask 0x000F000F passed in a VGPR so each
-// pair unpacks with one v_and_or_b32 (the 0x64006400 exponent from an SGPR).
-__device__ __forceinline__ half8_t v_codes_to_f16_m(uint32_t w, uint32_t mask) {
-  const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
-  half2_t p0 = as_h2((w & mask) | 0x64006400u) - off;
-  half2_t p1 = as_h2(((w >> 4) & mask) | 0x64006400u) - off;
-  half2_t p2 = as_h2(((w >> 8) & mask) | 0x64006400u) - off;
-  half2_t p3 = as_h2(((w >> 12) & mask) | 0x64006400u) - off;
-  half8_t r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-  return r;
+__device__ __forceinline__ half8_t v_codes_to_f16(uint32_t w) {
+  return v_codes_to_f16_m(w, NIB_LO, NIB_HI);
 }
 
 // One Q4_0 key word (dims 8w..8w+7, nibble order of the V words) -> eight
 // f16 values d * (code - 8); d2 holds the block scale in both halves.
-__device__ __forceinline__ half8_t k4_codes_to_f16(uint32_t w, uint32_t mask, half2_t d2) {
+__device__ __forceinline__ half8_t k4_codes_to_f16(uint32_t w, uint32_t mlo, uint32_t mhi, half2_t d2) {
   const half8_t d8 = __builtin_shufflevector(d2, d2, 0, 1, 0, 1, 0, 1, 0, 1);
-  return v_codes_to_f16_m(w, mask) * d8;
+  return v_codes_to_f16_m(w, mlo, mhi) * d8;
 }
 
 // One Q5_1 key word (low nibbles as a Q4_0 key word) and its byte e of fifth
 // bits (dim 8w + 2p at bit p, 8w + 2p + 1 at bit 4 + p) -> eight f16 values
 // d * code + m (one rounding); d2, m2 hold the block's d and m in both halves.
-__device__ __forceinline__ half8_t k5_codes_to_f16(uint32_t w, uint32_t e, half2_t d2, half2_t m2) {
-  const uint32_t hs = ((e & 0xFu) << 4) | ((e & 0xF0u) << 16);
-  const half2_t off = {(_Float16)1024.0f, (_Float16)1024.0f};
-  half8_t r;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t c = ((w >> (4 * p)) & 0x000F000Fu) | ((hs >> p) & 0x00100010u);
-    const half2_t v = __builtin_elementwise_fma(as_h2(c | 0x64006400u) - off, d2, m2);
-    r[2 * p] = v[0];
-    r[2 * p + 1] = v[1];
-  }
+// The fifth bit goes just above its nibble: bit 4 (16 + 4) under 2^10, bit 8
+// (24) under 2^6, where the 5-bit code still reads 1024 + code or 64 + code.
+// e * 0x10010 puts e's bits 0-3 at bits 4-7 and bits 4-7 at bits 20-23.
+__device__ __forceinline__ half8_t k5_codes_to_f16(uint32_t w, uint32_t e, uint32_t mlo, uint32_t mhi,
+                                                   half2_t d2, half2_t m2) {
+  const uint32_t hs = e * 0x10010u;
+  const uint32_t t = w >> 8;
+  const half2_t off_lo = {(_Float16)1024.0f, (_Float16)1024.0f};
+  const half2_t off_hi = {(_Float16)64.0f, (_Float16)64.0f};
+  const uint32_t c0 = ((w & mlo) | EXP_1024) | (hs & 0x00100010u);
+  const uint32_t c1 = ((w & mhi) | EXP_64) | ((hs << 3) & 0x01000100u);
+  const uint32_t c2 = ((t & mlo) | EXP_1024) | ((hs >> 2) & 0x00100010u);
+  const uint32_t c3 = ((t & mhi) | EXP_64) | ((hs << 1) & 0x01000100u);
+  const half2_t v0 = __builtin_elementwise_fma(as_h2(c0) - off_lo, d2, m2);
+  const half2_t v1 = __builtin_elementwise_fma(as_h2(c1) - off_hi, d2, m2);
+  const half2_t v2 = __builtin_elementwise_fma(as_h2(c2) - off_lo, d2, m2);
+  const half2_t v3 = __builtin_elementwise_fma(as_h2(c3) - off_hi, d2, m2);
+  half8_t r = {v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
   return r;
+}
+__device__ __forceinline__ half8_t k5_codes_to_f16(uint32_t w, uint32_t e, half2_t d2, half2_t m2) {
+  return k5_codes_to_f16(w, e, NIB_LO, NIB_HI, d2, m2);
 }
 
 __device__ __forceinline__ u32x4 load16(const uint8_t* p) {

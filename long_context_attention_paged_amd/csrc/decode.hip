@@ -171,9 +171,9 @@ struct State {
 };
 
 template <int NT, int KT, bool V8, typename MidFn>
-__device__ __forceinline__ void compute_tile(State<NT>& st, const uint8_t* slot, int64_t tok0,
+__device__ __forceinline__ void compute_tile(State<NT>& st, uint8_t* slot, int64_t tok0,
                                              int64_t kv_len, int64_t min_limit, int lane, int r16,
-                                             int g, uint32_t nib_mask, MidFn&& after_keys) {
+                                             int g, uint32_t nib_lo, uint32_t nib_hi, MidFn&& after_keys) {
   // ---- S^T = Khat . Q'^T --------------------------------------------------
   // Both 16-token halves (m) share each q' operand read.
   floatx4 s[2][NT];
@@ -211,9 +211,9 @@ __device__ __forceinline__ void compute_tile(State<NT>& st, const uint8_t* slot,
               slot + SLOT_K + k4base(2 * m + (kr16 >> 3)) + k4pos(kr16 & 7, 2 * kg + hh) + 4 * q4);
           if constexpr (KT == 2) {
             const uint32_t e = slot[SLOT_KH + (16 * m + kr16) * 32 + 8 * kg + ks];
-            a[m] = k5_codes_to_f16(w, e, hh ? dhi[m] : dlo[m], hh ? mhi[m] : mlo[m]);
+            a[m] = k5_codes_to_f16(w, e, nib_lo, nib_hi, hh ? dhi[m] : dlo[m], hh ? mhi[m] : mlo[m]);
           } else {
-            a[m] = k4_codes_to_f16(w, nib_mask, hh ? dhi[m] : dlo[m]);
+            a[m] = k4_codes_to_f16(w, nib_lo, nib_hi, hh ? dhi[m] : dlo[m]);
           }
         }
 #pragma unroll
@@ -257,7 +257,6 @@ __device__ __forceinline__ void compute_tile(State<NT>& st, const uint8_t* slot,
   // the key half of the slot has been read: let the caller refill it
   after_keys();
   // ---- masks: causal rows, tokens past kv_len ------------------------------
-  u32x4 vmask = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
   if (__builtin_expect(tok0 + 31 > min_limit, 0)) {
 #pragma unroll
     for (int m = 0; m < 2; ++m)
@@ -266,16 +265,23 @@ __device__ __forceinline__ void compute_tile(State<NT>& st, const uint8_t* slot,
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (tok0 + 16 * m + 4 * g + i > st.limit[nt]) s[m][nt][i] = neg_inf();
-    // slots past kv_len hold unwritten bytes: zero their V scales
-    uint32_t mk[4];
+    // Slots past kv_len hold unwritten bytes: their V scales are zeroed in
+    // this wave's slot (the values have landed; only this wave reads the
+    // slot, and its LDS accesses complete in order), so the PV loop reads the
+    // scales as they are. Scale word k (block k / 16, slot group (k / 4) % 4,
+    // pair k % 4) holds slots 2(k % 4) and 2(k % 4) + 1 of that group.
+    if (tok0 + 32 > kv_len) {  // uniform
+      uint32_t* vs = reinterpret_cast<uint32_t*>(slot + SLOT_VS<KT, V8>);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int j0 = 2 * p, j1 = 2 * p + 1;
-      const int u0 = 16 * (j0 >> 2) + 4 * g + (j0 & 3);
-      const int u1 = 16 * (j1 >> 2) + 4 * g + (j1 & 3);
-      mk[p] = (tok0 + u0 < kv_len ? 0x0000FFFFu : 0u) | (tok0 + u1 < kv_len ? 0xFFFF0000u : 0u);
+      for (int k0 = 0; k0 < 128; k0 += 64) {
+        const int k = k0 + lane, gg = (k >> 2) & 3, j0 = 2 * (k & 3), j1 = j0 + 1;
+        const int u0 = 16 * (j0 >> 2) + 4 * gg + (j0 & 3);
+        const int u1 = 16 * (j1 >> 2) + 4 * gg + (j1 & 3);
+        const uint32_t mk =
+            (tok0 + u0 < kv_len ? 0x0000FFFFu : 0u) | (tok0 + u1 < kv_len ? 0xFFFF0000u : 0u);
+        vs[k] &= mk;
+      }
     }
-    vmask = u32x4{mk[0], mk[1], mk[2], mk[3]};
   }
   // ---- online softmax (base 2, lazy reference max) ------------------------
   half8_t pb[NT];
@@ -325,8 +331,7 @@ __device__ __forceinline__ void compute_tile(State<NT>& st, const uint8_t* slot,
       v8cur = vw[0];
       if (b < 7) vw[0] = *reinterpret_cast<const u32x4*>(slot + SLOT_V<KT> + (b + 1) * 1024 + lane * 16);
     }
-    const u32x4 sc =
-        *reinterpret_cast<const u32x4*>(slot + SLOT_VS<KT, V8> + (b * 4 + g) * 16) & vmask;
+    const u32x4 sc = *reinterpret_cast<const u32x4*>(slot + SLOT_VS<KT, V8> + (b * 4 + g) * 16);
     const uint32_t scw[4] = {sc.x, sc.y, sc.z, sc.w};
     half8_t bb[NT];
 #pragma unroll
@@ -347,7 +352,7 @@ __device__ __forceinline__ void compute_tile(State<NT>& st, const uint8_t* slot,
       } else {
         const u32x4 vq = vw[mt >> 2];
         const uint32_t w = (mt & 3) == 0 ? vq.x : (mt & 3) == 1 ? vq.y : (mt & 3) == 2 ? vq.z : vq.w;
-        a = v_codes_to_f16_m(w, nib_mask);
+        a = v_codes_to_f16_m(w, nib_lo, nib_hi);
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) st.o[nt][mt] = mfma16(a, bb[nt], st.o[nt][mt]);
@@ -748,8 +753,11 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
     for (int mt = 0; mt < 16; ++mt) st.o[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
   const int64_t min_limit = p.kv_len - p.n_q_tok;
-  uint32_t nib_mask;  // kept in a VGPR so the nibble unpack fuses into v_and_or
-  __asm__ volatile("v_mov_b32 %0, 0x000f000f" : "=v"(nib_mask));
+  // the nibble masks are kept in VGPRs so each pair unpacks with one
+  // v_and_or_b32 (its exponent bits from an SGPR)
+  uint32_t nib_lo, nib_hi;
+  __asm__ volatile("v_mov_b32 %0, 0x000f000f" : "=v"(nib_lo));
+  __asm__ volatile("v_mov_b32 %0, 0x00f000f0" : "=v"(nib_hi));
 
   const int64_t u0 = (int64_t)p.n_units * split / p.n_splits;
   const int64_t u1 = (int64_t)p.n_units * (split + 1) / p.n_splits;
@@ -902,7 +910,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
       }
     };
     if (valid) {
-      compute_tile<NT, KT, V8>(st, slot, tok, p.kv_len, min_limit, lane, r16, g, nib_mask, refill_keys);
+      compute_tile<NT, KT, V8>(st, slot, tok, p.kv_len, min_limit, lane, r16, g, nib_lo, nib_hi,
+                               refill_keys);
     } else {
       refill_keys();
     }

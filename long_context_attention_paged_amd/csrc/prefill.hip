@@ -242,8 +242,8 @@ __device__ __forceinline__ void dequant_raw(const uint8_t* raw, _Float16* stage,
       *reinterpret_cast<half8_t*>(krow + 0) = k5_codes_to_f16(hh ? in.k.z : in.k.x, kh & 0xFFu, d2, m2);
       *reinterpret_cast<half8_t*>(krow + 8) = k5_codes_to_f16(hh ? in.k.w : in.k.y, (kh >> 8) & 0xFFu, d2, m2);
     } else if constexpr (KT == 1) {  // words 4b + 2hh, +1: dims 32b + 16hh + 0..7, 8..15
-      *reinterpret_cast<half8_t*>(krow + 0) = k4_codes_to_f16(hh ? in.k.z : in.k.x, 0x000F000Fu, d2);
-      *reinterpret_cast<half8_t*>(krow + 8) = k4_codes_to_f16(hh ? in.k.w : in.k.y, 0x000F000Fu, d2);
+      *reinterpret_cast<half8_t*>(krow + 0) = k4_codes_to_f16(hh ? in.k.z : in.k.x, NIB_LO, NIB_HI, d2);
+      *reinterpret_cast<half8_t*>(krow + 8) = k4_codes_to_f16(hh ? in.k.w : in.k.y, NIB_LO, NIB_HI, d2);
     } else {
       *reinterpret_cast<half8_t*>(krow + 0) = k_codes_to_f16(in.k.x, in.k.y, d2);
       *reinterpret_cast<half8_t*>(krow + 8) = k_codes_to_f16(in.k.z, in.k.w, d2);
