@@ -371,6 +371,31 @@ kvattn_status kvattn_decode_partials(const kvattn_geom *geom, const float *q,
                                      int32_t n_splits, float *o_part,
                                      float *lse_part, void *stream);
 
+/* a1 + a3 — kvattn_append_decode's append with kvattn_decode_partials'
+ * partials, without the merge: the new tokens (and the summary of a page they
+ * complete) are written exactly as kvattn_append_decode writes them, and
+ * o_part / lse_part receive the n_splits partials of the key set after the
+ * append, exactly as kvattn_decode_partials writes them, so
+ * kvattn_merge_lse of them is kvattn_append_decode's out and lse bit for bit
+ * at the same n_splits (1 <= n_splits <= the unit count, which
+ * kvattn_append_decode never exceeds). The partials of the key set that holds the new
+ * tokens can then meet the partials of other key sets (pages streamed from
+ * the host, another device's pages) in a single merge ([RDNA4] "Online
+ * Log-Sum-Exp": partial results over streamed pages combined by LSE).
+ * Arguments as kvattn_append_decode, with n_splits, o_part and lse_part as
+ * kvattn_decode_partials; no workspace. */
+kvattn_status kvattn_append_decode_partials(const kvattn_geom *geom, const float *k_new,
+                                            const float *v_new, int32_t n_new,
+                                            const float *q, int32_t n_q_tok,
+                                            uint8_t *k_pool, uint8_t *v_pool,
+                                            const int32_t *page_table,
+                                            int32_t n_logical_pages,
+                                            const int32_t *blocks, int32_t n_blk,
+                                            int64_t kv_len, float scale,
+                                            float *k_summary, int32_t n_splits,
+                                            float *o_part, float *lse_part,
+                                            void *stream);
+
 /* The split count kvattn_decode chooses (n_splits = 0) for n_units units on
  * the current device; 0 if geom is invalid or n_units < 1. */
 int32_t kvattn_decode_splits(const kvattn_geom *geom, int32_t n_units);

@@ -13,7 +13,8 @@ import os
 __all__ = [
     "Geom", "KvattnError", "library_path", "load_library",
     "kvattn_quantize_pages", "kvattn_select_blocks", "kvattn_decode",
-    "kvattn_decode_partials", "kvattn_decode_splits", "kvattn_prefill_chunk",
+    "kvattn_decode_partials", "kvattn_append_decode_partials", "kvattn_decode_splits",
+    "kvattn_prefill_chunk",
     "kvattn_prefill_partials", "kvattn_prefill_groups", "kvattn_merge_lse",
     "kvattn_prefetch_pages", "kvattn_select_count", "workspace", "workspace_error",
     "K_RECORD_BYTES", "V_RECORD_BYTES", "HEAD_DIM", "PAGE_TOKENS",
@@ -86,6 +87,8 @@ def load_library():
                                   I32, P, SZP, P], I32),
         "kvattn_append_decode_noalloc": ([G, P, P, I32, P, I32, P, P, P, I32, P, I32, I64, F32, P,
                                           P, P, I32, P], I32),
+        "kvattn_append_decode_partials": ([G, P, P, I32, P, I32, P, P, P, I32, P, I32, I64, F32,
+                                           P, I32, P, P, P], I32),
         "kvattn_decode_splits": ([G, I32], I32),
         "kvattn_prefill_chunk": ([G, P, I32, P, P, P, I32, I64, F32, P, P, I32, P, SZP, P], I32),
         "kvattn_prefill_partials": ([G, P, I32, P, P, P, I32, I64, F32, I32, P, P, P], I32),
@@ -368,6 +371,39 @@ def _decode_args(geom, q, k_pool, v_pool, page_table, blocks):
             raise ValueError("blocks must be [n_kv_heads, n_blk]")
         n_blk = blocks.shape[1]
     return n_blk
+
+
+def kvattn_append_decode_partials(geom, k_new, v_new, q, k_pool, v_pool, page_table, kv_len,
+                                  scale, n_splits, blocks=None, k_summary=None, o_part=None,
+                                  lse_part=None, stream=None):
+    """The append of kvattn_append_decode with the partials of kvattn_decode_partials
+    (a1 + a3), no merge: -> (o_part [n_splits, n_q_tok*n_heads, 256], lse_part)."""
+    torch = _torch()
+    lib = load_library()
+    n_blk = _decode_args(geom, q, k_pool, v_pool, page_table, blocks)
+    n_new = k_new.shape[0]
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _need(t, name, torch.float32)
+        _size(t, name, n_new * geom.n_kv_heads * HEAD_DIM)
+    if k_summary is not None:
+        _need(k_summary, "k_summary", torch.float32)
+        _size(k_summary, "k_summary", geom.n_kv_heads * page_table.numel() * HEAD_DIM)
+    rows = q.shape[0] * q.shape[1]
+    if o_part is None:
+        o_part = torch.empty((n_splits, rows, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((n_splits, rows), dtype=torch.float32, device=q.device)
+    _need(o_part, "o_part", torch.float32)
+    _need(lse_part, "lse_part", torch.float32)
+    _size(o_part, "o_part", n_splits * rows * HEAD_DIM)
+    _size(lse_part, "lse_part", n_splits * rows)
+    _check("kvattn_append_decode_partials",
+           lib.kvattn_append_decode_partials(
+               ctypes.byref(geom), _ptr(k_new), _ptr(v_new), n_new, _ptr(q), q.shape[0],
+               _ptr(k_pool), _ptr(v_pool), _ptr(page_table), page_table.numel(), _ptr(blocks),
+               n_blk, int(kv_len), float(scale), _ptr(k_summary), int(n_splits), _ptr(o_part),
+               _ptr(lse_part), _stream(stream)))
+    return o_part, lse_part
 
 
 def kvattn_decode_splits(geom, n_units):

@@ -592,6 +592,28 @@ kvattn_status kvattn_decode_partials(const kvattn_geom* geom, const float* q, in
                                 static_cast<hipStream_t>(stream));
 }
 
+kvattn_status kvattn_append_decode_partials(const kvattn_geom* geom, const float* k_new,
+                                            const float* v_new, int32_t n_new, const float* q,
+                                            int32_t n_q_tok, uint8_t* k_pool, uint8_t* v_pool,
+                                            const int32_t* page_table, int32_t n_logical_pages,
+                                            const int32_t* blocks, int32_t n_blk, int64_t kv_len,
+                                            float scale, float* k_summary, int32_t n_splits,
+                                            float* o_part, float* lse_part, void* stream) {
+  if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16)) return KVATTN_E_INVALID;
+  if (n_new < 1 || n_new > KVATTN_MAX_APPEND_TOKENS || n_new > kv_len) return KVATTN_E_INVALID;
+  if (k_summary && !aligned(k_summary, 16)) return KVATTN_E_INVALID;
+  int32_t n_units = 0;
+  kvattn_status st = check_decode(geom, q, n_q_tok, k_pool, v_pool, page_table, n_logical_pages,
+                                  blocks, n_blk, kv_len, scale, &n_units);
+  if (st) return st;
+  if (!o_part || !lse_part || !aligned(o_part, 16) || n_splits < 1) return KVATTN_E_INVALID;
+  if ((st = current_device(nullptr))) return st;
+  const AppendArgs app{k_new, v_new, k_pool, v_pool, n_new, k_summary};
+  return launch_decode_partials(geom, q, n_q_tok, k_pool, v_pool, page_table, n_logical_pages,
+                                blocks, n_blk, kv_len, scale, n_units, n_splits, o_part, lse_part,
+                                static_cast<hipStream_t>(stream), &app);
+}
+
 int32_t kvattn_prefill_groups(const kvattn_geom* geom, int32_t chunk, int64_t pos0) {
   if (check_geom(geom) != KVATTN_OK || chunk < 1 || pos0 < 0) return 0;
   int n_cu = 256;

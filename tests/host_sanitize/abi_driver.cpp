@@ -104,6 +104,17 @@ int main() {
                               0.0625f, nullptr, PF, PF, 0, nullptr, &nb, nullptr), INV);
   EXPECT(kvattn_append_decode(&g, PF, PF, 4, PF, 4, P8, P8, PI, 8, nullptr, 0, 1000, 0.0625f, PF,
                               PF, PF, 0, nullptr, &nb, nullptr), OK);
+  // append + partials, no merge
+  EXPECT(kvattn_append_decode_partials(&g, PF, PF, INT32_MAX, PF, 1, P8, P8, PI, 8, nullptr, 0,
+                                       1000, 0.0625f, nullptr, 8, PF, PF, nullptr), INV);
+  EXPECT(kvattn_append_decode_partials(&g, PF, PF, 1, PF, 1, P8, P8, PI, 8, nullptr, 0,
+                                       INT64_MIN, 0.0625f, nullptr, 8, PF, PF, nullptr), INV);
+  EXPECT(kvattn_append_decode_partials(&g, PF, PF, 1, PF, 1, P8, P8, PI, 8, PI, INT32_MAX,
+                                       INT64_MAX, 0.0625f, nullptr, 8, PF, PF, nullptr), INV);
+  EXPECT(kvattn_append_decode_partials(&g, PF, PF, 1, PF, 1, P8, P8, PI, 8, nullptr, 0, 1000,
+                                       0.0625f, nullptr, INT32_MIN, PF, PF, nullptr), INV);
+  EXPECT(kvattn_append_decode_partials(&g, PF, PF, 1, PF, 1, P8, P8, PI, 8, nullptr, 0, 1000,
+                                       0.0625f, PF, INT32_MAX, PF, PF, nullptr), DEV);
   kvattn_geom big = geom(1 << 14, 8, 1 << 16);
   EXPECT(kvattn_append_decode_noalloc(&big, PF, PF, 1, PF, 4, P8, P8, PI, 1 << 16, nullptr, 0,
                                       (int64_t)128 << 16, 0.0625f, nullptr, PF, PF, 64, nullptr),

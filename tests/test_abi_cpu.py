@@ -153,6 +153,35 @@ def test_append_decode_noalloc_validation():
     assert 64 * 8 * 32 * 1028 > kv.NOALLOC_SCRATCH_BYTES >= 32 * 8 * 32 * 1028 + 512
 
 
+def append_decode_partials(g, **kw):
+    a = dict(k_new=FAKE, v_new=FAKE, n_new=4, q=FAKE, n_q_tok=4, k_pool=FAKE, v_pool=FAKE,
+             table=FAKE, n_logical=16, blocks=None, n_blk=0, kv_len=1000, scale=0.0625,
+             summ=None, n_splits=8, o_part=FAKE, lse_part=FAKE)
+    a.update(kw)
+    return kv.load_library().kvattn_append_decode_partials(
+        ctypes.byref(g), P(a["k_new"]), P(a["v_new"]), a["n_new"], P(a["q"]), a["n_q_tok"],
+        P(a["k_pool"]), P(a["v_pool"]), P(a["table"]), a["n_logical"], P(a["blocks"]), a["n_blk"],
+        a["kv_len"], a["scale"], P(a["summ"]), a["n_splits"], P(a["o_part"]), P(a["lse_part"]),
+        None)
+
+
+def test_append_decode_partials_validation():
+    g = geom()
+    assert append_decode_partials(g, k_new=0) == E_INVALID
+    assert append_decode_partials(g, v_new=FAKE + 4) == E_INVALID      # misaligned
+    assert append_decode_partials(g, n_new=0) == E_INVALID
+    assert append_decode_partials(g, n_new=33) == E_INVALID
+    assert append_decode_partials(g, n_new=5, n_q_tok=1, kv_len=4) == E_INVALID
+    assert append_decode_partials(g, summ=FAKE + 4) == E_INVALID
+    assert append_decode_partials(g, o_part=0) == E_INVALID
+    assert append_decode_partials(g, lse_part=0) == E_INVALID
+    assert append_decode_partials(g, o_part=FAKE + 4) == E_INVALID    # misaligned
+    assert append_decode_partials(g, n_splits=0) == E_INVALID
+    assert append_decode_partials(g, n_q_tok=6) == E_UNSUPPORTED     # decode's own checks apply
+    assert append_decode_partials(g, kv_len=16 * 128 + 1) == E_INVALID
+    assert append_decode_partials(g, blocks=FAKE, n_blk=0) == E_INVALID
+
+
 def test_prefill_range_validation():
     lib = kv.load_library()
     g = geom()

@@ -197,3 +197,45 @@ def test_append_summary_of_large_q8_keys():
     assert np.abs(kh).sum(axis=-2).max() * 2.0 ** 24 >= 2.0 ** 53  # the fallback is taken
     assert torch.equal(summ[:, 1], summ2[:, 1])
     assert (host(summ)[:, 1].view(np.uint32) == ref_s[:, 1].view(np.uint32)).all()
+
+
+@pytest.mark.parametrize("k_type,sparse,n_new,kv_len,n_splits", [
+    (kv.K_Q8_0, False, 4, 3 * 128 + 2, 5),     # the new tokens complete page 2
+    (kv.K_Q4_0, True, 1, 7 * 128, 3),          # sparse list; the append completes page 6
+    (kv.K_Q5_1, False, 32, 6 * 128 - 50, 4),   # 32 new tokens; uneven splits of six pages
+])
+def test_append_decode_partials_merge_to_append_decode(k_type, sparse, n_new, kv_len, n_splits):
+    """kvattn_append_decode_partials writes the bytes and summaries
+    kvattn_append_decode writes, and kvattn_merge_lse of its partials is
+    kvattn_append_decode's result at the same split count, bit for bit."""
+    n_kv, gqa, n_q_tok = 2, 6, 2
+    g = np.random.default_rng(kv_len + n_new)
+    n_pages = (kv_len + 127) // 128
+    table = g.permutation(n_pages + 2)[:n_pages].astype(np.int32)
+    pools = Pools(n_pages + 2, n_kv, gqa, init_seed=kv_len, k_type=k_type)
+    pos0 = kv_len - n_new
+    pools.write(g.standard_normal((pos0, n_kv, 256)).astype(np.float32),
+                g.standard_normal((pos0, n_kv, 256)).astype(np.float32), 0, table)
+    Kn = gpu(g.standard_normal((n_new, n_kv, 256)).astype(np.float32))
+    Vn = gpu(g.standard_normal((n_new, n_kv, 256)).astype(np.float32))
+    q = gpu(g.standard_normal((n_q_tok, n_kv * gqa, 256)).astype(np.float32))
+    blocks = None
+    if sparse:
+        rows = [sorted(set(g.choice(n_pages - 1, 3, replace=False).tolist()) | {n_pages - 1})
+                for _ in range(n_kv)]
+        blocks = gpu(np.array(rows, np.int32), torch.int32)
+    table_d = gpu(table, torch.int32)
+    gk2, gv2 = pools.gk.clone(), pools.gv.clone()
+    summ = torch.zeros((n_kv, n_pages, 256), dtype=torch.float32, device=DEV)
+    summ2 = summ.clone()
+    o_part, l_part = kv.kvattn_append_decode_partials(pools.geom, Kn, Vn, q, pools.gk, pools.gv,
+                                                      table_d, kv_len, 1 / 16, n_splits,
+                                                      blocks=blocks, k_summary=summ)
+    rows_n = n_q_tok * n_kv * gqa
+    out, lse = kv.kvattn_merge_lse(o_part, l_part)
+    o2, l2 = kv.kvattn_append_decode(pools.geom, Kn, Vn, q, gk2, gv2, table_d, kv_len, 1 / 16,
+                                     blocks=blocks, k_summary=summ2, n_splits=n_splits)
+    torch.cuda.synchronize()
+    assert torch.equal(pools.gk, gk2) and torch.equal(pools.gv, gv2)
+    assert torch.equal(summ, summ2)
+    assert torch.equal(out, o2.view(rows_n, 256)) and torch.equal(lse, l2.view(rows_n))
