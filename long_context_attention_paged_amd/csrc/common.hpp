@@ -168,6 +168,25 @@ __device__ __forceinline__ float row_swap_combine32(float x, bool is_max) {
   const float p = __builtin_bit_cast(float, a0), q = __builtin_bit_cast(float, a1);
   return is_max ? fmaxf(p, q) : p + q;
 }
+// x combined over its group of eight lanes (8k .. 8k+7) by DPP moves: swap
+// neighbours, swap pairs, then mirror the half row. Each step adds (or takes
+// the max of) the same two values on both lanes of a pair, so all eight lanes
+// end with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float group8_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm [1, 0, 3, 2]
+  x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm [2, 3, 0, 1]
+  return fmaxf(x, dpp_f<0x141>(x));  // row_half_mirror
+}
+__device__ __forceinline__ float group8_sum(float x) {
+  x = x + dpp_f<0xB1>(x);
+  x = x + dpp_f<0x4E>(x);
+  return x + dpp_f<0x141>(x);
+}
 __device__ __forceinline__ float wave_max_xor_16_32(float x) {
   return row_swap_combine32(row_swap_combine16(x, true), true);
 }

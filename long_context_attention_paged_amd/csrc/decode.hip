@@ -953,18 +953,22 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
   if (sum_ph1 != 0) summary_issue<KT>(sum_rec, sl);
   constexpr int RS = 260;  // padded row stride of the combine buffer
   const int64_t rows_total = (int64_t)p.n_q_tok * n_heads;
-  __shared__ float s_f[WAVES][32];  // wave w's weight for row r: exp2(m_w - M) / L
+  // Wave w's weight for row r, exp2(m_w - M) / L, and the row's lse, from
+  // eight consecutive lanes per row (lane w of the eight holds wave w's max
+  // and sum; the butterflies give every lane of the group the same M and L).
+  // The lse is written here, while the waves dump their rows below.
+  static_assert(WAVES == 8, "one row per eight lanes");
+  __shared__ float s_f[WAVES][32];
   if (threadIdx.x < WAVES * NT * 16) {
-    const int w = threadIdx.x / (NT * 16), row = threadIdx.x % (NT * 16);
-    float M = neg_inf();
-#pragma unroll
-    for (int v = 0; v < WAVES; ++v) M = fmaxf(M, s_m[v][row]);
-    float L = 0.f;
-#pragma unroll
-    for (int v = 0; v < WAVES; ++v)
-      if (s_m[v][row] != neg_inf()) L += s_l[v][row] * __builtin_amdgcn_exp2f(s_m[v][row] - M);
-    s_f[w][row] =
-        (L > 0.f && s_m[w][row] != neg_inf()) ? __builtin_amdgcn_exp2f(s_m[w][row] - M) / L : 0.f;
+    const int row = threadIdx.x >> 3, w = threadIdx.x & 7;
+    const float mw = s_m[w][row];
+    const float M = group8_max(mw);
+    const float e = mw != neg_inf() ? __builtin_amdgcn_exp2f(mw - M) : 0.f;
+    const float L = group8_sum(s_l[w][row] * e);
+    s_f[w][row] = L > 0.f ? e / L : 0.f;
+    if (w == 0 && row < R)
+      p.lse_part[(int64_t)split * rows_total + s_rowg[row]] =
+          L > 0.f ? (M + __log2f(L)) * LN2 : neg_inf();
   }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -998,17 +1002,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(DecodeParams p) {
         reinterpret_cast<floatx4*>(p.o_part + ((int64_t)split * rows_total + rowg) * D)[c4] = v[0];
       }
     }
-    __syncthreads();
-  }
-  if (threadIdx.x < R) {
-    const int r = threadIdx.x;
-    const int64_t rowg = s_rowg[r];
-    float M = neg_inf();
-    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][r]);
-    float L = 0.f;
-    for (int w = 0; w < WAVES; ++w)
-      if (s_m[w][r] != neg_inf()) L += s_l[w][r] * __builtin_amdgcn_exp2f(s_m[w][r] - M);
-    p.lse_part[(int64_t)split * rows_total + rowg] = (L > 0.f) ? (M + __log2f(L)) * LN2 : neg_inf();
+    // the next round's dump, or the summary's partial sums, reuse the buffer
+    if (nt + 1 < NT || sum_ph1 != 0) __syncthreads();
   }
   if (sum_ph1 != 0)  // the combine buffer is free after the partial's last barrier
     summary_finish<KT, THREADS>(sum_rec, sl, p.k_summary + ((int64_t)h * p.n_logical + p.sum_page) * D,
