@@ -46,14 +46,14 @@ WARM_SECONDS = 0.3             # untimed graph replays before each timed region
 # once either has changed.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
-    "decode": {"sources": {"decode.hip": "6a88e369e9d98000", "common.hpp": "abcffce6ae06d4dc",
+    "decode": {"sources": {"decode.hip": "dbc6eef8a9502dd5", "common.hpp": "924544650c6d5f87",
                            "launch.hpp": "525dbebac0e478f8", "qround.hpp": "bfca159575b5ee34"},
                "flags": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-               "fetch_kib": 213561.0, "write_kib": 6168.0},
-    "prefill": {"sources": {"prefill.hip": "d8a770e575036885", "common.hpp": "abcffce6ae06d4dc",
+               "fetch_kib": 213559.0, "write_kib": 6168.0},
+    "prefill": {"sources": {"prefill.hip": "a3b889b2a455db80", "common.hpp": "924544650c6d5f87",
                             "launch.hpp": "525dbebac0e478f8"},
                 "flags": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
-                "fetch_kib": 369364.0, "write_kib": 199420.0},
+                "fetch_kib": 369651.0, "write_kib": 199318.5},
 }
 
 
