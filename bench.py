@@ -797,8 +797,9 @@ def cpu_model():
 def profile_kernels(dev, layers, reps):
     """A short fixed sequence for counter runs (rocprofv3 --pmc): a device copy
     of 1 GiB (the calibration kernel: reads and writes exactly 1 GiB), then the
-    decode kernel on verify-262k and the prefill kernel on prefill-512-after-262k,
-    each over `layers` per-layer pools, `reps` times."""
+    decode kernel on verify-262k (Q8_0 keys, then Q4_0 and Q5_1 keys) and the
+    prefill kernel on prefill-512-after-262k, each over `layers` per-layer
+    pools, `reps` times."""
     import torch
     import long_context_attention_paged_amd as kv
     from dataclasses import replace
@@ -823,7 +824,20 @@ def profile_kernels(dev, layers, reps):
                                       o_part=o_part, lse_part=lse_part)
     torch.cuda.synchronize()
     log(f"profile: decode_kernel x {reps * layers}, {w.kv_len * w.n_kv * 416} KV bytes each")
-    del pools, o_part, lse_part
+    del pools
+    # the nibble-key pairs (q4_0/q4_0, q5_1/q4_0): the same launches
+    for k_type, k_bytes in ((kv.K_Q4_0, 144), (kv.K_Q5_1, 192)):
+        pools = LayerPools(w, dev, k_type=k_type)
+        for _ in range(reps):
+            for layer in range(layers):
+                kv.kvattn_decode_partials(pools.geom, pools.q[layer], pools.kp[layer],
+                                          pools.vp[layer], pools.table, w.kv_len, 1.0 / 16.0, S,
+                                          o_part=o_part, lse_part=lse_part)
+        torch.cuda.synchronize()
+        log(f"profile: decode_kernel (key type {k_type}) x {reps * layers}, "
+            f"{w.kv_len * w.n_kv * (k_bytes + 144)} KV bytes each")
+        del pools
+    del o_part, lse_part
     torch.cuda.empty_cache()
     w = replace(synth.WORKLOADS[4], n_layers=layers)
     pools = LayerPools(w, dev)

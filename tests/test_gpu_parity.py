@@ -262,6 +262,41 @@ def test_decode_deterministic_and_page_permutation_invariant():
     assert torch.equal(o1, o3) and torch.equal(l1, l3)
 
 
+def test_ten_launches_bit_identical():
+    """Every kernel of the path sums in a fixed order, whatever the timing of
+    the workgroups: ten launches of each give the same bits (verify shape,
+    library-chosen splits; the append rewrites the same tokens each time;
+    prefill with its page groups and counter waits)."""
+    n_kv, gqa, kv_len = 4, 6, 64 * 128 + 37
+    pools, table, K, V = fill(n_kv, gqa, kv_len, seed=51)
+    g = np.random.default_rng(52)
+    q = gpu(g.standard_normal((4, n_kv * gqa, 256)).astype(np.float32))
+    t = gpu(table, torch.int32)
+    first = None
+    for i in range(10):
+        o, l = kv.kvattn_decode(pools.geom, q, pools.gk, pools.gv, t, kv_len, 1 / 16)
+        if first is None:
+            first = (o.clone(), l.clone())
+        assert torch.equal(o, first[0]) and torch.equal(l, first[1]), f"decode launch {i}"
+    kn, vn = gpu(K[-4:]), gpu(V[-4:])
+    first = None
+    for i in range(10):
+        o, l = kv.kvattn_append_decode(pools.geom, kn, vn, q, pools.gk, pools.gv, t, kv_len,
+                                       1 / 16)
+        if first is None:
+            first = (o.clone(), l.clone())
+        assert torch.equal(o, first[0]) and torch.equal(l, first[1]), f"append-decode launch {i}"
+    chunk = 300
+    qp = gpu(g.standard_normal((chunk, n_kv * gqa, 256)).astype(np.float32))
+    first = None
+    for i in range(10):
+        o, l = kv.kvattn_prefill_chunk(pools.geom, qp, pools.gk, pools.gv, t, kv_len - chunk,
+                                       1 / 16)
+        if first is None:
+            first = (o.clone(), l.clone())
+        assert torch.equal(o, first[0]) and torch.equal(l, first[1]), f"prefill launch {i}"
+
+
 def test_merge_parity():
     """Partials with lse = -inf contribute nothing, whatever their rows hold
     (NaN here for the GPU; zeros for the oracle). Part counts cover every
