@@ -177,6 +177,21 @@ __device__ __forceinline__ float dpp_f(float x) {
   return __builtin_bit_cast(
       float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
+// The value held by a partner lane in the same group of eight: lane l ^ 1
+// (o = 1), l ^ 2 (o = 2), or 7 - l within the group (o = 4, row_half_mirror,
+// which pairs every lane with one of the other quad). Three steps with o = 1,
+// 2, 4 reduce any commutative, associative selection over the eight lanes
+// onto all of them, as three xor shuffles would. o must be a constant.
+__device__ __forceinline__ uint32_t peer8(uint32_t x, int o) {
+  return o == 1   ? (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false)
+         : o == 2 ? (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false)
+                  : (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float peer8(float x, int o) {
+  return __builtin_bit_cast(float, peer8(__builtin_bit_cast(uint32_t, x), o));
+}
+__device__ __forceinline__ int peer8(int x, int o) { return (int)peer8((uint32_t)x, o); }
+
 __device__ __forceinline__ float group8_max(float x) {
   x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm [1, 0, 3, 2]
   x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm [2, 3, 0, 1]

@@ -459,8 +459,8 @@ __device__ __forceinline__ void append_finish(const DecodeParams& p, AppendTile&
         float mx = fmaxf(fmaxf(xe[0], xe[1]), fmaxf(xe[2], xe[3]));
 #pragma unroll
         for (int o = 1; o < 8; o <<= 1) {
-          mn = fminf(mn, __shfl_xor(mn, o));
-          mx = fmaxf(mx, __shfl_xor(mx, o));
+          mn = fminf(mn, peer8(mn, o));
+          mx = fmaxf(mx, peer8(mx, o));
         }
         const _Float16 d16 = q5_scale(mx, mn), m16 = (_Float16)mn;
         const float dk = (float)d16, mk = (float)m16;
@@ -474,8 +474,8 @@ __device__ __forceinline__ void append_finish(const DecodeParams& p, AppendTile&
           part |= (code & 0xFu) << v_slot_bit(k);
           hpart |= (code >> 4) << k5_hi_bit(k);
         }
-        const uint32_t word = part | __shfl_xor(part, 1);
-        const uint32_t hbyte = hpart | __shfl_xor(hpart, 1);
+        const uint32_t word = part | peer8(part, 1);
+        const uint32_t hbyte = hpart | peer8(hpart, 1);
         const int wi = 4 * b + (s >> 1);
         if ((s & 1) == 0) {
           *reinterpret_cast<uint32_t*>(krec + t * (D / 2) + 4 * wi) = word;
@@ -499,8 +499,8 @@ __device__ __forceinline__ void append_finish(const DecodeParams& p, AppendTile&
           }
 #pragma unroll
         for (int o = 1; o < 8; o <<= 1) {
-          const float ak2 = __shfl_xor(ak, o), mk2 = __shfl_xor(mk, o);
-          const int ik2 = __shfl_xor(ik, o);
+          const float ak2 = peer8(ak, o), mk2 = peer8(mk, o);
+          const int ik2 = peer8(ik, o);
           if (ak2 > ak || (ak2 == ak && ik2 < ik)) {
             ak = ak2;
             mk = mk2;
@@ -516,7 +516,7 @@ __device__ __forceinline__ void append_finish(const DecodeParams& p, AppendTile&
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           part |= (live ? q4_code(xe[j], inv) : 8u) << v_slot_bit(4 * (s & 1) + j);
-        const uint32_t word = part | __shfl_xor(part, 1);
+        const uint32_t word = part | peer8(part, 1);
         if ((s & 1) == 0)
           *reinterpret_cast<uint32_t*>(krec + t * (D / 2) + 4 * (4 * b + (s >> 1))) = word;
         if (s == 0)
@@ -525,9 +525,9 @@ __device__ __forceinline__ void append_finish(const DecodeParams& p, AppendTile&
       } else {
       // keys: Q8_0
       float amax = fmaxf(fmaxf(fabsf(xe[0]), fabsf(xe[1])), fmaxf(fabsf(xe[2]), fabsf(xe[3])));
-      amax = fmaxf(amax, __shfl_xor(amax, 1));
-      amax = fmaxf(amax, __shfl_xor(amax, 2));
-      amax = fmaxf(amax, __shfl_xor(amax, 4));
+      amax = fmaxf(amax, peer8(amax, 1));
+      amax = fmaxf(amax, peer8(amax, 2));
+      amax = fmaxf(amax, peer8(amax, 4));
       const _Float16 d16 = q8_scale(amax);
       const float d = (float)d16;
       uint32_t kw = 0u;
@@ -543,9 +543,9 @@ __device__ __forceinline__ void append_finish(const DecodeParams& p, AppendTile&
       }
       if constexpr (V8) {  // values: Q8_0, the key rule
         float vmax = fmaxf(fmaxf(fabsf(ye[0]), fabsf(ye[1])), fmaxf(fabsf(ye[2]), fabsf(ye[3])));
-        vmax = fmaxf(vmax, __shfl_xor(vmax, 1));
-        vmax = fmaxf(vmax, __shfl_xor(vmax, 2));
-        vmax = fmaxf(vmax, __shfl_xor(vmax, 4));
+        vmax = fmaxf(vmax, peer8(vmax, 1));
+        vmax = fmaxf(vmax, peer8(vmax, 2));
+        vmax = fmaxf(vmax, peer8(vmax, 4));
         const _Float16 dq16 = q8_scale(vmax);
         const float dq = (float)dq16;
         const float inv = dq != 0.0f ? 1.0f / dq : 0.0f;
@@ -571,8 +571,8 @@ __device__ __forceinline__ void append_finish(const DecodeParams& p, AppendTile&
         }
 #pragma unroll
       for (int o = 1; o < 8; o <<= 1) {
-        const float am2 = __shfl_xor(am, o), m2 = __shfl_xor(m, o);
-        const int idx2 = __shfl_xor(idx, o);
+        const float am2 = peer8(am, o), m2 = peer8(m, o);
+        const int idx2 = peer8(idx, o);
         if (am2 > am || (am2 == am && idx2 < idx)) {
           am = am2;
           m = m2;
