@@ -46,14 +46,14 @@ WARM_SECONDS = 0.3             # untimed graph replays before each timed region
 # once either has changed.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
-    "decode": {"sources": {"decode.hip": "dbc6eef8a9502dd5", "common.hpp": "924544650c6d5f87",
+    "decode": {"sources": {"decode.hip": "371fd331fe4199d7", "common.hpp": "5e5d1f7f34499a89",
                            "launch.hpp": "525dbebac0e478f8", "qround.hpp": "bfca159575b5ee34"},
                "flags": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-               "fetch_kib": 213559.0, "write_kib": 6168.0},
-    "prefill": {"sources": {"prefill.hip": "a3b889b2a455db80", "common.hpp": "924544650c6d5f87",
+               "fetch_kib": 213555.25, "write_kib": 6168.0},
+    "prefill": {"sources": {"prefill.hip": "a3b889b2a455db80", "common.hpp": "5e5d1f7f34499a89",
                             "launch.hpp": "525dbebac0e478f8"},
                 "flags": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
-                "fetch_kib": 369651.0, "write_kib": 199318.5},
+                "fetch_kib": 369622.25, "write_kib": 199322.0},
 }
 
 
