@@ -34,7 +34,11 @@ constexpr int PF_THREADS = 64 * PF_WAVES;
 constexpr int PF_NT = 2;                        // 16-row N-tiles per wave
 constexpr int PF_ROWS = PF_WAVES * 16 * PF_NT;  // rows per workgroup
 constexpr int K_LDS_STRIDE = 264;               // halves per key row (256 + pad)
-constexpr int V_LDS_STRIDE = 40;                // halves per value dim row (32 + pad)
+// A value dim row holds 32 slots (64 bytes, no pad); its four 16-byte slot
+// groups are stored in the order g ^ ((dim >> 2) & 3), so the 16 rows one
+// matrix-core operand read touches fall on distinct banks.
+constexpr int V_LDS_STRIDE = 32;                // halves per value dim row
+__device__ __forceinline__ int v_group(int dim, int g) { return g ^ ((dim >> 2) & 3); }
 constexpr int K_LDS_HALVES = 32 * K_LDS_STRIDE;
 constexpr int V_LDS_HALVES = D * V_LDS_STRIDE;
 constexpr int STAGE_HALVES = K_LDS_HALVES + V_LDS_HALVES;  // one f16 sub-tile
@@ -277,7 +281,7 @@ __device__ __forceinline__ void dequant_raw(const uint8_t* raw, _Float16* stage,
         val[2 * p] = r[0];
         val[2 * p + 1] = r[1];
       }
-      *reinterpret_cast<half8_t*>(vbase + dim * V_LDS_STRIDE + 8 * g) = val;
+      *reinterpret_cast<half8_t*>(vbase + dim * V_LDS_STRIDE + 8 * v_group(dim, g)) = val;
     }
   }
 }
@@ -468,7 +472,8 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(PrefillParams p) {
       __asm__ __volatile__("" : "+v"(ln));  // recompute lane offsets here, do not hold them
       const _Float16* kbase = lds + st * STAGE_HALVES + (ln & 15) * K_LDS_STRIDE + 64 * (ln >> 4);
       const _Float16* vbase =
-          lds + st * STAGE_HALVES + K_LDS_HALVES + (ln & 15) * V_LDS_STRIDE + 8 * (ln >> 4);
+          lds + st * STAGE_HALVES + K_LDS_HALVES + (ln & 15) * V_LDS_STRIDE +
+          8 * v_group(ln & 15, ln >> 4);  // rows 16 (f - 16) + (ln & 15): same swizzle
       auto frag = [&](int f) -> half8_t {
         return f < 16 ? *reinterpret_cast<const half8_t*>(kbase + 16 * (f & 1) * K_LDS_STRIDE +
                                                           8 * (f >> 1))
