@@ -232,8 +232,10 @@ kvattn_status kvattn_quantize_pages(const kvattn_geom *geom, const float *k,
  *              be full pages whose summary has been written.
  *  n_blocks    1 <= n_blocks <= n_logical_pages. n_recent, k_top >= 0.
  *  out_blocks  int32 [n_kv_heads][kvattn_select_count(...)].
- *  workspace   8 * n_kv_heads * (NB - R) bytes (fp64 scores); query with
- *              workspace == NULL. */
+ *  workspace   2048 + 8 * n_kv_heads * (NB - R) bytes, rounded up; query
+ *              with workspace == NULL. When 0 < k_top < NB - R the call
+ *              leaves the scores there: binary64 [n_kv_heads][NB - R] from
+ *              byte 2048. */
 kvattn_status kvattn_select_blocks(const kvattn_geom *geom, const float *q,
                                    const float *k_summary,
                                    int32_t n_logical_pages, int32_t n_blocks,

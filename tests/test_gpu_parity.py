@@ -102,6 +102,30 @@ def test_select_bitexact(n_blocks, n_recent, k_top):
     run_select(summ, q, gqa, n_blocks, n_recent, k_top)
 
 
+@pytest.mark.parametrize("n_kv,gqa,n_blocks,n_recent,k_top", [
+    (3, 6, 300, 16, 40), (4, 6, 4088, 128, 256), (2, 1, 130, 0, 7), (1, 16, 700, 10, 100),
+    (2, 9, 257, 3, 50), (1, 6, 65, 0, 1)])
+def test_select_scores_bitexact(n_kv, gqa, n_blocks, n_recent, k_top):
+    """The binary64 scores the ranking uses (left in the workspace from byte
+    2048) equal the fixed-order sums bit for bit, including groups of more
+    than eight query heads and a ragged last workgroup of candidates."""
+    g = np.random.default_rng(n_blocks + gqa)
+    summ = (g.standard_normal((n_kv, n_blocks, 256)) * 0.05).astype(np.float32)
+    summ *= np.exp2(g.integers(-20, 20, (n_kv, n_blocks, 1))).astype(np.float32)
+    q = g.standard_normal((n_kv * gqa, 256)).astype(np.float32)
+    n_cand = n_blocks - min(n_recent, n_blocks)
+    ws = torch.zeros(2048 + 8 * n_kv * n_cand + 4096, dtype=torch.uint8, device=DEV)
+    kv.kvattn_select_blocks(kv.Geom(n_kv, gqa, 1), gpu(q), gpu(summ), n_blocks, n_blocks,
+                            n_recent, k_top, workspace=ws)
+    torch.cuda.synchronize()
+    got = host(ws[2048:2048 + 8 * n_kv * n_cand]).view(np.float64).reshape(n_kv, n_cand)
+    qs = oracle.query_sum(q, gqa)
+    for h in range(n_kv):
+        ref = np.asarray(oracle.block_scores(qs[h], summ[h, :n_cand]), np.float64)
+        bad = np.flatnonzero(got[h].view(np.uint64) != ref.view(np.uint64))
+        assert bad.size == 0, f"head {h}: {bad.size} scores differ, first {bad[:4]}"
+
+
 def test_select_wide_range_and_many_candidates():
     """Scores of both signs spanning many binade (the radix select starts at
     the highest bit where candidates differ), and more candidates than the
