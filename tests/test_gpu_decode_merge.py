@@ -35,6 +35,10 @@ def counters(ws):
     (2, 8, 3, 2000, 7),
     (4, 6, 4, 64 * 128 + 77, 64),
     (1, 32, 1, 700, 5),
+    # many KV heads with few rows each; 28 x 64 splits: more workgroups than
+    # fit on the device at once
+    (28, 1, 3, 600, 0),
+    (28, 1, 4, 64 * 128 + 3, 64),
 ])
 def test_decode_is_partials_plus_merge(n_kv, gqa, n_q_tok, kv_len, n_splits):
     pools, table, _, _ = fill(n_kv, gqa, kv_len, seed=kv_len + n_kv, init_seed=3)
