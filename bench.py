@@ -149,20 +149,27 @@ def time_graph(step_fn, steps, warmup):
     return (time.perf_counter() - t0) * 1e3 / steps, g
 
 
+MIN_CALLS_PER_GRAPH = 16
+
+
 def time_launches(call_fn, n_layers, reps):
     """Average duration of one call with HIP events on the stream the work is
     launched on: the n_layers calls (one per layer, so every call reads its own
-    pool) are captured back to back in one graph, and a pair of events brackets
-    reps replays of it; the figure is the bracketed time over reps * n_layers
-    (it includes the short gaps between consecutive launches)."""
+    pool) are captured back to back in one graph, cycling through the layers
+    until the graph holds at least MIN_CALLS_PER_GRAPH calls (so a one-layer
+    workload is not timed against the graph's own launch), and a pair of
+    events brackets reps replays of it; the figure is the bracketed time over
+    the calls replayed (it includes the short gaps between consecutive
+    launches)."""
     import torch
+    n_calls = max(n_layers, MIN_CALLS_PER_GRAPH)
     for layer in range(n_layers):
         call_fn(layer)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for layer in range(n_layers):
-            call_fn(layer)
+        for i in range(n_calls):
+            call_fn(i % n_layers)
     g.replay()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -171,7 +178,7 @@ def time_launches(call_fn, n_layers, reps):
         g.replay()
     end.record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / (reps * n_layers)
+    return start.elapsed_time(end) / (reps * n_calls)
 
 
 def bench_decode(w, dev, steps, warmup, sparse=False, v_type=0, k_type=0):
