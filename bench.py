@@ -50,10 +50,10 @@ TRAFFIC = {
                            "launch.hpp": "525dbebac0e478f8", "qround.hpp": "bfca159575b5ee34"},
                "flags": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
                "fetch_kib": 213555.25, "write_kib": 6168.0},
-    "prefill": {"sources": {"prefill.hip": "f208a5e21dfe78ac", "common.hpp": "5e5d1f7f34499a89",
+    "prefill": {"sources": {"prefill.hip": "cebe84ebe7996b0d", "common.hpp": "5e5d1f7f34499a89",
                             "launch.hpp": "525dbebac0e478f8"},
                 "flags": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
-                "fetch_kib": 371226.5, "write_kib": 199140.0},
+                "fetch_kib": 372737.3, "write_kib": 204382.27},
 }
 
 
