@@ -197,62 +197,115 @@ __device__ __forceinline__ void compute_tile(State<NT>& st, uint8_t* slot, int64
   int ln = lane;
   __asm__ volatile("" : "+v"(ln));
   const int kr16 = ln & 15, kg = ln >> 4;
+  // Each step's LDS operands (key words, fifth bits, query fragments) are read
+  // one step ahead, before the previous step is converted and multiplied, so
+  // their latency hides behind that work; the scheduling barrier at the end
+  // of a step keeps the reads there.
+  auto qfrag = [&](int ks, int nt) -> half8_t {
+    return *reinterpret_cast<const half8_t*>(st.q_lds + (nt * 16 + r16) * Q_LDS_STRIDE + 64 * g +
+                                             8 * ks);
+  };
   if constexpr (KT != 0) {
     // dims 64g + 8ks .. +7 are word 8g + ks of the row: chunk 2g + ks/4, word ks%4
+    auto kword = [&](int ks, int m) -> uint32_t {
+      return *reinterpret_cast<const uint32_t*>(slot + SLOT_K + k4base(2 * m + (kr16 >> 3)) +
+                                                k4pos(kr16 & 7, 2 * kg + (ks >> 2)) + 4 * (ks & 3));
+    };
+    auto kfifth = [&](int ks, int m) -> uint32_t {
+      return slot[SLOT_KH + (16 * m + kr16) * 32 + 8 * kg + ks];
+    };
+    uint32_t wc[2], ec[2] = {0u, 0u};
+    half8_t qc[NT];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int m = 0; m < 2; ++m) {
+      wc[m] = kword(0, m);
+      if constexpr (KT == 2) ec[m] = kfifth(0, m);
+    }
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int ks = 4 * hh + q4;
-        half8_t a[2];
+    for (int nt = 0; nt < NT; ++nt) qc[nt] = qfrag(0, nt);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int hh = ks >> 2;
+      uint32_t wn[2] = {0u, 0u}, en[2] = {0u, 0u};
+      half8_t qn[NT];
+      if (ks < 7) {
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(
-              slot + SLOT_K + k4base(2 * m + (kr16 >> 3)) + k4pos(kr16 & 7, 2 * kg + hh) + 4 * q4);
-          if constexpr (KT == 2) {
-            const uint32_t e = slot[SLOT_KH + (16 * m + kr16) * 32 + 8 * kg + ks];
-            a[m] = k5_codes_to_f16(w, e, nib_lo, nib_hi, hh ? dhi[m] : dlo[m], hh ? mhi[m] : mlo[m]);
-          } else {
-            a[m] = k4_codes_to_f16(w, nib_lo, nib_hi, hh ? dhi[m] : dlo[m]);
-          }
+          wn[m] = kword(ks + 1, m);
+          if constexpr (KT == 2) en[m] = kfifth(ks + 1, m);
         }
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const half8_t qb = *reinterpret_cast<const half8_t*>(
-              st.q_lds + (nt * 16 + r16) * Q_LDS_STRIDE + 64 * g + 8 * ks);
+        for (int nt = 0; nt < NT; ++nt) qn[nt] = qfrag(ks + 1, nt);
+      }
+      half8_t a[2];
 #pragma unroll
-          for (int m = 0; m < 2; ++m) s[m][nt] = mfma16(a[m], qb, s[m][nt]);
+      for (int m = 0; m < 2; ++m) {
+        if constexpr (KT == 2) {
+          a[m] = k5_codes_to_f16(wc[m], ec[m], nib_lo, nib_hi, hh ? dhi[m] : dlo[m],
+                                 hh ? mhi[m] : mlo[m]);
+        } else {
+          a[m] = k4_codes_to_f16(wc[m], nib_lo, nib_hi, hh ? dhi[m] : dlo[m]);
         }
-        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) s[m][nt] = mfma16(a[m], qc[nt], s[m][nt]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks < 7) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) wc[m] = wn[m], ec[m] = en[m];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) qc[nt] = qn[nt];
       }
     }
   } else {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
     // bytes 64g + 16j of token 16m + r16: load 4m + r16/4, row r16%4, chunk 4g + j
+    auto kwords = [&](int j, int m) -> u32x4 {
+      return *reinterpret_cast<const u32x4*>(slot + SLOT_K + kbase(4 * m + (kr16 >> 2)) +
+                                             16 * kpos(kr16 & 3, 4 * kg + j));
+    };
     u32x4 w4[2];
+    half8_t qc[NT];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-      w4[m] = *reinterpret_cast<const u32x4*>(
-          slot + SLOT_K + kbase(4 * m + (kr16 >> 2)) + 16 * kpos(kr16 & 3, 4 * kg + j));
+    for (int m = 0; m < 2; ++m) w4[m] = kwords(0, m);
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int ks = 2 * j + h2;
-      half8_t a[2];
+    for (int nt = 0; nt < NT; ++nt) qc[nt] = qfrag(0, nt);
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
-        a[m] = k_codes_to_f16(h2 ? w4[m].z : w4[m].x, h2 ? w4[m].w : w4[m].y,
-                              ks < 4 ? dlo[m] : dhi[m]);
+    for (int j = 0; j < 4; ++j) {
+      u32x4 w4n[2];
+      if (j < 3) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const half8_t qb = *reinterpret_cast<const half8_t*>(
-            st.q_lds + (nt * 16 + r16) * Q_LDS_STRIDE + 64 * g + 8 * ks);
-#pragma unroll
-        for (int m = 0; m < 2; ++m) s[m][nt] = mfma16(a[m], qb, s[m][nt]);
+        for (int m = 0; m < 2; ++m) w4n[m] = kwords(j + 1, m);
       }
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int ks = 2 * j + h2;
+        half8_t qn[NT];
+        if (ks < 7) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) qn[nt] = qfrag(ks + 1, nt);
+        }
+        half8_t a[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          a[m] = k_codes_to_f16(h2 ? w4[m].z : w4[m].x, h2 ? w4[m].w : w4[m].y,
+                                ks < 4 ? dlo[m] : dhi[m]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int m = 0; m < 2; ++m) s[m][nt] = mfma16(a[m], qc[nt], s[m][nt]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks < 7) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) qc[nt] = qn[nt];
+        }
+      }
+      if (j < 3) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) w4[m] = w4n[m];
+      }
     }
-  }
   }
   // the key half of the slot has been read: let the caller refill it
   after_keys();
@@ -324,6 +377,11 @@ __device__ __forceinline__ void compute_tile(State<NT>& st, uint8_t* slot, int64
     for (int q = 0; q < 4; ++q)
       vw[q] = *reinterpret_cast<const u32x4*>(slot + SLOT_V<KT> + q * 1024 + lane * 16);
   }
+  // the value scales of block b are read one block ahead, as the operands above
+  auto vscale = [&](int b) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(slot + SLOT_VS<KT, V8> + (b * 4 + g) * 16);
+  };
+  u32x4 scn = vscale(0);
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
     u32x4 v8cur;
@@ -331,7 +389,8 @@ __device__ __forceinline__ void compute_tile(State<NT>& st, uint8_t* slot, int64
       v8cur = vw[0];
       if (b < 7) vw[0] = *reinterpret_cast<const u32x4*>(slot + SLOT_V<KT> + (b + 1) * 1024 + lane * 16);
     }
-    const u32x4 sc = *reinterpret_cast<const u32x4*>(slot + SLOT_VS<KT, V8> + (b * 4 + g) * 16);
+    const u32x4 sc = scn;
+    if (b < 7) scn = vscale(b + 1);
     const uint32_t scw[4] = {sc.x, sc.y, sc.z, sc.w};
     half8_t bb[NT];
 #pragma unroll
