@@ -46,10 +46,10 @@ WARM_SECONDS = 0.3             # untimed graph replays before each timed region
 # once either has changed.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
-    "decode": {"sources": {"decode.hip": "371fd331fe4199d7", "common.hpp": "5e5d1f7f34499a89",
+    "decode": {"sources": {"decode.hip": "2477d5fb9d026551", "common.hpp": "5e5d1f7f34499a89",
                            "launch.hpp": "525dbebac0e478f8", "qround.hpp": "bfca159575b5ee34"},
                "flags": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-               "fetch_kib": 213555.25, "write_kib": 6168.0},
+               "fetch_kib": 213557.85, "write_kib": 6168.0},
     "prefill": {"sources": {"prefill.hip": "cebe84ebe7996b0d", "common.hpp": "5e5d1f7f34499a89",
                             "launch.hpp": "525dbebac0e478f8"},
                 "flags": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
