@@ -55,13 +55,20 @@ template <bool V8> constexpr int RAW_VS = V8 ? 2112 : 1600;
 template <int KT, bool V8> constexpr int RAW_WAVE = (V8 ? 2176 : 1664) + (KT == 2 ? 64 : 0);
 template <int KT, bool V8> constexpr int RAW_STAGE = PF_WAVES * RAW_WAVE<KT, V8>;
 constexpr int RAW_DEPTH = 2;                    // sub-tile i+2 refills sub-tile i's slot
-constexpr int RAW_LOADS = 3;                    // direct loads per wave per sub-tile
+constexpr int RAW_LOADS = 4;                    // direct loads per wave per sub-tile
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* lds_dst) {
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (lds_void*)(lds_dst), 16,
-                                   0, 0);
+// 16 bytes per lane from a page record straight into LDS (lane l's bytes land
+// at lds_dst + 16 l). Buffer loads with the record in scalar registers, not
+// global ones: the compiler counts a global load into LDS against the LDS
+// counter as well, which turns every wait for the operand reads of the
+// products into a wait for all of them.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rec_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rec, int off, uint8_t* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rec, (lds_void*)(lds_dst), 16, off, 0, 0, 0);
 }
 
 template <int N>
@@ -116,30 +123,36 @@ template <int KT, bool V8>
 __device__ __forceinline__ void issue_raw(uint8_t* raw, const uint8_t* krec, const uint8_t* vrec,
                                           int c, int w, int lane) {
   const int q = w >> 1, gh = w & 1;
+  const __amdgpu_buffer_rsrc_t kr = rec_rsrc(krec, KREC_OF<KT>);
+  const __amdgpu_buffer_rsrc_t vr = rec_rsrc(vrec, V8 ? V8_REC : V_REC);
   if constexpr (KT == 2) {  // lanes 32-39: the fifth bits of rows 4w..4w+3 (32 B each)
-    const uint8_t* src =
-        lane < 32 ? krec + (c * 32 + 4 * w + (lane & 3)) * (D / 2) + 16 * ((lane >> 2) & 7)
-                  : krec + K5_HI_OFF + (c * 32 + 4 * w + ((lane - 32) >> 1)) * 32 + 16 * (lane & 1);
-    if (lane < 40) dma16(src, raw + RAW_K);
+    const int off = lane < 32 ? (c * 32 + 4 * w + (lane & 3)) * (D / 2) + 16 * ((lane >> 2) & 7)
+                              : K5_HI_OFF + (c * 32 + 4 * w + ((lane - 32) >> 1)) * 32 + 16 * (lane & 1);
+    if (lane < 40) dma16(kr, off, raw + RAW_K);
   } else if constexpr (KT == 1) {
     if (lane < 32)
-      dma16(krec + (c * 32 + 4 * w + (lane & 3)) * (D / 2) + 16 * ((lane >> 2) & 7), raw + RAW_K);
+      dma16(kr, (c * 32 + 4 * w + (lane & 3)) * (D / 2) + 16 * ((lane >> 2) & 7), raw + RAW_K);
   } else {
-    dma16(krec + (c * 32 + 4 * w + (lane & 3)) * D + 32 * ((lane >> 2) & 7) + 16 * (lane >> 5),
+    dma16(kr, (c * 32 + 4 * w + (lane & 3)) * D + 32 * ((lane >> 2) & 7) + 16 * (lane >> 5),
           raw + RAW_K);
   }
   if constexpr (V8)
-    dma16(vrec + c * 8192 + (2 * q + (lane >> 5)) * 1024 + 2 * gh * 256 + (lane & 31) * 16,
+    dma16(vr, c * 8192 + (2 * q + (lane >> 5)) * 1024 + 2 * gh * 256 + (lane & 31) * 16,
           raw + RAW_V);
   else if (lane < 32)
-    dma16(vrec + (((c * 4 + q) * 4 + 2 * gh) * 64) * 4 + lane * 16, raw + RAW_V);
-  if (lane < (KT == 2 ? 12 : 8)) {  // lanes 8-11: Q5_1 block minimums of rows 4w..4w+3
+    dma16(vr, (((c * 4 + q) * 4 + 2 * gh) * 64) * 4 + lane * 16, raw + RAW_V);
+  // scales, two loads (one per record): lanes 0-3 key rows 4w..4w+3, lanes
+  // 8-11 their Q5_1 block minimums; lanes 4-7 value blocks 2q, 2q+1 of the two
+  // lane groups
+  if (lane < 4 || (KT == 2 && lane >= 8 && lane < 12)) {
+    const int off = lane < 4 ? KSCALE_OF<KT> + (c * 32 + 4 * w + lane) * 16
+                             : K5_M_OFF + (c * 32 + 4 * w + lane - 8) * 16;
+    dma16(kr, off, raw + RAW_KS<V8>);
+  }
+  if (lane >= 4 && lane < 8) {
     const int vs_off = V8 ? K_SCALE_OFF : V_SCALE_OFF;
-    const uint8_t* src =
-        lane < 4   ? krec + KSCALE_OF<KT> + (c * 32 + 4 * w + lane) * 16
-        : lane < 8 ? vrec + vs_off + ((c * 8 + 2 * q + ((lane - 4) >> 1)) * 4 + 2 * gh + (lane & 1)) * 16
-                   : krec + K5_M_OFF + (c * 32 + 4 * w + lane - 8) * 16;
-    dma16(src, raw + RAW_KS<V8>);
+    dma16(vr, vs_off + ((c * 8 + 2 * q + ((lane - 4) >> 1)) * 4 + 2 * gh + (lane & 1)) * 16,
+          raw + RAW_KS<V8>);
   }
 }
 
