@@ -50,10 +50,10 @@ TRAFFIC = {
                            "launch.hpp": "525dbebac0e478f8", "qround.hpp": "bfca159575b5ee34"},
                "flags": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
                "fetch_kib": 213557.85, "write_kib": 6168.0},
-    "prefill": {"sources": {"prefill.hip": "cebe84ebe7996b0d", "common.hpp": "5e5d1f7f34499a89",
+    "prefill": {"sources": {"prefill.hip": "12c73f4a90ae4e66", "common.hpp": "5e5d1f7f34499a89",
                             "launch.hpp": "525dbebac0e478f8"},
                 "flags": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
-                "fetch_kib": 372737.3, "write_kib": 204382.27},
+                "fetch_kib": 374638.28, "write_kib": 204858.67},
 }
 
 
